@@ -1,0 +1,233 @@
+/*
+ * ccv_oracle.c -- plain, slow, single-threaded fp64 oracle for the causal
+ * depthwise conv1d forward.  TEST INFRASTRUCTURE ONLY: loaded by the tests,
+ * the smoke check and the bench's cpu_baseline leg, never by the product.
+ *
+ * Every output is computed on its own from the definition (see ccv_oracle.h
+ * for the formula and its sources); there is no tiling, no reuse of partial
+ * sums and no reordering of the terms.  Build: gcc -O2 -ffp-contract=off
+ * (no fused multiply-add, no fast-math), so the fp64 arithmetic is exactly
+ * what is written here.
+ */
+#include "ccv_oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+/* ---- storage decoding ----------------------------------------------------- */
+
+/* bfloat16 is the upper 16 bits of an IEEE binary32: widen and reinterpret. */
+double ora_bf16_to_f64(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double ora_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24);                 /* subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = (m == 0) ? INFINITY : NAN;
+  } else {
+    v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+  }
+  return sign ? -v : v;
+}
+
+double ora_decode(const void* base, int32_t dtype, int64_t off) {
+  switch (dtype) {
+    case ORA_F32: {
+      float f;
+      memcpy(&f, (const char*)base + off * 4, 4);
+      return (double)f;
+    }
+    case ORA_F16: {
+      uint16_t h;
+      memcpy(&h, (const char*)base + off * 2, 2);
+      return ora_f16_to_f64(h);
+    }
+    case ORA_BF16: {
+      uint16_t h;
+      memcpy(&h, (const char*)base + off * 2, 2);
+      return ora_bf16_to_f64(h);
+    }
+  }
+  return NAN;
+}
+
+static int elt_size(int32_t dtype) { return dtype == ORA_F32 ? 4 : 2; }
+
+/* ---- rounding to storage ---------------------------------------------------- */
+
+/* fp64 -> binary32: the C conversion rounds to nearest, ties to even, in the
+ * default floating-point environment; overflow gives +-inf. */
+float ora_f64_to_f32(double v) { return (float)v; }
+
+/* Round-half-to-even of a non-negative double to an integer-valued double,
+ * written out (no dependence on the current rounding mode). */
+static double rne_int(double q) {
+  double fl = floor(q);
+  double frac = q - fl;
+  if (frac > 0.5) return fl + 1.0;
+  if (frac < 0.5) return fl;
+  return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* binary32 -> bfloat16, round to nearest even.  The kept value is the upper
+ * 16 bits; the dropped 16 bits decide: above half -> round up, below -> down,
+ * exactly half -> towards the even kept pattern.  Rounding the largest finite
+ * values up carries into the exponent and yields infinity, as it should. */
+uint16_t ora_f32_to_bf16(float v) {
+  uint32_t bits;
+  memcpy(&bits, &v, 4);
+  if (isnan(v)) return (uint16_t)((bits >> 16) | 0x0040);   /* quiet NaN */
+  uint32_t upper = bits >> 16;
+  uint32_t lower = bits & 0xffffu;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+/* binary32 -> binary16, round to nearest even, by scaling |v| exactly into the
+ * target's integer significand range and rounding that. */
+uint16_t ora_f32_to_f16(float v) {
+  uint32_t bits;
+  memcpy(&bits, &v, 4);
+  uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+  if (isnan(v)) return (uint16_t)(sign | 0x7e00u);
+  double a = fabs((double)v);
+  if (isinf(v)) return (uint16_t)(sign | 0x7c00u);
+  /* Largest finite binary16 is 65504 = (2 - 2^-10) * 2^15; the midpoint to the
+   * next step (65536) is 65520, and a tie there goes to the even pattern,
+   * which is the overflow.  So |v| >= 65520 rounds to infinity. */
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: value = q * 2^-24 with integer q in [0, 1024];
+     * q == 1024 is the smallest normal, whose encoding is also 1024. */
+    double q = rne_int(a * ldexp(1.0, 24));
+    return (uint16_t)(sign | (uint16_t)q);
+  }
+  int e;
+  (void)frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1) -> a in [2^(e-1), 2^e) */
+  int ue = e - 1;              /* unbiased exponent: a in [2^ue, 2^(ue+1)) */
+  double m = rne_int(ldexp(a, 10 - ue));   /* significand in [1024, 2048] */
+  if (m == 2048.0) { m = 1024.0; ue += 1; }
+  if (ue > 15) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (uint16_t)((ue + 15) << 10) | (uint16_t)(m - 1024.0));
+}
+
+void ora_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_f32_to_bf16(in[i]);
+}
+void ora_f32_to_f16_array(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_f32_to_f16(in[i]);
+}
+void ora_f16_to_f64_array(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_f16_to_f64(in[i]);
+}
+void ora_bf16_to_f64_array(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_bf16_to_f64(in[i]);
+}
+
+void ora_round_out(int32_t dtype, const double* y, int64_t n, void* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    float o32 = ora_f64_to_f32(y[i]);
+    if (dtype == ORA_F32) {
+      memcpy((char*)out + i * 4, &o32, 4);
+    } else {
+      uint16_t h = (dtype == ORA_BF16) ? ora_f32_to_bf16(o32) : ora_f32_to_f16(o32);
+      memcpy((char*)out + i * 2, &h, 2);
+    }
+  }
+}
+
+/* ---- the method ------------------------------------------------------------ */
+
+/* Extended input: X~[b,c,j] = x[b,c,j] for j >= 0; for -(K-1) <= j < 0 the
+ * history to the left of the block, initial_states[b,c,j+K-1] (time
+ * ascending, so index K-2 is the step just before t = 0), or zero without it. */
+double ora_xt(const ora_problem_t* p, int64_t b, int64_t c, int64_t j) {
+  if (j >= 0)
+    return ora_decode(p->x, p->x_dtype, b * p->xs[0] + c * p->xs[1] + j * p->xs[2]);
+  if (p->init == NULL) return 0.0;
+  int64_t i = j + p->K - 1;
+  return ora_decode(p->init, p->x_dtype, b * p->is[0] + c * p->is[1] + i * p->is[2]);
+}
+
+int ora_point(const ora_problem_t* p, int64_t b, int64_t c, int64_t t,
+              double* y, double* z, double* sabs) {
+  if (b < 0 || b >= p->B || c < 0 || c >= p->C || t < 0 || t >= p->L) return -1;
+  const int K = p->K;
+  double acc = 0.0, s = 0.0;
+  if (p->bias != NULL) {
+    double beta = ora_decode(p->bias, p->w_dtype, c);
+    acc = beta;
+    s = fabs(beta);
+  }
+  for (int k = 0; k < K; ++k) {
+    int64_t src = t - K + 1 + k;              /* w[c,K-1] meets the current step */
+    if (p->seq != NULL) {
+      if (src < 0) continue;                  /* no sequence id left of t = 0 */
+      if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;   /* dropped */
+    }
+    double term = ora_decode(p->w, p->w_dtype, c * K + k) * ora_xt(p, b, c, src);
+    acc += term;
+    s += fabs(term);
+  }
+  double out = acc;
+  if (p->silu) out = acc / (1.0 + exp(-acc));
+  if (y) *y = out;
+  if (z) *z = acc;
+  if (sabs) *sabs = s;
+  return 0;
+}
+
+int ora_fwd(const ora_problem_t* p, double* y, double* sabs) {
+  for (int64_t b = 0; b < p->B; ++b)
+    for (int64_t c = 0; c < p->C; ++c)
+      for (int64_t t = 0; t < p->L; ++t) {
+        int64_t o = (b * p->C + c) * p->L + t;
+        double yy, ss;
+        if (ora_point(p, b, c, t, &yy, NULL, &ss) != 0) return -1;
+        if (y) y[o] = yy;
+        if (sabs) sabs[o] = ss;
+      }
+  return 0;
+}
+
+int ora_points(const ora_problem_t* p, int64_t n, const int64_t* idx,
+               double* y, double* sabs) {
+  for (int64_t i = 0; i < n; ++i) {
+    double yy, ss;
+    if (ora_point(p, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], &yy, NULL, &ss) != 0)
+      return -1;
+    if (y) y[i] = yy;
+    if (sabs) sabs[i] = ss;
+  }
+  return 0;
+}
+
+int ora_final_states(const ora_problem_t* p, void* fs) {
+  const int K = p->K;
+  const int es = elt_size(p->x_dtype);
+  for (int64_t b = 0; b < p->B; ++b)
+    for (int64_t c = 0; c < p->C; ++c)
+      for (int i = 0; i < K - 1; ++i) {
+        int64_t j = p->L - K + 1 + i;         /* the last K-1 positions of X~ */
+        char* dst = (char*)fs + ((b * p->C + c) * (K - 1) + i) * es;
+        if (j >= 0) {
+          memcpy(dst, (const char*)p->x + (b * p->xs[0] + c * p->xs[1] + j * p->xs[2]) * es, es);
+        } else if (p->init != NULL) {
+          int64_t ii = j + K - 1;
+          memcpy(dst, (const char*)p->init + (b * p->is[0] + c * p->is[1] + ii * p->is[2]) * es, es);
+        } else {
+          memset(dst, 0, es);
+        }
+      }
+  return 0;
+}

@@ -1,0 +1,357 @@
+"""Pins that tie the oracle to facts other than its own code.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with:
+  * hand-worked examples of the stencil equation (tests/golden/),
+  * closed forms (decimal digit read-out, one-hot weights, a delta input, a
+    constant input),
+  * a library routine that implements the same cross-correlation
+    (torch.nn.functional.conv1d in fp64 on the CPU, grouped by channel),
+  * invariants the definition implies (chunking with carried states, packed
+    sequences equal separate runs, layout independence, masked NaN not leaking),
+  * torch's own dtype conversions and SiLU.
+
+The functions take the ``oracle`` module so that ``test_oracle_mutants`` can run
+them against deliberately broken builds of the oracle.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _raw(t: torch.Tensor) -> np.ndarray:
+    t = t.contiguous()
+    return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _cf_case(ora, x, w, bias=None, seq=None, init=None, silu=False):
+    """Oracle case for a contiguous [B,C,L] torch tensor x (any of the 3 dtypes)."""
+    B, C, L = x.shape
+    K = w.shape[1]
+    kw = {}
+    if init is not None:
+        kw.update(init=_raw(init), init_strides=init.stride())
+    return ora.Case(B=B, C=C, L=L, K=K, x=_raw(x), x_dtype=_name(x), x_strides=x.stride(),
+                    w=_raw(w), w_dtype=_name(w), bias=None if bias is None else _raw(bias),
+                    seq=None if seq is None else seq.numpy(), silu=silu, **kw)
+
+
+def _name(t):
+    return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[t.dtype]
+
+
+def _gen(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+# ---- golden fixtures ------------------------------------------------------------
+
+def load_golden():
+    cases = []
+    for fn in sorted(os.listdir(GOLDEN)):
+        if not fn.endswith(".txt"):
+            continue
+        d = {}
+        with open(os.path.join(GOLDEN, fn)) as f:
+            for line in f:
+                line = line.split("#", 1)[0].strip()
+                if not line:
+                    continue
+                key, *vals = line.split()
+                d[key] = [float(v) for v in vals]
+        d["name"] = fn
+        cases.append(d)
+    return cases
+
+
+def pin_golden(ora):
+    cases = load_golden()
+    assert len(cases) >= 7
+    for d in cases:
+        K = int(d["K"][0])
+        for dt in ("f32", "f16", "bf16"):
+            x = torch.tensor(d["x"], dtype=torch.float64).to(DT[dt]).reshape(1, 1, -1)
+            w = torch.tensor(d["w"], dtype=torch.float64).to(DT[dt]).reshape(1, K)
+            bias = torch.tensor(d["bias"], dtype=torch.float64).to(DT[dt]) if "bias" in d else None
+            init = (torch.tensor(d["init"], dtype=torch.float64).to(DT[dt]).reshape(1, 1, K - 1)
+                    if "init" in d else None)
+            seq = torch.tensor([int(v) for v in d["seq"]], dtype=torch.int32).reshape(1, -1) if "seq" in d else None
+            c = _cf_case(ora, x, w, bias, seq, init)
+            y, _ = c.fwd()
+            assert np.array_equal(y.reshape(-1), np.array(d["z"])), (d["name"], dt, y.reshape(-1), d["z"])
+            if "final" in d:
+                fs = ora.decode(dt, c.final_states()).reshape(-1)
+                assert np.array_equal(fs, np.array(d["final"])), (d["name"], dt, fs, d["final"])
+
+
+# ---- closed forms ---------------------------------------------------------------
+
+def pin_digits(ora):
+    """w = (1, 10, ..., 10^(K-1)) and inputs in 0..9: z[t] is an integer whose
+    decimal digits are x[t], x[t-1], ..., x[t-K+1] (newest first)."""
+    g = np.random.default_rng(7)
+    for K in (2, 3, 4):
+        for dt in ("f32", "bf16", "f16"):
+            L = 37
+            xd = g.integers(0, 10, size=L)
+            hd = g.integers(0, 10, size=K - 1)
+            x = torch.tensor(xd, dtype=torch.float64).to(DT[dt]).reshape(1, 1, L)
+            w = torch.tensor([10.0 ** k for k in range(K)], dtype=torch.float64).to(DT[dt]).reshape(1, K)
+            init = torch.tensor(hd, dtype=torch.float64).to(DT[dt]).reshape(1, 1, K - 1)
+            y, _ = _cf_case(ora, x, w, init=init).fwd()
+            ext = np.concatenate([hd, xd])
+            for t in range(L):
+                window = ext[t:t + K]            # x~[t-K+1 .. t], oldest first
+                z = int(y[0, 0, t])
+                assert z == y[0, 0, t]
+                digits = [int(ch) for ch in str(z).zfill(K)]
+                assert digits == list(window[::-1]), (K, dt, t, z, window)
+
+
+def pin_one_hot(ora):
+    """w = e_k (no bias, no activation) shifts the extended input: z[t] = x~[t-K+1+k]."""
+    g = _gen(11)
+    for K in (2, 3, 4):
+        for dt in ("f32", "bf16", "f16"):
+            B, C, L = 2, 3, 29
+            x = torch.randn(B, C, L, generator=g).to(DT[dt])
+            init = torch.randn(B, C, K - 1, generator=g).to(DT[dt])
+            ext = torch.cat([init, x], dim=2).double()
+            for k in range(K):
+                w = torch.zeros(C, K, dtype=DT[dt])
+                w[:, k] = 1
+                y, _ = _cf_case(ora, x, w, init=init).fwd()
+                expect = ext[:, :, k:k + L].numpy()
+                assert np.array_equal(y, expect), (K, dt, k)
+
+
+def pin_delta(ora):
+    """x = delta(t - t0) with zero history returns the weights reversed after t0:
+    z[t0 + j] = bias + w[K-1-j] for 0 <= j < K, and bias elsewhere."""
+    g = _gen(12)
+    for K in (2, 3, 4):
+        C, L, t0 = 4, 16, 5
+        x = torch.zeros(1, C, L)
+        x[:, :, t0] = 1
+        w = torch.randn(C, K, generator=g)
+        bias = torch.randn(C, generator=g)
+        y, _ = _cf_case(ora, x, w, bias).fwd()
+        expect = np.repeat(bias.double().numpy()[:, None], L, axis=1)
+        for j in range(K):
+            expect[:, t0 + j] = (bias.double() + w[:, K - 1 - j].double()).numpy()
+        assert np.array_equal(y[0], expect), K
+
+
+def pin_constant(ora):
+    """x = a with zero history: z[t] = bias + a * sum_{k >= K-1-t} w[k] (t < K-1),
+    then bias + a * sum(w)."""
+    for K in (2, 3, 4):
+        a = 0.75
+        w = torch.tensor([[1.0, 2.0, 4.0, 8.0][:K]])
+        bias = torch.tensor([0.5])
+        L = 9
+        x = torch.full((1, 1, L), a)
+        y, _ = _cf_case(ora, x, w, bias).fwd()
+        for t in range(L):
+            expect = 0.5 + a * sum(float(w[0, k]) for k in range(K) if k >= K - 1 - t)
+            assert y[0, 0, t] == expect, (K, t, y[0, 0, t], expect)
+
+
+# ---- library routine --------------------------------------------------------------
+
+def _torch_ref(x, w, bias, init, silu):
+    """torch.nn.functional.conv1d in fp64 (grouped per channel) over the input
+    extended on the left by the history: the cross-correlation Conv1d computes."""
+    B, C, L = x.shape
+    K = w.shape[1]
+    hist = init.double() if init is not None else torch.zeros(B, C, K - 1, dtype=torch.float64)
+    ext = torch.cat([hist, x.double()], dim=2)
+    z = torch.nn.functional.conv1d(ext, w.double().reshape(C, 1, K),
+                                   None if bias is None else bias.double(), groups=C)
+    sabs = torch.nn.functional.conv1d(ext.abs(), w.double().abs().reshape(C, 1, K),
+                                      None if bias is None else bias.double().abs(), groups=C)
+    y = torch.nn.functional.silu(z) if silu else z
+    return y.numpy(), sabs.numpy()
+
+
+def pin_conv1d(ora):
+    g = _gen(13)
+    combos = [("f32", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f32", "f16"),
+              ("f16", "bf16")]
+    for K in (2, 3, 4):
+        for xd, wd in combos:
+            for use_bias, use_init, silu in ((True, False, True), (False, True, False), (True, True, True)):
+                B, C, L = 2, 5, 67
+                x = (torch.randn(B, C, L, generator=g) * 2).to(DT[xd])
+                w = torch.randn(C, K, generator=g).to(DT[wd])
+                bias = torch.randn(C, generator=g).to(DT[wd]) if use_bias else None
+                init = torch.randn(B, C, K - 1, generator=g).to(DT[xd]) if use_init else None
+                y, s = _cf_case(ora, x, w, bias, init=init, silu=silu).fwd()
+                ry, rs = _torch_ref(x, w, bias, init, silu)
+                tol = 1e-14 * rs + 1e-300
+                assert np.all(np.abs(y - ry) <= tol), (K, xd, wd, np.max(np.abs(y - ry) / tol))
+                assert np.all(np.abs(s - rs) <= 1e-14 * rs + 1e-300), (K, xd, wd)
+
+
+# ---- invariants -------------------------------------------------------------------
+
+def pin_chunking(ora):
+    """Running [x1 | x2] equals running x1, then x2 with x1's final states as its
+    initial states: every output bit-identical, and the same final states."""
+    g = _gen(14)
+    for K in (2, 3, 4):
+        for dt in ("f32", "bf16", "f16"):
+            B, C, L = 2, 3, 40
+            x = torch.randn(B, C, L, generator=g).to(DT[dt])
+            w = torch.randn(C, K, generator=g).to(DT[dt])
+            bias = torch.randn(C, generator=g).to(DT[dt])
+            init = torch.randn(B, C, K - 1, generator=g).to(DT[dt])
+            full = _cf_case(ora, x, w, bias, init=init, silu=True)
+            y_full, _ = full.fwd()
+            fs_full = full.final_states()
+            for L1 in sorted({0, 1, K - 2, K - 1, K, 17, L}):
+                x1, x2 = x[:, :, :L1].contiguous(), x[:, :, L1:].contiguous()
+                c1 = _cf_case(ora, x1, w, bias, init=init, silu=True)
+                y1, _ = c1.fwd()
+                f1 = c1.final_states()
+                f1_t = (torch.from_numpy(f1.copy()) if dt == "f32"
+                        else torch.from_numpy(f1.view(np.int16).copy()).view(DT[dt]))
+                c2 = _cf_case(ora, x2, w, bias, init=f1_t, silu=True)
+                y2, _ = c2.fwd()
+                assert np.array_equal(np.concatenate([y1, y2], axis=2).view(np.uint64),
+                                      y_full.view(np.uint64)), (K, dt, L1)
+                assert np.array_equal(c2.final_states(), fs_full), (K, dt, L1)
+
+
+def pin_packing(ora):
+    """A packed run with seq_idx equals separate runs of each sequence (zero history)."""
+    g = _gen(15)
+    for K in (2, 3, 4):
+        for dt in ("f32", "bf16"):
+            lengths = [1, 5, K - 1, 9, 2, 13, K]
+            L = sum(lengths)
+            C = 3
+            x = torch.randn(1, C, L, generator=g).to(DT[dt])
+            w = torch.randn(C, K, generator=g).to(DT[dt])
+            bias = torch.randn(C, generator=g).to(DT[dt])
+            seq = torch.tensor(np.repeat(np.arange(len(lengths)), lengths), dtype=torch.int32).reshape(1, L)
+            y, _ = _cf_case(ora, x, w, bias, seq=seq, silu=True).fwd()
+            pos = 0
+            for n in lengths:
+                part = x[:, :, pos:pos + n].contiguous()
+                yp, _ = _cf_case(ora, part, w, bias, silu=True).fwd()
+                assert np.array_equal(y[:, :, pos:pos + n].view(np.uint64), yp.view(np.uint64)), (K, dt, n)
+                pos += n
+
+
+def pin_mask_nan(ora):
+    """A masked term is dropped, not multiplied by zero: a NaN in another sequence
+    does not reach this one, while a NaN inside the window does."""
+    K, L = 4, 8
+    x = torch.arange(1, L + 1, dtype=torch.float32).reshape(1, 1, L)
+    x[0, 0, 2] = float("nan")
+    w = torch.ones(1, K)
+    seq = torch.tensor([[0, 0, 0, 1, 1, 1, 1, 1]], dtype=torch.int32)
+    y, _ = _cf_case(ora, x, w, seq=seq).fwd()
+    assert np.isnan(y[0, 0, 2]) and np.isnan(y[0, 0, 1] + y[0, 0, 2])
+    assert not np.isnan(y[0, 0, 3:]).any(), y
+    assert list(y[0, 0, 3:]) == [4.0, 9.0, 15.0, 22.0, 26.0]
+    y2, _ = _cf_case(ora, x, w).fwd()
+    assert np.isnan(y2[0, 0, 2:6]).all() and not np.isnan(y2[0, 0, 6:]).any()
+
+
+def pin_layout(ora):
+    """The same logical x stored channel-first, channel-last, or as a strided view of a
+    wider buffer gives bit-identical results (offsets follow s_B, s_C, s_L)."""
+    g = _gen(16)
+    B, C, L, K = 2, 6, 23, 4
+    x = torch.randn(B, C, L, generator=g).to(torch.bfloat16)
+    w = torch.randn(C, K, generator=g).to(torch.bfloat16)
+    bias = torch.randn(C, generator=g).to(torch.bfloat16)
+    ref, _ = _cf_case(ora, x, w, bias, silu=True).fwd()
+    cl = x.transpose(1, 2).contiguous()              # [B, L, C]
+    c = ora.Case(B=B, C=C, L=L, K=K, x=_raw(cl), x_dtype="bf16", x_strides=(L * C, 1, C),
+                 w=_raw(w), w_dtype="bf16", bias=_raw(bias), silu=True)
+    assert np.array_equal(c.fwd()[0].view(np.uint64), ref.view(np.uint64))
+    wide = torch.full((B, L, C + 5), float("nan")).to(torch.bfloat16)
+    wide[:, :, 3:3 + C] = cl
+    c = ora.Case(B=B, C=C, L=L, K=K, x=_raw(wide), x_off=3, x_dtype="bf16",
+                 x_strides=(L * (C + 5), 1, C + 5), w=_raw(w), w_dtype="bf16", bias=_raw(bias), silu=True)
+    assert np.array_equal(c.fwd()[0].view(np.uint64), ref.view(np.uint64))
+
+
+# ---- activation and conversions ------------------------------------------------------
+
+def pin_silu(ora):
+    """SiLU against torch's fp64 silu, plus silu(0) = 0, the odd-part identity
+    silu(z) - silu(-z) = z, and the limits silu(z) -> z (z >> 0), -> 0 (z << 0)."""
+    zs = np.concatenate([np.linspace(-30, 30, 601), [0.0, 1e-30, -1e-30, 80.0, -80.0, 700.0, -700.0]])
+    L = zs.size
+    x = torch.tensor(zs, dtype=torch.float64).to(torch.float32).reshape(1, 1, L)
+    w = torch.tensor([[0.0, 0.0, 1.0]])             # one-hot on the current step: z = x
+    y, _ = _cf_case(ora, x, w, silu=True).fwd()
+    z = x.double().reshape(-1)
+    ref = torch.nn.functional.silu(z).numpy()
+    assert np.all(np.abs(y.reshape(-1) - ref) <= 1e-15 * np.abs(ref) + 1e-300)
+    y = y.reshape(-1)
+    zz = z.numpy()
+    i0 = int(np.where(zz == 0.0)[0][0])
+    assert y[i0] == 0.0
+    neg = {v: i for i, v in enumerate(zz)}
+    for i, v in enumerate(zz):
+        if -v in neg and abs(v) < 40:
+            assert abs((y[i] - y[neg[-v]]) - v) <= 1e-14 * max(1.0, abs(v)), v
+    assert y[list(zz).index(80.0)] == 80.0            # 80 - 80*e^-80 rounds to 80 in fp64
+    assert 0 < -y[list(zz).index(-80.0)] < 1e-30      # about -80*e^-80
+
+
+def pin_converters(ora):
+    """Decoding of every 16-bit pattern and RNE encoding of fp32 against torch."""
+    pats = np.arange(65536, dtype=np.uint16)
+    for dt, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        ref = torch.from_numpy(pats.view(np.int16)).view(tdt).double().numpy()
+        got = ora.decode(dt, pats)
+        both_nan = np.isnan(ref) & np.isnan(got)
+        assert np.array_equal(np.isnan(ref), np.isnan(got)), dt
+        assert np.array_equal(got[~both_nan], ref[~both_nan]), dt
+    g = np.random.default_rng(17)
+    vals = np.concatenate([
+        g.standard_normal(200_000).astype(np.float32) * np.float32(1000),
+        (g.standard_normal(100_000) * 1e-5).astype(np.float32),
+        g.integers(0, 2**32, 200_000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+        np.array([0.0, -0.0, 65504, 65519.99, 65520, 65536, -65520, 6e-8, 2.98e-8, 5.96e-8,
+                  6.1035e-5, 6.1e-5, 3.4e38, -3.4e38, np.inf, -np.inf, np.nan], dtype=np.float32),
+    ])
+    # exact ties for both formats
+    base = g.integers(0, 2**16, 50_000, dtype=np.uint32)
+    vals = np.concatenate([vals, ((base << 16) | 0x8000).view(np.float32),
+                           (np.float32(1.0) + np.float32(2.0 ** -11) * np.arange(1, 64, 2, dtype=np.float32))])
+    for dt, tdt, fn in (("bf16", torch.bfloat16, ora.f32_to_bf16), ("f16", torch.float16, ora.f32_to_f16)):
+        ref = torch.from_numpy(vals).to(tdt).view(torch.int16).numpy().view(np.uint16)
+        got = fn(vals)
+        rnan = np.isnan(torch.from_numpy(vals).to(tdt).float().numpy())
+        gnan = np.isnan(ora.decode(dt, got))
+        assert np.array_equal(rnan, gnan), dt
+        assert np.array_equal(got[~rnan], ref[~rnan]), (dt, vals[~rnan][got[~rnan] != ref[~rnan]][:5])
+
+
+def pin_round_out(ora):
+    """Output rounding: fp64 -> fp32 (RNE), then fp32 -> 16-bit (RNE), as torch does."""
+    g = np.random.default_rng(18)
+    y = np.concatenate([g.standard_normal(50_000) * 300, g.standard_normal(1000) * 1e-6, [0.0, -0.0]])
+    for dt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16), ("f16", torch.float16)):
+        got = ora.round_out(dt, y)
+        ref = torch.from_numpy(y).to(torch.float32).to(tdt)
+        ref = ref.numpy() if dt == "f32" else ref.view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got.view(np.uint32 if dt == "f32" else np.uint16),
+                              ref.view(np.uint32 if dt == "f32" else np.uint16)), dt
+
+
+ALL_PINS = [pin_golden, pin_digits, pin_one_hot, pin_delta, pin_constant, pin_conv1d,
+            pin_chunking, pin_packing, pin_mask_nan, pin_layout, pin_silu, pin_converters,
+            pin_round_out]

@@ -1,0 +1,66 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that the
+pins catch every one of them.  Each mutant is the oracle's C source with one
+textual change, compiled with the same gcc line into a temporary directory."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ccv_oracle.c")
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("taps_reversed", "ora_decode(p->w, p->w_dtype, c * K + k)", "ora_decode(p->w, p->w_dtype, c * K + (K - 1 - k))"),
+    ("source_off_by_one", "int64_t src = t - K + 1 + k;", "int64_t src = t - K + k;"),
+    ("oldest_tap_dropped", "for (int k = 0; k < K; ++k) {", "for (int k = 1; k < K; ++k) {"),
+    ("silu_sign", "acc / (1.0 + exp(-acc))", "acc / (1.0 + exp(acc))"),
+    ("silu_missing_z", "out = acc / (1.0 + exp(-acc));", "out = 1.0 / (1.0 + exp(-acc));"),
+    ("bias_dropped", "acc = beta;", "acc = 0.0;"),
+    ("history_reversed", "int64_t i = j + p->K - 1;\n  return", "int64_t i = -j - 1;\n  return"),
+    ("mask_never", "p->seq[b * p->L + src] != p->seq[b * p->L + t]", "p->seq[b * p->L + src] != p->seq[b * p->L + src]"),
+    ("mask_multiplies",
+     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;",
+     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) { acc += 0.0 * ora_xt(p, b, c, src); continue; }"),
+    ("final_off_by_one", "int64_t j = p->L - K + 1 + i;", "int64_t j = p->L - K + i;"),
+    ("f16_exponent_bias", "ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
+    ("bf16_ties_away", "(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
+    ("rne_ties_down", "return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl;"),
+    ("sabs_signed", "s += fabs(term);", "s += term;"),
+    ("x_stride_swapped", "b * p->xs[0] + c * p->xs[1] + j * p->xs[2]);\n  if (p->init", "b * p->xs[0] + c * p->xs[2] + j * p->xs[1]);\n  if (p->init"),
+    ("init_zero", "if (p->init == NULL) return 0.0;", "return 0.0;"),
+]
+
+
+def _build(tmp_path, name, src_text):
+    c = tmp_path / f"{name}.c"
+    c.write_text(src_text)
+    so = tmp_path / f"lib{name}.so"
+    hdr_dir = os.path.dirname(SRC)
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared", "-w",
+                    "-I", hdr_dir, "-o", str(so), str(c), "-lm"], check=True)
+    return str(so)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    so = _build(tmp_path, "clean", open(SRC).read())
+    with oracle.using_library(so):
+        for pin in ALL_PINS:
+            pin(oracle)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique"
+    so = _build(tmp_path, name, text.replace(old, new))
+    caught = []
+    with oracle.using_library(so):
+        for pin in ALL_PINS:
+            try:
+                pin(oracle)
+            except AssertionError:
+                caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
