@@ -1,0 +1,316 @@
+"""Bench: effective HBM bandwidth of the causal depthwise conv1d forward on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step is one forward call (validation, dispatch, one kernel) over one batch of
+synthetic input already resident in HBM.  The default workload is the
+channel-first bf16 call B=4, C=2048, L=4096, K=4 with bias and SiLU.  Its
+134 MB working set would fit in the 256 MB Infinity Cache, so the timed steps
+rotate over enough separate input/output buffer sets (>= 1 GiB in total) that
+every step reads inputs that have left the caches.
+
+Effective bandwidth = algorithmic bytes / time, where the algorithmic bytes count
+x read once, out written once, and weight, bias, seq_idx and the states once each
+(halo re-reads are not counted).  Time comes from HIP events recorded on the
+stream the kernels are launched on, around exactly K steps.
+
+Printed: one JSON line with the metric, a "roofline" object for the forward
+kernel (against MI355X's 8 TB/s HBM), and a "cpu_baseline" object (the CPU oracle
+timed on this host over the same workload, and the element-wise parity of this
+run's GPU output against it).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, decimal GB/s
+ROTATION_BYTES = 1 << 30        # >= 4x the 256 MB Infinity Cache
+METRIC = "causal conv1d fwd effective HBM GB/s and % of MI355X peak bandwidth"
+KERNEL_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_cf.hip",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_cl.hip",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_api.cpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(w) -> int:
+    es = w.x.element_size()
+    B, C, L, K = w.B, w.C, w.L, w.K
+    n = 2 * B * C * L * es                          # x once, out once
+    n += w.weight.numel() * w.weight.element_size()
+    if w.bias is not None:
+        n += w.bias.numel() * w.bias.element_size()
+    if w.seq_idx is not None:
+        n += B * L * 4
+    if w.initial_states is not None:
+        n += B * C * (K - 1) * es
+    if w.return_final_states:
+        n += B * C * (K - 1) * es
+    return n
+
+
+def profile_traffic(kernel_key: str, sha: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_sha or not m_tr or m_sha.group(1) != sha:
+        return None
+    return int(m_tr.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent timing the oracle")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the op needs no communication: batch or channel shards run independently)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import causal_depthwise_conv1d_amd as ccv
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ccv.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    t0 = time.time()
+    w = wl.workload(args.workload)
+    log(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s")
+    nbytes = algorithmic_bytes(w)
+    set_bytes = 2 * w.x.numel() * w.x.element_size()
+    if w.x_storage.numel() > w.x.numel():
+        set_bytes = (w.x_storage.numel() + w.x.numel()) * w.x.element_size()
+    nsets = max(2, math.ceil(ROTATION_BYTES / set_bytes))
+    if nsets * set_bytes > 0.5 * props.total_memory:
+        nsets = max(1, int(0.5 * props.total_memory // set_bytes))
+
+    # Inputs resident in HBM: nsets copies of x (with its real strides) and out.
+    weight = w.weight.to(dev)
+    bias = None if w.bias is None else w.bias.to(dev)
+    seq = None if w.seq_idx is None else w.seq_idx.to(dev)
+    init = None
+    if w.initial_states is not None:
+        init = w.init_storage.to(dev).as_strided(w.initial_states.shape, w.initial_states.stride(),
+                                                 w.initial_states.storage_offset())
+    sets = []
+    for i in range(nsets):
+        xs = w.x_storage.to(dev)
+        x = xs.as_strided(w.x.shape, w.x.stride(), w.x.storage_offset())
+        out = ccv.empty_like_layout(x)
+        fs = (torch.empty(w.B, w.K - 1, w.C, dtype=x.dtype, device=dev).transpose(1, 2)
+              if w.return_final_states else None)
+        a = ccv.make_args(x, weight, out, bias, seq, init, fs, w.activation)
+        sets.append((xs, x, out, fs, a))
+    st, plan = ccv.ccv_fwd_plan(sets[0][4])
+    assert st == 0, ccv.ccv_status_str(st)
+    plan = plan.as_dict()
+    log(f"[bench] {nsets} buffer sets of {set_bytes / 1e6:.0f} MB; plan {plan}")
+
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    fwd = ccv.lib().ccv_fwd
+    import ctypes
+    arg_refs = [ctypes.byref(s[4]) for s in sets]
+    sp = ctypes.c_void_p(sptr)
+
+    def step(i):
+        rc = fwd(arg_refs[i % nsets], sp)
+        if rc != 0:
+            raise RuntimeError(ccv.ccv_status_str(rc))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {gbps:.0f} GB/s")
+
+    # Context on the same GPU: a plain copy moving the same bytes, and the launch floor.
+    calib = ctypes.CDLL(ccv.CALIB_LIB_PATH)
+    calib.ccv_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    calib.ccv_calib_empty.argtypes = [ctypes.c_void_p]
+    half = (nbytes // 2) // 16 * 16
+    csets = max(2, math.ceil(ROTATION_BYTES / (2 * half)))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.zeros(half, dtype=torch.uint8, device=dev))
+            for _ in range(csets)]
+    for i in range(20):
+        d, s_ = bufs[i % csets]
+        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
+    ev0.record(stream)
+    for i in range(args.steps):
+        d, s_ = bufs[i % csets]
+        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = ev0.elapsed_time(ev1) / args.steps
+    copy_gbps = 2 * half / (copy_ms * 1e-3) / 1e9
+    del bufs
+    for _ in range(50):
+        calib.ccv_calib_empty(sp)
+    ev0.record(stream)
+    for _ in range(1000):
+        calib.ccv_calib_empty(sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    empty_us = ev0.elapsed_time(ev1)  # ms for 1000 launches = us per launch
+    log(f"[bench] copy of the same bytes: {copy_gbps:.0f} GB/s; empty kernel {empty_us:.2f} us")
+
+    kernel_key = ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
+        f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}"
+    sha = kernel_sources_sha256()
+    traffic = profile_traffic(kernel_key, sha)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.notes.get("description"),
+            "B": w.B, "C": w.C, "L": w.L, "K": w.K,
+            "x_strides": list(w.x.stride()),
+            "activation": w.activation,
+            "storage_dtype": w.x_dtype,
+            "algorithmic_bytes": nbytes,
+            "buffer_sets": nsets,
+            "kernel": kernel_key,
+            "plan": plan,
+        },
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "kernel": kernel_key,
+            "avg_launch_us": round(ms_per_step * 1e3, 3),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+        "context": {
+            "copy_same_bytes_GBps": round(copy_gbps, 1),
+            "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+            "empty_kernel_us": round(empty_us, 3),
+            "device": props.name,
+            "cu_count": props.multi_processor_count,
+            "kernel_sources_sha256": sha,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, sets[0][2], nbytes, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, out_gpu, nbytes, min_seconds):
+    """The oracle as written (single-threaded fp64 loop) on this host's CPU, over
+    the whole workload, repeated until at least `min_seconds` have passed; then the
+    GPU output of this run compared with it at every output."""
+    import torch
+
+    from oracle import compare as ocmp
+    from oracle import round_out
+    from oracle.from_torch import case, dtype_name, raw
+
+    c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
+    passes, t_total = 0, 0.0
+    y = s = None
+    while passes == 0 or t_total < min_seconds:
+        t0 = time.perf_counter()
+        y, s = c.fwd()
+        round_out(w.x_dtype, y)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    sec = t_total / passes
+    log(f"[bench] cpu oracle: {passes} passes, {sec:.2f} s per pass")
+    g = raw(out_gpu.cpu().contiguous())
+    res = ocmp.compare(dtype_name(out_gpu), w.K, g, y, s)
+    cpu_name = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": round(nbytes / sec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the whole workload ({w.B * w.C * w.L} outputs), {passes} pass(es) of the "
+                  "single-threaded fp64 oracle incl. rounding to the output dtype",
+        "seconds_per_pass": round(sec, 3),
+        "host_cpu": cpu_name,
+        "host_threads_available": os.cpu_count(),
+        "parity": {"outputs": res["n"], "out_of_tolerance": res["n_bad"], "max_ulp": res["max_ulp"],
+                   "max_rel": res["max_rel"], "floor_only": res["n_floor_only"],
+                   "bit_equal": res["bit_equal"]},
+    }
+
+
+if __name__ == "__main__":
+    main()

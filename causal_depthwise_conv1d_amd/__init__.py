@@ -1,0 +1,269 @@
+"""causal_depthwise_conv1d_amd -- Python binding of libccv (the causal depthwise
+conv1d forward for AMD gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI of ``include/ccv.h``; PyTorch provides device memory and
+streams.  There is no CPU fallback: without the built library, or with tensors
+that are not on a GPU, calls raise.
+
+Low level (same names as the C ABI):
+    ccv_fwd(args, stream=None), ccv_fwd_check(args), ccv_fwd_plan(args),
+    ccv_status_str(code), ccv_abi_version()
+High level (the full-sequence contract of Ch.4 "Dao interface and source map",
+section "Contract of the full-sequence interface"):
+    causal_conv1d_fwd(x, weight, bias=None, seq_idx=None, initial_states=None,
+                      return_final_states=False, final_states_out=None,
+                      activation=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libccv.so")
+CALIB_LIB_PATH = os.path.join(_HERE, "libccv_calib.so")
+
+CCV_ABI_VERSION = 1
+CCV_F32, CCV_F16, CCV_BF16 = 0, 1, 2
+CCV_ACT_NONE, CCV_ACT_SILU = 0, 1
+CCV_PATH_NONE, CCV_PATH_CHANNEL_FIRST, CCV_PATH_CHANNEL_LAST = 0, 1, 2
+STATUS = {
+    0: "CCV_OK", -1: "CCV_E_NULL", -2: "CCV_E_SHAPE", -3: "CCV_E_KSIZE", -4: "CCV_E_DTYPE",
+    -5: "CCV_E_LAYOUT", -6: "CCV_E_UNSUPPORTED", -7: "CCV_E_ALIAS", -8: "CCV_E_HIP",
+    -9: "CCV_E_INTERNAL", -10: "CCV_E_ABI",
+}
+DTYPE_CODE = {torch.float32: CCV_F32, torch.float16: CCV_F16, torch.bfloat16: CCV_BF16}
+
+_I64x3 = ctypes.c_int64 * 3
+
+
+class ccv_fwd_args_t(ctypes.Structure):
+    """Mirror of ``ccv_fwd_args_t`` in include/ccv.h (field order and types)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_int64),
+        ("B", ctypes.c_int64), ("C", ctypes.c_int64), ("L", ctypes.c_int64),
+        ("K", ctypes.c_int32), ("activation", ctypes.c_int32),
+        ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("x_stride", _I64x3),
+        ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("seq_idx", ctypes.c_void_p),
+        ("initial_states", ctypes.c_void_p), ("init_stride", _I64x3),
+        ("final_states_out", ctypes.c_void_p), ("final_stride", _I64x3),
+        ("out", ctypes.c_void_p), ("out_stride", _I64x3),
+    ]
+
+    def __init__(self, **kw):
+        super().__init__(**kw)
+        self.struct_size = ctypes.sizeof(ccv_fwd_args_t)
+
+
+class ccv_plan_t(ctypes.Structure):
+    """Mirror of ``ccv_plan_t`` in include/ccv.h."""
+    _fields_ = [
+        ("path", ctypes.c_int32), ("vector", ctypes.c_int32),
+        ("elems_per_lane", ctypes.c_int32), ("unroll", ctypes.c_int32),
+        ("grid", ctypes.c_int64), ("block", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+        ("work_items", ctypes.c_int64), ("span", ctypes.c_int64), ("channels_per_item", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class CcvError(RuntimeError):
+    def __init__(self, status: int, where: str = "ccv_fwd"):
+        self.status = status
+        super().__init__(f"{where} failed: {STATUS.get(status, status)}")
+
+
+class CcvArgumentError(CcvError, ValueError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libccv.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m causal_depthwise_conv1d_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(ccv_fwd_args_t)
+        L.ccv_fwd.argtypes = [P, ctypes.c_void_p]
+        L.ccv_fwd.restype = ctypes.c_int
+        L.ccv_fwd_check.argtypes = [P]
+        L.ccv_fwd_check.restype = ctypes.c_int
+        L.ccv_fwd_plan.argtypes = [P, ctypes.POINTER(ccv_plan_t)]
+        L.ccv_fwd_plan.restype = ctypes.c_int
+        L.ccv_status_str.argtypes = [ctypes.c_int]
+        L.ccv_status_str.restype = ctypes.c_char_p
+        L.ccv_abi_version.argtypes = []
+        L.ccv_abi_version.restype = ctypes.c_int
+        if L.ccv_abi_version() != CCV_ABI_VERSION:
+            raise RuntimeError("libccv ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+# ---- the C ABI, one to one ----------------------------------------------------------
+
+def ccv_fwd(args: ccv_fwd_args_t, stream=None) -> int:
+    """Enqueue the forward on `stream` (a torch stream, a raw hipStream_t int, or None
+    for torch's current stream).  Returns the status code."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return lib().ccv_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+
+
+def ccv_fwd_check(args: ccv_fwd_args_t) -> int:
+    return lib().ccv_fwd_check(ctypes.byref(args))
+
+
+def ccv_fwd_plan(args: ccv_fwd_args_t):
+    """(status, ccv_plan_t) without touching the device."""
+    p = ccv_plan_t()
+    st = lib().ccv_fwd_plan(ctypes.byref(args), ctypes.byref(p))
+    return st, p
+
+
+def ccv_status_str(status: int) -> str:
+    return lib().ccv_status_str(int(status)).decode()
+
+
+def ccv_abi_version() -> int:
+    return lib().ccv_abi_version()
+
+
+# ---- tensors -> args -------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _strides3(t: Optional[torch.Tensor]):
+    return _I64x3(*(t.stride() if t is not None else (0, 0, 0)))
+
+
+def make_args(x, weight, out, bias=None, seq_idx=None, initial_states=None,
+              final_states_out=None, activation=None) -> ccv_fwd_args_t:
+    """Fill a ccv_fwd_args_t from tensors (no checks beyond dtype codes)."""
+    B, C, L = x.shape
+    a = ccv_fwd_args_t()
+    a.B, a.C, a.L = B, C, L
+    a.K = weight.shape[1]
+    a.activation = CCV_ACT_SILU if activation in ("silu", "swish") else CCV_ACT_NONE
+    a.x_dtype = DTYPE_CODE[x.dtype]
+    a.w_dtype = DTYPE_CODE[weight.dtype]
+    a.x, a.x_stride = _ptr(x), _strides3(x)
+    a.weight = _ptr(weight)
+    a.bias = _ptr(bias)
+    a.seq_idx = _ptr(seq_idx)
+    a.initial_states, a.init_stride = _ptr(initial_states), _strides3(initial_states)
+    a.final_states_out, a.final_stride = _ptr(final_states_out), _strides3(final_states_out)
+    a.out, a.out_stride = _ptr(out), _strides3(out)
+    return a
+
+
+def _raise(status: int):
+    if status == 0:
+        return
+    if status == -8:
+        raise CcvError(status)
+    raise CcvArgumentError(status)
+
+
+def empty_like_layout(x: torch.Tensor) -> torch.Tensor:
+    """A new [B, C, L] tensor with x's dtype, device and unit-stride dimension."""
+    B, C, L = x.shape
+    if x.stride(2) == 1 or L <= 1 and x.stride(1) != 1:
+        return torch.empty(B, C, L, dtype=x.dtype, device=x.device)
+    return torch.empty(B, L, C, dtype=x.dtype, device=x.device).transpose(1, 2)
+
+
+def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                      seq_idx: Optional[torch.Tensor] = None,
+                      initial_states: Optional[torch.Tensor] = None,
+                      return_final_states: bool = False,
+                      final_states_out: Optional[torch.Tensor] = None,
+                      activation: Optional[str] = None, out: Optional[torch.Tensor] = None,
+                      info: Optional[dict] = None):
+    """Causal depthwise conv1d forward on the GPU.
+
+    x [B, C, L] (unit stride in time or in channels; any other strides are copied to
+    contiguous first and ``info["x_copied"]`` says so), weight [C, K] (oldest ->
+    current), bias [C] (weight dtype), seq_idx int32 [B, L], initial_states
+    [B, C, K-1] (x dtype).  Returns out [B, C, L] in x's dtype and layout, or
+    (out, final_states) when return_final_states.  final_states is [B, C, K-1] with
+    channel stride 1 unless ``final_states_out`` provides the storage.
+    """
+    if activation not in (None, "silu", "swish"):
+        raise ValueError(f"activation must be None, 'silu' or 'swish', not {activation!r}")
+    if final_states_out is not None and not return_final_states:
+        raise ValueError("final_states_out given but return_final_states is False")
+    if seq_idx is not None and (initial_states is not None or return_final_states):
+        raise ValueError("seq_idx cannot be combined with initial_states or final states")
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
+        raise ValueError("expected x [B, C, L] and weight [C, K]")
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor (there is no CPU path)")
+    for name, t in (("weight", weight), ("bias", bias), ("seq_idx", seq_idx),
+                    ("initial_states", initial_states), ("final_states_out", final_states_out),
+                    ("out", out)):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} must be on {x.device}")
+    B, C, L = x.shape
+    K = weight.shape[1]
+    copied = False
+    if not (x.stride(2) == 1 or x.stride(1) == 1 or L <= 1 or C <= 1):
+        x = x.contiguous()          # neither time nor channels unit-stride
+        copied = True
+    weight = weight.contiguous()
+    if bias is not None:
+        if bias.dtype != weight.dtype:
+            raise ValueError("bias must have the weight's dtype")
+        bias = bias.contiguous()
+    if seq_idx is not None:
+        if seq_idx.dtype != torch.int32 or tuple(seq_idx.shape) != (B, L):
+            raise ValueError("seq_idx must be int32 [B, L]")
+        seq_idx = seq_idx.contiguous()
+    if initial_states is not None:
+        if initial_states.dtype != x.dtype or tuple(initial_states.shape) != (B, C, K - 1):
+            raise ValueError("initial_states must be [B, C, K-1] in x's dtype")
+    fs = None
+    if return_final_states:
+        if final_states_out is not None:
+            if final_states_out.dtype != x.dtype or tuple(final_states_out.shape) != (B, C, K - 1):
+                raise ValueError("final_states_out must be [B, C, K-1] in x's dtype")
+            fs = final_states_out
+        else:
+            fs = torch.empty(B, K - 1, C, dtype=x.dtype, device=x.device).transpose(1, 2)
+    if out is None:
+        out = empty_like_layout(x)
+    elif out.dtype != x.dtype or tuple(out.shape) != (B, C, L):
+        raise ValueError("out must be [B, C, L] in x's dtype")
+    args = make_args(x, weight, out, bias, seq_idx, initial_states, fs, activation)
+    with torch.cuda.device(x.device):
+        st = ccv_fwd(args)
+    _raise(st)
+    if info is not None:
+        info["x_copied"] = copied
+    return (out, fs) if return_final_states else out
+
+
+def plan_for(x, weight, out=None, **kw) -> dict:
+    """The launch causal_conv1d_fwd would make for these tensors (no device work)."""
+    if out is None:
+        out = empty_like_layout(x)
+    st, p = ccv_fwd_plan(make_args(x, weight, out, **kw))
+    _raise(st)
+    return p.as_dict()

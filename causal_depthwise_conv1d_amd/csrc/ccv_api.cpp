@@ -1,0 +1,228 @@
+// ccv_api.cpp -- the C ABI of libccv: argument checks, kernel choice, launch.
+//
+// The checks follow the contract of Ch.4 "Dao interface and source map"
+// (section "Contract of the full-sequence interface", argument table; section
+// "Concrete limits of v1.5.0": K in {2,3,4}, three storage dtypes for x and
+// weight dispatched separately, bias in the weight dtype, states in x's dtype,
+// and no seq_idx together with initial or final states).  Two of that
+// version's limits are lifted because nothing in the arithmetic needs them:
+// states and seq_idx work with either layout, and channel-last needs no
+// multiple-of-8 alignment (an element-wise path serves unaligned views).
+//
+// Nothing here touches a device except ccv_fwd's single kernel launch.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/ccv.h"
+#include "ccv_launch.hpp"
+
+namespace {
+
+using namespace ccv;
+
+struct Plan {
+  ccv_plan_t pub;
+  bool silu, seq;
+  CfArgs cf;
+  ClArgs cl;
+};
+
+inline int elt_size(int dt) { return dt == CCV_F32 ? 4 : 2; }
+
+// Largest element offset of a [n0, n1, n2] view with strides s (all >= 0), or -1
+// when it does not fit in int64.
+int64_t max_offset(int64_t n0, int64_t n1, int64_t n2, const int64_t s[3]) {
+  int64_t total = 0;
+  const int64_t n[3] = {n0, n1, n2};
+  for (int d = 0; d < 3; ++d) {
+    if (n[d] <= 1) continue;
+    int64_t p;
+    if (__builtin_mul_overflow(n[d] - 1, s[d], &p)) return -1;
+    if (__builtin_add_overflow(total, p, &total)) return -1;
+  }
+  return total;
+}
+
+bool fits_bytes(int64_t max_off, int es) {
+  int64_t bytes;
+  return max_off >= 0 && !__builtin_mul_overflow(max_off + 1, (int64_t)es, &bytes);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The element stride of a dimension keeps 16-byte alignment (or is never used).
+bool stride_ok16(int64_t n, int64_t s, int es) { return n <= 1 || ((s * es) & 15) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+// Checks every argument and fills *plan (never NULL) with the launch to make.
+int validate(const ccv_fwd_args_t* a, Plan* plan) {
+  if (!a) return CCV_E_NULL;
+  if (a->struct_size != (int64_t)sizeof(ccv_fwd_args_t)) return CCV_E_ABI;
+  if (a->B < 0 || a->C < 0 || a->L < 0) return CCV_E_SHAPE;
+  if (a->C > INT32_MAX || a->L > INT32_MAX) return CCV_E_SHAPE;
+  if (a->K < 2 || a->K > 4) return CCV_E_KSIZE;
+  if (a->x_dtype < 0 || a->x_dtype > 2 || a->w_dtype < 0 || a->w_dtype > 2) return CCV_E_DTYPE;
+  if (a->activation != CCV_ACT_NONE && a->activation != CCV_ACT_SILU) return CCV_E_UNSUPPORTED;
+  if (a->seq_idx && (a->initial_states || a->final_states_out)) return CCV_E_UNSUPPORTED;
+  for (int d = 0; d < 3; ++d) {
+    if (a->x_stride[d] < 0 || a->out_stride[d] < 0) return CCV_E_LAYOUT;
+    if (a->initial_states && a->init_stride[d] < 0) return CCV_E_LAYOUT;
+    if (a->final_states_out && a->final_stride[d] < 0) return CCV_E_LAYOUT;
+  }
+
+  const int64_t B = a->B, C = a->C, L = a->L;
+  const int K = a->K;
+  const bool want_out = B > 0 && C > 0 && L > 0;
+  const bool want_fin = B > 0 && C > 0 && a->final_states_out != nullptr;
+  *plan = Plan{};
+  plan->pub.path = CCV_PATH_NONE;
+  if (!want_out && !want_fin) return CCV_OK;
+
+  if (want_out && (!a->x || !a->weight || !a->out)) return CCV_E_NULL;
+  if (want_out && a->out == a->x) return CCV_E_ALIAS;
+  if (a->final_states_out && a->initial_states && a->final_states_out == a->initial_states) return CCV_E_ALIAS;
+
+  // Kernel choice by the unit-stride dimension of x (Ch.4, section "Why one shape
+  // still has two layouts"); out must be unit-stride in the same dimension.  The
+  // stride of a dimension of size <= 1 is never used, so it matches either way.
+  const bool x_cf = a->x_stride[2] == 1 || L <= 1, x_cl = a->x_stride[1] == 1 || C <= 1;
+  const bool o_cf = !want_out || a->out_stride[2] == 1 || L <= 1;
+  const bool o_cl = !want_out || a->out_stride[1] == 1 || C <= 1;
+  int path;
+  if (a->x_stride[2] == 1 && L > 1 && o_cf) path = CCV_PATH_CHANNEL_FIRST;
+  else if (x_cl && o_cl) path = CCV_PATH_CHANNEL_LAST;
+  else if (x_cf && o_cf) path = CCV_PATH_CHANNEL_FIRST;
+  else return CCV_E_LAYOUT;
+
+  const int es = elt_size(a->x_dtype);
+  const int64_t xo = max_offset(B, C, L, a->x_stride);
+  if (!fits_bytes(xo, es)) return CCV_E_SHAPE;
+  if (want_out && !fits_bytes(max_offset(B, C, L, a->out_stride), es)) return CCV_E_SHAPE;
+  if (a->initial_states && !fits_bytes(max_offset(B, C, K - 1, a->init_stride), es)) return CCV_E_SHAPE;
+  if (a->final_states_out && !fits_bytes(max_offset(B, C, K - 1, a->final_stride), es)) return CCV_E_SHAPE;
+  int64_t bl;
+  if (a->seq_idx && __builtin_mul_overflow(B, L, &bl)) return CCV_E_SHAPE;
+
+  const int V = 16 / es;
+  Common m{};
+  m.x = a->x;
+  m.out = want_out ? a->out : nullptr;
+  m.w = a->weight;
+  m.bias = a->bias;
+  m.seq = a->seq_idx;
+  m.init = a->initial_states;
+  m.fin = a->final_states_out;
+  m.B = B; m.C = C; m.L = L;
+  m.is_b = a->init_stride[0]; m.is_c = a->init_stride[1]; m.is_i = a->init_stride[2];
+  m.fs_b = a->final_stride[0]; m.fs_c = a->final_stride[1]; m.fs_i = a->final_stride[2];
+  m.w_dtype = a->w_dtype;
+
+  const bool force_scalar = env_int("CCV_FORCE_SCALAR", 0) != 0;
+  ccv_plan_t& P = plan->pub;
+  P.path = path;
+  P.elems_per_lane = V;
+  P.block = 64 * kWavesPerGroup;
+  P.waves_per_group = kWavesPerGroup;
+  plan->silu = a->activation == CCV_ACT_SILU;
+  plan->seq = a->seq_idx != nullptr;
+  int64_t nwork;
+
+  if (path == CCV_PATH_CHANNEL_FIRST) {
+    CfArgs& c = plan->cf;
+    c.x_sb = a->x_stride[0]; c.x_sc = a->x_stride[1];
+    c.o_sb = a->out_stride[0]; c.o_sc = a->out_stride[1];
+    c.span = (int64_t)64 * V * kCfUnroll;
+    c.nseg = L > 0 ? (L + c.span - 1) / c.span : 1;
+    if (__builtin_mul_overflow(B * C, c.nseg, &nwork)) return CCV_E_SHAPE;
+    bool vec = aligned16(a->x) && stride_ok16(B, c.x_sb, es) && stride_ok16(C, c.x_sc, es);
+    if (want_out) vec = vec && aligned16(a->out) && stride_ok16(B, c.o_sb, es) && stride_ok16(C, c.o_sc, es);
+    if (a->seq_idx) vec = vec && aligned16(a->seq_idx) && (B <= 1 || (L & 3) == 0);
+    P.vector = vec && !force_scalar;
+    P.unroll = kCfUnroll;
+    P.span = c.span;
+    P.channels_per_item = 1;
+  } else {
+    ClArgs& c = plan->cl;
+    c.x_sb = a->x_stride[0]; c.x_sl = a->x_stride[2];
+    c.o_sb = a->out_stride[0]; c.o_sl = a->out_stride[2];
+    int tile = env_int("CCV_CL_TILE_T", 64);
+    if (tile < kClUnroll) tile = kClUnroll;
+    c.tile = tile;
+    c.ntt = L > 0 ? (L + tile - 1) / tile : 1;
+    c.ncg = (C + 64 * V - 1) / (64 * V);
+    if (__builtin_mul_overflow(B * c.ncg, c.ntt, &nwork)) return CCV_E_SHAPE;
+    bool vec = aligned16(a->x) && stride_ok16(B, c.x_sb, es) && stride_ok16(L, c.x_sl, es);
+    if (want_out) vec = vec && aligned16(a->out) && stride_ok16(B, c.o_sb, es) && stride_ok16(L, c.o_sl, es);
+    P.vector = vec && !force_scalar;
+    P.unroll = kClUnroll;
+    P.span = tile;
+    P.channels_per_item = 64 * V;
+  }
+  const int64_t grid = (nwork + kWavesPerGroup - 1) / kWavesPerGroup;
+  if (grid > INT32_MAX) return CCV_E_SHAPE;
+  m.nwork = nwork;
+  m.xcd_q = (uint32_t)(grid / 8);
+  m.xcd_r = (uint32_t)(grid % 8);
+  P.grid = grid;
+  P.work_items = nwork;
+  plan->cf.m = m;
+  plan->cl.m = m;
+  return CCV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ccv_fwd_check(const ccv_fwd_args_t* args) {
+  Plan p;
+  return validate(args, &p);
+}
+
+int ccv_fwd_plan(const ccv_fwd_args_t* args, ccv_plan_t* out) {
+  Plan p;
+  const int st = validate(args, &p);
+  if (st == CCV_OK && out) *out = p.pub;
+  return st;
+}
+
+int ccv_fwd(const ccv_fwd_args_t* args, void* hip_stream) {
+  Plan p;
+  const int st = validate(args, &p);
+  if (st != CCV_OK) return st;
+  if (p.pub.path == CCV_PATH_NONE || p.pub.grid == 0) return CCV_OK;
+  int err;
+  if (p.pub.path == CCV_PATH_CHANNEL_FIRST)
+    err = launch_cf(p.cf, args->x_dtype, args->K, p.silu, p.seq, p.pub.vector != 0,
+                    (uint32_t)p.pub.grid, hip_stream);
+  else
+    err = launch_cl(p.cl, args->x_dtype, args->K, p.silu, p.seq, p.pub.vector != 0,
+                    (uint32_t)p.pub.grid, hip_stream);
+  return err == 0 ? CCV_OK : CCV_E_HIP;
+}
+
+const char* ccv_status_str(int s) {
+  switch (s) {
+    case CCV_OK: return "CCV_OK";
+    case CCV_E_NULL: return "CCV_E_NULL";
+    case CCV_E_SHAPE: return "CCV_E_SHAPE";
+    case CCV_E_KSIZE: return "CCV_E_KSIZE";
+    case CCV_E_DTYPE: return "CCV_E_DTYPE";
+    case CCV_E_LAYOUT: return "CCV_E_LAYOUT";
+    case CCV_E_UNSUPPORTED: return "CCV_E_UNSUPPORTED";
+    case CCV_E_ALIAS: return "CCV_E_ALIAS";
+    case CCV_E_HIP: return "CCV_E_HIP";
+    case CCV_E_INTERNAL: return "CCV_E_INTERNAL";
+    case CCV_E_ABI: return "CCV_E_ABI";
+  }
+  return "CCV_E_UNKNOWN";
+}
+
+int ccv_abi_version(void) { return CCV_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// ccv_cf.hip -- channel-first forward (x and out have unit stride in time).
+//
+// Computes out[b,c,t] = act(bias[c] + sum_k keep * w[c,k] * X~[b,c,t-K+1+k]) (Ch.5
+// "Dao forward CUDA implementation", section "How adjacent threads and chunks
+// exchange history", stencil equation for z_i; fp32 accumulation, SiLU on the
+// accumulator, one rounding at the store).
+//
+// Work split (rethought for wave64 rather than taken from the pages' 128-thread
+// blocks): one wave owns one time segment of one (b, c) row.  Lane l of the wave
+// holds 16-byte vectors number (l, l + 64, l + 128, ...) of the segment, so every
+// load and store instruction of the wave covers 1 KB of consecutive addresses.
+// Each output needs the K-1 inputs before its vector; they come from lane l-1 by
+// a DPP wave shift, and lane 0 takes them from lane 63 of the previous vector
+// (v_readlane), or, for the segment's first vector, from memory just left of the
+// segment, initial_states, or zeros (Ch.5, section "Three kinds of boundary
+// handled separately").  Segments are independent, so long rows with few
+// channels still fill the GPU: the pages' design ties the block count to B*C
+// (Ch.5, section "Task split of the time-contiguous path"), which collapses for
+// long sequences with few channels.  There is no LDS and no barrier.
+#include "ccv_device.hpp"
+
+namespace ccv {
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC>
+__global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
+  constexpr int V = S::V;
+  constexpr int U = kCfUnroll;
+  using raw = typename S::raw;
+  const Common& m = a.m;
+
+  const int lane = threadIdx.x & 63;
+  const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
+  const int64_t item = (int64_t)g * kWavesPerGroup + (threadIdx.x >> 6);
+  if (item >= m.nwork) return;                      // whole wave leaves together
+
+  const int64_t row = item / a.nseg;
+  const int64_t seg = item - row * a.nseg;
+  const int64_t b = row / m.C;
+  const int64_t c = row - b * m.C;
+  const int64_t L = m.L;
+  const int64_t t0 = seg * a.span;
+
+  const raw* __restrict__ xr = static_cast<const raw*>(m.x) + b * a.x_sb + c * a.x_sc;
+  raw* __restrict__ orow = static_cast<raw*>(m.out) + b * a.o_sb + c * a.o_sc;
+  const int32_t* __restrict__ sr = SEQ ? m.seq + b * L : nullptr;
+
+  if (t0 < L) {
+    float w[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[k] = load_param(m.w, m.w_dtype, c * K + k);
+    const float beta = m.bias ? load_param(m.bias, m.w_dtype, c) : 0.0f;
+
+    // History for lane 0 of the segment's first vector: X~[t0-K+1 .. t0-1].
+    float carry[K - 1];
+    int carry_id[K - 1];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+      const int64_t src = t0 - (K - 1) + j;
+      if (src >= 0) {
+        carry[j] = S::to_f(xr[src]);
+      } else if (m.init) {
+        carry[j] = S::to_f(static_cast<const raw*>(m.init)[b * m.is_b + c * m.is_c + (src + K - 1) * m.is_i]);
+      } else {
+        carry[j] = 0.0f;
+      }
+      carry_id[j] = (SEQ && src >= 0) ? sr[src] : 0;
+    }
+    // With seq_idx a source left of t = 0 has no id and never counts.
+    bool first_ok[K - 1];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) first_ok[j] = !(SEQ && lane == 0 && t0 - (K - 1) + j < 0);
+
+    // Issue every load of the segment before any arithmetic.
+    float e[U][V];
+    int id[U][V];
+    const int64_t v0 = t0 / V;                      // first vector of the segment
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t te = (v0 + u * 64 + lane) * V;  // first element of this lane's vector
+      if (VEC && te + V <= L) {
+        S::unpack(load16(xr + te), e[u]);
+        if constexpr (SEQ) {
+          const u32x4 s0 = load16(sr + te);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) id[u][i] = (int)s0[i];
+          if constexpr (V == 8) {
+            const u32x4 s1 = load16(sr + te + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) id[u][4 + i] = (int)s1[i];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const bool in = te + i < L;
+          e[u][i] = in ? S::to_f(xr[te + i]) : 0.0f;
+          if constexpr (SEQ) id[u][i] = in ? sr[te + i] : 0;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // Halo of this lane's vector: the last K-1 inputs of the previous vector.
+      float h[K - 1];
+      int hid[K - 1];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) {
+        h[j] = shift_in(carry[j], e[u][V - (K - 1) + j]);
+        if constexpr (SEQ) hid[j] = shift_in(carry_id[j], id[u][V - (K - 1) + j]);
+      }
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) {
+        carry[j] = lane63(e[u][V - (K - 1) + j]);
+        if constexpr (SEQ) carry_id[j] = lane63(id[u][V - (K - 1) + j]);
+      }
+
+      float y[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float acc = beta;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int j = i - (K - 1) + k;            // source offset inside the vector
+          const float xv = j >= 0 ? e[u][j] : h[K - 1 + j];
+          if constexpr (SEQ) {
+            const int sid = j >= 0 ? id[u][j] : hid[K - 1 + j];
+            const bool ok = (j >= 0 || u > 0 || first_ok[K - 1 + j]) && sid == id[u][i];
+            acc = ok ? __builtin_fmaf(w[k], xv, acc) : acc;
+          } else {
+            acc = __builtin_fmaf(w[k], xv, acc);
+          }
+        }
+        y[i] = SILU ? silu(acc) : acc;
+      }
+
+      const int64_t te = (v0 + u * 64 + lane) * V;
+      if (VEC && te + V <= L) {
+        store16(orow + te, S::pack(y));
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (te + i < L) orow[te + i] = S::from_f(y[i]);
+      }
+    }
+  }
+
+  // final_states: the segment holding t = L-1 (segment 0 when L == 0) copies the
+  // last K-1 extended inputs bit for bit (Ch.5, section "Three kinds of boundary
+  // handled separately").
+  if (m.fin && (L == 0 ? seg == 0 : (t0 <= L - 1 && L - 1 < t0 + a.span)) && lane < K - 1) {
+    const int64_t j = L - (K - 1) + lane;
+    raw v;
+    if (j >= 0) v = xr[j];
+    else if (m.init) v = static_cast<const raw*>(m.init)[b * m.is_b + c * m.is_c + (j + K - 1) * m.is_i];
+    else v = 0;
+    static_cast<raw*>(m.fin)[b * m.fs_b + c * m.fs_c + lane * m.fs_i] = v;
+  }
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC>
+static int launch_one(const CfArgs& a, uint32_t grid, void* stream) {
+  void* args[] = {const_cast<CfArgs*>(&a)};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_kernel<S, K, SILU, SEQ, VEC>),
+                              dim3(grid), dim3(64 * kWavesPerGroup), args, 0,
+                              static_cast<hipStream_t>(stream));
+}
+
+template <class S, int K>
+static int launch_k(const CfArgs& a, bool silu, bool seq, bool vec, uint32_t grid, void* st) {
+  if (silu) {
+    if (seq) return vec ? launch_one<S, K, true, true, true>(a, grid, st) : launch_one<S, K, true, true, false>(a, grid, st);
+    return vec ? launch_one<S, K, true, false, true>(a, grid, st) : launch_one<S, K, true, false, false>(a, grid, st);
+  }
+  if (seq) return vec ? launch_one<S, K, false, true, true>(a, grid, st) : launch_one<S, K, false, true, false>(a, grid, st);
+  return vec ? launch_one<S, K, false, false, true>(a, grid, st) : launch_one<S, K, false, false, false>(a, grid, st);
+}
+
+template <class S>
+static int launch_s(const CfArgs& a, int K, bool silu, bool seq, bool vec, uint32_t grid, void* st) {
+  switch (K) {
+    case 2: return launch_k<S, 2>(a, silu, seq, vec, grid, st);
+    case 3: return launch_k<S, 3>(a, silu, seq, vec, grid, st);
+    case 4: return launch_k<S, 4>(a, silu, seq, vec, grid, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_cf(const CfArgs& a, int dtype, int K, bool silu, bool seq, bool vec, uint32_t grid,
+              void* stream) {
+  switch (dtype) {
+    case CCV_DT_F32: return launch_s<F32>(a, K, silu, seq, vec, grid, stream);
+    case CCV_DT_F16: return launch_s<F16>(a, K, silu, seq, vec, grid, stream);
+    case CCV_DT_BF16: return launch_s<BF16>(a, K, silu, seq, vec, grid, stream);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace ccv

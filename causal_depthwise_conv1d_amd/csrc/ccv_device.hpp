@@ -1,0 +1,131 @@
+// ccv_device.hpp -- device-side helpers shared by the two forward kernels:
+// storage types, fp32 <-> storage conversion, SiLU, lane shifts, and the
+// XCD-aware workgroup order.  gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ccv_launch.hpp"
+
+namespace ccv {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ---- storage types: V elements fill one 16-byte vector ---------------------------
+
+struct F32 {
+  using raw = uint32_t;
+  static constexpr int V = 4;
+  __device__ static inline float to_f(raw r) { return __builtin_bit_cast(float, r); }
+  __device__ static inline void unpack(const u32x4 v, float* e) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = __builtin_bit_cast(float, v[i]);
+  }
+  __device__ static inline u32x4 pack(const float* y) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(uint32_t, y[i]);
+    return v;
+  }
+  __device__ static inline raw from_f(float y) { return __builtin_bit_cast(uint32_t, y); }
+};
+
+// bfloat16: the upper half of a binary32.  Widening is a shift; narrowing uses the
+// gfx950 packed convert (round to nearest even, NaN stays NaN).
+struct BF16 {
+  using raw = uint16_t;
+  static constexpr int V = 8;
+  __device__ static inline float to_f(raw r) { return __builtin_bit_cast(float, (uint32_t)r << 16); }
+  __device__ static inline void unpack(const u32x4 v, float* e) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+      e[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+    }
+  }
+  __device__ static inline u32x4 pack(const float* y) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x2 p = {y[2 * i], y[2 * i + 1]};
+      v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+    }
+    return v;
+  }
+  __device__ static inline raw from_f(float y) {
+    return __builtin_bit_cast(uint16_t, (__bf16)y);
+  }
+};
+
+// IEEE binary16: hardware converts both ways (round to nearest even).
+struct F16 {
+  using raw = uint16_t;
+  static constexpr int V = 8;
+  __device__ static inline float to_f(raw r) { return (float)__builtin_bit_cast(_Float16, r); }
+  __device__ static inline void unpack(const u32x4 v, float* e) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x2 p = __builtin_convertvector(__builtin_bit_cast(f16x2, v[i]), f32x2);
+      e[2 * i] = p[0];
+      e[2 * i + 1] = p[1];
+    }
+  }
+  __device__ static inline u32x4 pack(const float* y) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x2 p = {y[2 * i], y[2 * i + 1]};
+      v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
+    }
+    return v;
+  }
+  __device__ static inline raw from_f(float y) { return __builtin_bit_cast(uint16_t, (_Float16)y); }
+};
+
+// Weight / bias element of any storage dtype, widened exactly to fp32.
+__device__ inline float load_param(const void* p, int dtype, int64_t i) {
+  if (dtype == CCV_DT_F32) return static_cast<const float*>(p)[i];
+  const uint16_t h = static_cast<const uint16_t*>(p)[i];
+  if (dtype == CCV_DT_BF16) return __builtin_bit_cast(float, (uint32_t)h << 16);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// SiLU on the fp32 accumulator: z * 1 / (1 + 2^(-z * log2(e))), with the hardware
+// base-2 exponential and reciprocal (about 1 ulp each).  IEEE edge cases fall out:
+// silu(+inf) = +inf, silu(-inf) = NaN (as z * sigmoid(z) evaluates), NaN -> NaN.
+__device__ inline float silu(float z) {
+  const float e = __builtin_amdgcn_exp2f(z * -1.44269504088896341f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Lane l receives lane l-1's value; lane 0 receives `carry`.  DPP wave_shr:1
+// (whole-wave shift right by one lane); every lane of the wave must be active.
+__device__ inline float shift_in(float carry, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, carry), __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, false));
+}
+__device__ inline int shift_in(int carry, int v) {
+  return __builtin_amdgcn_update_dpp(carry, v, 0x138, 0xf, 0xf, false);
+}
+__device__ inline float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ inline int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup g runs on XCD g % 8).
+// Renumber them so that each XCD owns one contiguous range of work: neighbouring
+// work items (which re-read each other's K-1 halo) then share that XCD's L2.
+// With G workgroups, q = G / 8 and r = G % 8, XCD x holds q + (x < r) of them.
+__device__ inline uint32_t xcd_order(uint32_t g, uint32_t q, uint32_t r) {
+  const uint32_t x = g & 7u, s = g >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+__device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
+__device__ inline void store16(void* p, u32x4 v) { *static_cast<u32x4*>(p) = v; }
+
+}  // namespace ccv

@@ -1,0 +1,60 @@
+// ccv_launch.hpp -- internal launch descriptors passed by value to the kernels,
+// and the launch entry of each kernel family.  Host and device code both see
+// this header; it holds no HIP types so the validation code compiles anywhere.
+#pragma once
+
+#include <stdint.h>
+
+namespace ccv {
+
+enum { CCV_DT_F32 = 0, CCV_DT_F16 = 1, CCV_DT_BF16 = 2 };
+
+// Fields common to both kernels.  Strides are in elements.
+struct Common {
+  const void* x;
+  void* out;
+  const void* w;        // [C, K] contiguous, w_dtype
+  const void* bias;     // [C] or nullptr, w_dtype
+  const int32_t* seq;   // [B, L] contiguous or nullptr
+  const void* init;     // [B, C, K-1] or nullptr, x dtype
+  void* fin;            // [B, C, K-1] or nullptr, x dtype
+  int64_t B, C, L;
+  int64_t is_b, is_c, is_i;   // initial_states strides
+  int64_t fs_b, fs_c, fs_i;   // final_states strides
+  int64_t nwork;              // wave work items
+  uint32_t xcd_q, xcd_r;      // workgroups per XCD (quotient / remainder of G / 8)
+  int32_t w_dtype;
+};
+
+// Channel-first (s_L == 1 for x and out): a work item is one time segment of one
+// (b, c) row, `span` steps long.
+struct CfArgs {
+  Common m;
+  int64_t x_sb, x_sc, o_sb, o_sc;
+  int64_t span;   // 64 lanes * V * U
+  int64_t nseg;   // segments per row
+};
+
+// Channel-last (s_C == 1 for x and out): a work item is `tile` time rows of one
+// group of 64 * V channels of one batch.
+struct ClArgs {
+  Common m;
+  int64_t x_sb, x_sl, o_sb, o_sl;
+  int64_t tile;   // time rows per work item
+  int64_t ntt;    // time tiles per (b, channel group)
+  int64_t ncg;    // channel groups
+};
+
+// Launch one kernel instance; returns a hipError_t value (0 = success).
+// dtype: CCV_DT_*; silu/seq/vec select the template instance.
+int launch_cf(const CfArgs& a, int dtype, int K, bool silu, bool seq, bool vec,
+              uint32_t grid, void* stream);
+int launch_cl(const ClArgs& a, int dtype, int K, bool silu, bool seq, bool vec,
+              uint32_t grid, void* stream);
+
+// Compile-time work per lane, shared by the planner and the kernels.
+constexpr int kWavesPerGroup = 4;
+constexpr int kCfUnroll = 4;     // 16-byte vectors per lane per segment
+constexpr int kClUnroll = 4;     // time rows loaded ahead per lane
+
+}  // namespace ccv

@@ -1,0 +1,141 @@
+/*
+ * ccv.h -- C ABI of libccv: the causal depthwise conv1d forward on AMD gfx950.
+ *
+ * The operation (Ch.5 "Dao forward CUDA implementation", section "How adjacent
+ * threads and chunks exchange history", stencil equation for z_i, with the
+ * argument meanings of Ch.4 "Dao interface and source map", section "Contract
+ * of the full-sequence interface", argument table):
+ *
+ *   out[b,c,t] = act( bias[c] + sum_{k=0}^{K-1} keep(b,t,k) * w[c,k] * X~[b,c,t-K+1+k] )
+ *
+ *   - K in {2,3,4}; w[c,k] is ordered oldest -> current, so w[c,K-1] meets x[b,c,t].
+ *   - X~[b,c,j] = x[b,c,j] for j >= 0.  For j < 0 it is the history left of the
+ *     block: initial_states[b,c,j+K-1] (time ascending: index K-2 is t = -1) when
+ *     given, otherwise 0 (Ch.5, section "Three kinds of boundary handled
+ *     separately").
+ *   - keep = 1 without seq_idx.  With seq_idx, a term counts only when its source
+ *     step s = t-K+1+k is >= 0 and seq_idx[b,s] == seq_idx[b,t]; other terms are
+ *     dropped (skipped, so a NaN in another sequence never reaches this one)
+ *     (same section, seq_idx paragraph).  Ids are compared for equality only.
+ *   - act is the identity or SiLU z*sigmoid(z) ("silu" and "swish" are the same
+ *     activation), applied to the fp32 accumulator before the single rounding to
+ *     the output dtype (Ch.5, same section as the stencil; Ch.4, section "How
+ *     autograd links forward and backward", on result dtype vs accumulation dtype).
+ *   - final_states_out[b,c,i] = X~[b,c,L-K+1+i], i = 0..K-2: the last K-1 conv
+ *     inputs (not activations), copied bit for bit; correct for L < K-1 and L = 0
+ *     (Ch.5, section "Three kinds of boundary handled separately").
+ *
+ * Layout: every tensor argument is a pointer plus element strides; the element
+ * at (b,c,t) is at base + b*s_B + c*s_C + t*s_L elements (Ch.4, section "Why one
+ * shape still has two layouts", offset equation).  x must have unit stride in
+ * time (channel-first kernel) or in channels (channel-last kernel); a slice of a
+ * wider projection buffer (s_L > C) is used as is, never repacked.  `out` must
+ * have unit stride in the same dimension as x.
+ *
+ * Ownership: the caller allocates and owns every buffer (device memory for all
+ * tensor pointers).  The library allocates nothing, keeps no pointer after a
+ * call returns, never synchronises, and is safe to call concurrently on
+ * different streams.  `out` must not overlap any input; views interleaved in one
+ * parent buffer are fine as long as the elements touched are disjoint.
+ *
+ * Errors: every call returns a ccv_status (0 = success, negative = error).  All
+ * argument checks run before anything is enqueued, so a call that fails writes
+ * nothing.  No C++ exception crosses this boundary.
+ */
+#ifndef CCV_H
+#define CCV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CCV_ABI_VERSION 1
+
+/* Storage dtypes of x / out / states (x_dtype) and of weight / bias (w_dtype).
+ * Ch.4, section "Concrete limits of v1.5.0": x and weight each take one of
+ * fp32, fp16, bf16, dispatched separately; bias has the weight's dtype; states
+ * have x's dtype. */
+typedef enum { CCV_F32 = 0, CCV_F16 = 1, CCV_BF16 = 2 } ccv_dtype_t;
+
+/* Activation flag (Ch.4, section "Contract of the full-sequence interface":
+ * activation is none, "silu" or "swish"; the last two are one activation). */
+typedef enum { CCV_ACT_NONE = 0, CCV_ACT_SILU = 1 } ccv_act_t;
+
+typedef enum {
+  CCV_OK = 0,
+  CCV_E_NULL = -1,        /* a pointer the call needs is NULL */
+  CCV_E_SHAPE = -2,       /* B, C or L negative, or sizes overflow int64 offsets */
+  CCV_E_KSIZE = -3,       /* K not in {2,3,4} */
+  CCV_E_DTYPE = -4,       /* x_dtype or w_dtype not a ccv_dtype_t */
+  CCV_E_LAYOUT = -5,      /* x (or out) has unit stride in neither time nor channels,
+                             out's unit-stride dim differs from x's, or a stride < 0 */
+  CCV_E_UNSUPPORTED = -6, /* seq_idx together with initial_states or final_states_out,
+                             or an activation value outside ccv_act_t */
+  CCV_E_ALIAS = -7,       /* out == x, or final_states_out == initial_states */
+  CCV_E_HIP = -8,         /* the HIP runtime refused the launch */
+  CCV_E_INTERNAL = -9,    /* an unexpected internal condition */
+  CCV_E_ABI = -10         /* struct_size does not match this library's struct */
+} ccv_status_t;
+
+/* All arguments of one forward call.  Strides are in elements. */
+typedef struct ccv_fwd_args {
+  int64_t struct_size;          /* = sizeof(ccv_fwd_args_t) */
+  int64_t B, C, L;              /* logical shape of x and out: [B, C, L] */
+  int32_t K;                    /* taps: 2, 3 or 4 */
+  int32_t activation;           /* ccv_act_t */
+  int32_t x_dtype;              /* ccv_dtype_t of x, out, initial_states, final_states_out */
+  int32_t w_dtype;              /* ccv_dtype_t of weight and bias */
+  const void* x;                /* device, x[b,c,t] */
+  int64_t x_stride[3];          /*   (s_B, s_C, s_L) */
+  const void* weight;           /* device, contiguous [C, K], oldest -> current */
+  const void* bias;             /* device [C] or NULL (pre-activation) */
+  const int32_t* seq_idx;       /* device, contiguous int32 [B, L], or NULL */
+  const void* initial_states;   /* device [B, C, K-1] or NULL (history left of t = 0) */
+  int64_t init_stride[3];       /*   (b, c, i) strides */
+  void* final_states_out;       /* device [B, C, K-1] or NULL (the last K-1 inputs) */
+  int64_t final_stride[3];      /*   (b, c, i) strides */
+  void* out;                    /* device [B, C, L] */
+  int64_t out_stride[3];        /*   (s_B, s_C, s_L) */
+} ccv_fwd_args_t;
+
+/* Which kernel a call would launch and how (host-only; for tests and benches). */
+typedef enum { CCV_PATH_NONE = 0, CCV_PATH_CHANNEL_FIRST = 1, CCV_PATH_CHANNEL_LAST = 2 } ccv_path_t;
+
+typedef struct ccv_plan {
+  int32_t path;            /* ccv_path_t; NONE when there is nothing to compute or write */
+  int32_t vector;          /* 1: 16-byte loads and stores; 0: element loads and stores */
+  int32_t elems_per_lane;  /* elements one lane holds per 16-byte vector (16 / element size) */
+  int32_t unroll;          /* vectors (channel-first) or time rows (channel-last) in flight per lane */
+  int64_t grid;            /* workgroups launched */
+  int32_t block;           /* threads per workgroup */
+  int32_t waves_per_group; /* independent wave work items per workgroup */
+  int64_t work_items;      /* wave work items (grid * waves_per_group rounded down to the need) */
+  int64_t span;            /* channel-first: time steps per work item; channel-last: time rows per work item */
+  int64_t channels_per_item; /* channel-last: channels per work item; channel-first: 1 */
+} ccv_plan_t;
+
+/* Enqueue the forward on `hip_stream` (a hipStream_t; NULL = the null stream) and
+ * return without waiting.  Returns CCV_OK, a validation error (nothing enqueued)
+ * or CCV_E_HIP.  Faults of the kernel itself surface at the caller's next
+ * synchronisation of that stream. */
+int ccv_fwd(const ccv_fwd_args_t* args, void* hip_stream);
+
+/* Validate `args` exactly as ccv_fwd does, without touching any device. */
+int ccv_fwd_check(const ccv_fwd_args_t* args);
+
+/* Validate and describe the launch ccv_fwd would make, without touching any
+ * device.  `plan` may be NULL. */
+int ccv_fwd_plan(const ccv_fwd_args_t* args, ccv_plan_t* plan);
+
+/* Static, NUL-terminated name of a status code ("CCV_OK", ...). */
+const char* ccv_status_str(int status);
+
+/* CCV_ABI_VERSION of the loaded library. */
+int ccv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CCV_H */

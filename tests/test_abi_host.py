@@ -1,0 +1,187 @@
+"""The C ABI on the CPU: the libraries load, export every declared symbol, and
+validate arguments exactly as documented, all without touching a device
+(ccv_fwd_check / ccv_fwd_plan never dereference the pointers they are given)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_depthwise_conv1d_amd as ccv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = {"ccv.h": ccv.LIB_PATH, "ccv_calib.h": ccv.CALIB_LIB_PATH}
+
+
+def declared_functions(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ccv_\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(HEADERS)
+
+
+@pytest.mark.parametrize("header", sorted(HEADERS))
+def test_library_exports_every_declared_symbol(header):
+    names = declared_functions(header)
+    assert names, header
+    lib = ctypes.CDLL(HEADERS[header])
+    dyn = subprocess.run(["nm", "-D", "--defined-only", HEADERS[header]], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", dyn, flags=re.M))
+    for n in names:
+        assert n in exported, (header, n)
+        getattr(lib, n)
+
+
+def test_abi_version_and_status_names():
+    assert ccv.ccv_abi_version() == ccv.CCV_ABI_VERSION == 1
+    for code, name in ccv.STATUS.items():
+        assert ccv.ccv_status_str(code) == name
+    assert ccv.ccv_status_str(12345) == "CCV_E_UNKNOWN"
+
+
+# Fake, never-dereferenced device addresses (16-byte aligned unless stated).
+X, W, BIAS, SEQ, INIT, FIN, OUT = (0x100000 * (i + 1) for i in range(7))
+
+
+def args(B=2, C=64, L=1000, K=4, layout="cf", **over):
+    a = ccv.ccv_fwd_args_t()
+    a.B, a.C, a.L, a.K = B, C, L, K
+    a.x_dtype = a.w_dtype = ccv.CCV_BF16
+    a.activation = ccv.CCV_ACT_SILU
+    a.x, a.weight, a.out = X, W, OUT
+    st = (C * L, L, 1) if layout == "cf" else (L * C, 1, C)
+    a.x_stride = type(a.x_stride)(*st)
+    a.out_stride = type(a.out_stride)(*st)
+    for k, v in over.items():
+        if k.endswith("stride"):
+            v = type(getattr(a, k))(*v)
+        setattr(a, k, v)
+    return a
+
+
+def check(a):
+    return ccv.STATUS[ccv.ccv_fwd_check(a)]
+
+
+def test_valid_calls():
+    assert check(args()) == "CCV_OK"
+    assert check(args(layout="cl")) == "CCV_OK"
+    assert check(args(bias=BIAS, seq_idx=SEQ)) == "CCV_OK"
+    assert check(args(initial_states=INIT, init_stride=(64 * 3, 1, 64),
+                      final_states_out=FIN, final_stride=(64 * 3, 1, 64))) == "CCV_OK"
+
+
+def test_struct_size_mismatch():
+    a = args()
+    a.struct_size = 8
+    assert check(a) == "CCV_E_ABI"
+
+
+def test_shapes_and_k():
+    assert check(args(B=-1)) == "CCV_E_SHAPE"
+    assert check(args(L=-5)) == "CCV_E_SHAPE"
+    assert check(args(C=2**31)) == "CCV_E_SHAPE"
+    for K in (0, 1, 5, 8):
+        assert check(args(K=K)) == "CCV_E_KSIZE"
+    assert check(args(x_stride=(2**62, 1000, 1))) == "CCV_E_SHAPE"      # offsets overflow
+
+
+def test_dtypes_and_activation():
+    assert check(args(x_dtype=3)) == "CCV_E_DTYPE"
+    assert check(args(w_dtype=-1)) == "CCV_E_DTYPE"
+    assert check(args(activation=2)) == "CCV_E_UNSUPPORTED"
+
+
+def test_null_pointers():
+    assert check(args(x=None)) == "CCV_E_NULL"
+    assert check(args(weight=None)) == "CCV_E_NULL"
+    assert check(args(out=None)) == "CCV_E_NULL"
+    assert ccv.lib().ccv_fwd_check(None) == -1
+
+
+def test_forbidden_combinations():
+    assert check(args(seq_idx=SEQ, initial_states=INIT, init_stride=(192, 1, 64))) == "CCV_E_UNSUPPORTED"
+    assert check(args(seq_idx=SEQ, final_states_out=FIN, final_stride=(192, 1, 64))) == "CCV_E_UNSUPPORTED"
+
+
+def test_aliasing():
+    assert check(args(out=X)) == "CCV_E_ALIAS"
+    assert check(args(initial_states=INIT, final_states_out=INIT, init_stride=(192, 1, 64),
+                      final_stride=(192, 1, 64))) == "CCV_E_ALIAS"
+
+
+def test_layouts():
+    # neither time nor channels unit-stride: the caller must copy
+    assert check(args(x_stride=(64 * 1000 * 2, 2000, 2))) == "CCV_E_LAYOUT"
+    # out unit-stride in the other dimension than x
+    assert check(args(out_stride=(64000, 1, 64))) == "CCV_E_LAYOUT"
+    assert check(args(x_stride=(64000, 1000, -1))) == "CCV_E_LAYOUT"
+    # a slice of a wider channel-last buffer (s_L > C) is accepted as is
+    assert check(args(layout="cl", x_stride=(1000 * 10240, 1, 10240))) == "CCV_E_OK".replace("E_", "")
+
+
+def test_nothing_to_do_needs_no_pointers():
+    for B, C, L in ((0, 4, 8), (2, 0, 8), (2, 4, 0)):
+        a = args(B=B, C=C, L=L, x=None, weight=None, out=None)
+        assert check(a) == "CCV_OK"
+        st, p = ccv.ccv_fwd_plan(a)
+        assert st == 0 and p.path == ccv.CCV_PATH_NONE
+
+
+def test_empty_sequence_still_writes_final_states():
+    a = args(L=0, x=None, weight=None, out=None, initial_states=INIT, init_stride=(192, 3, 1),
+             final_states_out=FIN, final_stride=(192, 3, 1))
+    st, p = ccv.ccv_fwd_plan(a)
+    assert st == 0 and p.path != ccv.CCV_PATH_NONE and p.grid > 0
+
+
+def test_plan_channel_first():
+    st, p = ccv.ccv_fwd_plan(args(B=4, C=2048, L=4096))
+    assert st == 0
+    assert p.path == ccv.CCV_PATH_CHANNEL_FIRST and p.vector == 1 and p.elems_per_lane == 8
+    seg = 64 * 8 * p.unroll
+    assert p.span == seg
+    assert p.work_items == 4 * 2048 * -(-4096 // seg)
+    assert p.grid == -(-p.work_items // p.waves_per_group)
+
+
+def test_plan_channel_last_strided_view():
+    st, p = ccv.ccv_fwd_plan(args(B=8, C=4096, L=8192, layout="cl", x_stride=(8192 * 10240, 1, 10240)))
+    assert st == 0
+    assert p.path == ccv.CCV_PATH_CHANNEL_LAST and p.vector == 1
+    assert p.channels_per_item == 512
+    assert p.work_items == 8 * (4096 // 512) * -(-8192 // p.span)
+
+
+def test_plan_falls_back_to_element_access_when_unaligned():
+    # channel offset 3 in a bf16 buffer: base not 16-byte aligned
+    _, p = ccv.ccv_fwd_plan(args(layout="cl", x=X + 6, x_stride=(1000 * 72, 1, 72)))
+    assert p.vector == 0
+    # odd time stride breaks alignment of every row after the first
+    _, p = ccv.ccv_fwd_plan(args(layout="cl", x_stride=(1000 * 67, 1, 67)))
+    assert p.vector == 0
+    _, p = ccv.ccv_fwd_plan(args(layout="cf", x_stride=(64 * 1001, 1001, 1)))
+    assert p.vector == 0
+    _, p = ccv.ccv_fwd_plan(args(layout="cf", seq_idx=SEQ + 4))
+    assert p.vector == 0
+    _, p = ccv.ccv_fwd_plan(args(layout="cf", seq_idx=SEQ, L=1002))
+    assert p.vector == 0
+
+
+def test_size_one_dims_take_either_stride():
+    # L == 1: any time stride; C == 1: any channel stride
+    assert check(args(L=1, x_stride=(64, 1, 999), out_stride=(64, 1, 7))) == "CCV_OK"
+    assert check(args(C=1, layout="cl", x_stride=(1000, 77, 1), out_stride=(1000, 5, 1))) == "CCV_OK"
+
+
+def test_wrapper_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 8)
+    w = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_fwd(x, w)

@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by element.
+
+Small shapes that span several wave segments / time tiles and ragged tails, every
+dtype, K and layout (channel-first, channel-last, strided views of wider buffers,
+unaligned views that take the element-wise path), with and without bias, SiLU,
+seq_idx, initial and final states; seeded random shapes; edge cases; invariants
+that must hold bit for bit on the GPU."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import causal_depthwise_conv1d_amd as ccv
+import workloads as wl
+from gpu_support import (assert_close, assert_final_states, bits_equal, check_full, gpu_args, log,
+                         oracle_case, run_gpu, to_gpu_view)
+from oracle.from_torch import raw
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    ccv.lib()
+
+DTYPES = ["f32", "bf16", "f16"]
+KS = [2, 3, 4]
+LAYOUTS = ["cf", "cf_pitch", "cf_view", "cl", "cl_view", "cl_misaligned"]
+ES = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def layout_kw(layout, dtype, C, L):
+    V = 16 // ES[dtype]
+    if layout == "cf":
+        return dict(layout="cf")
+    if layout == "cf_pitch":          # rows 16-byte aligned but longer than L
+        return dict(layout="cf", t_pad=(-L) % V + V)
+    if layout == "cf_view":           # unaligned window of a bigger buffer
+        return dict(layout="cf", c_pad=3, c_off=1, t_pad=13, t_off=5)
+    if layout == "cl":
+        return dict(layout="cl")
+    if layout == "cl_view":           # channels [0, C) of a wider [B, L, C + pad] buffer
+        return dict(layout="cl", c_pad=(-C) % V + 2 * V)
+    if layout == "cl_misaligned":     # channel offset 3: not 16-byte aligned
+        return dict(layout="cl", c_pad=5, c_off=3, t_pad=2, t_off=1)
+    raise ValueError(layout)
+
+
+def seq_lengths(L, n, seed):
+    n = max(1, min(n, L))
+    return wl.packed_lengths(L, n, 1, seed).tolist()
+
+
+# (L, C, B, features) -- L spans 1, K-1, K, several wave segments / time tiles, ragged tails
+def matrix_cases(K):
+    return [
+        (1, 7, 2, dict(bias=True, activation="silu")),
+        (K - 1, 8, 1, dict(init=True, final=True)),
+        (K, 64, 2, dict(bias=True, init=True, final=True, activation="silu")),
+        (255, 130, 2, dict(bias=True, seq=9, activation="silu")),
+        (257, 8, 3, dict(bias=False, activation=None)),
+        (513, 64, 1, dict(init=True, final=True, activation="silu")),
+        (2049, 7, 2, dict(bias=True, activation="silu")),
+        (4099, 72, 1, dict(bias=True, seq=40, activation=None)),
+    ]
+
+
+def build(L, C, B, K, dtype, layout, feats, seed, w_dtype=None):
+    f = dict(feats)
+    nseq = f.pop("seq", None)
+    return wl.make_case(B=B, C=C, L=L, K=K, x_dtype=dtype, w_dtype=w_dtype, seed=seed,
+                        seq_lengths=seq_lengths(L, nseq, seed) if nseq else None,
+                        **layout_kw(layout, dtype, C, L), **f)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("K", KS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_matrix(dtype, K, layout):
+    for i, (L, C, B, feats) in enumerate(matrix_cases(K)):
+        w = build(L, C, B, K, dtype, layout, feats, seed=100 * K + i)
+        log(f"  case L={L} C={C} B={B} {feats}")
+        check_full(w, where=f"[{dtype} K={K} {layout} L={L} C={C}]")
+
+
+def test_random_shapes():
+    g = np.random.default_rng(2024)
+    for i in range(150):
+        K = int(g.integers(2, 5))
+        dtype = DTYPES[g.integers(0, 3)]
+        w_dtype = DTYPES[g.integers(0, 3)]
+        layout = LAYOUTS[g.integers(0, len(LAYOUTS))]
+        B = int(g.integers(1, 4))
+        C = int(g.integers(1, 300))
+        L = int(g.integers(0, 3000)) if g.random() < 0.9 else int(g.integers(0, 8))
+        use_seq = g.random() < 0.25 and L > 0
+        feats = dict(bias=bool(g.random() < 0.5), activation=["silu", "swish", None][g.integers(0, 3)])
+        if use_seq:
+            feats["seq"] = int(g.integers(1, 20))
+        else:
+            feats["init"] = bool(g.random() < 0.5)
+            feats["final"] = bool(g.random() < 0.5)
+        w = build(L, C, B, K, dtype, layout, feats, seed=5000 + i, w_dtype=w_dtype)
+        log(f"  random {i}: {dtype}/{w_dtype} K={K} {layout} B={B} C={C} L={L} {feats}")
+        check_full(w, where=f"[random {i}]")
+
+
+def test_empty_extents():
+    for B, C, L in ((0, 8, 16), (2, 0, 16), (2, 8, 0)):
+        w = wl.make_case(B=B, C=C, L=L, K=4, x_dtype="bf16", layout="cf", seed=1)
+        out, _ = run_gpu(w)
+        assert tuple(out.shape) == (B, C, L)
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_zero_length_final_states_are_the_history(dtype, layout):
+    for init in (True, False):
+        w = wl.make_case(B=2, C=5, L=0, K=4, x_dtype=dtype, layout=layout, init=init, final=True, seed=3)
+        out, fs = run_gpu(w)
+        assert out.numel() == 0
+        assert_final_states(w, fs)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_mixed_weight_dtypes(dtype):
+    for wd in DTYPES:
+        for layout in ("cf", "cl"):
+            w = wl.make_case(B=2, C=40, L=700, K=4, x_dtype=dtype, w_dtype=wd, layout=layout,
+                             bias=True, init=True, final=True, activation="silu", seed=77)
+            check_full(w, where=f"[x {dtype} w {wd} {layout}]")
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_down_convert_rounds_to_nearest_even(dtype, layout):
+    """With one nonzero tap, no bias and no activation, z = w*x is exact in fp32, so
+    the only rounding is the store: the GPU must return RNE(z) bit for bit."""
+    g = torch.Generator().manual_seed(9)
+    B, C, L = 2, 520, 1100
+    w = wl.make_case(B=B, C=C, L=L, K=2, x_dtype=dtype, layout=layout, bias=False, activation=None, seed=9)
+    wt = torch.zeros(C, 2)
+    wt[:, 1] = torch.rand(C, generator=g) * 3 + 0.1
+    w.weight = wt.to(wl.TORCH_DTYPES[dtype])
+    out, _ = run_gpu(w)
+    y, _ = oracle_case(w).fwd(want_sabs=False)
+    import oracle
+    ref = oracle.round_out(dtype, y)
+    assert np.array_equal(raw(out), ref), "down-convert is not round-to-nearest-even"
+
+
+def test_nonfinite_values_propagate():
+    for layout in ("cf", "cl"):
+        w = wl.make_case(B=1, C=16, L=300, K=4, x_dtype="f32", layout=layout, bias=True,
+                         activation="silu", seed=4)
+        xv = w.x
+        xv[0, 0, 10] = float("nan")
+        xv[0, 1, 20] = float("inf")
+        xv[0, 2, 30] = float("-inf")
+        xv[0, 3, 40] = 3e38
+        check_full(w, where=f"[nonfinite {layout}]")
+
+
+def test_masked_nan_does_not_leak():
+    for layout in ("cf", "cl"):
+        lengths = [50, 3, 97, 150]
+        w = wl.make_case(B=1, C=20, L=300, K=4, x_dtype="bf16", layout=layout, bias=True,
+                         activation="silu", seq_lengths=lengths, seed=5)
+        w.x[0, :, 49] = float("nan")       # last step of sequence 0
+        w.x[0, :, 52] = float("nan")       # last step of sequence 1
+        out, _ = run_gpu(w)
+        o = out.float()
+        assert torch.isnan(o[0, :, 49]).all() and torch.isnan(o[0, :, 52]).all()
+        assert not torch.isnan(o[0, :, 53:]).any(), "NaN crossed a sequence boundary"
+        assert not torch.isnan(o[0, :, 50:52]).any()
+        check_full(w, where=f"[masked nan {layout}]")
+
+
+def _guarded(shape_alloc, view_fn, dtype, n_guard=4096):
+    numel = int(np.prod(shape_alloc))
+    buf = torch.full((n_guard + numel + n_guard,), float("nan"), dtype=dtype, device="cuda")
+    inner = buf[n_guard:n_guard + numel].view(*shape_alloc)
+    return buf, view_fn(inner)
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+def test_guard_bands_untouched(layout):
+    """out and final_states live inside NaN-filled buffers: everything outside the
+    views must be untouched (elements are written exactly once, in place)."""
+    B, C, L, K = 2, 72, 1037, 4
+    w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype="bf16", layout=layout, bias=True, init=True,
+                     final=True, activation="silu", seed=6)
+    kw = gpu_args(w)
+    dt = kw["x"].dtype
+    if layout == "cf":
+        obuf, out = _guarded((B, C + 2, L + 8), lambda t: t[:, 1:1 + C, :L], dt)
+    else:
+        obuf, out = _guarded((B, L, C + 8), lambda t: t[:, :, :C].transpose(1, 2), dt)
+    fbuf, fs = _guarded((B, K - 1, C + 4), lambda t: t[:, :, 2:2 + C].transpose(1, 2), dt)
+    snap_o, snap_f = obuf.clone(), fbuf.clone()
+    out_r, fs_r = ccv.causal_conv1d_fwd(out=out, final_states_out=fs, **kw)
+    torch.cuda.synchronize()
+    assert out_r.data_ptr() == out.data_ptr() and fs_r.data_ptr() == fs.data_ptr()
+    mask_o = torch.ones_like(obuf, dtype=torch.bool)
+    mask_o[out.storage_offset() + torch.as_strided(torch.arange(obuf.numel(), device="cuda"),
+                                                   out.shape, out.stride(), 0).reshape(-1)] = False
+    assert bits_equal(obuf[mask_o].cpu(), snap_o[mask_o].cpu()), "write outside out"
+    mask_f = torch.ones_like(fbuf, dtype=torch.bool)
+    mask_f[fs.storage_offset() + torch.as_strided(torch.arange(fbuf.numel(), device="cuda"),
+                                                  fs.shape, fs.stride(), 0).reshape(-1)] = False
+    assert bits_equal(fbuf[mask_f].cpu(), snap_f[mask_f].cpu()), "write outside final_states"
+    y, s = oracle_case(w).fwd()
+    assert_close(w, out.cpu().contiguous(), y, s)
+    assert_final_states(w, fs.cpu().contiguous())
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+def test_unused_channels_poisoned(layout):
+    """Every storage element outside the view is NaN; a read outside the view would
+    poison an output."""
+    w = wl.make_case(B=2, C=100, L=900, K=4, x_dtype="bf16", layout=layout, bias=True,
+                     c_pad=28, c_off=0 if layout == "cl" else 5, t_pad=16, t_off=8,
+                     init=True, final=True, activation="silu", seed=7, poison_unused=True)
+    res = check_full(w, where="[poisoned]")
+    assert res["n_bad"] == 0
+
+
+def test_repeat_runs_bit_identical():
+    for layout in ("cf", "cl"):
+        w = wl.make_case(B=2, C=300, L=3000, K=4, x_dtype="bf16", layout=layout, bias=True,
+                         activation="silu", seed=8)
+        a, _ = run_gpu(w)
+        for _ in range(3):
+            b, _ = run_gpu(w)
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_chunking_bit_exact(dtype, layout):
+    """run([x1 | x2]) == run(x1) -> final_states -> run(x2, initial_states=...),
+    bit for bit, for split points at and around the history length and the
+    kernels' segment / tile sizes."""
+    K = 4
+    B, C, L = 2, 136, 3000
+    w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype=dtype, layout=layout, bias=True, init=True,
+                     final=True, activation="silu", seed=10)
+    kw = gpu_args(w)
+    full, fs_full = ccv.causal_conv1d_fwd(**kw)
+    for L1 in (0, 1, K - 2, K - 1, K, 63, 64, 65, 511, 513, 1024, 2047, 2049, L):
+        k1 = dict(kw, x=kw["x"][:, :, :L1])
+        o1, f1 = ccv.causal_conv1d_fwd(**k1)
+        k2 = dict(kw, x=kw["x"][:, :, L1:], initial_states=f1)
+        o2, f2 = ccv.causal_conv1d_fwd(**k2)
+        torch.cuda.synchronize()
+        assert bits_equal(torch.cat([o1, o2], dim=2).cpu(), full.cpu()), L1
+        assert torch.equal(f2.cpu().view(torch.int16 if dtype != "f32" else torch.int32),
+                           fs_full.cpu().view(torch.int16 if dtype != "f32" else torch.int32)), L1
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+def test_packed_equals_separate(layout):
+    lengths = [1, 2, 3, 4, 5, 64, 65, 300, 511, 2, 1000]
+    L = sum(lengths)
+    w = wl.make_case(B=1, C=96, L=L, K=4, x_dtype="bf16", layout=layout, bias=True,
+                     activation="silu", seq_lengths=lengths, seed=11)
+    kw = gpu_args(w)
+    packed = ccv.causal_conv1d_fwd(**kw)
+    pos = 0
+    for n in lengths:
+        part = ccv.causal_conv1d_fwd(**dict(kw, x=kw["x"][:, :, pos:pos + n], seq_idx=None))
+        torch.cuda.synchronize()
+        assert bits_equal(packed[:, :, pos:pos + n].cpu(), part.cpu()), (pos, n)
+        pos += n
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_channel_first_equals_channel_last(dtype):
+    """Both kernels take the terms in the same order, so they agree bit for bit."""
+    w = wl.make_case(B=2, C=200, L=2500, K=4, x_dtype=dtype, layout="cf", bias=True, init=True,
+                     final=True, activation="silu", seed=12)
+    kw = gpu_args(w)
+    a, fa = ccv.causal_conv1d_fwd(**kw)
+    x_cl = kw["x"].transpose(1, 2).contiguous().transpose(1, 2)
+    b, fb = ccv.causal_conv1d_fwd(**dict(kw, x=x_cl))
+    assert ccv.plan_for(x=x_cl, weight=kw["weight"])["path"] == ccv.CCV_PATH_CHANNEL_LAST
+    torch.cuda.synchronize()
+    assert bits_equal(a.cpu(), b.cpu())
+    assert bits_equal(fa.cpu(), fb.cpu())
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+def test_element_path_equals_vector_path(layout, monkeypatch):
+    w = wl.make_case(B=2, C=136, L=1500, K=3, x_dtype="bf16", layout=layout, bias=True,
+                     init=True, final=True, activation="silu", seed=13)
+    kw = gpu_args(w)
+    assert ccv.plan_for(x=kw["x"], weight=kw["weight"])["vector"] == 1
+    a, fa = ccv.causal_conv1d_fwd(**kw)
+    monkeypatch.setenv("CCV_FORCE_SCALAR", "1")
+    assert ccv.plan_for(x=kw["x"], weight=kw["weight"])["vector"] == 0
+    b, fb = ccv.causal_conv1d_fwd(**kw)
+    torch.cuda.synchronize()
+    assert bits_equal(a.cpu(), b.cpu()) and bits_equal(fa.cpu(), fb.cpu())
+
+
+def test_channel_last_tile_sweep_bit_identical(monkeypatch):
+    w = wl.make_case(B=2, C=520, L=2000, K=4, x_dtype="f16", layout="cl", bias=True, init=True,
+                     final=True, activation="silu", seed=14)
+    kw = gpu_args(w)
+    ref, fref = ccv.causal_conv1d_fwd(**kw)
+    for tile in (4, 8, 13, 32, 100, 256, 4096):
+        monkeypatch.setenv("CCV_CL_TILE_T", str(tile))
+        o, f = ccv.causal_conv1d_fwd(**kw)
+        torch.cuda.synchronize()
+        assert bits_equal(o.cpu(), ref.cpu()) and bits_equal(f.cpu(), fref.cpu()), tile
+
+
+def test_noncontiguous_input_is_copied_and_reported():
+    w = wl.make_case(B=2, C=16, L=100, K=4, x_dtype="f32", layout="cf", seed=15)
+    x = w.x.cuda()
+    y = torch.empty(2, 16, 200, device="cuda")[:, :, ::2]
+    y.copy_(x)
+    info = {}
+    out = ccv.causal_conv1d_fwd(y, w.weight.cuda(), info=info)
+    assert info["x_copied"] is True
+    ref = ccv.causal_conv1d_fwd(x, w.weight.cuda())
+    torch.cuda.synchronize()
+    assert bits_equal(out.cpu(), ref.cpu())
+
+
+def test_argument_errors_raise():
+    x = torch.zeros(1, 4, 8, device="cuda")
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_fwd(x, torch.zeros(4, 5, device="cuda"))
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_fwd(x, torch.zeros(4, 4, device="cuda"), activation="relu")
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_fwd(x, torch.zeros(4, 4, device="cuda"),
+                              seq_idx=torch.zeros(1, 8, dtype=torch.int32, device="cuda"),
+                              return_final_states=True)

@@ -168,12 +168,17 @@ def make_case(*, B, C, L, K, x_dtype="f32", w_dtype=None, layout="cf", bias=True
     n = int(np.prod(shape))
     xs = draw(n, seed, X_ID, x_dist, x_scale).reshape(shape)
     if poison_unused and n:
-        mask = np.ones(shape, dtype=bool)
+        # every storage element outside the [B, C, L] window becomes NaN
         if layout == "cf":
-            mask[:, c_off:c_off + C, t_off:t_off + L] = False
+            xs[:, :c_off] = np.nan
+            xs[:, c_off + C:] = np.nan
+            xs[:, c_off:c_off + C, :t_off] = np.nan
+            xs[:, c_off:c_off + C, t_off + L:] = np.nan
         else:
-            mask[:, t_off:t_off + L, c_off:c_off + C] = False
-        xs[mask] = np.nan
+            xs[:, :t_off] = np.nan
+            xs[:, t_off + L:] = np.nan
+            xs[:, t_off:t_off + L, :c_off] = np.nan
+            xs[:, t_off:t_off + L, c_off + C:] = np.nan
     x_storage = to_storage(xs, x_dtype)
     x = _x_view(x_storage, layout, B, C, L, c_off, t_off)
     weight = to_storage(draw(C * K, seed, W_ID, "normal", math.sqrt(w_var)).reshape(C, K), w_dtype)
