@@ -30,7 +30,8 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
 
   const int lane = threadIdx.x & 63;
   const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
-  const int64_t item = (int64_t)g * kWavesPerGroup + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item = (int64_t)g * kWavesPerGroup + wave;
   if (item >= m.nwork) return;                      // whole wave leaves together
 
   const int64_t row = item / a.nseg;
@@ -45,56 +46,84 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
   const int32_t* __restrict__ sr = SEQ ? m.seq + b * L : nullptr;
 
   if (t0 < L) {
-    float w[K];
+    // Lane l's u-th vector starts at element t0 + (u*64 + l)*V.  A segment that lies
+    // wholly inside the row takes the straight-line path (the condition is the same
+    // for the whole wave): its U loads are issued first, before the parameter and
+    // history loads, so they are in flight together.
+    const bool fast = VEC && t0 + a.span <= L;
+    const raw* __restrict__ xl = xr + t0 + lane * V;
+    const int32_t* __restrict__ sl = SEQ ? sr + t0 + lane * V : nullptr;
+    u32x4 rv[U];
+    u32x4 sv[U][V / 4];
+    if (fast) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) w[k] = load_param(m.w, m.w_dtype, c * K + k);
+      for (int u = 0; u < U; ++u) rv[u] = load16(xl + u * 64 * V);
+      if constexpr (SEQ) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < V / 4; ++q) sv[u][q] = load16(sl + u * 64 * V + 4 * q);
+      }
+    }
+
+    float w[K];
+    load_params<K>(m.w, m.w_dtype, c * K, w);
     const float beta = m.bias ? load_param(m.bias, m.w_dtype, c) : 0.0f;
 
     // History for lane 0 of the segment's first vector: X~[t0-K+1 .. t0-1].
     float carry[K - 1];
     int carry_id[K - 1];
+    if (t0 >= K - 1) {                               // inside the row: K-1 plain loads
 #pragma unroll
-    for (int j = 0; j < K - 1; ++j) {
-      const int64_t src = t0 - (K - 1) + j;
-      if (src >= 0) {
-        carry[j] = S::to_f(xr[src]);
-      } else if (m.init) {
-        carry[j] = S::to_f(static_cast<const raw*>(m.init)[b * m.is_b + c * m.is_c + (src + K - 1) * m.is_i]);
-      } else {
-        carry[j] = 0.0f;
+      for (int j = 0; j < K - 1; ++j) {
+        carry[j] = S::to_f(xr[t0 - (K - 1) + j]);
+        carry_id[j] = SEQ ? sr[t0 - (K - 1) + j] : 0;
       }
-      carry_id[j] = (SEQ && src >= 0) ? sr[src] : 0;
+    } else {
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) {
+        const int64_t src = t0 - (K - 1) + j;
+        if (src >= 0) {
+          carry[j] = S::to_f(xr[src]);
+        } else if (m.init) {
+          carry[j] = S::to_f(static_cast<const raw*>(m.init)[b * m.is_b + c * m.is_c + (src + K - 1) * m.is_i]);
+        } else {
+          carry[j] = 0.0f;
+        }
+        carry_id[j] = (SEQ && src >= 0) ? sr[src] : 0;
+      }
     }
     // With seq_idx a source left of t = 0 has no id and never counts.
     bool first_ok[K - 1];
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) first_ok[j] = !(SEQ && lane == 0 && t0 - (K - 1) + j < 0);
 
-    // Issue every load of the segment before any arithmetic.
     float e[U][V];
     int id[U][V];
-    const int64_t v0 = t0 / V;                      // first vector of the segment
+    if (fast) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t te = (v0 + u * 64 + lane) * V;  // first element of this lane's vector
-      if (VEC && te + V <= L) {
-        S::unpack(load16(xr + te), e[u]);
-        if constexpr (SEQ) {
-          const u32x4 s0 = load16(sr + te);
+      for (int u = 0; u < U; ++u) S::unpack(rv[u], e[u]);
+      if constexpr (SEQ) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) id[u][i] = (int)s0[i];
-          if constexpr (V == 8) {
-            const u32x4 s1 = load16(sr + te + 4);
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) id[u][4 + i] = (int)s1[i];
-          }
+          for (int q = 0; q < V / 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) id[u][4 * q + i] = (int)dword(sv[u][q], i);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t te = t0 + (int64_t)(u * 64 + lane) * V;
+        if (VEC && te + V <= L) {
+          S::unpack(load16(xr + te), e[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < V; ++i) e[u][i] = te + i < L ? S::to_f(xr[te + i]) : 0.0f;
         }
-      } else {
+        if constexpr (SEQ) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-          const bool in = te + i < L;
-          e[u][i] = in ? S::to_f(xr[te + i]) : 0.0f;
-          if constexpr (SEQ) id[u][i] = in ? sr[te + i] : 0;
+          for (int i = 0; i < V; ++i) id[u][i] = te + i < L ? sr[te + i] : 0;
         }
       }
     }
@@ -134,13 +163,17 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
         y[i] = SILU ? silu(acc) : acc;
       }
 
-      const int64_t te = (v0 + u * 64 + lane) * V;
-      if (VEC && te + V <= L) {
-        store16(orow + te, S::pack(y));
+      if (fast) {
+        store16(orow + t0 + (int64_t)(u * 64 + lane) * V, S::pack(y));
       } else {
+        const int64_t te = t0 + (int64_t)(u * 64 + lane) * V;
+        if (VEC && te + V <= L) {
+          store16(orow + te, S::pack(y));
+        } else {
 #pragma unroll
-        for (int i = 0; i < V; ++i)
-          if (te + i < L) orow[te + i] = S::from_f(y[i]);
+          for (int i = 0; i < V; ++i)
+            if (te + i < L) orow[te + i] = S::from_f(y[i]);
+        }
       }
     }
   }

@@ -31,7 +31,8 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
 
   const int lane = threadIdx.x & 63;
   const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
-  const int64_t item = (int64_t)g * kWavesPerGroup + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item = (int64_t)g * kWavesPerGroup + wave;
   if (item >= m.nwork) return;                      // whole wave leaves together
 
   const int64_t tt = item % a.ntt;
@@ -42,6 +43,8 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
   const int64_t c0 = cg * (64 * V) + lane * V;      // this lane's first channel
   const int nch = (int)(m.C - c0 < V ? (m.C - c0 > 0 ? m.C - c0 : 0) : V);
   const bool full = VEC && nch == V;
+  // Every lane of the wave holds a whole aligned vector (same value for the wave).
+  const bool wave_full = VEC && (cg + 1) * (64 * V) <= m.C;
   const int64_t t0 = tt * a.tile;
   const int64_t t1 = (t0 + a.tile < L) ? t0 + a.tile : L;
 
@@ -52,12 +55,20 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
 
   if (t0 < t1) {
     float w[V][K], beta[V];
+    if (nch == V) {
+      load_params<V * K>(m.w, m.w_dtype, c0 * K, &w[0][0]);
+      if (m.bias) load_params<V>(m.bias, m.w_dtype, c0, beta);
+      else
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const bool in = i < nch;
+        for (int i = 0; i < V; ++i) beta[i] = 0.0f;
+    } else {
 #pragma unroll
-      for (int k = 0; k < K; ++k) w[i][k] = in ? load_param(m.w, m.w_dtype, (c0 + i) * K + k) : 0.0f;
-      beta[i] = (in && m.bias) ? load_param(m.bias, m.w_dtype, c0 + i) : 0.0f;
+      for (int i = 0; i < V; ++i) {
+        const bool in = i < nch;
+#pragma unroll
+        for (int k = 0; k < K; ++k) w[i][k] = in ? load_param(m.w, m.w_dtype, (c0 + i) * K + k) : 0.0f;
+        beta[i] = (in && m.bias) ? load_param(m.bias, m.w_dtype, c0 + i) : 0.0f;
+      }
     }
 
     // History rows X~[t0-H .. t0-1] for this lane's channels.
@@ -91,21 +102,36 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
     for (int64_t t = t0; t < t1; t += U) {
       float e[U][V];
       int id[U];
+      // A batch of U rows inside the tile, across a wave of whole vectors, takes the
+      // straight-line path: all U row loads are issued before any arithmetic.
+      const bool fast = wave_full && t + U <= t1;
+      if (fast) {
+        u32x4 rv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t tr = t + u;
-        if (tr < t1) {
-          if (full) {
-            S::unpack(load16(xb + tr * a.x_sl), e[u]);
+        for (int u = 0; u < U; ++u) rv[u] = load16(xb + (t + u) * a.x_sl);
+        if constexpr (SEQ) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) id[u] = sr[t + u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) S::unpack(rv[u], e[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t tr = t + u;
+          if (tr < t1) {
+            if (full) {
+              S::unpack(load16(xb + tr * a.x_sl), e[u]);
+            } else {
+#pragma unroll
+              for (int i = 0; i < V; ++i) e[u][i] = i < nch ? S::to_f(xb[tr * a.x_sl + i]) : 0.0f;
+            }
+            if constexpr (SEQ) id[u] = sr[tr];
           } else {
 #pragma unroll
-            for (int i = 0; i < V; ++i) e[u][i] = i < nch ? S::to_f(xb[tr * a.x_sl + i]) : 0.0f;
+            for (int i = 0; i < V; ++i) e[u][i] = 0.0f;
+            if constexpr (SEQ) id[u] = 0;
           }
-          if constexpr (SEQ) id[u] = sr[tr];
-        } else {
-#pragma unroll
-          for (int i = 0; i < V; ++i) e[u][i] = 0.0f;
-          if constexpr (SEQ) id[u] = 0;
         }
       }
 
@@ -129,7 +155,9 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
           }
           y[i] = SILU ? silu(acc) : acc;
         }
-        if (tr < t1) {
+        if (fast) {
+          store16(ob + tr * a.o_sl, S::pack(y));
+        } else if (tr < t1) {
           if (full) {
             store16(ob + tr * a.o_sl, S::pack(y));
           } else {

@@ -15,6 +15,25 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Element i of a 16-byte vector as a plain 32-bit value.  Never apply
+// __builtin_bit_cast to a vector subscript directly: clang reads element 0 for
+// every i when the operand is a vector-element lvalue.
+__device__ inline uint32_t dword(const u32x4 v, int i) {
+  const uint32_t w = v[i];
+  return w;
+}
+
+// The fp32 value itself, materialised in a register.  Before a down-convert this
+// keeps the compiler from fusing the last multiply (or FMA) with the conversion
+// into one mixed-precision instruction (v_fma_mixlo_*), which rounds the exact
+// product once to 16 bits instead of rounding it to fp32 first; the two differ in
+// about one output in 2^14, so fused and unfused code paths would disagree.
+// The empty asm statement emits no instruction.
+__device__ inline float as_f32(float v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 // ---- storage types: V elements fill one 16-byte vector ---------------------------
 
 struct F32 {
@@ -23,7 +42,7 @@ struct F32 {
   __device__ static inline float to_f(raw r) { return __builtin_bit_cast(float, r); }
   __device__ static inline void unpack(const u32x4 v, float* e) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = __builtin_bit_cast(float, v[i]);
+    for (int i = 0; i < 4; ++i) e[i] = __builtin_bit_cast(float, dword(v, i));
   }
   __device__ static inline u32x4 pack(const float* y) {
     u32x4 v;
@@ -43,21 +62,22 @@ struct BF16 {
   __device__ static inline void unpack(const u32x4 v, float* e) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      e[2 * i] = __builtin_bit_cast(float, v[i] << 16);
-      e[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+      const uint32_t w = dword(v, i);
+      e[2 * i] = __builtin_bit_cast(float, w << 16);
+      e[2 * i + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
     }
   }
   __device__ static inline u32x4 pack(const float* y) {
     u32x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f32x2 p = {y[2 * i], y[2 * i + 1]};
+      f32x2 p = {as_f32(y[2 * i]), as_f32(y[2 * i + 1])};
       v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
     }
     return v;
   }
   __device__ static inline raw from_f(float y) {
-    return __builtin_bit_cast(uint16_t, (__bf16)y);
+    return __builtin_bit_cast(uint16_t, (__bf16)as_f32(y));
   }
 };
 
@@ -69,7 +89,7 @@ struct F16 {
   __device__ static inline void unpack(const u32x4 v, float* e) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f32x2 p = __builtin_convertvector(__builtin_bit_cast(f16x2, v[i]), f32x2);
+      f32x2 p = __builtin_convertvector(__builtin_bit_cast(f16x2, dword(v, i)), f32x2);
       e[2 * i] = p[0];
       e[2 * i + 1] = p[1];
     }
@@ -78,12 +98,12 @@ struct F16 {
     u32x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f32x2 p = {y[2 * i], y[2 * i + 1]};
+      f32x2 p = {as_f32(y[2 * i]), as_f32(y[2 * i + 1])};
       v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
     }
     return v;
   }
-  __device__ static inline raw from_f(float y) { return __builtin_bit_cast(uint16_t, (_Float16)y); }
+  __device__ static inline raw from_f(float y) { return __builtin_bit_cast(uint16_t, (_Float16)as_f32(y)); }
 };
 
 // Weight / bias element of any storage dtype, widened exactly to fp32.
@@ -92,6 +112,26 @@ __device__ inline float load_param(const void* p, int dtype, int64_t i) {
   const uint16_t h = static_cast<const uint16_t*>(p)[i];
   if (dtype == CCV_DT_BF16) return __builtin_bit_cast(float, (uint32_t)h << 16);
   return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// n consecutive parameters starting at element i0, widened to fp32.  One branch
+// on the dtype, then n independent loads, so they are in flight together.
+template <int N>
+__device__ inline void load_params(const void* p, int dtype, int64_t i0, float* out) {
+  if (dtype == CCV_DT_F32) {
+    const float* q = static_cast<const float*>(p) + i0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) out[k] = q[k];
+  } else {
+    const uint16_t* q = static_cast<const uint16_t*>(p) + i0;
+    uint16_t h[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) h[k] = q[k];
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      out[k] = dtype == CCV_DT_BF16 ? __builtin_bit_cast(float, (uint32_t)h[k] << 16)
+                                    : (float)__builtin_bit_cast(_Float16, h[k]);
+  }
 }
 
 // SiLU on the fp32 accumulator: z * 1 / (1 + 2^(-z * log2(e))), with the hardware

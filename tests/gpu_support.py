@@ -81,8 +81,27 @@ def check_full(w, where=""):
     return res
 
 
-def bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
+class _Equal:
+    """Truthy when two tensors hold the same values (+0 == -0, NaN == NaN); its repr
+    names the first differing elements."""
+
+    def __init__(self, a: torch.Tensor, b: torch.Tensor):
+        a64, b64 = a.double(), b.double()
+        same = (a64 == b64) | (torch.isnan(a64) & torch.isnan(b64))
+        self.ok = bool(same.all())
+        self.detail = ""
+        if not self.ok:
+            bad = (~same).nonzero()[:6].tolist()
+            self.detail = f"{int((~same).sum())} differ; first at " + ", ".join(
+                f"{tuple(i)}: {a64[tuple(i)].item()!r} vs {b64[tuple(i)].item()!r}" for i in bad)
+
+    def __bool__(self):
+        return self.ok
+
+    def __repr__(self):
+        return self.detail or "equal"
+
+
+def bits_equal(a: torch.Tensor, b: torch.Tensor) -> "_Equal":
     """Same values, where +0 == -0 and NaN == NaN."""
-    a64, b64 = a.double(), b.double()
-    both_nan = torch.isnan(a64) & torch.isnan(b64)
-    return bool(((a64 == b64) | both_nan).all())
+    return _Equal(a, b)

@@ -148,6 +148,44 @@ def test_down_convert_rounds_to_nearest_even(dtype, layout):
     assert np.array_equal(raw(out), ref), "down-convert is not round-to-nearest-even"
 
 
+@pytest.mark.parametrize("force_scalar", [False, True])
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_one_hot_weight_copies_input_bits(dtype, layout, force_scalar, monkeypatch):
+    """w = e_k, no bias, no activation: out[t] = x~[t-K+1+k] exactly, so every path
+    (16-byte and element-wise) must reproduce the input bits, subnormals included."""
+    if force_scalar:
+        monkeypatch.setenv("CCV_FORCE_SCALAR", "1")
+    K, B, C, L = 4, 2, 256, 2100
+    w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype=dtype, layout=layout, bias=False, activation=None,
+                     init=True, final=True, seed=16)
+    tdt = wl.TORCH_DTYPES[dtype]
+    # every subnormal pattern of the format, both signs, tiled over the input
+    nbits = 16 if dtype != "f32" else 32
+    if nbits == 16:
+        mant = 1023 if dtype == "f16" else 127
+        pats = torch.arange(1, mant + 1, dtype=torch.int32)
+        pats = torch.cat([pats, pats | 0x8000]).to(torch.int16)
+        sub = pats.view(tdt)
+    else:
+        pats = torch.randint(1, 1 << 23, (4096,), generator=torch.Generator().manual_seed(1), dtype=torch.int32)
+        sub = torch.cat([pats, pats | (-(1 << 31))]).view(torch.float32)
+    n = B * C * L
+    vals = sub.repeat(n // sub.numel() + 1)[:n].reshape(B, C, L)
+    mix = torch.rand(B, C, L, generator=torch.Generator().manual_seed(2)) < 0.5
+    w.x.copy_(torch.where(mix, vals, w.x))
+    ext = torch.cat([w.initial_states, w.x], dim=2)
+    for k in range(K):
+        wt = torch.zeros(C, K)
+        wt[:, k] = 1
+        w.weight = wt.to(tdt)
+        out, fs = run_gpu(w)
+        ref = ext[:, :, k:k + L].contiguous()
+        iv = torch.int16 if nbits == 16 else torch.int32
+        diff = (out.view(iv) != ref.view(iv)).nonzero()[:5].tolist()
+        assert not diff, (k, [(i, out[tuple(i)].item(), ref[tuple(i)].item()) for i in diff])
+
+
 def test_nonfinite_values_propagate():
     for layout in ("cf", "cl"):
         w = wl.make_case(B=1, C=16, L=300, K=4, x_dtype="f32", layout=layout, bias=True,
@@ -252,7 +290,8 @@ def test_chunking_bit_exact(dtype, layout):
         k2 = dict(kw, x=kw["x"][:, :, L1:], initial_states=f1)
         o2, f2 = ccv.causal_conv1d_fwd(**k2)
         torch.cuda.synchronize()
-        assert bits_equal(torch.cat([o1, o2], dim=2).cpu(), full.cpu()), L1
+        eq = bits_equal(torch.cat([o1, o2], dim=2).cpu(), full.cpu())
+        assert eq, (L1, eq)
         assert torch.equal(f2.cpu().view(torch.int16 if dtype != "f32" else torch.int32),
                            fs_full.cpu().view(torch.int16 if dtype != "f32" else torch.int32)), L1
 
@@ -289,8 +328,10 @@ def test_channel_first_equals_channel_last(dtype):
 
 
 @pytest.mark.parametrize("layout", ["cf", "cl"])
-def test_element_path_equals_vector_path(layout, monkeypatch):
-    w = wl.make_case(B=2, C=136, L=1500, K=3, x_dtype="bf16", layout=layout, bias=True,
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_element_path_equals_vector_path(dtype, layout, monkeypatch):
+    """The 16-byte and the element-wise code paths round identically."""
+    w = wl.make_case(B=2, C=136, L=1504, K=3, x_dtype=dtype, layout=layout, bias=True,
                      init=True, final=True, activation="silu", seed=13)
     kw = gpu_args(w)
     assert ccv.plan_for(x=kw["x"], weight=kw["weight"])["vector"] == 1
@@ -299,7 +340,9 @@ def test_element_path_equals_vector_path(layout, monkeypatch):
     assert ccv.plan_for(x=kw["x"], weight=kw["weight"])["vector"] == 0
     b, fb = ccv.causal_conv1d_fwd(**kw)
     torch.cuda.synchronize()
-    assert bits_equal(a.cpu(), b.cpu()) and bits_equal(fa.cpu(), fb.cpu())
+    eq = bits_equal(a.cpu(), b.cpu())
+    assert eq, eq
+    assert bits_equal(fa.cpu(), fb.cpu())
 
 
 def test_channel_last_tile_sweep_bit_identical(monkeypatch):
