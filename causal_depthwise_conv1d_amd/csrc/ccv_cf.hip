@@ -6,7 +6,7 @@
 // accumulator, one rounding at the store).
 //
 // Work split (rethought for wave64 rather than taken from the pages' 128-thread
-// blocks): one wave owns one time segment of one (b, c) row.  Lane l of the wave
+// blocks): a segment is 64 * V * U consecutive steps of one (b, c) row.  Lane l
 // holds 16-byte vectors number (l, l + 64, l + 128, ...) of the segment, so every
 // load and store instruction of the wave covers 1 KB of consecutive addresses.
 // Each output needs the K-1 inputs before its vector; they come from lane l-1 by
@@ -14,199 +14,349 @@
 // (v_readlane), or, for the segment's first vector, from memory just left of the
 // segment, initial_states, or zeros (Ch.5, section "Three kinds of boundary
 // handled separately").  Segments are independent, so long rows with few
-// channels still fill the GPU: the pages' design ties the block count to B*C
-// (Ch.5, section "Task split of the time-contiguous path"), which collapses for
-// long sequences with few channels.  There is no LDS and no barrier.
+// channels still fill the GPU, where the pages' design ties the block count to
+// B*C (Ch.5, section "Task split of the time-contiguous path").
+//
+// Wave w of the grid takes segments w, w + W, w + 2W, ... (W = waves launched):
+// at any moment the waves work on one compact window of the tensors, and each
+// wave issues all loads of its next segment (data, weights, bias, halo) before
+// the arithmetic of the current one.  x and out are streamed with non-temporal
+// loads and stores.  There is no LDS and no barrier.
 #include "ccv_device.hpp"
 
 namespace ccv {
 
-template <class S, int K, bool SILU, bool SEQ, bool VEC>
-__global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
-  constexpr int V = S::V;
-  constexpr int U = kCfUnroll;
-  using raw = typename S::raw;
-  const Common& m = a.m;
+// Zeros to load from where an operand is absent (no bias, history left of t = 0
+// without initial_states, no next segment), so that every load is unconditional.
+__device__ const uint32_t kZeroSrc[4] = {0u, 0u, 0u, 0u};
 
-  const int lane = threadIdx.x & 63;
-  const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t item = (int64_t)g * kWavesPerGroup + wave;
-  if (item >= m.nwork) return;                      // whole wave leaves together
+// Everything one whole segment needs, loaded ahead of its arithmetic: the lane's
+// U data vectors (and sequence ids), the channel's raw weights and bias, and the
+// raw history just left of the segment.  The loads are unconditional and go
+// straight into their registers; nothing is converted until the arithmetic, so
+// the compiler knows exactly how many memory operations are in flight and waits
+// only for the ones it needs.
+template <class S, int K, bool SEQ, int WB>
+struct SegLoads {
+  u32x4 d[kCfUnroll];
+  u32x4 sid[SEQ ? kCfUnroll : 1][S::V / 4];
+  uint32_t w[K];
+  uint32_t bias;
+  typename S::raw hist[K - 1];
+  int hist_id[K - 1];
+};
 
-  const int64_t row = item / a.nseg;
-  const int64_t seg = item - row * a.nseg;
+struct SegPos {
+  int64_t b, c, t0;
+};
+
+__device__ inline SegPos row_pos(const Common& m, int64_t row, int64_t t0) {
   const int64_t b = row / m.C;
-  const int64_t c = row - b * m.C;
-  const int64_t L = m.L;
-  const int64_t t0 = seg * a.span;
+  return SegPos{b, row - b * m.C, t0};
+}
 
-  const raw* __restrict__ xr = static_cast<const raw*>(m.x) + b * a.x_sb + c * a.x_sc;
-  raw* __restrict__ orow = static_cast<raw*>(m.out) + b * a.o_sb + c * a.o_sc;
-  const int32_t* __restrict__ sr = SEQ ? m.seq + b * L : nullptr;
+// Loads through global-address-space pointers made from integer addresses, and a
+// select of addresses without a branch: the prefetch below stays one straight
+// sequence of global loads.
+template <class T>
+__device__ inline T gload(uintptr_t addr) {
+  return *reinterpret_cast<const T __attribute__((address_space(1)))*>(addr);
+}
+__device__ inline u32x4 gload16_stream(uintptr_t addr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 __attribute__((address_space(1)))*>(addr));
+}
+__device__ inline uintptr_t pick(bool c, uintptr_t a, uintptr_t b) {
+  const uintptr_t mask = (uintptr_t)0 - (uintptr_t)c;
+  return (a & mask) | (b & ~mask);
+}
 
-  if (t0 < L) {
-    // Lane l's u-th vector starts at element t0 + (u*64 + l)*V.  A segment that lies
-    // wholly inside the row takes the straight-line path (the condition is the same
-    // for the whole wave): its U loads are issued first, before the parameter and
-    // history loads, so they are in flight together.
-    const bool fast = VEC && t0 + a.span <= L;
-    const raw* __restrict__ xl = xr + t0 + lane * V;
-    const int32_t* __restrict__ sl = SEQ ? sr + t0 + lane * V : nullptr;
-    u32x4 rv[U];
-    u32x4 sv[U][V / 4];
-    if (fast) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) rv[u] = load16(xl + u * 64 * V);
-      if constexpr (SEQ) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int q = 0; q < V / 4; ++q) sv[u][q] = load16(sl + u * 64 * V + 4 * q);
-      }
-    }
+// Raw weight / bias element: WB == 4 for fp32 parameters, 2 for bf16 / fp16.
+template <int WB>
+__device__ inline uint32_t load_param_raw(uintptr_t addr) {
+  if constexpr (WB == 4) return gload<uint32_t>(addr);
+  else return gload<uint16_t>(addr);
+}
 
-    float w[K];
-    load_params<K>(m.w, m.w_dtype, c * K, w);
-    const float beta = m.bias ? load_param(m.bias, m.w_dtype, c) : 0.0f;
-
-    // History for lane 0 of the segment's first vector: X~[t0-K+1 .. t0-1].
-    float carry[K - 1];
-    int carry_id[K - 1];
-    if (t0 >= K - 1) {                               // inside the row: K-1 plain loads
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) {
-        carry[j] = S::to_f(xr[t0 - (K - 1) + j]);
-        carry_id[j] = SEQ ? sr[t0 - (K - 1) + j] : 0;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) {
-        const int64_t src = t0 - (K - 1) + j;
-        if (src >= 0) {
-          carry[j] = S::to_f(xr[src]);
-        } else if (m.init) {
-          carry[j] = S::to_f(static_cast<const raw*>(m.init)[b * m.is_b + c * m.is_c + (src + K - 1) * m.is_i]);
-        } else {
-          carry[j] = 0.0f;
-        }
-        carry_id[j] = (SEQ && src >= 0) ? sr[src] : 0;
-      }
-    }
-    // With seq_idx a source left of t = 0 has no id and never counts.
-    bool first_ok[K - 1];
-#pragma unroll
-    for (int j = 0; j < K - 1; ++j) first_ok[j] = !(SEQ && lane == 0 && t0 - (K - 1) + j < 0);
-
-    float e[U][V];
-    int id[U][V];
-    if (fast) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) S::unpack(rv[u], e[u]);
-      if constexpr (SEQ) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int q = 0; q < V / 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) id[u][4 * q + i] = (int)dword(sv[u][q], i);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t te = t0 + (int64_t)(u * 64 + lane) * V;
-        if (VEC && te + V <= L) {
-          S::unpack(load16(xr + te), e[u]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < V; ++i) e[u][i] = te + i < L ? S::to_f(xr[te + i]) : 0.0f;
-        }
-        if constexpr (SEQ) {
-#pragma unroll
-          for (int i = 0; i < V; ++i) id[u][i] = te + i < L ? sr[te + i] : 0;
-        }
-      }
-    }
-
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // Halo of this lane's vector: the last K-1 inputs of the previous vector.
-      float h[K - 1];
-      int hid[K - 1];
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) {
-        h[j] = shift_in(carry[j], e[u][V - (K - 1) + j]);
-        if constexpr (SEQ) hid[j] = shift_in(carry_id[j], id[u][V - (K - 1) + j]);
-      }
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) {
-        carry[j] = lane63(e[u][V - (K - 1) + j]);
-        if constexpr (SEQ) carry_id[j] = lane63(id[u][V - (K - 1) + j]);
-      }
-
-      float y[V];
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        float acc = beta;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const int j = i - (K - 1) + k;            // source offset inside the vector
-          const float xv = j >= 0 ? e[u][j] : h[K - 1 + j];
-          if constexpr (SEQ) {
-            const int sid = j >= 0 ? id[u][j] : hid[K - 1 + j];
-            const bool ok = (j >= 0 || u > 0 || first_ok[K - 1 + j]) && sid == id[u][i];
-            acc = ok ? __builtin_fmaf(w[k], xv, acc) : acc;
-          } else {
-            acc = __builtin_fmaf(w[k], xv, acc);
-          }
-        }
-        y[i] = SILU ? silu(acc) : acc;
-      }
-
-      if (fast) {
-        store16(orow + t0 + (int64_t)(u * 64 + lane) * V, S::pack(y));
-      } else {
-        const int64_t te = t0 + (int64_t)(u * 64 + lane) * V;
-        if (VEC && te + V <= L) {
-          store16(orow + te, S::pack(y));
-        } else {
-#pragma unroll
-          for (int i = 0; i < V; ++i)
-            if (te + i < L) orow[te + i] = S::from_f(y[i]);
-        }
-      }
-    }
-  }
-
-  // final_states: the segment holding t = L-1 (segment 0 when L == 0) copies the
-  // last K-1 extended inputs bit for bit (Ch.5, section "Three kinds of boundary
-  // handled separately").
-  if (m.fin && (L == 0 ? seg == 0 : (t0 <= L - 1 && L - 1 < t0 + a.span)) && lane < K - 1) {
-    const int64_t j = L - (K - 1) + lane;
-    raw v;
-    if (j >= 0) v = xr[j];
-    else if (m.init) v = static_cast<const raw*>(m.init)[b * m.is_b + c * m.is_c + (j + K - 1) * m.is_i];
-    else v = 0;
-    static_cast<raw*>(m.fin)[b * m.fs_b + c * m.fs_c + lane * m.fs_i] = v;
+template <int WB>
+__device__ inline float param_f32(uint32_t r, int dtype) {
+  if constexpr (WB == 4) {
+    return __builtin_bit_cast(float, r);
+  } else {
+    const float bf = __builtin_bit_cast(float, r << 16);
+    const float hf = (float)__builtin_bit_cast(_Float16, (uint16_t)r);
+    return dtype == CCV_DT_BF16 ? bf : hf;
   }
 }
 
-template <class S, int K, bool SILU, bool SEQ, bool VEC>
+// Issue the loads of whole segment p (when `valid`; otherwise harmless loads of
+// zeros, so the instruction stream is the same either way).
+template <class S, int K, bool SEQ, int WB>
+__device__ inline void issue_segment(const CfArgs& a, const SegPos& p, bool valid, int lane,
+                                     SegLoads<S, K, SEQ, WB>& q) {
+  constexpr int V = S::V;
+  constexpr int H = K - 1;
+  constexpr int ES = sizeof(typename S::raw);
+  using raw = typename S::raw;
+  const Common& m = a.m;
+  const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
+  const uintptr_t xrow = reinterpret_cast<uintptr_t>(m.x) + (p.b * a.x_sb + p.c * a.x_sc) * ES;
+  const uintptr_t srow = reinterpret_cast<uintptr_t>(m.seq) + p.b * m.L * 4;
+
+  const uintptr_t dbase = pick(valid, xrow + (p.t0 + lane * V) * ES, zero);
+  const uintptr_t dstep = valid ? 64 * V * ES : 0;
+#pragma unroll
+  for (int u = 0; u < kCfUnroll; ++u) q.d[u] = gload16_stream(dbase + u * dstep);
+  if constexpr (SEQ) {
+    const uintptr_t sbase = pick(valid, srow + (p.t0 + lane * V) * 4, zero);
+    const uintptr_t sstep = valid ? 64 * V * 4 : 0;
+    const uintptr_t squad = valid ? 16 : 0;
+#pragma unroll
+    for (int u = 0; u < kCfUnroll; ++u)
+#pragma unroll
+      for (int r = 0; r < V / 4; ++r) q.sid[u][r] = gload<u32x4>(sbase + u * sstep + r * squad);
+  }
+  const uintptr_t wbase = pick(valid, reinterpret_cast<uintptr_t>(m.w) + p.c * K * WB, zero);
+  const uintptr_t wstep = valid ? WB : 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) q.w[k] = load_param_raw<WB>(wbase + k * wstep);
+  q.bias = load_param_raw<WB>(pick(valid && m.bias, reinterpret_cast<uintptr_t>(m.bias) + p.c * WB, zero));
+  const uintptr_t irow = reinterpret_cast<uintptr_t>(m.init) + (p.b * m.is_b + p.c * m.is_c) * ES;
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const int64_t src = p.t0 - H + j;
+    const uintptr_t from_init = pick(m.init != nullptr, irow + (src + H) * m.is_i * ES, zero);
+    const uintptr_t from_x = xrow + src * ES;
+    q.hist[j] = gload<raw>(pick(valid, pick(src >= 0, from_x, from_init), zero));
+    if constexpr (SEQ)
+      q.hist_id[j] = gload<int32_t>(pick(valid && src >= 0, srow + src * 4, zero));
+    else
+      q.hist_id[j] = 0;
+  }
+}
+
+// One output vector per lane: the K-tap stencil on fp32 values (Ch.5, stencil
+// equation for z_i), SiLU, and the lane's halo carried in from lane-1 / `carry`.
+template <class S, int K, bool SILU, bool SEQ>
+__device__ inline void stencil_vector(const float (&e)[S::V], const int (&id)[S::V], float (&carry)[K - 1],
+                                      int (&carry_id)[K - 1], bool first_vec, const bool (&first_ok)[K - 1],
+                                      const float (&w)[K], float beta, float (&y)[S::V]) {
+  constexpr int V = S::V;
+  constexpr int H = K - 1;
+  float h[H];
+  int hid[H];
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    h[j] = shift_in(carry[j], e[V - H + j]);
+    if constexpr (SEQ) hid[j] = shift_in(carry_id[j], id[V - H + j]);
+  }
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    carry[j] = lane63(e[V - H + j]);
+    if constexpr (SEQ) carry_id[j] = lane63(id[V - H + j]);
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    float acc = beta;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int j = i - H + k;                       // source offset inside the vector
+      const float xv = j >= 0 ? e[j] : h[H + j];
+      if constexpr (SEQ) {
+        const int sid = j >= 0 ? id[j] : hid[H + j];
+        const bool ok = (j >= 0 || !first_vec || first_ok[H + j]) && sid == id[i];
+        acc = ok ? __builtin_fmaf(w[k], xv, acc) : acc;
+      } else {
+        acc = __builtin_fmaf(w[k], xv, acc);
+      }
+    }
+    y[i] = SILU ? silu(acc) : acc;
+  }
+}
+
+template <int K, bool SEQ>
+__device__ inline void first_flags(int64_t t0, int lane, bool (&first_ok)[K - 1]) {
+  // With seq_idx a source left of t = 0 has no id and never counts.
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) first_ok[j] = !(SEQ && lane == 0 && t0 - (K - 1) + j < 0);
+}
+
+// Arithmetic and stores of a whole segment from its prefetched loads.
+template <class S, int K, bool SILU, bool SEQ, int WB>
+__device__ inline void compute_whole(const CfArgs& a, const SegPos& p, int lane,
+                                     const SegLoads<S, K, SEQ, WB>& q) {
+  constexpr int V = S::V;
+  constexpr int H = K - 1;
+  using raw = typename S::raw;
+  const Common& m = a.m;
+  float w[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) w[k] = param_f32<WB>(q.w[k], m.w_dtype);
+  const float beta = param_f32<WB>(q.bias, m.w_dtype);
+  float carry[H];
+  int carry_id[H];
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    carry[j] = S::to_f(q.hist[j]);
+    carry_id[j] = q.hist_id[j];
+  }
+  bool first_ok[H];
+  first_flags<K, SEQ>(p.t0, lane, first_ok);
+  raw* __restrict__ ol = static_cast<raw*>(m.out) + p.b * a.o_sb + p.c * a.o_sc + p.t0 + lane * V;
+#pragma unroll
+  for (int u = 0; u < kCfUnroll; ++u) {
+    float e[V], y[V];
+    int id[V];
+    S::unpack(q.d[u], e);
+    if constexpr (SEQ) {
+#pragma unroll
+      for (int r = 0; r < V / 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) id[4 * r + i] = (int)dword(q.sid[u][r], i);
+    }
+    stencil_vector<S, K, SILU, SEQ>(e, id, carry, carry_id, u == 0, first_ok, w, beta, y);
+    store16_stream(ol + u * 64 * V, S::pack(y));
+  }
+}
+
+// A segment that is not whole (the row's last, ragged one) or not 16-byte
+// aligned: element loads and stores, bounds-checked against L.
+template <class S, int K, bool SILU, bool SEQ>
+__device__ inline void compute_partial(const CfArgs& a, const SegPos& p, int lane) {
+  constexpr int V = S::V;
+  constexpr int H = K - 1;
+  using raw = typename S::raw;
+  const Common& m = a.m;
+  const int64_t L = m.L;
+  const raw* __restrict__ xr = static_cast<const raw*>(m.x) + p.b * a.x_sb + p.c * a.x_sc;
+  raw* __restrict__ orow = static_cast<raw*>(m.out) + p.b * a.o_sb + p.c * a.o_sc;
+  const int32_t* __restrict__ sr = SEQ ? m.seq + p.b * L : nullptr;
+  float w[K];
+  load_params<K>(m.w, m.w_dtype, p.c * K, w);
+  const float beta = m.bias ? load_param(m.bias, m.w_dtype, p.c) : 0.0f;
+  float carry[H];
+  int carry_id[H];
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const int64_t src = p.t0 - H + j;
+    if (src >= 0) carry[j] = S::to_f(xr[src]);
+    else if (m.init)
+      carry[j] = S::to_f(static_cast<const raw*>(m.init)[p.b * m.is_b + p.c * m.is_c + (src + H) * m.is_i]);
+    else carry[j] = 0.0f;
+    carry_id[j] = (SEQ && src >= 0) ? sr[src] : 0;
+  }
+  bool first_ok[H];
+  first_flags<K, SEQ>(p.t0, lane, first_ok);
+#pragma unroll
+  for (int u = 0; u < kCfUnroll; ++u) {
+    const int64_t te = p.t0 + (int64_t)(u * 64 + lane) * V;
+    float e[V], y[V];
+    int id[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const bool in = te + i < L;
+      e[i] = in ? S::to_f(xr[te + i]) : 0.0f;
+      id[i] = (SEQ && in) ? sr[te + i] : 0;
+    }
+    stencil_vector<S, K, SILU, SEQ>(e, id, carry, carry_id, u == 0, first_ok, w, beta, y);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (te + i < L) orow[te + i] = S::from_f(y[i]);
+  }
+}
+
+// final_states of one row: the last K-1 extended inputs, bit for bit (Ch.5,
+// section "Three kinds of boundary handled separately").
+template <class S, int K>
+__device__ inline void final_states_row(const CfArgs& a, const SegPos& p, int lane) {
+  constexpr int H = K - 1;
+  using raw = typename S::raw;
+  const Common& m = a.m;
+  if (lane >= H) return;
+  const int64_t j = m.L - H + lane;
+  raw v;
+  if (j >= 0) v = static_cast<const raw*>(m.x)[p.b * a.x_sb + p.c * a.x_sc + j];
+  else if (m.init) v = static_cast<const raw*>(m.init)[p.b * m.is_b + p.c * m.is_c + (j + H) * m.is_i];
+  else v = 0;
+  static_cast<raw*>(m.fin)[p.b * m.fs_b + p.c * m.fs_c + lane * m.fs_i] = v;
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
+__global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
+  const Common& m = a.m;
+  const int lane = threadIdx.x & 63;
+  const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t w0 = (int64_t)g * kWavesPerGroup + wave;
+  if (w0 >= a.nwaves) return;                       // whole wave leaves together
+  const int64_t W = a.nwaves;
+  const int64_t rows = m.B * m.C;
+
+  // Phase 1: whole segments, two sets of loads in flight.  The next segment's
+  // loads are issued before the current segment's arithmetic; the body is
+  // written twice so the sets swap roles without register copies.
+  const int64_t nfull = VEC ? a.nfull : 0;
+  const int64_t n1 = rows * nfull;
+  if constexpr (VEC) if (w0 < n1) {
+    SegLoads<S, K, SEQ, WB> qa, qb;
+    int64_t i = w0;
+    SegPos pa = row_pos(m, i / nfull, (i % nfull) * a.span), pb;
+    issue_segment<S, K, SEQ, WB>(a, pa, true, lane, qa);
+    while (true) {
+      const int64_t i1 = i + W;
+      if (i1 >= n1) {                               // last segment of this wave
+        compute_whole<S, K, SILU, SEQ, WB>(a, pa, lane, qa);
+        break;
+      }
+      pb = row_pos(m, i1 / nfull, (i1 % nfull) * a.span);
+      issue_segment<S, K, SEQ, WB>(a, pb, true, lane, qb);
+      compute_whole<S, K, SILU, SEQ, WB>(a, pa, lane, qa);
+      const int64_t i2 = i1 + W;
+      if (i2 >= n1) {
+        compute_whole<S, K, SILU, SEQ, WB>(a, pb, lane, qb);
+        break;
+      }
+      pa = row_pos(m, i2 / nfull, (i2 % nfull) * a.span);
+      issue_segment<S, K, SEQ, WB>(a, pa, true, lane, qa);
+      compute_whole<S, K, SILU, SEQ, WB>(a, pb, lane, qb);
+      i = i2;
+    }
+  }
+
+  // Phase 2: the other segments (ragged tails, or all of them when unaligned).
+  const int64_t ntail = a.nseg - nfull;
+  const int64_t n2 = m.L > 0 ? rows * ntail : 0;
+  for (int64_t j = w0; j < n2; j += W) {
+    const int64_t row = j / ntail;
+    compute_partial<S, K, SILU, SEQ>(a, row_pos(m, row, (nfull + j % ntail) * a.span), lane);
+  }
+
+  // Phase 3: final states.
+  if (m.fin)
+    for (int64_t r = w0; r < rows; r += W) final_states_row<S, K>(a, row_pos(m, r, 0), lane);
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
 static int launch_one(const CfArgs& a, uint32_t grid, void* stream) {
   void* args[] = {const_cast<CfArgs*>(&a)};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_kernel<S, K, SILU, SEQ, VEC>),
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_kernel<S, K, SILU, SEQ, VEC, WB>),
                               dim3(grid), dim3(64 * kWavesPerGroup), args, 0,
                               static_cast<hipStream_t>(stream));
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC>
+static int launch_w(const CfArgs& a, uint32_t grid, void* st) {
+  return a.m.w_dtype == CCV_DT_F32 ? launch_one<S, K, SILU, SEQ, VEC, 4>(a, grid, st)
+                                   : launch_one<S, K, SILU, SEQ, VEC, 2>(a, grid, st);
 }
 
 template <class S, int K>
 static int launch_k(const CfArgs& a, bool silu, bool seq, bool vec, uint32_t grid, void* st) {
   if (silu) {
-    if (seq) return vec ? launch_one<S, K, true, true, true>(a, grid, st) : launch_one<S, K, true, true, false>(a, grid, st);
-    return vec ? launch_one<S, K, true, false, true>(a, grid, st) : launch_one<S, K, true, false, false>(a, grid, st);
+    if (seq) return vec ? launch_w<S, K, true, true, true>(a, grid, st) : launch_w<S, K, true, true, false>(a, grid, st);
+    return vec ? launch_w<S, K, true, false, true>(a, grid, st) : launch_w<S, K, true, false, false>(a, grid, st);
   }
-  if (seq) return vec ? launch_one<S, K, false, true, true>(a, grid, st) : launch_one<S, K, false, true, false>(a, grid, st);
-  return vec ? launch_one<S, K, false, false, true>(a, grid, st) : launch_one<S, K, false, false, false>(a, grid, st);
+  if (seq) return vec ? launch_w<S, K, false, true, true>(a, grid, st) : launch_w<S, K, false, true, false>(a, grid, st);
+  return vec ? launch_w<S, K, false, false, true>(a, grid, st) : launch_w<S, K, false, false, false>(a, grid, st);
 }
 
 template <class S>

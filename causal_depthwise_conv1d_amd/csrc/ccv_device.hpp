@@ -168,4 +168,12 @@ __device__ inline uint32_t xcd_order(uint32_t g, uint32_t q, uint32_t r) {
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 __device__ inline void store16(void* p, u32x4 v) { *static_cast<u32x4*>(p) = v; }
 
+// Streaming (non-temporal) 16-byte accesses for data touched once: x and out.
+__device__ inline u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+__device__ inline void store16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+}
+
 }  // namespace ccv

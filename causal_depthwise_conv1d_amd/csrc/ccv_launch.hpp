@@ -26,13 +26,19 @@ struct Common {
   int32_t w_dtype;
 };
 
-// Channel-first (s_L == 1 for x and out): a work item is one time segment of one
-// (b, c) row, `span` steps long.
+// Channel-first (s_L == 1 for x and out): a segment is `span` consecutive steps of
+// one (b, c) row; a row has `nseg` segments, of which the first `nfull` lie wholly
+// inside the row and take the 16-byte path (0 when the views are not aligned).
+// Wave w of the `nwaves` launched takes, in three phases, whole segments
+// w, w + nwaves, ... (numbered row by row), then the remaining partial segments,
+// then the final states of rows w, w + nwaves, ...
 struct CfArgs {
   Common m;
   int64_t x_sb, x_sc, o_sb, o_sc;
-  int64_t span;   // 64 lanes * V * U
-  int64_t nseg;   // segments per row
+  int64_t span;    // 64 lanes * V * U
+  int64_t nseg;    // segments per row
+  int64_t nfull;   // whole 16-byte segments per row
+  int64_t nwaves;  // waves launched
 };
 
 // Channel-last (s_C == 1 for x and out): a work item is `tile` time rows of one
