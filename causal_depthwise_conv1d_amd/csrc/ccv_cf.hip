@@ -26,10 +26,6 @@
 
 namespace ccv {
 
-// Zeros to load from where an operand is absent (no bias, history left of t = 0
-// without initial_states, no next segment), so that every load is unconditional.
-__device__ const uint32_t kZeroSrc[4] = {0u, 0u, 0u, 0u};
-
 // Everything one whole segment needs, loaded ahead of its arithmetic: the lane's
 // U data vectors (and sequence ids), the channel's raw weights and bias, and the
 // raw history just left of the segment.  The loads are unconditional and go
@@ -53,39 +49,6 @@ struct SegPos {
 __device__ inline SegPos row_pos(const Common& m, int64_t row, int64_t t0) {
   const int64_t b = row / m.C;
   return SegPos{b, row - b * m.C, t0};
-}
-
-// Loads through global-address-space pointers made from integer addresses, and a
-// select of addresses without a branch: the prefetch below stays one straight
-// sequence of global loads.
-template <class T>
-__device__ inline T gload(uintptr_t addr) {
-  return *reinterpret_cast<const T __attribute__((address_space(1)))*>(addr);
-}
-__device__ inline u32x4 gload16_stream(uintptr_t addr) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 __attribute__((address_space(1)))*>(addr));
-}
-__device__ inline uintptr_t pick(bool c, uintptr_t a, uintptr_t b) {
-  const uintptr_t mask = (uintptr_t)0 - (uintptr_t)c;
-  return (a & mask) | (b & ~mask);
-}
-
-// Raw weight / bias element: WB == 4 for fp32 parameters, 2 for bf16 / fp16.
-template <int WB>
-__device__ inline uint32_t load_param_raw(uintptr_t addr) {
-  if constexpr (WB == 4) return gload<uint32_t>(addr);
-  else return gload<uint16_t>(addr);
-}
-
-template <int WB>
-__device__ inline float param_f32(uint32_t r, int dtype) {
-  if constexpr (WB == 4) {
-    return __builtin_bit_cast(float, r);
-  } else {
-    const float bf = __builtin_bit_cast(float, r << 16);
-    const float hf = (float)__builtin_bit_cast(_Float16, (uint16_t)r);
-    return dtype == CCV_DT_BF16 ? bf : hf;
-  }
 }
 
 // Issue the loads of whole segment p (when `valid`; otherwise harmless loads of

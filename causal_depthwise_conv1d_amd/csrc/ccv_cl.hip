@@ -14,208 +14,381 @@
 // the channel-contiguous path reorganises": time tiles as independent blocks,
 // each reading its own left halo).  Since a lane already computes along time for
 // fixed channels, no LDS transpose is needed for either the loads or the stores.
-// seq_idx ids are shared by all channels of a time row, so the masks are
-// wave-uniform.
+//
+// Items are numbered with the channel group fastest, so the waves running at
+// one time read neighbouring 1 KB pieces of the same rows.  A whole tile of
+// whole channel vectors runs on a straight-line path: its parameter, history and
+// first row-batch loads are issued before any wait, and each next batch of rows
+// is issued before the current batch's arithmetic.  seq_idx ids are shared by all
+// channels of a row, so the masks are wave-uniform, and a batch whose window
+// holds one sequence skips the masking altogether.
 #include "ccv_device.hpp"
 
 namespace ccv {
 
-template <class S, int K, bool SILU, bool SEQ, bool VEC>
-__global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
+struct TilePos {
+  int64_t b, cg, tt;
+};
+
+__device__ inline TilePos tile_pos(const ClArgs& a, int64_t item) {
+  const int64_t cg = item % a.ncg;
+  const int64_t rest = item / a.ncg;
+  return TilePos{rest / a.ntt, cg, rest % a.ntt};
+}
+
+// The K-tap stencil (and SiLU) for one time row of this lane's V channels.
+// rows[k] is the extended input row t-H+k (k = K-1 is row t itself).
+template <class S, int K, bool SILU>
+__device__ inline void row_stencil(const float (&w)[S::V][K], const float (&beta)[S::V],
+                                   const float* const (&rows)[K], const bool (&keep)[K],
+                                   bool masked, float (&y)[S::V]) {
+#pragma unroll
+  for (int i = 0; i < S::V; ++i) {
+    float acc = beta[i];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (masked) acc = keep[k] ? __builtin_fmaf(w[i][k], rows[k][i], acc) : acc;
+      else acc = __builtin_fmaf(w[i][k], rows[k][i], acc);
+    }
+    y[i] = SILU ? silu(acc) : acc;
+  }
+}
+
+// ---- whole tiles: straight-line path ---------------------------------------------
+
+// Addresses are a wave-uniform base plus this lane's 32-bit offset, so the loads
+// and stores use the scalar-base addressing mode.
+template <class S, int K, bool SILU, bool SEQ, int WB>
+__device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
   constexpr int V = S::V;
   constexpr int U = kClUnroll;
   constexpr int H = K - 1;
-  static_assert(U >= H, "a batch of rows must cover the history window");
-  using raw = typename S::raw;
+  constexpr int ES = sizeof(typename S::raw);
+  constexpr int NWV = V * K * WB / 16;               // weight vectors per lane
+  constexpr int NBV = V * WB / 16;                   // bias vectors per lane
+  static_assert(U == 4 && U >= H, "a row batch is 4 rows and covers the history");
   const Common& m = a.m;
+  const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
+  const int64_t cbase = p.cg * (64 * V);             // the wave's first channel
+  const int64_t t0 = p.tt * a.tile;
+  const uint32_t lx = (uint32_t)lane * (V * ES);     // lane offset inside a row
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(m.x) + (p.b * a.x_sb + cbase) * ES;
+  const uintptr_t ob = reinterpret_cast<uintptr_t>(m.out) + (p.b * a.o_sb + cbase) * ES;
+  const uintptr_t xs = a.x_sl * ES, os = a.o_sl * ES;
+  const uintptr_t sr = reinterpret_cast<uintptr_t>(m.seq) + p.b * m.L * 4;
 
-  const int lane = threadIdx.x & 63;
-  const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t item = (int64_t)g * kWavesPerGroup + wave;
-  if (item >= m.nwork) return;                      // whole wave leaves together
-
-  const int64_t tt = item % a.ntt;
-  const int64_t rest = item / a.ntt;
-  const int64_t cg = rest % a.ncg;
-  const int64_t b = rest / a.ncg;
-  const int64_t L = m.L;
-  const int64_t c0 = cg * (64 * V) + lane * V;      // this lane's first channel
-  const int nch = (int)(m.C - c0 < V ? (m.C - c0 > 0 ? m.C - c0 : 0) : V);
-  const bool full = VEC && nch == V;
-  // Every lane of the wave holds a whole aligned vector (same value for the wave).
-  const bool wave_full = VEC && (cg + 1) * (64 * V) <= m.C;
-  const int64_t t0 = tt * a.tile;
-  const int64_t t1 = (t0 + a.tile < L) ? t0 + a.tile : L;
-
-  const raw* __restrict__ xb = static_cast<const raw*>(m.x) + b * a.x_sb + c0;
-  raw* __restrict__ ob = static_cast<raw*>(m.out) + b * a.o_sb + c0;
-  const raw* __restrict__ ib = static_cast<const raw*>(m.init);
-  const int32_t* __restrict__ sr = SEQ ? m.seq + b * L : nullptr;
-
-  if (t0 < t1) {
-    float w[V][K], beta[V];
-    if (nch == V) {
-      load_params<V * K>(m.w, m.w_dtype, c0 * K, &w[0][0]);
-      if (m.bias) load_params<V>(m.bias, m.w_dtype, c0, beta);
-      else
+  // Parameters and history first: waiting for them later leaves the row batches
+  // issued after them in flight.
+  u32x4 wv[NWV], bv[NBV];
+  const uintptr_t wl = reinterpret_cast<uintptr_t>(m.w) + cbase * K * WB;
+  const uint32_t lw = (uint32_t)lane * (V * K * WB);
 #pragma unroll
-        for (int i = 0; i < V; ++i) beta[i] = 0.0f;
-    } else {
+  for (int q = 0; q < NWV; ++q) wv[q] = gload<u32x4>(wl + q * 16 + lw);
+  const uintptr_t bl = pick(m.bias != nullptr, reinterpret_cast<uintptr_t>(m.bias) + cbase * WB, zero);
+  const uint32_t lb = (uint32_t)lane * (V * WB);
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const bool in = i < nch;
+  for (int q = 0; q < NBV; ++q) bv[q] = gload<u32x4>(bl + q * 16 + lb);
+  u32x4 hv[H];
+  const uintptr_t il = reinterpret_cast<uintptr_t>(m.init) + (p.b * m.is_b + cbase) * ES;
 #pragma unroll
-        for (int k = 0; k < K; ++k) w[i][k] = in ? load_param(m.w, m.w_dtype, (c0 + i) * K + k) : 0.0f;
-        beta[i] = (in && m.bias) ? load_param(m.bias, m.w_dtype, c0 + i) : 0.0f;
-      }
+  for (int j = 0; j < H; ++j) {
+    const uintptr_t from_x = xb + (t0 - H + j) * xs;
+    const uintptr_t from_init = pick(m.init != nullptr, il + j * m.is_i * ES, zero);
+    hv[j] = gload<u32x4>(pick(t0 >= H, from_x, from_init) + lx);
+  }
+  u32x4 hid_v = {0u, 0u, 0u, 0u};
+  if constexpr (SEQ) hid_v = gload<u32x4>(pick(t0 >= U, sr + (t0 - U) * 4, zero));
+
+  // Row batches: A holds the current batch, B the next one.
+  u32x4 ra[U], rb[U], ia = {0u, 0u, 0u, 0u}, ib = {0u, 0u, 0u, 0u};
+  auto issue = [&](int64_t t, u32x4 (&r)[U], u32x4& iv) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = gload16_stream(xb + (t + u) * xs + lx);
+    if constexpr (SEQ) iv = gload<u32x4>(sr + t * 4);
+  };
+  issue(t0, ra, ia);
+
+  // Convert parameters and history (waits for them only).
+  float w[V][K], beta[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int f = i * K + k;                       // element of the lane's weight block
+      const uint32_t r = WB == 4 ? dword(wv[f / 4], f % 4)
+                                 : (dword(wv[f / 8], (f / 2) % 4) >> (16 * (f % 2))) & 0xffffu;
+      w[i][k] = param_f32<WB>(r, m.w_dtype);
     }
-
-    // History rows X~[t0-H .. t0-1] for this lane's channels.
-    float h[H][V];
+    const uint32_t r = WB == 4 ? dword(bv[i / 4], i % 4)
+                               : (dword(bv[i / 8], (i / 2) % 4) >> (16 * (i % 2))) & 0xffffu;
+    beta[i] = param_f32<WB>(r, m.w_dtype);
+  }
+  // Sliding window of the last K rows as fp32: win[0] is the oldest.
+  float win[K][V];
 #pragma unroll
-    for (int j = 0; j < H; ++j) {
-      const int64_t src = t0 - H + j;
-      if (src >= 0) {
-        if (full) {
-          S::unpack(load16(xb + src * a.x_sl), h[j]);
-        } else {
+  for (int j = 0; j < H; ++j) S::unpack(hv[j], win[j + 1]);
+  // Ids of the window rows; rows left of t = 0 have none and never count.
+  int wid[K];
+  bool wok[K];
 #pragma unroll
-          for (int i = 0; i < V; ++i) h[j][i] = i < nch ? S::to_f(xb[src * a.x_sl + i]) : 0.0f;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-          h[j][i] = (ib && i < nch) ? S::to_f(ib[b * m.is_b + (c0 + i) * m.is_c + (src + H) * m.is_i]) : 0.0f;
-      }
-    }
-    // Sequence ids of the history rows (wave-uniform); rows left of t = 0 have none.
-    int hid[H];
-    bool hok[H];
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-      const int64_t src = t0 - H + j;
-      hok[j] = src >= 0;
-      hid[j] = (SEQ && src >= 0) ? sr[src] : 0;
-    }
-
-    for (int64_t t = t0; t < t1; t += U) {
-      float e[U][V];
-      int id[U];
-      // A batch of U rows inside the tile, across a wave of whole vectors, takes the
-      // straight-line path: all U row loads are issued before any arithmetic.
-      const bool fast = wave_full && t + U <= t1;
-      if (fast) {
-        u32x4 rv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) rv[u] = load16(xb + (t + u) * a.x_sl);
-        if constexpr (SEQ) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) id[u] = sr[t + u];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) S::unpack(rv[u], e[u]);
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t tr = t + u;
-          if (tr < t1) {
-            if (full) {
-              S::unpack(load16(xb + tr * a.x_sl), e[u]);
-            } else {
-#pragma unroll
-              for (int i = 0; i < V; ++i) e[u][i] = i < nch ? S::to_f(xb[tr * a.x_sl + i]) : 0.0f;
-            }
-            if constexpr (SEQ) id[u] = sr[tr];
-          } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i) e[u][i] = 0.0f;
-            if constexpr (SEQ) id[u] = 0;
-          }
-        }
-      }
-
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t tr = t + u;
-        float y[V];
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          float acc = beta[i];
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            const int r = u - H + k;                 // source row relative to this batch
-            const float xv = r >= 0 ? e[r][i] : h[H + r][i];
-            if constexpr (SEQ) {
-              const bool ok = r >= 0 ? (id[r] == id[u]) : (hok[H + r] && hid[H + r] == id[u]);
-              acc = ok ? __builtin_fmaf(w[i][k], xv, acc) : acc;
-            } else {
-              acc = __builtin_fmaf(w[i][k], xv, acc);
-            }
-          }
-          y[i] = SILU ? silu(acc) : acc;
-        }
-        if (fast) {
-          store16(ob + tr * a.o_sl, S::pack(y));
-        } else if (tr < t1) {
-          if (full) {
-            store16(ob + tr * a.o_sl, S::pack(y));
-          } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i)
-              if (i < nch) ob[tr * a.o_sl + i] = S::from_f(y[i]);
-          }
-        }
-      }
-
-      // Slide the history window: the last H rows of this batch become the history.
-#pragma unroll
-      for (int j = 0; j < H; ++j) {
-#pragma unroll
-        for (int i = 0; i < V; ++i) h[j][i] = e[U - H + j][i];
-        if constexpr (SEQ) {
-          hid[j] = id[U - H + j];
-          hok[j] = true;
-        }
-      }
-    }
+  for (int j = 0; j < H; ++j) {
+    wid[j + 1] = SEQ ? __builtin_amdgcn_readfirstlane((int)dword(hid_v, U - H + j)) : 0;
+    wok[j + 1] = t0 - H + j >= 0;
   }
 
-  // final_states: the tile holding t = L-1 (tile 0 when L == 0) copies the last
-  // K-1 extended inputs of its channels bit for bit (Ch.5, section "Three kinds
-  // of boundary handled separately").
-  if (m.fin && tt == a.ntt - 1) {
-    raw* __restrict__ fb = static_cast<raw*>(m.fin) + b * m.fs_b;
-    for (int i = 0; i < nch; ++i) {
+  auto compute = [&](int64_t t, const u32x4 (&r)[U], const u32x4& iv) {
+    int id[U];
+    bool masked = false;
+    if constexpr (SEQ) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) id[u] = __builtin_amdgcn_readfirstlane((int)dword(iv, u));
+      // One sequence across the whole window (history and batch): no masking.
+      bool one = true;
+#pragma unroll
+      for (int u = 1; u < U; ++u) one = one && id[u] == id[0];
+#pragma unroll
+      for (int j = 1; j < K; ++j) one = one && wok[j] && wid[j] == id[0];
+      masked = !one;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // Slide: drop the oldest row, append row t + u.
 #pragma unroll
       for (int j = 0; j < H; ++j) {
-        const int64_t src = L - H + j;
-        raw v;
-        if (src >= 0) v = xb[src * a.x_sl + i];
-        else if (ib) v = ib[b * m.is_b + (c0 + i) * m.is_c + (src + H) * m.is_i];
-        else v = 0;
-        fb[(c0 + i) * m.fs_c + j * m.fs_i] = v;
+#pragma unroll
+        for (int i = 0; i < V; ++i) win[j][i] = win[j + 1][i];
+        wid[j] = wid[j + 1];
+        wok[j] = wok[j + 1];
       }
+      S::unpack(r[u], win[H]);
+      wid[H] = SEQ ? id[u] : 0;
+      wok[H] = true;
+      const float* rows[K];
+      bool keep[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        rows[k] = win[k];
+        keep[k] = !SEQ || (wok[k] && wid[k] == wid[H]);
+      }
+      float y[V];
+      row_stencil<S, K, SILU>(w, beta, rows, keep, masked, y);
+      gstore16_stream(ob + (t + u) * os + lx, S::pack(y));
+    }
+  };
+
+  const int64_t nb = a.tile / U;
+  int64_t j = 0;
+  while (true) {
+    if (j + 1 >= nb) {
+      compute(t0 + j * U, ra, ia);
+      break;
+    }
+    issue(t0 + (j + 1) * U, rb, ib);
+    compute(t0 + j * U, ra, ia);
+    ++j;
+    if (j + 1 >= nb) {
+      compute(t0 + j * U, rb, ib);
+      break;
+    }
+    issue(t0 + (j + 1) * U, ra, ia);
+    compute(t0 + j * U, rb, ib);
+    ++j;
+  }
+}
+
+// ---- any tile: element-wise general path ---------------------------------------
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC>
+__device__ inline void tile_general(const ClArgs& a, const TilePos& p, int lane) {
+  constexpr int V = S::V;
+  constexpr int U = kClUnroll;
+  constexpr int H = K - 1;
+  using raw = typename S::raw;
+  const Common& m = a.m;
+  const int64_t L = m.L;
+  const int64_t c0 = p.cg * (64 * V) + lane * V;
+  const int nch = (int)(m.C - c0 < V ? (m.C - c0 > 0 ? m.C - c0 : 0) : V);
+  const bool full = VEC && nch == V;
+  const int64_t t0 = p.tt * a.tile;
+  const int64_t t1 = (t0 + a.tile < L) ? t0 + a.tile : L;
+  if (t0 >= t1) return;
+
+  const raw* __restrict__ xb = static_cast<const raw*>(m.x) + p.b * a.x_sb + c0;
+  raw* __restrict__ ob = static_cast<raw*>(m.out) + p.b * a.o_sb + c0;
+  const raw* __restrict__ ib = static_cast<const raw*>(m.init);
+  const int32_t* __restrict__ sr = SEQ ? m.seq + p.b * L : nullptr;
+
+  float w[V][K], beta[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const bool in = i < nch;
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[i][k] = in ? load_param(m.w, m.w_dtype, (c0 + i) * K + k) : 0.0f;
+    beta[i] = (in && m.bias) ? load_param(m.bias, m.w_dtype, c0 + i) : 0.0f;
+  }
+
+  // History rows X~[t0-H .. t0-1] for this lane's channels.
+  float hist[H][V];
+  int hid[H];
+  bool hok[H];
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const int64_t src = t0 - H + j;
+    if (src >= 0) {
+      if (full) {
+        S::unpack(load16(xb + src * a.x_sl), hist[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) hist[j][i] = i < nch ? S::to_f(xb[src * a.x_sl + i]) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        hist[j][i] = (ib && i < nch) ? S::to_f(ib[p.b * m.is_b + (c0 + i) * m.is_c + (src + H) * m.is_i]) : 0.0f;
+    }
+    hok[j] = src >= 0;                               // rows left of t = 0 have no id
+    hid[j] = (SEQ && src >= 0) ? sr[src] : 0;
+  }
+
+  for (int64_t t = t0; t < t1; t += U) {
+    float e[U][V];
+    int id[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tr = t + u;
+      if (tr < t1) {
+        if (full) {
+          S::unpack(load16(xb + tr * a.x_sl), e[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < V; ++i) e[u][i] = i < nch ? S::to_f(xb[tr * a.x_sl + i]) : 0.0f;
+        }
+        id[u] = SEQ ? sr[tr] : 0;
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) e[u][i] = 0.0f;
+        id[u] = 0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tr = t + u;
+      const float* rows[K];
+      bool keep[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int rr = u - H + k;
+        rows[k] = rr >= 0 ? e[rr] : hist[H + rr];
+        keep[k] = !SEQ || (rr >= 0 ? id[rr] == id[u] : (hok[H + rr] && hid[H + rr] == id[u]));
+      }
+      float y[V];
+      row_stencil<S, K, SILU>(w, beta, rows, keep, SEQ, y);
+      if (tr < t1) {
+        if (full) {
+          store16(ob + tr * a.o_sl, S::pack(y));
+        } else {
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+            if (i < nch) ob[tr * a.o_sl + i] = S::from_f(y[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) hist[j][i] = e[U - H + j][i];
+      hid[j] = id[U - H + j];
+      hok[j] = true;
     }
   }
 }
 
-template <class S, int K, bool SILU, bool SEQ, bool VEC>
+// final_states of one (batch, channel group): the last K-1 extended inputs of the
+// lane's channels, bit for bit (Ch.5, section "Three kinds of boundary handled
+// separately").
+template <class S, int K>
+__device__ inline void final_states_group(const ClArgs& a, int64_t b, int64_t cg, int lane) {
+  constexpr int V = S::V;
+  constexpr int H = K - 1;
+  using raw = typename S::raw;
+  const Common& m = a.m;
+  const int64_t L = m.L;
+  const int64_t c0 = cg * (64 * V) + lane * V;
+  const int nch = (int)(m.C - c0 < V ? (m.C - c0 > 0 ? m.C - c0 : 0) : V);
+  const raw* __restrict__ xb = static_cast<const raw*>(m.x) + b * a.x_sb + c0;
+  const raw* __restrict__ ib = static_cast<const raw*>(m.init);
+  raw* __restrict__ fb = static_cast<raw*>(m.fin) + b * m.fs_b;
+  for (int i = 0; i < nch; ++i) {
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const int64_t src = L - H + j;
+      raw v;
+      if (src >= 0) v = xb[src * a.x_sl + i];
+      else if (ib) v = ib[b * m.is_b + (c0 + i) * m.is_c + (src + H) * m.is_i];
+      else v = 0;
+      fb[(c0 + i) * m.fs_c + j * m.fs_i] = v;
+    }
+  }
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
+__global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
+  constexpr int V = S::V;
+  const Common& m = a.m;
+  const int lane = threadIdx.x & 63;
+  const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t w0 = (int64_t)g * kWavesPerGroup + wave;
+  if (w0 >= a.nwaves) return;                       // whole wave leaves together
+  const int64_t W = a.nwaves;
+  // The straight-line path exists when a lane's weight and bias blocks are whole
+  // 16-byte vectors.
+  constexpr bool kFastShape = (V * K * WB) % 16 == 0 && (V * WB) % 16 == 0;
+
+  if (m.L > 0) {
+    for (int64_t it = w0; it < m.nwork; it += W) {
+      const TilePos p = tile_pos(a, it);
+      if constexpr (VEC && kFastShape) {
+        const int64_t t0 = p.tt * a.tile;
+        const bool fast = a.vec_par && (a.tile % kClUnroll) == 0 && (p.cg + 1) * (64 * V) <= m.C &&
+                          t0 + a.tile <= m.L &&
+                          (t0 >= K - 1 || m.init == nullptr || a.vec_init) && (!SEQ || a.vec_seq);
+        if (fast) {
+          tile_fast<S, K, SILU, SEQ, WB>(a, p, lane);
+          continue;
+        }
+      }
+      tile_general<S, K, SILU, SEQ, VEC>(a, p, lane);
+    }
+  }
+  if (m.fin) {
+    const int64_t pairs = m.B * a.ncg;
+    for (int64_t r = w0; r < pairs; r += W) final_states_group<S, K>(a, r / a.ncg, r % a.ncg, lane);
+  }
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
 static int launch_one(const ClArgs& a, uint32_t grid, void* stream) {
   void* args[] = {const_cast<ClArgs*>(&a)};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cl_fwd_kernel<S, K, SILU, SEQ, VEC>),
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cl_fwd_kernel<S, K, SILU, SEQ, VEC, WB>),
                               dim3(grid), dim3(64 * kWavesPerGroup), args, 0,
                               static_cast<hipStream_t>(stream));
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC>
+static int launch_w(const ClArgs& a, uint32_t grid, void* st) {
+  return a.m.w_dtype == CCV_DT_F32 ? launch_one<S, K, SILU, SEQ, VEC, 4>(a, grid, st)
+                                   : launch_one<S, K, SILU, SEQ, VEC, 2>(a, grid, st);
 }
 
 template <class S, int K>
 static int launch_k(const ClArgs& a, bool silu, bool seq, bool vec, uint32_t grid, void* st) {
   if (silu) {
-    if (seq) return vec ? launch_one<S, K, true, true, true>(a, grid, st) : launch_one<S, K, true, true, false>(a, grid, st);
-    return vec ? launch_one<S, K, true, false, true>(a, grid, st) : launch_one<S, K, true, false, false>(a, grid, st);
+    if (seq) return vec ? launch_w<S, K, true, true, true>(a, grid, st) : launch_w<S, K, true, true, false>(a, grid, st);
+    return vec ? launch_w<S, K, true, false, true>(a, grid, st) : launch_w<S, K, true, false, false>(a, grid, st);
   }
-  if (seq) return vec ? launch_one<S, K, false, true, true>(a, grid, st) : launch_one<S, K, false, true, false>(a, grid, st);
-  return vec ? launch_one<S, K, false, false, true>(a, grid, st) : launch_one<S, K, false, false, false>(a, grid, st);
+  if (seq) return vec ? launch_w<S, K, false, true, true>(a, grid, st) : launch_w<S, K, false, true, false>(a, grid, st);
+  return vec ? launch_w<S, K, false, false, true>(a, grid, st) : launch_w<S, K, false, false, false>(a, grid, st);
 }
 
 template <class S>

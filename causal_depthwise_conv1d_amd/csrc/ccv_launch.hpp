@@ -41,14 +41,21 @@ struct CfArgs {
   int64_t nwaves;  // waves launched
 };
 
-// Channel-last (s_C == 1 for x and out): a work item is `tile` time rows of one
-// group of 64 * V channels of one batch.
+// Channel-last (s_C == 1 for x and out): a work item is a tile of `tile` time
+// rows of one group of 64 * V channels of one batch; items are numbered with the
+// channel group fastest, then the time tile, then the batch.  Wave w of the
+// `nwaves` launched takes items w, w + nwaves, ..., then writes the final states
+// of (batch, channel group) pairs w, w + nwaves, ...
 struct ClArgs {
   Common m;
   int64_t x_sb, x_sl, o_sb, o_sl;
-  int64_t tile;   // time rows per work item
-  int64_t ntt;    // time tiles per (b, channel group)
-  int64_t ncg;    // channel groups
+  int64_t tile;      // time rows per work item (a multiple of the row batch)
+  int64_t ntt;       // time tiles per (b, channel group)
+  int64_t ncg;       // channel groups
+  int64_t nwaves;    // waves launched
+  int32_t vec_init;  // initial_states rows load as aligned 16-byte channel vectors
+  int32_t vec_seq;   // seq_idx rows load as aligned 16-byte vectors of 4 ids
+  int32_t vec_par;   // weight and bias blocks of a lane load as aligned 16-byte vectors
 };
 
 // Launch one kernel instance; returns a hipError_t value (0 = success).
