@@ -247,9 +247,12 @@ template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
 __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
   const Common& m = a.m;
   const int lane = threadIdx.x & 63;
-  const uint32_t g = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
+  // Workgroups keep the hardware's numbering: rows share only a K-1 step halo
+  // between segments, and dealing consecutive segments to all 8 XCDs at once
+  // spreads the concurrent streams over more memory channels than giving each
+  // XCD one contiguous range does.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t w0 = (int64_t)g * kWavesPerGroup + wave;
+  const int64_t w0 = (int64_t)blockIdx.x * kWavesPerGroup + wave;
   if (w0 >= a.nwaves) return;                       // whole wave leaves together
   const int64_t W = a.nwaves;
   const int64_t rows = m.B * m.C;

@@ -22,7 +22,7 @@ struct Common {
   int64_t is_b, is_c, is_i;   // initial_states strides
   int64_t fs_b, fs_c, fs_i;   // final_states strides
   int64_t nwork;              // wave work items
-  uint32_t xcd_q, xcd_r;      // workgroups per XCD (quotient / remainder of G / 8)
+  uint32_t xcd_q, xcd_r;      // workgroups per XCD (quotient / remainder of G / 8); channel-last only
   int32_t w_dtype;
 };
 
