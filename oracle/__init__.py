@@ -65,6 +65,9 @@ def _load(path):
     L.ora_fwd.argtypes = [P, vp, vp]
     L.ora_points.argtypes = [P, i64, vp, vp, vp]
     L.ora_final_states.argtypes = [P, vp]
+    L.ora_point_f32.argtypes = [P, i64, i64, i64, ctypes.POINTER(ctypes.c_float)]
+    L.ora_fwd_f32.argtypes = [P, vp]
+    L.ora_points_f32.argtypes = [P, i64, vp, vp]
     L.ora_round_out.argtypes = [ctypes.c_int32, vp, i64, vp]
     L.ora_f64_to_f32.argtypes = [ctypes.c_double]
     L.ora_f64_to_f32.restype = ctypes.c_float
@@ -173,6 +176,24 @@ class Case:
                             s.ctypes.data) != 0:
             raise IndexError("sample index out of range")
         return y, s
+
+    def fwd_f32(self):
+        """Diagnostic binary32 mode for every output, [B, C, L] float32: the stencil
+        summed with one fused multiply-add per kept term, bias first, k ascending;
+        no activation."""
+        z = np.empty(self.B * self.C * self.L, dtype=np.float32)
+        if lib().ora_fwd_f32(ctypes.byref(self._p), z.ctypes.data) != 0:
+            raise RuntimeError("ora_fwd_f32 failed")
+        return z.reshape(self.B, self.C, self.L)
+
+    def points_f32(self, idx):
+        """Diagnostic binary32 mode at n sampled (b, c, t) triples."""
+        idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1, 3))
+        z = np.empty(idx.shape[0], dtype=np.float32)
+        if lib().ora_points_f32(ctypes.byref(self._p), idx.shape[0], idx.ctypes.data,
+                                z.ctypes.data) != 0:
+            raise IndexError("sample index out of range")
+        return z
 
     def final_states(self):
         """Raw storage [B, C, K-1] of the last K-1 extended inputs."""

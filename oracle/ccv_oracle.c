@@ -231,3 +231,45 @@ int ora_final_states(const ora_problem_t* p, void* fs) {
       }
   return 0;
 }
+
+/* ---- diagnostic binary32 mode ------------------------------------------------ */
+
+/* The same stencil (same extended input, same dropped terms) evaluated as a
+ * binary32 accumulation with fused multiply-adds: acc starts at the bias (zero
+ * without one) and takes acc = fmaf(w[c,k], X~, acc) for the kept terms in
+ * ascending k, each step rounded once.  Every stored value is exact in binary32,
+ * so only the K roundings of the running sum differ from the fp64 result.  No
+ * activation.  A diagnostic, not the parity reference: the pages fix only that
+ * the accumulation is fp32, not its order. */
+int ora_point_f32(const ora_problem_t* p, int64_t b, int64_t c, int64_t t, float* z) {
+  if (b < 0 || b >= p->B || c < 0 || c >= p->C || t < 0 || t >= p->L) return -1;
+  const int K = p->K;
+  float acc = 0.0f;
+  if (p->bias != NULL) acc = (float)ora_decode(p->bias, p->w_dtype, c);
+  for (int k = 0; k < K; ++k) {
+    int64_t src = t - K + 1 + k;
+    if (p->seq != NULL) {
+      if (src < 0) continue;
+      if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;
+    }
+    float wv = (float)ora_decode(p->w, p->w_dtype, c * K + k);
+    float xv = (float)ora_xt(p, b, c, src);
+    acc = fmaf(wv, xv, acc);
+  }
+  *z = acc;
+  return 0;
+}
+
+int ora_fwd_f32(const ora_problem_t* p, float* z) {
+  for (int64_t b = 0; b < p->B; ++b)
+    for (int64_t c = 0; c < p->C; ++c)
+      for (int64_t t = 0; t < p->L; ++t)
+        if (ora_point_f32(p, b, c, t, &z[(b * p->C + c) * p->L + t]) != 0) return -1;
+  return 0;
+}
+
+int ora_points_f32(const ora_problem_t* p, int64_t n, const int64_t* idx, float* z) {
+  for (int64_t i = 0; i < n; ++i)
+    if (ora_point_f32(p, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], &z[i]) != 0) return -1;
+  return 0;
+}

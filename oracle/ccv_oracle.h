@@ -89,6 +89,12 @@ void     ora_f32_to_f16_array(const float* in, uint16_t* out, int64_t n);
 void     ora_f16_to_f64_array(const uint16_t* in, double* out, int64_t n);
 void     ora_bf16_to_f64_array(const uint16_t* in, double* out, int64_t n);
 
+/* Diagnostic binary32 mode: acc = bias (or 0), then acc = fmaf(w[c,k], X~, acc)
+ * over the kept terms in ascending k; no activation.  Writes the binary32 sum. */
+int ora_point_f32(const ora_problem_t* p, int64_t b, int64_t c, int64_t t, float* z);
+int ora_fwd_f32(const ora_problem_t* p, float* z);            /* z[(b*C+c)*L+t] */
+int ora_points_f32(const ora_problem_t* p, int64_t n, const int64_t* idx, float* z);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,7 +8,9 @@ Each ``pin_*`` function raises AssertionError when the oracle disagrees with:
     (torch.nn.functional.conv1d in fp64 on the CPU, grouped by channel),
   * invariants the definition implies (chunking with carried states, packed
     sequences equal separate runs, layout independence, masked NaN not leaking),
-  * torch's own dtype conversions and SiLU.
+  * torch's own dtype conversions and SiLU,
+  * for the diagnostic binary32 mode: an exact-rational emulation of its
+    fused multiply-add chain, exactness on integer data, and the K-rounding bound.
 
 The functions take the ``oracle`` module so that ``test_oracle_mutants`` can run
 them against deliberately broken builds of the oracle.
@@ -352,6 +354,120 @@ def pin_round_out(ora):
                               ref.view(np.uint32 if dt == "f32" else np.uint16)), dt
 
 
+# ---- diagnostic binary32 mode -------------------------------------------------------
+
+def _rne_f32(q):
+    """Round an exact rational to the nearest binary32 (ties to even), with gradual
+    underflow and overflow to infinity, written from the IEEE-754 definition.  An
+    exact zero gives +0 (the sums below never cancel to zero)."""
+    from fractions import Fraction
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                     # below 2^-126 the spacing stays 2^-149
+    ulp = Fraction(2) ** (e - 23)
+    n = a / ulp
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * ulp
+    if v >= Fraction(2) ** 128:
+        return sign * float("inf")
+    return sign * float(v)
+
+
+def _f32_cases(g, K, dt_x, dt_w, *, bias, seq, init, integer=False, B=2, C=3, L=11):
+    def draw(*shape, dt):
+        v = torch.randint(-8, 9, shape, generator=g).float() if integer else torch.randn(*shape, generator=g)
+        return v.to(DT[dt])
+    x = draw(B, C, L, dt=dt_x)
+    w = draw(C, K, dt=dt_w)
+    b = draw(C, dt=dt_w) if bias else None
+    h = draw(B, C, K - 1, dt=dt_x) if init else None
+    s = None
+    if seq:
+        ids = np.repeat(np.arange(4), [2, 1, 5, L - 8])
+        s = torch.tensor(np.stack([ids, ids[::-1].copy()]), dtype=torch.int32)[:B]
+    return x, w, b, s, h
+
+
+def pin_f32_mode_exact_rational(ora):
+    """The binary32 mode against an exact-rational emulation of its definition: each
+    step is w*x + acc computed exactly and rounded once to binary32, bias first,
+    k ascending, dropped terms skipped."""
+    from fractions import Fraction
+    g = _gen(19)
+    for K in (2, 3, 4):
+        for dt_x, dt_w in (("f32", "f32"), ("bf16", "bf16"), ("f16", "f32")):
+            for bias, seq, init in ((True, False, True), (False, True, False), (True, True, False)):
+                x, w, b, s, h = _f32_cases(g, K, dt_x, dt_w, bias=bias, seq=seq, init=init)
+                got = _cf_case(ora, x, w, b, seq=s, init=h).fwd_f32()
+                B, C, L = x.shape
+                xe = torch.cat([h if h is not None else torch.zeros(B, C, K - 1, dtype=x.dtype), x], 2)
+                xe = xe.double().numpy()
+                wd = w.double().numpy()
+                for bb in range(B):
+                    for c in range(C):
+                        for t in range(L):
+                            acc = Fraction(float(b[c])) if b is not None else Fraction(0)
+                            for k in range(K):
+                                src = t - K + 1 + k
+                                if s is not None and (src < 0 or int(s[bb, src]) != int(s[bb, t])):
+                                    continue
+                                acc = Fraction(_rne_f32(Fraction(float(wd[c, k])) * Fraction(float(xe[bb, c, src + K - 1])) + acc))
+                            want = np.float32(float(acc))
+                            assert got[bb, c, t].view(np.uint32) == want.view(np.uint32), (
+                                K, dt_x, dt_w, bias, seq, init, bb, c, t, got[bb, c, t], want)
+
+
+def pin_f32_mode_integers_are_exact(ora):
+    """With small integer inputs every partial sum is an integer below 2^24, so the
+    binary32 mode must equal the fp64 oracle exactly, in every layout, with and
+    without history, mask and bias."""
+    g = _gen(20)
+    for K in (2, 3, 4):
+        for dt in ("f32", "bf16", "f16"):
+            for bias, seq, init in ((True, False, True), (False, True, False), (False, False, False)):
+                x, w, b, s, h = _f32_cases(g, K, dt, dt, bias=bias, seq=seq, init=init, integer=True,
+                                           C=5, L=37)
+                case = _cf_case(ora, x, w, b, seq=s, init=h)
+                z64, _ = case.fwd()
+                z32 = case.fwd_f32()
+                assert np.array_equal(z32.astype(np.float64), z64), (K, dt, bias, seq, init)
+                # the same problem stored channel-last
+                xl = x.transpose(1, 2).contiguous().transpose(1, 2)
+                kw = {} if h is None else dict(init=_raw(h), init_strides=h.stride())
+                cl = ora.Case(B=x.shape[0], C=x.shape[1], L=x.shape[2], K=K, x=_raw(xl.transpose(1, 2)),
+                              x_dtype=dt, x_strides=xl.stride(), w=_raw(w), w_dtype=dt,
+                              bias=None if b is None else _raw(b), seq=None if s is None else s.numpy(), **kw)
+                assert np.array_equal(cl.fwd_f32(), z32), (K, dt, bias, seq, init)
+
+
+def pin_f32_mode_error_bound(ora):
+    """On random data the binary32 mode stays within K roundings of the fp64 result:
+    |z32 - z64| <= K * 2^-24 * S, S = |bias| + sum of |kept terms|; and sampled
+    points agree with the whole-array call."""
+    g = _gen(21)
+    for K in (2, 3, 4):
+        for dt in ("f32", "bf16"):
+            x, w, b, s, h = _f32_cases(g, K, dt, dt, bias=True, seq=False, init=True, C=8, L=300)
+            case = _cf_case(ora, x, w, b, init=h)
+            z64, sabs = case.fwd()
+            z32 = case.fwd_f32().astype(np.float64)
+            assert np.all(np.abs(z32 - z64) <= K * 2.0 ** -24 * sabs * (1 + 1e-6)), (K, dt)
+            assert np.any(z32 != z64), "binary32 mode rounds nothing"
+            idx = np.array([[1, 7, 299], [0, 0, 0], [1, 3, 150]])
+            assert np.array_equal(case.points_f32(idx), case.fwd_f32()[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
 ALL_PINS = [pin_golden, pin_digits, pin_one_hot, pin_delta, pin_constant, pin_conv1d,
             pin_chunking, pin_packing, pin_mask_nan, pin_layout, pin_silu, pin_converters,
-            pin_round_out]
+            pin_round_out, pin_f32_mode_exact_rational, pin_f32_mode_integers_are_exact,
+            pin_f32_mode_error_bound]

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import causal_depthwise_conv1d_amd as ccv
+import oracle
 import workloads as wl
 from gpu_support import (assert_close, assert_final_states, bits_equal, check_full, gpu_args, log,
                          oracle_case, run_gpu, to_gpu_view)
@@ -80,6 +81,65 @@ def test_matrix(dtype, K, layout):
         w = build(L, C, B, K, dtype, layout, feats, seed=100 * K + i)
         log(f"  case L={L} C={C} B={B} {feats}")
         check_full(w, where=f"[{dtype} K={K} {layout} L={L} C={C}]")
+
+
+def _raw_bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+def _fma_chain_reference(w):
+    """The oracle's binary32 mode (bias first, one fused multiply-add per kept term,
+    k ascending), rounded to the output dtype: raw storage [B, C, L]."""
+    z = oracle_case(w).fwd_f32()
+    if w.x_dtype == "f32":
+        return z
+    return oracle.f32_to_bf16(z) if w.x_dtype == "bf16" else oracle.f32_to_f16(z)
+
+
+_INF_BITS = {"bf16": 0x7f80, "f16": 0x7c00}
+
+
+def assert_same_bits(got: np.ndarray, want: np.ndarray, dtype: str, where=""):
+    """Bit-identical raw storage (the sign of zero included); NaN equals any NaN."""
+    g, r = _raw_bits(got), _raw_bits(want)
+    assert g.shape == r.shape, where
+    if dtype == "f32":
+        nan = np.isnan(got) & np.isnan(want)
+    else:
+        nan = ((g & 0x7fff) > _INF_BITS[dtype]) & ((r & 0x7fff) > _INF_BITS[dtype])
+    diff = (g != r) & ~nan
+    if diff.any():
+        bad = np.argwhere(diff)[:6]
+        raise AssertionError(f"{where}: {int(diff.sum())} of {diff.size} differ; first at " + ", ".join(
+            f"{tuple(i)}: {g[tuple(i)]:#x} vs {r[tuple(i)]:#x}" for i in bad.tolist()))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_no_activation_is_the_fp32_fma_chain(dtype, layout, monkeypatch):
+    """Without an activation every kernel path sums exactly as the oracle's binary32
+    mode does, so its output is bit-identical to that sum rounded to the output
+    dtype: vector and element paths, with bias, history, seq_idx and weights of
+    every dtype."""
+    for force_scalar in ("0", "1"):
+        monkeypatch.setenv("CCV_FORCE_SCALAR", force_scalar)
+        for K in KS:
+            cases = [
+                (1, 7, 2, dict(bias=True), None),
+                (K - 1, 8, 1, dict(init=True, final=True), None),
+                (257, 8, 3, dict(bias=False), None),
+                (513, 64, 1, dict(bias=True, init=True, final=True), "f32"),
+                (1537, 72, 2, dict(bias=True, seq=13), None),
+                (4099, 9, 1, dict(bias=True, seq=40), "bf16"),
+                (2050, 130, 1, dict(bias=True), "f16"),
+            ]
+            for i, (L, C, B, feats, w_dtype) in enumerate(cases):
+                w = build(L, C, B, K, dtype, layout, dict(feats, activation=None), seed=7000 + 10 * K + i,
+                          w_dtype=w_dtype)
+                log(f"  fma chain: scalar={force_scalar} K={K} L={L} C={C} B={B} w={w.w_dtype} {feats}")
+                out, _ = run_gpu(w)
+                assert_same_bits(raw(out), _fma_chain_reference(w), dtype,
+                                 where=f"[{dtype}/{w.w_dtype} K={K} {layout} L={L} scalar={force_scalar}]")
 
 
 def test_random_shapes():

@@ -77,6 +77,30 @@ def channel_slice_check(w, kw, out_gpu, c0, c1, b=0):
     return res
 
 
+def fma_chain_check(w, out_gpu, extra_t, c0, c1, n_random=200_000, seed=1):
+    """Without an activation the kernel sums exactly as the oracle's binary32 mode
+    does (bias first, one fused multiply-add per kept term, k ascending): sampled
+    outputs and one whole channel slice must be bit-identical to it."""
+    assert w.activation is None and w.x_dtype == "f32"
+    B, C, L = w.B, w.C, w.L
+    g = np.random.default_rng(seed)
+    idx = np.stack([g.integers(0, B, n_random), g.integers(0, C, n_random), g.integers(0, L, n_random)], 1)
+    bb, cc, tt = np.meshgrid(np.arange(B), g.choice(C, min(C, 32), replace=False), extra_t, indexing="ij")
+    idx = np.concatenate([idx, np.stack([bb.ravel(), cc.ravel(), tt.ravel()], 1)])
+    want = oracle_case(w).points_f32(idx)
+    ti = torch.from_numpy(idx).cuda()
+    got = out_gpu[ti[:, 0], ti[:, 1], ti[:, 2]].cpu().numpy()
+    diff = got.view(np.uint32) != want.view(np.uint32)
+    assert not diff.any(), f"{int(diff.sum())} sampled outputs differ, first at {idx[diff][:4].tolist()}"
+    init = None if w.initial_states is None else w.initial_states[:1, c0:c1]
+    sub = case(w.x[:1, c0:c1], w.weight[c0:c1], None if w.bias is None else w.bias[c0:c1], None, init, None)
+    want = sub.fwd_f32()
+    got = out_gpu[:1, c0:c1].cpu().contiguous().numpy()
+    diff = got.view(np.uint32) != want.view(np.uint32)
+    assert not diff.any(), f"{int(diff.sum())} outputs of channels [{c0},{c1}) differ"
+    log(f"  binary32 chain: {len(idx)} samples and channels [{c0},{c1}) bit-identical")
+
+
 def test_workload_1_small_channel_first_all_outputs():
     w = wl.workload(1)
     kw, plan, out, _ = run(w)
@@ -142,3 +166,4 @@ def test_workload_5_long_sequence_channel_first():
     sampled_check(w, out, boundary_times(w.L, plan["span"], w.K))
     channel_slice_check(w, kw, out, 0, 2, b=0)
     channel_slice_check(w, kw, out, 126, 128, b=1)
+    fma_chain_check(w, out, boundary_times(w.L, plan["span"], w.K), 40, 41)

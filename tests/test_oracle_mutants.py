@@ -13,17 +13,20 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ccv_oracle.c")
 
 # (name, original text, mutated text)
 MUTANTS = [
-    ("taps_reversed", "ora_decode(p->w, p->w_dtype, c * K + k)", "ora_decode(p->w, p->w_dtype, c * K + (K - 1 - k))"),
-    ("source_off_by_one", "int64_t src = t - K + 1 + k;", "int64_t src = t - K + k;"),
-    ("oldest_tap_dropped", "for (int k = 0; k < K; ++k) {", "for (int k = 1; k < K; ++k) {"),
+    ("taps_reversed", "double term = ora_decode(p->w, p->w_dtype, c * K + k)",
+     "double term = ora_decode(p->w, p->w_dtype, c * K + (K - 1 - k))"),
+    ("source_off_by_one", "int64_t src = t - K + 1 + k;              /*", "int64_t src = t - K + k;              /*"),
+    ("oldest_tap_dropped", "for (int k = 0; k < K; ++k) {\n    int64_t src = t - K + 1 + k;              /*",
+     "for (int k = 1; k < K; ++k) {\n    int64_t src = t - K + 1 + k;              /*"),
     ("silu_sign", "acc / (1.0 + exp(-acc))", "acc / (1.0 + exp(acc))"),
     ("silu_missing_z", "out = acc / (1.0 + exp(-acc));", "out = 1.0 / (1.0 + exp(-acc));"),
     ("bias_dropped", "acc = beta;", "acc = 0.0;"),
     ("history_reversed", "int64_t i = j + p->K - 1;\n  return", "int64_t i = -j - 1;\n  return"),
-    ("mask_never", "p->seq[b * p->L + src] != p->seq[b * p->L + t]", "p->seq[b * p->L + src] != p->seq[b * p->L + src]"),
+    ("mask_never", "p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;   /*",
+     "p->seq[b * p->L + src] != p->seq[b * p->L + src]) continue;   /*"),
     ("mask_multiplies",
-     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;",
-     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) { acc += 0.0 * ora_xt(p, b, c, src); continue; }"),
+     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;   /*",
+     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) { acc += 0.0 * ora_xt(p, b, c, src); continue; }   /*"),
     ("final_off_by_one", "int64_t j = p->L - K + 1 + i;", "int64_t j = p->L - K + i;"),
     ("f16_exponent_bias", "ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
     ("bf16_ties_away", "(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
@@ -31,6 +34,13 @@ MUTANTS = [
     ("sabs_signed", "s += fabs(term);", "s += term;"),
     ("x_stride_swapped", "b * p->xs[0] + c * p->xs[1] + j * p->xs[2]);\n  if (p->init", "b * p->xs[0] + c * p->xs[2] + j * p->xs[1]);\n  if (p->init"),
     ("init_zero", "if (p->init == NULL) return 0.0;", "return 0.0;"),
+    # the diagnostic binary32 mode
+    ("f32_two_roundings", "acc = fmaf(wv, xv, acc);", "acc = acc + wv * xv;"),
+    ("f32_k_descending", "for (int k = 0; k < K; ++k) {\n    int64_t src = t - K + 1 + k;\n",
+     "for (int kk = 0; kk < K; ++kk) {\n    int k = K - 1 - kk;\n    int64_t src = t - K + 1 + k;\n"),
+    ("f32_bias_dropped", "if (p->bias != NULL) acc = (float)ora_decode(p->bias, p->w_dtype, c);", ""),
+    ("f32_taps_reversed", "float wv = (float)ora_decode(p->w, p->w_dtype, c * K + k);",
+     "float wv = (float)ora_decode(p->w, p->w_dtype, c * K + (K - 1 - k));"),
 ]
 
 
