@@ -8,12 +8,15 @@ that are not on a GPU, calls raise.
 
 Low level (same names as the C ABI):
     ccv_fwd(args, stream=None), ccv_fwd_check(args), ccv_fwd_plan(args),
+    ccv_update(args, stream=None), ccv_update_check(args),
     ccv_status_str(code), ccv_abi_version()
 High level (the full-sequence contract of Ch.4 "Dao interface and source map",
-section "Contract of the full-sequence interface"):
+section "Contract of the full-sequence interface"; and the update kernel of the
+same page's section "Reading the source along the call chain"):
     causal_conv1d_fwd(x, weight, bias=None, seq_idx=None, initial_states=None,
                       return_final_states=False, final_states_out=None,
                       activation=None)
+    causal_conv1d_update(x, conv_state, weight, bias=None, activation=None)
 """
 from __future__ import annotations
 
@@ -62,6 +65,25 @@ class ccv_fwd_args_t(ctypes.Structure):
         self.struct_size = ctypes.sizeof(ccv_fwd_args_t)
 
 
+class ccv_update_args_t(ctypes.Structure):
+    """Mirror of ``ccv_update_args_t`` in include/ccv.h (field order and types)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_int64),
+        ("B", ctypes.c_int64), ("C", ctypes.c_int64), ("L", ctypes.c_int64),
+        ("K", ctypes.c_int32), ("activation", ctypes.c_int32),
+        ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("x_stride", _I64x3),
+        ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("state", ctypes.c_void_p), ("state_stride", _I64x3),
+        ("out", ctypes.c_void_p), ("out_stride", _I64x3),
+    ]
+
+    def __init__(self, **kw):
+        super().__init__(**kw)
+        self.struct_size = ctypes.sizeof(ccv_update_args_t)
+
+
 class ccv_plan_t(ctypes.Structure):
     """Mirror of ``ccv_plan_t`` in include/ccv.h."""
     _fields_ = [
@@ -103,6 +125,11 @@ def lib() -> ctypes.CDLL:
         L.ccv_fwd_check.restype = ctypes.c_int
         L.ccv_fwd_plan.argtypes = [P, ctypes.POINTER(ccv_plan_t)]
         L.ccv_fwd_plan.restype = ctypes.c_int
+        U = ctypes.POINTER(ccv_update_args_t)
+        L.ccv_update.argtypes = [U, ctypes.c_void_p]
+        L.ccv_update.restype = ctypes.c_int
+        L.ccv_update_check.argtypes = [U]
+        L.ccv_update_check.restype = ctypes.c_int
         L.ccv_status_str.argtypes = [ctypes.c_int]
         L.ccv_status_str.restype = ctypes.c_char_p
         L.ccv_abi_version.argtypes = []
@@ -115,14 +142,18 @@ def lib() -> ctypes.CDLL:
 
 # ---- the C ABI, one to one ----------------------------------------------------------
 
+def _stream_handle(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
 def ccv_fwd(args: ccv_fwd_args_t, stream=None) -> int:
     """Enqueue the forward on `stream` (a torch stream, a raw hipStream_t int, or None
     for torch's current stream).  Returns the status code."""
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif isinstance(stream, torch.cuda.Stream):
-        stream = stream.cuda_stream
-    return lib().ccv_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    return lib().ccv_fwd(ctypes.byref(args), ctypes.c_void_p(_stream_handle(stream)))
 
 
 def ccv_fwd_check(args: ccv_fwd_args_t) -> int:
@@ -134,6 +165,15 @@ def ccv_fwd_plan(args: ccv_fwd_args_t):
     p = ccv_plan_t()
     st = lib().ccv_fwd_plan(ctypes.byref(args), ctypes.byref(p))
     return st, p
+
+
+def ccv_update(args: ccv_update_args_t, stream=None) -> int:
+    """Enqueue one update (decode) call on `stream`; returns the status code."""
+    return lib().ccv_update(ctypes.byref(args), ctypes.c_void_p(_stream_handle(stream)))
+
+
+def ccv_update_check(args: ccv_update_args_t) -> int:
+    return lib().ccv_update_check(ctypes.byref(args))
 
 
 def ccv_status_str(status: int) -> str:
@@ -174,12 +214,29 @@ def make_args(x, weight, out, bias=None, seq_idx=None, initial_states=None,
     return a
 
 
-def _raise(status: int):
+def make_update_args(x, weight, state, out, bias=None, activation=None) -> ccv_update_args_t:
+    """Fill a ccv_update_args_t from tensors: x and out [B, C, L], state [B, C, K-1]."""
+    B, C, L = x.shape
+    a = ccv_update_args_t()
+    a.B, a.C, a.L = B, C, L
+    a.K = weight.shape[1]
+    a.activation = CCV_ACT_SILU if activation in ("silu", "swish") else CCV_ACT_NONE
+    a.x_dtype = DTYPE_CODE[x.dtype]
+    a.w_dtype = DTYPE_CODE[weight.dtype]
+    a.x, a.x_stride = _ptr(x), _strides3(x)
+    a.weight = _ptr(weight)
+    a.bias = _ptr(bias)
+    a.state, a.state_stride = _ptr(state), _strides3(state)
+    a.out, a.out_stride = _ptr(out), _strides3(out)
+    return a
+
+
+def _raise(status: int, where: str = "ccv_fwd"):
     if status == 0:
         return
     if status == -8:
-        raise CcvError(status)
-    raise CcvArgumentError(status)
+        raise CcvError(status, where)
+    raise CcvArgumentError(status, where)
 
 
 def empty_like_layout(x: torch.Tensor) -> torch.Tensor:
@@ -267,3 +324,49 @@ def plan_for(x, weight, out=None, **kw) -> dict:
     st, p = ccv_fwd_plan(make_args(x, weight, out, **kw))
     _raise(st)
     return p.as_dict()
+
+
+def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, activation: Optional[str] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One update (decode) call on the GPU: convolve the new steps x against the
+    history in ``conv_state`` and advance ``conv_state`` in place.
+
+    x [B, C] (one step) or [B, C, L]; conv_state [B, C, K-1] in x's dtype, time
+    ascending (the last K-1 inputs seen so far); weight [C, K] (oldest -> current);
+    bias [C] in the weight's dtype.  Any strides are used as they are.  Returns out
+    with x's shape and dtype.  Afterwards conv_state holds the last K-1 inputs of
+    (old state followed by x), exactly as ``causal_conv1d_fwd`` would return them as
+    final states.
+    """
+    if activation not in (None, "silu", "swish"):
+        raise ValueError(f"activation must be None, 'silu' or 'swish', not {activation!r}")
+    one_step = x.dim() == 2
+    x3 = x.unsqueeze(2) if one_step else x
+    if x3.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x3.shape[1]:
+        raise ValueError("expected x [B, C] or [B, C, L] and weight [C, K]")
+    if not x3.is_cuda:
+        raise ValueError("x must be a GPU tensor (there is no CPU path)")
+    for name, t in (("conv_state", conv_state), ("weight", weight), ("bias", bias), ("out", out)):
+        if t is not None and t.device != x3.device:
+            raise ValueError(f"{name} must be on {x3.device}")
+    B, C, L = x3.shape
+    K = weight.shape[1]
+    if conv_state.dtype != x3.dtype or tuple(conv_state.shape) != (B, C, K - 1):
+        raise ValueError("conv_state must be [B, C, K-1] in x's dtype")
+    weight = weight.contiguous()
+    if bias is not None:
+        if bias.dtype != weight.dtype:
+            raise ValueError("bias must have the weight's dtype")
+        bias = bias.contiguous()
+    if out is None:
+        out3 = torch.empty(B, C, L, dtype=x3.dtype, device=x3.device)
+    else:
+        if out.dtype != x3.dtype or tuple(out.shape) != tuple(x.shape):
+            raise ValueError("out must have x's shape and dtype")
+        out3 = out.unsqueeze(2) if one_step else out
+    args = make_update_args(x3, weight, conv_state, out3, bias, activation)
+    with torch.cuda.device(x3.device):
+        st = ccv_update(args)
+    _raise(st, "ccv_update")
+    return out3.squeeze(2) if one_step else out3

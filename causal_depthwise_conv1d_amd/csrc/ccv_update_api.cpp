@@ -1,0 +1,133 @@
+// ccv_update_api.cpp -- C ABI of the update (decode) call: argument checks and
+// the single kernel launch.  The operation and its contract are stated in ccv.h
+// beside ccv_update; the checks mirror ccv_fwd's (K in {2,3,4}, three storage
+// dtypes for x and weight, bias in the weight dtype, the state in x's dtype:
+// Ch.4 "Dao interface and source map", section "Concrete limits of v1.5.0"),
+// plus what an in-place update needs: the state and out layouts may not map two
+// logical elements to one address, and no two of x, state, out may coincide.
+//
+// Nothing here touches a device except ccv_update's kernel launch.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "ccv.h"
+#include "ccv_update_launch.hpp"
+
+namespace {
+
+using namespace ccv;
+
+inline int elt_size(int dt) { return dt == CCV_F32 ? 4 : 2; }
+
+// Largest element offset of an [n0, n1, n2] view with strides s (all >= 0), or
+// -1 when it does not fit in int64.
+int64_t max_offset(const int64_t n[3], const int64_t s[3]) {
+  int64_t total = 0;
+  for (int d = 0; d < 3; ++d) {
+    if (n[d] <= 1) continue;
+    int64_t p;
+    if (__builtin_mul_overflow(n[d] - 1, s[d], &p)) return -1;
+    if (__builtin_add_overflow(total, p, &total)) return -1;
+  }
+  return total;
+}
+
+bool fits_bytes(int64_t max_off, int es) {
+  int64_t bytes;
+  return max_off >= 0 && !__builtin_mul_overflow(max_off + 1, (int64_t)es, &bytes);
+}
+
+// True when no two index triples of an [n0, n1, n2] view with strides s share an
+// offset, shown by the usual sufficient test: taking the dimensions of extent > 1
+// in ascending stride order, each stride exceeds the largest offset reachable
+// with the dimensions before it.  (Called after max_offset succeeded, so the
+// partial sums cannot overflow.)
+bool non_overlapping(const int64_t n[3], const int64_t s[3]) {
+  int order[3] = {0, 1, 2};
+  std::sort(order, order + 3, [&](int p, int q) { return s[p] < s[q]; });
+  int64_t reach = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int d = order[i];
+    if (n[d] <= 1) continue;
+    if (s[d] <= reach) return false;
+    reach += (n[d] - 1) * s[d];
+  }
+  return true;
+}
+
+int validate(const ccv_update_args_t* a, UpdArgs* u, uint32_t* grid) {
+  if (!a) return CCV_E_NULL;
+  if (a->struct_size != (int64_t)sizeof(ccv_update_args_t)) return CCV_E_ABI;
+  if (a->B < 0 || a->C < 0 || a->L < 0) return CCV_E_SHAPE;
+  if (a->K < 2 || a->K > 4) return CCV_E_KSIZE;
+  if (a->x_dtype < 0 || a->x_dtype > 2 || a->w_dtype < 0 || a->w_dtype > 2) return CCV_E_DTYPE;
+  if (a->activation != CCV_ACT_NONE && a->activation != CCV_ACT_SILU) return CCV_E_UNSUPPORTED;
+  for (int d = 0; d < 3; ++d)
+    if (a->x_stride[d] < 0 || a->out_stride[d] < 0 || a->state_stride[d] < 0) return CCV_E_LAYOUT;
+
+  const int64_t B = a->B, C = a->C, L = a->L;
+  const int K = a->K;
+  *grid = 0;
+  int64_t rows;
+  if (__builtin_mul_overflow(B, C, &rows)) return CCV_E_SHAPE;
+  if (rows == 0 || L == 0) return CCV_OK;        // nothing to compute; the state stays as it is
+
+  if (!a->x || !a->weight || !a->state || !a->out) return CCV_E_NULL;
+  if (a->out == a->x || a->state == a->x || a->state == a->out) return CCV_E_ALIAS;
+
+  const int es = elt_size(a->x_dtype);
+  const int64_t nx[3] = {B, C, L}, ns[3] = {B, C, K - 1};
+  if (!fits_bytes(max_offset(nx, a->x_stride), es)) return CCV_E_SHAPE;
+  if (!fits_bytes(max_offset(nx, a->out_stride), es)) return CCV_E_SHAPE;
+  if (!fits_bytes(max_offset(ns, a->state_stride), es)) return CCV_E_SHAPE;
+  if (!non_overlapping(nx, a->out_stride) || !non_overlapping(ns, a->state_stride)) return CCV_E_LAYOUT;
+
+  const int64_t g = (rows + kUpdateBlock - 1) / kUpdateBlock;
+  if (g > INT32_MAX) return CCV_E_SHAPE;
+
+  *u = UpdArgs{};
+  u->x = a->x;
+  u->out = a->out;
+  u->w = a->weight;
+  u->bias = a->bias;
+  u->state = a->state;
+  u->C = C;
+  u->L = L;
+  u->rows = rows;
+  u->x_sb = a->x_stride[0];
+  u->x_sc = a->x_stride[1];
+  u->x_sl = a->x_stride[2];
+  u->o_sb = a->out_stride[0];
+  u->o_sc = a->out_stride[1];
+  u->o_sl = a->out_stride[2];
+  u->s_sb = a->state_stride[0];
+  u->s_sc = a->state_stride[1];
+  u->s_si = a->state_stride[2];
+  u->w_dtype = a->w_dtype;
+  *grid = (uint32_t)g;
+  return CCV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ccv_update_check(const ccv_update_args_t* args) {
+  UpdArgs u;
+  uint32_t grid;
+  return validate(args, &u, &grid);
+}
+
+int ccv_update(const ccv_update_args_t* args, void* hip_stream) {
+  UpdArgs u;
+  uint32_t grid;
+  const int st = validate(args, &u, &grid);
+  if (st != CCV_OK) return st;
+  if (grid == 0) return CCV_OK;
+  const int err = launch_update(u, args->x_dtype, args->K, args->activation == CCV_ACT_SILU, grid,
+                                hip_stream);
+  return err == 0 ? CCV_OK : CCV_E_HIP;
+}
+
+}  // extern "C"

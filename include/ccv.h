@@ -129,6 +129,59 @@ int ccv_fwd_check(const ccv_fwd_args_t* args);
  * device.  `plan` may be NULL. */
 int ccv_fwd_plan(const ccv_fwd_args_t* args, ccv_plan_t* plan);
 
+/* ---- update (decode): advance a K-1 step history in place ------------------------
+ *
+ * The step after a forward over a prompt: a few new steps per (b, c) row are
+ * convolved against the history that precedes them, and the history is then
+ * replaced by the last K-1 inputs, in the same buffer (Ch.4 "Dao interface and
+ * source map", section "Reading the source along the call chain": the update
+ * kernel reads the history and advances the state in place).  With
+ * X~ = state[b,c,0..K-2] followed by x[b,c,0..L-1]:
+ *
+ *   out[b,c,t]   = act( bias[c] + sum_{k=0}^{K-1} w[c,k] * X~[t+k] ),  t = 0..L-1
+ *   state[b,c,i] <- X~[L+i],                                           i = 0..K-2
+ *
+ * which is exactly ccv_fwd with initial_states = final_states_out = state (the
+ * stencil of Ch.5 "Dao forward CUDA implementation", section "How adjacent
+ * threads and chunks exchange history"; the state as the history left of the
+ * block and as the last K-1 inputs, Ch.5, section "Three kinds of boundary
+ * handled separately").  The arithmetic is the forward's, term for term and in
+ * the same order, so decoding one step at a time gives the forward's bits.
+ * There is no seq_idx: every row is one sequence.  Any L works, but each row is
+ * processed sequentially by one thread, so long runs belong to ccv_fwd.
+ *
+ * state is read before it is written, row by row, so it is updated in place;
+ * it must not overlap x or out, and the state and out layouts must not map two
+ * logical elements to one address (CCV_E_LAYOUT).  L = 0 leaves state as it is
+ * and enqueues nothing.  Any element strides are accepted for every tensor. */
+typedef struct ccv_update_args {
+  int64_t struct_size;          /* = sizeof(ccv_update_args_t) */
+  int64_t B, C, L;              /* x and out: [B, C, L] new steps (decode: L = 1) */
+  int32_t K;                    /* taps: 2, 3 or 4 */
+  int32_t activation;           /* ccv_act_t */
+  int32_t x_dtype;              /* ccv_dtype_t of x, out and state */
+  int32_t w_dtype;              /* ccv_dtype_t of weight and bias */
+  const void* x;                /* device, x[b,c,t] */
+  int64_t x_stride[3];          /*   (s_B, s_C, s_L) */
+  const void* weight;           /* device, contiguous [C, K], oldest -> current */
+  const void* bias;             /* device [C] or NULL (pre-activation) */
+  void* state;                  /* device [B, C, K-1], time ascending; read, then overwritten */
+  int64_t state_stride[3];      /*   (b, c, i) strides */
+  void* out;                    /* device [B, C, L] */
+  int64_t out_stride[3];        /*   (s_B, s_C, s_L) */
+} ccv_update_args_t;
+
+/* Enqueue one update on `hip_stream` (NULL = the null stream) and return without
+ * waiting.  Returns CCV_OK, a validation error (nothing enqueued) or CCV_E_HIP.
+ * Errors: CCV_E_NULL (x, weight, state or out missing when B*C*L > 0),
+ * CCV_E_SHAPE, CCV_E_KSIZE, CCV_E_DTYPE, CCV_E_UNSUPPORTED (activation value),
+ * CCV_E_ALIAS (any two of x, state, out share a base address), CCV_E_LAYOUT (a
+ * negative stride, or a state / out layout that overlaps itself), CCV_E_ABI. */
+int ccv_update(const ccv_update_args_t* args, void* hip_stream);
+
+/* Validate `args` exactly as ccv_update does, without touching any device. */
+int ccv_update_check(const ccv_update_args_t* args);
+
 /* Static, NUL-terminated name of a status code ("CCV_OK", ...). */
 const char* ccv_status_str(int status);
 

@@ -205,3 +205,84 @@ def test_wrapper_refuses_cpu_tensors():
     w = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         ccv.causal_conv1d_fwd(x, w)
+
+
+# ---- update (decode) -----------------------------------------------------------------
+
+def uargs(B=2, C=64, L=1, K=4, state_layout="bci", **over):
+    a = ccv.ccv_update_args_t()
+    a.B, a.C, a.L, a.K = B, C, L, K
+    a.x_dtype = a.w_dtype = ccv.CCV_BF16
+    a.activation = ccv.CCV_ACT_SILU
+    a.x, a.weight, a.state, a.out = X, W, INIT, OUT
+    a.x_stride = type(a.x_stride)(C * L, L, 1)
+    a.out_stride = type(a.out_stride)(C * L, L, 1)
+    H = K - 1
+    st = (C * H, H, 1) if state_layout == "bci" else (H * C, 1, C)
+    a.state_stride = type(a.state_stride)(*st)
+    for k, v in over.items():
+        if k.endswith("stride"):
+            v = type(getattr(a, k))(*v)
+        setattr(a, k, v)
+    return a
+
+
+def ucheck(a):
+    return ccv.STATUS[ccv.ccv_update_check(a)]
+
+
+def test_update_valid_calls():
+    assert ucheck(uargs()) == "CCV_OK"
+    assert ucheck(uargs(state_layout="bic")) == "CCV_OK"
+    assert ucheck(uargs(L=5, bias=BIAS, activation=ccv.CCV_ACT_NONE)) == "CCV_OK"
+    # channel-last new steps and a state that is a slice of a longer per-row buffer
+    assert ucheck(uargs(L=3, x_stride=(3 * 64, 1, 64), out_stride=(3 * 64, 1, 64),
+                        state_stride=(64 * 8, 8, 1))) == "CCV_OK"
+    # any dtype pair
+    assert ucheck(uargs(x_dtype=ccv.CCV_F32, w_dtype=ccv.CCV_F16)) == "CCV_OK"
+
+
+def test_update_argument_errors():
+    a = uargs()
+    a.struct_size = 8
+    assert ucheck(a) == "CCV_E_ABI"
+    assert ucheck(uargs(B=-1)) == "CCV_E_SHAPE"
+    assert ucheck(uargs(L=-1)) == "CCV_E_SHAPE"
+    for K in (1, 5):
+        assert ucheck(uargs(K=K)) == "CCV_E_KSIZE"
+    assert ucheck(uargs(x_dtype=7)) == "CCV_E_DTYPE"
+    assert ucheck(uargs(activation=3)) == "CCV_E_UNSUPPORTED"
+    for name in ("x", "weight", "state", "out"):
+        assert ucheck(uargs(**{name: None})) == "CCV_E_NULL", name
+    assert ccv.lib().ccv_update_check(None) == -1
+    assert ucheck(uargs(state=X)) == "CCV_E_ALIAS"
+    assert ucheck(uargs(out=X)) == "CCV_E_ALIAS"
+    assert ucheck(uargs(state=OUT)) == "CCV_E_ALIAS"
+    assert ucheck(uargs(state_stride=(192, 3, -1))) == "CCV_E_LAYOUT"
+    assert ucheck(uargs(x_stride=(2**62, 1, 1), B=4)) == "CCV_E_SHAPE"
+
+
+def test_update_written_layouts_must_not_overlap():
+    # every batch row of the state at one address
+    assert ucheck(uargs(state_stride=(0, 3, 1))) == "CCV_E_LAYOUT"
+    # channels and history steps interleaved onto the same elements
+    assert ucheck(uargs(state_stride=(192, 1, 1))) == "CCV_E_LAYOUT"
+    assert ucheck(uargs(state_stride=(192, 2, 1))) == "CCV_E_LAYOUT"
+    # out with two steps on one element
+    assert ucheck(uargs(L=2, out_stride=(128, 2, 0))) == "CCV_E_LAYOUT"
+    # x may overlap itself (it is only read): a broadcast input is fine
+    assert ucheck(uargs(L=2, x_stride=(0, 1, 0))) == "CCV_OK"
+    # size-1 dimensions never overlap, whatever their stride
+    assert ucheck(uargs(B=1, state_stride=(0, 3, 1))) == "CCV_OK"
+
+
+def test_update_nothing_to_do_needs_no_pointers():
+    for B, C, L in ((0, 4, 1), (2, 0, 1), (2, 4, 0)):
+        assert ucheck(uargs(B=B, C=C, L=L, x=None, weight=None, state=None, out=None)) == "CCV_OK"
+
+
+def test_update_wrapper_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 4)
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_update(x, torch.zeros(2, 4, 3), torch.zeros(4, 4))
