@@ -36,20 +36,26 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, decimal GB/s
 ROTATION_BYTES = 1 << 30        # >= 4x the 256 MB Infinity Cache
 METRIC = "causal conv1d fwd effective HBM GB/s and % of MI355X peak bandwidth"
+UPDATE_METRIC = "causal conv1d update (decode) effective HBM GB/s and % of MI355X peak bandwidth"
 KERNEL_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_cf.hip",
                   "causal_depthwise_conv1d_amd/csrc/ccv_cl.hip",
                   "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_api.cpp"]
+UPDATE_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_update.hip",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_update_launch.hpp",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_update_api.cpp"]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha256() -> str:
+def kernel_sources_sha256(files=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in files or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -91,6 +97,8 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--op", default="fwd", choices=["fwd", "update"],
+                    help="fwd: the forward on --workload (default); update: the decode step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
@@ -113,6 +121,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+
+    if args.op == "update":
+        bench_update(args, dev, props)
+        return
 
     t0 = time.time()
     w = wl.workload(args.workload)
@@ -176,35 +188,7 @@ def main():
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {gbps:.0f} GB/s")
 
-    # Context on the same GPU: a plain copy moving the same bytes, and the launch floor.
-    calib = ctypes.CDLL(ccv.CALIB_LIB_PATH)
-    calib.ccv_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    calib.ccv_calib_empty.argtypes = [ctypes.c_void_p]
-    half = (nbytes // 2) // 16 * 16
-    csets = max(2, math.ceil(ROTATION_BYTES / (2 * half)))
-    bufs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.zeros(half, dtype=torch.uint8, device=dev))
-            for _ in range(csets)]
-    for i in range(20):
-        d, s_ = bufs[i % csets]
-        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
-    ev0.record(stream)
-    for i in range(args.steps):
-        d, s_ = bufs[i % csets]
-        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = ev0.elapsed_time(ev1) / args.steps
-    copy_gbps = 2 * half / (copy_ms * 1e-3) / 1e9
-    del bufs
-    for _ in range(50):
-        calib.ccv_calib_empty(sp)
-    ev0.record(stream)
-    for _ in range(1000):
-        calib.ccv_calib_empty(sp)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    empty_us = ev0.elapsed_time(ev1)  # ms for 1000 launches = us per launch
-    log(f"[bench] copy of the same bytes: {copy_gbps:.0f} GB/s; empty kernel {empty_us:.2f} us")
+    copy_gbps, empty_us = context_measurements(nbytes, dev, stream, args.steps)
 
     kernel_key = ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
         f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}"
@@ -262,6 +246,216 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, sets[0][2], nbytes, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def context_measurements(nbytes, dev, stream, steps):
+    """Context on the same GPU: a plain copy kernel moving the same bytes (half read,
+    half written, rotated over >= 1 GiB), and the launch floor of an empty kernel."""
+    import ctypes
+
+    import torch
+
+    import causal_depthwise_conv1d_amd as ccv
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    calib = ctypes.CDLL(ccv.CALIB_LIB_PATH)
+    calib.ccv_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    calib.ccv_calib_empty.argtypes = [ctypes.c_void_p]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    half = (nbytes // 2) // 16 * 16
+    csets = max(2, math.ceil(ROTATION_BYTES / (2 * half)))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.zeros(half, dtype=torch.uint8, device=dev))
+            for _ in range(csets)]
+    for i in range(20):
+        d, s_ = bufs[i % csets]
+        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
+    ev0.record(stream)
+    for i in range(steps):
+        d, s_ = bufs[i % csets]
+        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = ev0.elapsed_time(ev1) / steps
+    copy_gbps = 2 * half / (copy_ms * 1e-3) / 1e9
+    del bufs
+    for _ in range(50):
+        calib.ccv_calib_empty(sp)
+    ev0.record(stream)
+    for _ in range(1000):
+        calib.ccv_calib_empty(sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    empty_us = ev0.elapsed_time(ev1)  # ms for 1000 launches = us per launch
+    log(f"[bench] copy of the same bytes: {copy_gbps:.0f} GB/s; empty kernel {empty_us:.2f} us")
+    return copy_gbps, empty_us
+
+
+def update_bytes(w) -> int:
+    """Algorithmic bytes of one update call: x and out once, the state read and
+    written once, weight and bias once."""
+    es = w.x.element_size()
+    B, C, L, K = w.B, w.C, w.L, w.K
+    n = 2 * B * C * L * es + 2 * B * C * (K - 1) * es
+    n += w.weight.numel() * w.weight.element_size()
+    if w.bias is not None:
+        n += w.bias.numel() * w.bias.element_size()
+    return n
+
+
+def bench_update(args, dev, props):
+    """The update (decode) call on the decode workload: one parity-checked call,
+    then W warm-up and K timed calls rotating over >= 1 GiB of (x, state, out)
+    sets, so every call reads its inputs from HBM."""
+    import ctypes
+
+    import torch
+
+    import causal_depthwise_conv1d_amd as ccv
+    import workloads as wl
+
+    w = wl.decode_workload()
+    B, C, L, K = w.B, w.C, w.L, w.K
+    es = w.x.element_size()
+    nbytes = update_bytes(w)
+    set_bytes = (2 * B * C * L + B * C * (K - 1)) * es
+    nsets = max(2, math.ceil(ROTATION_BYTES / set_bytes))
+    weight = w.weight.to(dev)
+    bias = None if w.bias is None else w.bias.to(dev)
+    sets = []
+    for _ in range(nsets):
+        x = w.x.to(dev).contiguous()
+        state = w.initial_states.to(dev).contiguous()
+        out = torch.empty(B, C, L, dtype=x.dtype, device=dev)
+        sets.append((x, state, out, ccv.make_update_args(x, weight, state, out, bias, w.activation)))
+    st, plan = ccv.ccv_update_plan(sets[0][3])
+    assert st == 0, ccv.ccv_status_str(st)
+    plan = plan.as_dict()
+    log(f"[bench] update: {nsets} buffer sets of {set_bytes / 1e6:.1f} MB; plan {plan}")
+
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    upd = ccv.lib().ccv_update
+    refs = [ctypes.byref(s[3]) for s in sets]
+
+    # One call checked against the oracle before the states start to move.
+    rc = upd(refs[0], sp)
+    if rc != 0:
+        raise RuntimeError(ccv.ccv_status_str(rc))
+    torch.cuda.synchronize()
+    parity = update_parity(w, sets[0][2], sets[0][1])
+    log(f"[bench] update parity: {parity}")
+
+    def step(i):
+        rc = upd(refs[i % nsets], sp)
+        if rc != 0:
+            raise RuntimeError(ccv.ccv_status_str(rc))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] update: {ms_per_step * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+    copy_gbps, empty_us = context_measurements(nbytes, dev, stream, args.steps)
+
+    kernel_key = f"update_{w.x_dtype}_B{B}_C{C}_L{L}_K{K}"
+    sha = kernel_sources_sha256(UPDATE_SOURCES)
+    result = {
+        "metric": UPDATE_METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.notes.get("description"),
+            "B": B, "C": C, "L": L, "K": K,
+            "activation": w.activation,
+            "storage_dtype": w.x_dtype,
+            "algorithmic_bytes": nbytes,
+            "buffer_sets": nsets,
+            "kernel": kernel_key,
+            "plan": plan,
+        },
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "traffic": profile_traffic(kernel_key, sha),
+            "kernel": kernel_key,
+            "avg_launch_us": round(ms_per_step * 1e3, 3),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+        "parity": parity,
+        "context": {
+            "copy_same_bytes_GBps": round(copy_gbps, 1),
+            "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+            "empty_kernel_us": round(empty_us, 3),
+            "device": props.name,
+            "cu_count": props.multi_processor_count,
+            "kernel_sources_sha256": sha,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = update_cpu_baseline(w, nbytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def update_parity(w, out_gpu, state_gpu):
+    """One update call against the oracle: out within tolerance of the forward with
+    the old state as initial states, the new state bit-exact to its final states."""
+    import numpy as np
+
+    from oracle import compare as ocmp
+    from oracle.from_torch import case, dtype_name, raw
+
+    c = case(w.x, w.weight, w.bias, None, w.initial_states, w.activation)
+    y, s = c.fwd()
+    g = raw(out_gpu.cpu().contiguous())
+    res = ocmp.compare(dtype_name(out_gpu), w.K, g, y, s)
+    got = raw(state_gpu.cpu().contiguous())
+    want = c.final_states()
+    bits = np.uint32 if got.dtype == np.float32 else np.uint16
+    return {"outputs": res["n"], "out_of_tolerance": res["n_bad"], "max_ulp": res["max_ulp"],
+            "bit_equal": res["bit_equal"],
+            "state_bit_exact": bool(np.array_equal(got.view(bits), want.view(bits)))}
+
+
+def update_cpu_baseline(w, nbytes, min_seconds):
+    """The oracle as written for one update call (its forward with the state as
+    initial states, plus the final states), repeated for at least `min_seconds`."""
+    from oracle import round_out
+    from oracle.from_torch import case
+
+    c = case(w.x, w.weight, w.bias, None, w.initial_states, w.activation)
+    passes, t_total = 0, 0.0
+    while passes == 0 or t_total < min_seconds:
+        t0 = time.perf_counter()
+        y, _ = c.fwd(want_sabs=False)
+        round_out(w.x_dtype, y)
+        c.final_states()
+        t_total += time.perf_counter() - t0
+        passes += 1
+    sec = t_total / passes
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole decode call ({w.B * w.C} rows), {passes} passes of the single-threaded "
+                      "fp64 oracle incl. rounding and the new state",
+            "seconds_per_pass": round(sec, 4)}
 
 
 def cpu_baseline(w, out_gpu, nbytes, min_seconds):

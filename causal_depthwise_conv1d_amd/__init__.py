@@ -8,7 +8,7 @@ that are not on a GPU, calls raise.
 
 Low level (same names as the C ABI):
     ccv_fwd(args, stream=None), ccv_fwd_check(args), ccv_fwd_plan(args),
-    ccv_update(args, stream=None), ccv_update_check(args),
+    ccv_update(args, stream=None), ccv_update_check(args), ccv_update_plan(args),
     ccv_status_str(code), ccv_abi_version()
 High level (the full-sequence contract of Ch.4 "Dao interface and source map",
 section "Contract of the full-sequence interface"; and the update kernel of the
@@ -33,7 +33,7 @@ CALIB_LIB_PATH = os.path.join(_HERE, "libccv_calib.so")
 CCV_ABI_VERSION = 1
 CCV_F32, CCV_F16, CCV_BF16 = 0, 1, 2
 CCV_ACT_NONE, CCV_ACT_SILU = 0, 1
-CCV_PATH_NONE, CCV_PATH_CHANNEL_FIRST, CCV_PATH_CHANNEL_LAST = 0, 1, 2
+CCV_PATH_NONE, CCV_PATH_CHANNEL_FIRST, CCV_PATH_CHANNEL_LAST, CCV_PATH_UPDATE = 0, 1, 2, 3
 STATUS = {
     0: "CCV_OK", -1: "CCV_E_NULL", -2: "CCV_E_SHAPE", -3: "CCV_E_KSIZE", -4: "CCV_E_DTYPE",
     -5: "CCV_E_LAYOUT", -6: "CCV_E_UNSUPPORTED", -7: "CCV_E_ALIAS", -8: "CCV_E_HIP",
@@ -130,6 +130,8 @@ def lib() -> ctypes.CDLL:
         L.ccv_update.restype = ctypes.c_int
         L.ccv_update_check.argtypes = [U]
         L.ccv_update_check.restype = ctypes.c_int
+        L.ccv_update_plan.argtypes = [U, ctypes.POINTER(ccv_plan_t)]
+        L.ccv_update_plan.restype = ctypes.c_int
         L.ccv_status_str.argtypes = [ctypes.c_int]
         L.ccv_status_str.restype = ctypes.c_char_p
         L.ccv_abi_version.argtypes = []
@@ -174,6 +176,13 @@ def ccv_update(args: ccv_update_args_t, stream=None) -> int:
 
 def ccv_update_check(args: ccv_update_args_t) -> int:
     return lib().ccv_update_check(ctypes.byref(args))
+
+
+def ccv_update_plan(args: ccv_update_args_t):
+    """(status, ccv_plan_t) of an update call, without touching the device."""
+    p = ccv_plan_t()
+    st = lib().ccv_update_plan(ctypes.byref(args), ctypes.byref(p))
+    return st, p
 
 
 def ccv_status_str(status: int) -> str:
@@ -335,7 +344,7 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
     x [B, C] (one step) or [B, C, L]; conv_state [B, C, K-1] in x's dtype, time
     ascending (the last K-1 inputs seen so far); weight [C, K] (oldest -> current);
     bias [C] in the weight's dtype.  Any strides are used as they are.  Returns out
-    with x's shape and dtype.  Afterwards conv_state holds the last K-1 inputs of
+    with x's shape and dtype, allocated with x's unit-stride dimension.  Afterwards conv_state holds the last K-1 inputs of
     (old state followed by x), exactly as ``causal_conv1d_fwd`` would return them as
     final states.
     """
@@ -360,7 +369,7 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
             raise ValueError("bias must have the weight's dtype")
         bias = bias.contiguous()
     if out is None:
-        out3 = torch.empty(B, C, L, dtype=x3.dtype, device=x3.device)
+        out3 = empty_like_layout(x3)
     else:
         if out.dtype != x3.dtype or tuple(out.shape) != tuple(x.shape):
             raise ValueError("out must have x's shape and dtype")
@@ -370,3 +379,12 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
         st = ccv_update(args)
     _raise(st, "ccv_update")
     return out3.squeeze(2) if one_step else out3
+
+
+def update_plan_for(x, conv_state, weight, bias=None, activation=None) -> dict:
+    """The launch causal_conv1d_update would make for these tensors (no device work)."""
+    x3 = x.unsqueeze(2) if x.dim() == 2 else x
+    out = empty_like_layout(x3)
+    st, p = ccv_update_plan(make_update_args(x3, weight.contiguous(), conv_state, out, bias, activation))
+    _raise(st, "ccv_update")
+    return p.as_dict()

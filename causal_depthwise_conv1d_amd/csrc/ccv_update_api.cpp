@@ -8,6 +8,7 @@
 //
 // Nothing here touches a device except ccv_update's kernel launch.
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -56,7 +57,29 @@ bool non_overlapping(const int64_t n[3], const int64_t s[3]) {
   return true;
 }
 
-int validate(const ccv_update_args_t* a, UpdArgs* u, uint32_t* grid) {
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The element stride of a dimension keeps 16-byte alignment (or is never used).
+bool stride_ok16(int64_t n, int64_t s, int es) { return n <= 1 || ((s * es) & 15) == 0; }
+
+// Whether the 16-byte path of the kernel applies (see launch_update).
+bool vector_path(const ccv_update_args_t* a) {
+  const int es = elt_size(a->x_dtype);
+  const int V = 16 / es;
+  const int64_t B = a->B, C = a->C, L = a->L, H = a->K - 1;
+  if (getenv("CCV_FORCE_SCALAR") && atoi(getenv("CCV_FORCE_SCALAR")) != 0) return false;
+  if (a->w_dtype != a->x_dtype || C % V != 0) return false;
+  if (!aligned16(a->weight) || (a->bias && !aligned16(a->bias))) return false;
+  const bool x_ok = (a->x_stride[1] == 1 || C <= 1) && aligned16(a->x) &&
+                    stride_ok16(B, a->x_stride[0], es) && stride_ok16(L, a->x_stride[2], es);
+  const bool o_ok = (a->out_stride[1] == 1 || C <= 1) && aligned16(a->out) &&
+                    stride_ok16(B, a->out_stride[0], es) && stride_ok16(L, a->out_stride[2], es);
+  const bool s_ok = a->state_stride[2] == 1 && (a->state_stride[1] == H || C <= 1) &&
+                    aligned16(a->state) && stride_ok16(B, a->state_stride[0], es);
+  return x_ok && o_ok && s_ok;
+}
+
+int validate(const ccv_update_args_t* a, UpdArgs* u, uint32_t* grid, bool* vec) {
   if (!a) return CCV_E_NULL;
   if (a->struct_size != (int64_t)sizeof(ccv_update_args_t)) return CCV_E_ABI;
   if (a->B < 0 || a->C < 0 || a->L < 0) return CCV_E_SHAPE;
@@ -83,7 +106,9 @@ int validate(const ccv_update_args_t* a, UpdArgs* u, uint32_t* grid) {
   if (!fits_bytes(max_offset(ns, a->state_stride), es)) return CCV_E_SHAPE;
   if (!non_overlapping(nx, a->out_stride) || !non_overlapping(ns, a->state_stride)) return CCV_E_LAYOUT;
 
-  const int64_t g = (rows + kUpdateBlock - 1) / kUpdateBlock;
+  *vec = vector_path(a);
+  const int64_t per_group = (int64_t)kUpdateBlock * (*vec ? 16 / es : kUpdateRowsPerLane);
+  const int64_t g = (rows + per_group - 1) / per_group;
   if (g > INT32_MAX) return CCV_E_SHAPE;
 
   *u = UpdArgs{};
@@ -116,16 +141,40 @@ extern "C" {
 int ccv_update_check(const ccv_update_args_t* args) {
   UpdArgs u;
   uint32_t grid;
-  return validate(args, &u, &grid);
+  bool vec;
+  return validate(args, &u, &grid, &vec);
+}
+
+int ccv_update_plan(const ccv_update_args_t* args, ccv_plan_t* plan) {
+  UpdArgs u;
+  uint32_t grid;
+  bool vec = false;
+  const int st = validate(args, &u, &grid, &vec);
+  if (st != CCV_OK || !plan) return st;
+  *plan = ccv_plan_t{};
+  plan->path = grid ? CCV_PATH_UPDATE : CCV_PATH_NONE;
+  if (!grid) return st;
+  const int rows_per_lane = vec ? 16 / elt_size(args->x_dtype) : kUpdateRowsPerLane;
+  plan->vector = vec ? 1 : 0;
+  plan->elems_per_lane = rows_per_lane;
+  plan->unroll = 1;
+  plan->grid = grid;
+  plan->block = kUpdateBlock;
+  plan->waves_per_group = kUpdateBlock / 64;
+  plan->work_items = args->B * args->C;
+  plan->span = args->L;
+  plan->channels_per_item = rows_per_lane;
+  return st;
 }
 
 int ccv_update(const ccv_update_args_t* args, void* hip_stream) {
   UpdArgs u;
   uint32_t grid;
-  const int st = validate(args, &u, &grid);
+  bool vec = false;
+  const int st = validate(args, &u, &grid, &vec);
   if (st != CCV_OK) return st;
   if (grid == 0) return CCV_OK;
-  const int err = launch_update(u, args->x_dtype, args->K, args->activation == CCV_ACT_SILU, grid,
+  const int err = launch_update(u, args->x_dtype, args->K, args->activation == CCV_ACT_SILU, vec, grid,
                                 hip_stream);
   return err == 0 ? CCV_OK : CCV_E_HIP;
 }

@@ -6,7 +6,10 @@
 
 namespace ccv {
 
-// One thread per (b, c) row, rows numbered r = b * C + c.  Strides are in elements.
+// Rows are numbered r = b * C + c.  Element path: wave w takes rows
+// [w * 64 * R, (w + 1) * 64 * R), lane l of it rows w * 64 * R + j * 64 + l, j < R.
+// 16-byte path (V = 16 / element size): wave w takes rows [w * 64 * V, (w + 1) * 64 * V),
+// lane l of it the V rows from w * 64 * V + l * V.  Strides are in elements.
 struct UpdArgs {
   const void* x;        // [B, C, L], x dtype
   void* out;            // [B, C, L], x dtype
@@ -20,9 +23,13 @@ struct UpdArgs {
   int32_t w_dtype;
 };
 
-constexpr int kUpdateBlock = 256;
+constexpr int kUpdateBlock = 256;          // 4 waves
+constexpr int kUpdateRowsPerLane = 4;      // R
 
-// Launch one instance; returns a hipError_t value (0 = success).
-int launch_update(const UpdArgs& a, int dtype, int K, bool silu, uint32_t grid, void* stream);
+// Launch one instance; returns a hipError_t value (0 = success).  vec selects the
+// 16-byte path, which needs: weight and bias in x's dtype; C a multiple of V; x and
+// out unit-stride in channels; the state stored [B, C, K-1] contiguously (s_i = 1,
+// s_c = K-1); every base pointer and every used stride 16-byte aligned.
+int launch_update(const UpdArgs& a, int dtype, int K, bool silu, bool vec, uint32_t grid, void* stream);
 
 }  // namespace ccv

@@ -101,7 +101,10 @@ typedef struct ccv_fwd_args {
 } ccv_fwd_args_t;
 
 /* Which kernel a call would launch and how (host-only; for tests and benches). */
-typedef enum { CCV_PATH_NONE = 0, CCV_PATH_CHANNEL_FIRST = 1, CCV_PATH_CHANNEL_LAST = 2 } ccv_path_t;
+typedef enum {
+  CCV_PATH_NONE = 0, CCV_PATH_CHANNEL_FIRST = 1, CCV_PATH_CHANNEL_LAST = 2,
+  CCV_PATH_UPDATE = 3      /* the update (decode) kernel; see ccv_update_plan */
+} ccv_path_t;
 
 typedef struct ccv_plan {
   int32_t path;            /* ccv_path_t; NONE when there is nothing to compute or write */
@@ -181,6 +184,16 @@ int ccv_update(const ccv_update_args_t* args, void* hip_stream);
 
 /* Validate `args` exactly as ccv_update does, without touching any device. */
 int ccv_update_check(const ccv_update_args_t* args);
+
+/* Validate and describe the launch ccv_update would make, without touching any
+ * device (`plan` may be NULL): path CCV_PATH_UPDATE (NONE when nothing is
+ * enqueued); vector 1 when each lane moves whole 16-byte vectors of V = 16 /
+ * element size consecutive channels (weight and bias in x's dtype, C a multiple
+ * of V, x and out unit-stride in channels, the state stored [B, C, K-1]
+ * contiguously, all 16-byte aligned), else 0; elems_per_lane and
+ * channels_per_item: rows per lane; grid, block, waves_per_group: the launch;
+ * work_items: B*C rows; span: L; unroll: 1. */
+int ccv_update_plan(const ccv_update_args_t* args, ccv_plan_t* plan);
 
 /* Static, NUL-terminated name of a status code ("CCV_OK", ...). */
 const char* ccv_status_str(int status);

@@ -286,3 +286,33 @@ def test_update_wrapper_refuses_cpu_tensors():
     x = torch.zeros(2, 4)
     with pytest.raises(ValueError):
         ccv.causal_conv1d_update(x, torch.zeros(2, 4, 3), torch.zeros(4, 4))
+
+
+def uplan(a):
+    st, p = ccv.ccv_update_plan(a)
+    assert st == 0, ccv.STATUS[st]
+    return p
+
+
+def test_update_plan_takes_16_byte_path_on_standard_layouts():
+    p = uplan(uargs(B=4, C=512))                     # x [B, C], state [B, C, K-1] contiguous
+    assert p.path == ccv.CCV_PATH_UPDATE and p.vector == 1 and p.elems_per_lane == 8
+    assert p.grid == -(-4 * 512 // (256 * 8)) and p.work_items == 4 * 512
+    p = uplan(uargs(C=64, L=3, x_stride=(3 * 64, 1, 64), out_stride=(3 * 64, 1, 64)))
+    assert p.vector == 1                             # channel-last steps
+    a = uargs(C=64)
+    a.x_dtype = a.w_dtype = ccv.CCV_F32
+    p = uplan(a)
+    assert p.vector == 1 and p.elems_per_lane == 4
+
+
+def test_update_plan_falls_back_to_element_path():
+    assert uplan(uargs(state_layout="bic")).vector == 0            # channels-fastest state
+    assert uplan(uargs(C=60)).vector == 0                          # C not a multiple of 8
+    assert uplan(uargs(w_dtype=ccv.CCV_F32)).vector == 0           # weights in another dtype
+    assert uplan(uargs(x=X + 2)).vector == 0                       # x not 16-byte aligned
+    assert uplan(uargs(bias=BIAS + 2)).vector == 0
+    assert uplan(uargs(L=3, x_stride=(192, 3, 1), out_stride=(192, 3, 1))).vector == 0
+    p = uplan(uargs(C=60))
+    assert p.elems_per_lane == 4 and p.grid == -(-2 * 60 // (256 * 4))
+    assert uplan(uargs(L=0, x=None, weight=None, state=None, out=None)).path == ccv.CCV_PATH_NONE

@@ -96,26 +96,61 @@ def test_update_matches_oracle(dtype, K):
         (1, 1, 7, "cf", "bci", True, None, None),
         (5, 513, 2, "cl", "bic", True, "swish", "bf16"),
         (1, 2000, 1, "2d", "slice", False, "silu", "f16"),
+        # the 16-byte path: C a multiple of 8, [B, C, K-1] state, weights in x's dtype
+        (4, 256, 1, "2d", "bci", True, "silu", None),
+        (2, 512, 3, "cl", "bci", False, None, None),
+        (3, 1024, 1, "cf", "bci", True, None, None),
     ]
     for i, (B, C, L, xl, sl, bias, act, w_dtype) in enumerate(cases):
         seed = 900 + 10 * K + i
         x = x_view(B, C, L, dtype, xl, seed)
         st = state_view(B, C, H, dtype, sl, seed)
         w, b = params(C, K, w_dtype or dtype, bias, seed)
-        log(f"  update {dtype}/{w.dtype} K={K} B={B} C={C} L={L} x={xl} state={sl} bias={bias} act={act}")
+        plan = ccv.update_plan_for(x, st, w, b, act)
+        assert plan["vector"] == (1 if i >= 6 else 0), (i, plan)
+        log(f"  update {dtype}/{w.dtype} K={K} B={B} C={C} L={L} x={xl} state={sl} bias={bias} act={act} "
+            f"vector={plan['vector']}")
         check_update(x, st, w, b, act, f"[{dtype} K={K} case {i}]")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_update_vector_path_equals_element_path(dtype, monkeypatch):
+    """The 16-byte path and the element path give the same bits (out and new state)."""
+    for K in KS:
+        for L, xl in ((1, "2d"), (4, "cl")):
+            B, C = 3, 1024
+            seed = 960 + K + L
+            x = x_view(B, C, L, dtype, xl, seed)
+            st0 = state_view(B, C, K - 1, dtype, "bci", seed)
+            w, b = params(C, K, dtype, True, seed)
+            res = []
+            for force in ("0", "1"):
+                monkeypatch.setenv("CCV_FORCE_SCALAR", force)
+                assert ccv.update_plan_for(x, st0, w, b, "silu")["vector"] == (force == "0")
+                st = st0.clone()
+                out = ccv.causal_conv1d_update(x, st, w, b, "silu")
+                torch.cuda.synchronize()
+                res.append((raw(out.cpu().contiguous()), raw(st.cpu())))
+            bits = np.uint32 if dtype == "f32" else np.uint16
+            assert np.array_equal(res[0][0].view(bits), res[1][0].view(bits)), (K, L, "out")
+            assert np.array_equal(res[0][1].view(bits), res[1][1].view(bits)), (K, L, "state")
+
+
+@pytest.mark.parametrize("C", [130, 256])
 @pytest.mark.parametrize("act", [None, "silu"])
 @pytest.mark.parametrize("K", KS)
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_decode_equals_forward(dtype, K, act):
+def test_decode_equals_forward(dtype, K, act, C):
     """The forward over 41 steps from a history h0, and the same steps fed to the
     update in chunks of 1, 2, 3 and 5 from the same h0: identical bits for every
-    output and for the final state."""
-    B, C, L, H = 2, 130, 41, K - 1
+    output and for the final state.  C = 130 takes the element path of the update,
+    C = 256 its 16-byte path (the steps are then given channel-last)."""
+    B, L, H = 2, 41, K - 1
     seed = 950 + K
-    x = rand((B, C, L), dtype, seed, 0).cuda()
+    if C % 8:
+        x = rand((B, C, L), dtype, seed, 0).cuda()
+    else:
+        x = rand((B, L, C), dtype, seed, 0).cuda().transpose(1, 2)
     h0 = rand((B, C, H), dtype, seed, 1).cuda()
     w, b = params(C, K, dtype, True, seed)
     ref, fs = ccv.causal_conv1d_fwd(x, w, b, initial_states=h0, return_final_states=True,
@@ -123,6 +158,7 @@ def test_decode_equals_forward(dtype, K, act):
     for chunks in ([1] * L, [2] * 20 + [1], [3, 5, 1, 5, 3, 5, 5, 5, 5, 4]):
         assert sum(chunks) == L
         state = h0.clone()
+        assert ccv.update_plan_for(x[:, :, :1], state, w, b, act)["vector"] == (C % 8 == 0)
         outs, t = [], 0
         for n in chunks:
             xs = x[:, :, t:t + n]
@@ -155,13 +191,16 @@ def test_update_no_activation_is_the_fp32_fma_chain(dtype):
         assert np.array_equal(got.view(bits), want.view(bits)), (dtype, K)
 
 
-def test_update_many_rows():
-    """262,400 rows: more than one workgroup per 256 rows, a ragged last one."""
-    B, C, K = 64, 4100, 4
+@pytest.mark.parametrize("C", [4100, 4096])
+def test_update_many_rows(C):
+    """About 262,000 rows over many workgroups: C = 4100 on the element path (a
+    ragged last workgroup), C = 4096 on the 16-byte path."""
+    B, K = 64, 4
     x = rand((B, C), "bf16", 990, 0).cuda()
     st = state_view(B, C, K - 1, "bf16", "bci", 990)
     w, b = params(C, K, "bf16", True, 990)
-    check_update(x, st, w, b, "silu", "[many rows]")
+    assert ccv.update_plan_for(x, st, w, b, "silu")["vector"] == (C % 8 == 0)
+    check_update(x, st, w, b, "silu", f"[many rows C={C}]")
 
 
 def test_update_writes_only_its_elements():

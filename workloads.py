@@ -255,3 +255,20 @@ def workload(i: int, poison_unused: bool = False, L_override: Optional[int] = No
     w.name = WORKLOAD_KEYS[i]
     w.notes["description"] = WORKLOADS[i]
     return w
+
+
+# ---- the update (decode) bench case ---------------------------------------------
+
+DECODE_DESCRIPTION = ("decode step bf16: B=256 sequences, C=4096 channels, one new step each, K=4, "
+                      "state [B,C,3] time-fastest, SiLU, no bias")
+
+
+def decode_workload() -> Workload:
+    """The update (decode) bench case, seed 1006: x [B, C, 1] ~ N(0,1), weight
+    ~ N(0, 1/4), the state (carried as initial_states, stored [B, C, K-1]) ~ N(0,1);
+    the channel count and dtype of the strided channel-last workload."""
+    w = make_case(B=256, C=4096, L=1, K=4, x_dtype="bf16", layout="cf", bias=False, init=True,
+                  init_layout="time_fast", activation="silu", seed=1006, w_var=0.25)
+    w.name = "update_bf16_B256_C4096_L1_K4_silu"
+    w.notes["description"] = DECODE_DESCRIPTION
+    return w
