@@ -46,6 +46,11 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _Grad(ctypes.Structure):
+    _fields_ = [("dout", ctypes.c_void_p), ("ds", ctypes.c_int64 * 3),
+                ("dfs", ctypes.c_void_p), ("fs", ctypes.c_int64 * 3)]
+
+
 _lib = None
 
 
@@ -65,6 +70,7 @@ def _load(path):
     L.ora_fwd.argtypes = [P, vp, vp]
     L.ora_points.argtypes = [P, i64, vp, vp, vp]
     L.ora_final_states.argtypes = [P, vp]
+    L.ora_bwd.argtypes = [P, ctypes.POINTER(_Grad)] + [vp] * 8
     L.ora_point_f32.argtypes = [P, i64, i64, i64, ctypes.POINTER(ctypes.c_float)]
     L.ora_fwd_f32.argtypes = [P, vp]
     L.ora_points_f32.argtypes = [P, i64, vp, vp]
@@ -194,6 +200,40 @@ class Case:
                                 z.ctypes.data) != 0:
             raise IndexError("sample index out of range")
         return z
+
+    def bwd(self, dout, dout_strides, dout_off=0, dfs=None, dfs_strides=None, dfs_off=0):
+        """Gradients in fp64 (the chain rule of the forward) and their error scales.
+
+        dout: flat storage in x's dtype, dout[b,c,t] at dout_off + b*s0 + c*s1 + t*s2;
+        dfs: None or flat storage of dfinal_states [B, C, K-1] in x's dtype.
+        Returns dict(dx, dinit, dw, db, ex, einit, ew, eb) of float64 arrays
+        ([B,C,L], [B,C,K-1] or None, [C,K], [C] and the same for the scales)."""
+        st = _NP_STORAGE[self.x_dtype]
+        dout = np.ascontiguousarray(np.asarray(dout).reshape(-1)).view(st)
+        es = dout.itemsize
+        g = _Grad()
+        g.dout = dout.ctypes.data + int(dout_off) * es
+        g.ds = (ctypes.c_int64 * 3)(*[int(v) for v in dout_strides])
+        if dfs is not None:
+            dfs = np.ascontiguousarray(np.asarray(dfs).reshape(-1)).view(st)
+            g.dfs = dfs.ctypes.data + int(dfs_off) * es
+            g.fs = (ctypes.c_int64 * 3)(*[int(v) for v in dfs_strides])
+        else:
+            g.dfs = None
+            g.fs = (ctypes.c_int64 * 3)(0, 0, 0)
+        B, C, L, K = self.B, self.C, self.L, self.K
+        has_init = self._init is not None
+        out = {
+            "dx": np.zeros((B, C, L)), "ex": np.zeros((B, C, L)),
+            "dinit": np.zeros((B, C, K - 1)) if has_init else None,
+            "einit": np.zeros((B, C, K - 1)) if has_init else None,
+            "dw": np.zeros((C, K)), "ew": np.zeros((C, K)), "db": np.zeros(C), "eb": np.zeros(C),
+        }
+        ptrs = [_ptr(out[k]) for k in ("dx", "dinit", "dw", "db", "ex", "einit", "ew", "eb")]
+        if lib().ora_bwd(ctypes.byref(self._p), ctypes.byref(g), *ptrs) != 0:
+            raise RuntimeError("ora_bwd failed")
+        _keep = (dout, dfs)   # noqa: F841  (buffers stay alive through the call)
+        return out
 
     def final_states(self):
         """Raw storage [B, C, K-1] of the last K-1 extended inputs."""

@@ -12,6 +12,7 @@
 #include "ccv_oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ---- storage decoding ----------------------------------------------------- */
@@ -271,5 +272,92 @@ int ora_fwd_f32(const ora_problem_t* p, float* z) {
 int ora_points_f32(const ora_problem_t* p, int64_t n, const int64_t* idx, float* z) {
   for (int64_t i = 0; i < n; ++i)
     if (ora_point_f32(p, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], &z[i]) != 0) return -1;
+  return 0;
+}
+
+/* ---- backward ------------------------------------------------------------------ */
+
+/* Whether term k of output t counts (the forward's mask). */
+static int ora_keep(const ora_problem_t* p, int64_t b, int64_t t, int k) {
+  if (p->seq == NULL) return 1;
+  int64_t src = t - p->K + 1 + k;
+  if (src < 0) return 0;
+  return p->seq[b * p->L + src] == p->seq[b * p->L + t];
+}
+
+int ora_bwd(const ora_problem_t* p, const ora_grad_t* g, double* dx, double* dinit,
+            double* dw, double* db, double* ex, double* einit, double* ew, double* eb) {
+  const int K = p->K;
+  const int64_t B = p->B, C = p->C, L = p->L, H = K - 1;
+  double* dz = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double* edz = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  if (!dz || !edz) {
+    free(dz);
+    free(edz);
+    return -1;
+  }
+  for (int64_t c = 0; c < C; ++c) {
+    for (int k = 0; k < K; ++k) {
+      if (dw) dw[c * K + k] = 0.0;
+      if (ew) ew[c * K + k] = 0.0;
+    }
+    if (db) db[c] = 0.0;
+    if (eb) eb[c] = 0.0;
+  }
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t c = 0; c < C; ++c) {
+      /* dz over the row: the pre-activation z is recomputed from the forward's terms. */
+      for (int64_t t = 0; t < L; ++t) {
+        double y, z, sz;
+        ora_point(p, b, c, t, &y, &z, &sz);
+        double go = ora_decode(g->dout, p->x_dtype, b * g->ds[0] + c * g->ds[1] + t * g->ds[2]);
+        double slope = 1.0;
+        if (p->silu) {
+          double s = 1.0 / (1.0 + exp(-z));
+          slope = s * (1.0 + z * (1.0 - s));
+        }
+        dz[t] = go * slope;
+        edz[t] = fabs(dz[t]) + fabs(go) * sz;     /* |dz| plus its sensitivity to z's error */
+      }
+      /* dX~ at every extended position j, from the outputs t = j+K-1-k that read it. */
+      for (int64_t j = -H; j < L; ++j) {
+        double acc = 0.0, e = 0.0;
+        for (int k = 0; k < K; ++k) {
+          int64_t t = j + K - 1 - k;
+          if (t < 0 || t >= L || !ora_keep(p, b, t, k)) continue;
+          double wk = ora_decode(p->w, p->w_dtype, c * K + k);
+          acc += wk * dz[t];
+          e += fabs(wk) * edz[t];
+        }
+        if (g->dfs != NULL && j >= L - H) {
+          int64_t i = j - (L - H);
+          double v = ora_decode(g->dfs, p->x_dtype, b * g->fs[0] + c * g->fs[1] + i * g->fs[2]);
+          acc += v;
+          e += fabs(v);
+        }
+        if (j >= 0) {
+          int64_t o = (b * C + c) * L + j;
+          if (dx) dx[o] = acc;
+          if (ex) ex[o] = e;
+        } else if (p->init != NULL) {
+          int64_t o = (b * C + c) * H + (j + H);
+          if (dinit) dinit[o] = acc;
+          if (einit) einit[o] = e;
+        }
+      }
+      /* Parameter gradients: every kept (t, k) term, summed over b and t. */
+      for (int64_t t = 0; t < L; ++t) {
+        for (int k = 0; k < K; ++k) {
+          if (!ora_keep(p, b, t, k)) continue;
+          double xv = ora_xt(p, b, c, t - K + 1 + k);
+          if (dw) dw[c * K + k] += dz[t] * xv;
+          if (ew) ew[c * K + k] += edz[t] * fabs(xv);
+        }
+        if (db) db[c] += dz[t];
+        if (eb) eb[c] += edz[t];
+      }
+    }
+  free(dz);
+  free(edz);
   return 0;
 }

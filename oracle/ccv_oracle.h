@@ -89,6 +89,33 @@ void     ora_f32_to_f16_array(const float* in, uint16_t* out, int64_t n);
 void     ora_f16_to_f64_array(const uint16_t* in, double* out, int64_t n);
 void     ora_bf16_to_f64_array(const uint16_t* in, double* out, int64_t n);
 
+/* ---- backward ------------------------------------------------------------------
+ * The gradient of the forward, written out by the chain rule (Ch.4 "Dao interface
+ * and source map", section "How autograd links forward and backward": the
+ * backward takes dout and, when the forward returned states, dfinal_states; it
+ * returns dx, dweight, dbias and, with initial_states, their gradient; seq_idx
+ * has none).  With z the pre-activation and X~ the extended input:
+ *   dz[b,c,t]   = dout[b,c,t] * act'(z[b,c,t])      (SiLU': s(z) * (1 + z * (1 - s(z))))
+ *   dX~[b,c,j]  = sum_k keep(t,k) w[c,k] dz[b,c,t] over t = j+K-1-k in [0, L)
+ *                 + dfinal_states[b,c,j-(L-K+1)] when j >= L-K+1
+ *   dx[b,c,t]   = dX~[b,c,t];   dinitial_states[b,c,i] = dX~[b,c,i-(K-1)]
+ *   dw[c,k]     = sum_{b,t} keep(t,k) dz[b,c,t] X~[b,c,t-K+1+k];  db[c] = sum_{b,t} dz[b,c,t]
+ * The error scales bound how far an fp32 evaluation may stray: for each gradient
+ * element, the sum of the magnitudes of its terms, where each dz also carries
+ * |dout| * S_z (the forward's sum of magnitudes of z). */
+typedef struct {
+  const void* dout;        /* dout[b,c,t] at dout + b*ds[0] + c*ds[1] + t*ds[2], x_dtype */
+  int64_t ds[3];
+  const void* dfs;         /* NULL or dfinal_states[b,c,i] at dfs + b*fs[0] + c*fs[1] + i*fs[2] */
+  int64_t fs[3];
+} ora_grad_t;
+
+/* dx [B*C*L], dinit [B*C*(K-1)] (NULL when there are no initial_states), dw [C*K],
+ * db [C], and their error scales ex, einit, ew, eb (same shapes; any may be NULL).
+ * Returns 0, or -1 when scratch memory cannot be had. */
+int ora_bwd(const ora_problem_t* p, const ora_grad_t* g, double* dx, double* dinit,
+            double* dw, double* db, double* ex, double* einit, double* ew, double* eb);
+
 /* Diagnostic binary32 mode: acc = bias (or 0), then acc = fmaf(w[c,k], X~, acc)
  * over the kept terms in ascending k; no activation.  Writes the binary32 sum. */
 int ora_point_f32(const ora_problem_t* p, int64_t b, int64_t c, int64_t t, float* z);

@@ -46,5 +46,16 @@ def case(x, weight, bias=None, seq_idx=None, initial_states=None, activation=Non
                 silu=activation in ("silu", "swish"), **kw)
 
 
+def bwd(c: Case, dout: torch.Tensor, dfinal_states=None) -> dict:
+    """Oracle gradients of case `c` for dout [B,C,L] and dfinal_states [B,C,K-1] (any
+    strides, x's dtype)."""
+    db_, do = _base_and_offset(dout)
+    kw = {}
+    if dfinal_states is not None:
+        fb, fo = _base_and_offset(dfinal_states)
+        kw = dict(dfs=fb, dfs_off=fo, dfs_strides=tuple(dfinal_states.stride()))
+    return c.bwd(db_, tuple(dout.stride()), do, **kw)
+
+
 def case_from_workload(w) -> Case:
     return case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)

@@ -10,7 +10,9 @@ Each ``pin_*`` function raises AssertionError when the oracle disagrees with:
     sequences equal separate runs, layout independence, masked NaN not leaking),
   * torch's own dtype conversions and SiLU,
   * for the diagnostic binary32 mode: an exact-rational emulation of its
-    fused multiply-add chain, exactness on integer data, and the K-rounding bound.
+    fused multiply-add chain, exactness on integer data, and the K-rounding bound,
+  * for the backward: torch autograd in fp64, central finite differences of the
+    forward oracle, and the packing and chunking invariants of the gradients.
 
 The functions take the ``oracle`` module so that ``test_oracle_mutants`` can run
 them against deliberately broken builds of the oracle.
@@ -467,7 +469,159 @@ def pin_f32_mode_error_bound(ora):
             assert np.array_equal(case.points_f32(idx), case.fwd_f32()[idx[:, 0], idx[:, 1], idx[:, 2]])
 
 
+# ---- backward -------------------------------------------------------------------------
+
+def _bwd(ora, x, w, b=None, seq=None, init=None, silu=False, dout=None, dfs=None):
+    from oracle.from_torch import bwd
+    c = _cf_case(ora, x, w, b, seq=seq, init=init, silu=silu)
+    return bwd(c, dout, dfs)
+
+
+def _autograd(x, w, b, init, silu, dout, dfs):
+    """torch autograd in fp64 through grouped conv1d on the history-extended input."""
+    K = w.shape[1]
+    xd = x.double().requires_grad_()
+    wd = w.double().requires_grad_()
+    bd = None if b is None else b.double().requires_grad_()
+    hd = (init.double() if init is not None else torch.zeros(x.shape[0], x.shape[1], K - 1,
+                                                             dtype=torch.float64)).requires_grad_()
+    xt = torch.cat([hd, xd], 2)
+    z = torch.nn.functional.conv1d(xt, wd[:, None, :], bd, groups=x.shape[1])
+    y = torch.nn.functional.silu(z) if silu else z
+    loss = (y * dout.double()).sum()
+    if dfs is not None:
+        loss = loss + (xt[:, :, xt.shape[2] - (K - 1):] * dfs.double()).sum()
+    loss.backward()
+    return dict(dx=xd.grad, dw=wd.grad, db=None if b is None else bd.grad,
+                dinit=hd.grad if init is not None else None)
+
+
+def pin_bwd_autograd(ora):
+    """Every gradient against torch autograd (fp64, CPU), all K, storage dtypes, with
+    and without bias, history, dfinal_states and SiLU, including L < K-1."""
+    g = _gen(22)
+    for K in (2, 3, 4):
+        for dt, wdt in (("f32", "f32"), ("bf16", "bf16"), ("f16", "f32")):
+            for L, bias, init, dfs_on, silu in ((13, True, True, True, True), (9, False, False, False, False),
+                                                (max(1, K - 2), True, True, True, True), (1, True, False, True, True)):
+                B, C = 2, 3
+                x = torch.randn(B, C, L, generator=g).to(DT[dt])
+                w = (torch.randn(C, K, generator=g) * 0.5).to(DT[wdt])
+                b = torch.randn(C, generator=g).to(DT[wdt]) if bias else None
+                h = torch.randn(B, C, K - 1, generator=g).to(DT[dt]) if init else None
+                dout = torch.randn(B, C, L, generator=g).to(DT[dt])
+                dfs = torch.randn(B, C, K - 1, generator=g).to(DT[dt]) if dfs_on else None
+                r = _bwd(ora, x, w, b, init=h, silu=silu, dout=dout, dfs=dfs)
+                ref = _autograd(x, w, b, h, silu, dout, dfs)
+                for name in ("dx", "dw", "db", "dinit"):
+                    if ref[name] is None:
+                        continue
+                    want = ref[name].numpy()
+                    scale = np.maximum(np.abs(want), 1.0)
+                    assert np.all(np.abs(r[name] - want) <= 1e-12 * scale), (K, dt, L, name)
+
+
+def _loss(ora, x, w, b, seq, init, silu, dout, dfs):
+    c = _cf_case(ora, x, w, b, seq=seq, init=init, silu=silu)
+    y, _ = c.fwd(want_sabs=False)
+    loss = float(np.sum(y * dout.double().numpy()))
+    if dfs is not None:
+        K = w.shape[1]
+        xt = torch.cat([init if init is not None else torch.zeros(x.shape[0], x.shape[1], K - 1), x], 2)
+        loss += float((xt[:, :, xt.shape[2] - (K - 1):].double() * dfs.double()).sum())
+    return loss
+
+
+def pin_bwd_finite_differences(ora):
+    """Central differences of the forward oracle's loss sum(dout * y) + sum(dfs * fs)
+    on dyadic data (so x +- h is exact in fp32): every gradient entry, with a
+    seq_idx mask and with history."""
+    g = _gen(23)
+    h = 2.0 ** -10
+
+    def dyadic(*shape):
+        return torch.randint(-256, 257, shape, generator=g).float() / 128.0
+
+    for K, L, seq, init in ((3, 9, [0, 0, 0, 1, 1, 2, 2, 2, 2], False), (4, 7, None, True)):
+        B, C = 1, 2
+        x, w, b = dyadic(B, C, L), dyadic(C, K) / 2, dyadic(C)
+        hist = dyadic(B, C, K - 1) if init else None
+        s = None if seq is None else torch.tensor([seq], dtype=torch.int32)
+        dout = dyadic(B, C, L)
+        dfs = dyadic(B, C, K - 1) if init else None
+        r = _bwd(ora, x, w, b, seq=s, init=hist, silu=True, dout=dout, dfs=dfs)
+        params = {"dx": x, "dw": w, "db": b}
+        if init:
+            params["dinit"] = hist
+        for name, t in params.items():
+            flat = t.view(-1)
+            for i in range(flat.numel()):
+                v = float(flat[i])
+                flat[i] = v + h
+                up = _loss(ora, x, w, b, s, hist, True, dout, dfs)
+                flat[i] = v - h
+                dn = _loss(ora, x, w, b, s, hist, True, dout, dfs)
+                flat[i] = v
+                fd = (up - dn) / (2 * h)
+                got = r[name].reshape(-1)[i]
+                assert abs(got - fd) <= 1e-4 * max(1.0, abs(fd)), (name, i, got, fd)
+
+
+def pin_bwd_packing(ora):
+    """A packed backward with seq_idx equals separate backward runs of each sequence:
+    dx bit for bit (the same terms in the same order), dw and db as the sums."""
+    g = _gen(24)
+    for K in (2, 3, 4):
+        lengths = [1, 5, K - 1, 9, 2, 13, K]
+        L, C = sum(lengths), 3
+        x = torch.randn(1, C, L, generator=g)
+        w = torch.randn(C, K, generator=g) * 0.5
+        b = torch.randn(C, generator=g)
+        dout = torch.randn(1, C, L, generator=g)
+        seq = torch.tensor(np.repeat(np.arange(len(lengths)), lengths), dtype=torch.int32).reshape(1, L)
+        r = _bwd(ora, x, w, b, seq=seq, silu=True, dout=dout)
+        pos, dw, db = 0, 0.0, 0.0
+        for n in lengths:
+            part = _bwd(ora, x[:, :, pos:pos + n].contiguous(), w, b, silu=True,
+                        dout=dout[:, :, pos:pos + n].contiguous())
+            assert np.array_equal(r["dx"][:, :, pos:pos + n], part["dx"]), (K, n)
+            dw, db = dw + part["dw"], db + part["db"]
+            pos += n
+        assert np.allclose(r["dw"], dw, rtol=1e-13, atol=1e-13), K
+        assert np.allclose(r["db"], db, rtol=1e-13, atol=1e-13), K
+
+
+def pin_bwd_chunking(ora):
+    """The backward of [x1 | x2] equals chunk 2's backward (history = chunk 1's final
+    states) followed by chunk 1's backward with dfinal_states = chunk 2's
+    d(initial_states): dx, d(initial_states) and the summed dw, db.  Dyadic data and
+    no activation keep every sum exact, so the comparison is exact too (the
+    d(initial_states) handed between chunks is stored in fp32)."""
+    g = _gen(25)
+
+    def dyadic(*shape):
+        return torch.randint(-64, 65, shape, generator=g).float() / 32.0
+
+    for K in (2, 3, 4):
+        B, C, L = 2, 3, 30
+        x, w, b = dyadic(B, C, L), dyadic(C, K), dyadic(C)
+        h, dout, dfs = dyadic(B, C, K - 1), dyadic(B, C, L), dyadic(B, C, K - 1)
+        full = _bwd(ora, x, w, b, init=h, dout=dout, dfs=dfs)
+        for L1 in sorted({1, K - 2, K - 1, K, 17} - {0}):
+            x1, x2 = x[:, :, :L1].contiguous(), x[:, :, L1:].contiguous()
+            f1 = torch.from_numpy(_cf_case(ora, x1, w, b, init=h).final_states().copy())
+            r2 = _bwd(ora, x2, w, b, init=f1, dout=dout[:, :, L1:].contiguous(), dfs=dfs)
+            d2 = torch.from_numpy(r2["dinit"]).float()
+            assert np.array_equal(d2.double().numpy(), r2["dinit"])       # exact in fp32
+            r1 = _bwd(ora, x1, w, b, init=h, dout=dout[:, :, :L1].contiguous(), dfs=d2)
+            assert np.array_equal(np.concatenate([r1["dx"], r2["dx"]], 2), full["dx"]), (K, L1)
+            assert np.array_equal(r1["dinit"], full["dinit"]), (K, L1)
+            assert np.array_equal(r1["dw"] + r2["dw"], full["dw"]), (K, L1)
+            assert np.array_equal(r1["db"] + r2["db"], full["db"]), (K, L1)
+
+
 ALL_PINS = [pin_golden, pin_digits, pin_one_hot, pin_delta, pin_constant, pin_conv1d,
             pin_chunking, pin_packing, pin_mask_nan, pin_layout, pin_silu, pin_converters,
             pin_round_out, pin_f32_mode_exact_rational, pin_f32_mode_integers_are_exact,
-            pin_f32_mode_error_bound]
+            pin_f32_mode_error_bound, pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_packing,
+            pin_bwd_chunking]

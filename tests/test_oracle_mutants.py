@@ -41,6 +41,19 @@ MUTANTS = [
     ("f32_bias_dropped", "if (p->bias != NULL) acc = (float)ora_decode(p->bias, p->w_dtype, c);", ""),
     ("f32_taps_reversed", "float wv = (float)ora_decode(p->w, p->w_dtype, c * K + k);",
      "float wv = (float)ora_decode(p->w, p->w_dtype, c * K + (K - 1 - k));"),
+    # the backward
+    ("bwd_no_activation_slope", "dz[t] = go * slope;", "dz[t] = go;"),
+    ("bwd_slope_sign", "slope = s * (1.0 + z * (1.0 - s));", "slope = s * (1.0 - z * (1.0 - s));"),
+    ("bwd_dx_taps_reversed", "int64_t t = j + K - 1 - k;", "int64_t t = j + k;"),
+    ("bwd_dx_mask_ignored", "if (t < 0 || t >= L || !ora_keep(p, b, t, k)) continue;",
+     "if (t < 0 || t >= L) continue;"),
+    ("bwd_dfinal_ignored", "acc += v;", "acc += 0.0 * v;"),
+    ("bwd_dfinal_reversed", "int64_t i = j - (L - H);", "int64_t i = (H - 1) - (j - (L - H));"),
+    ("bwd_dinit_reversed", "int64_t o = (b * C + c) * H + (j + H);",
+     "int64_t o = (b * C + c) * H + (H - 1 - (j + H));"),
+    ("bwd_dw_mask_ignored", "if (!ora_keep(p, b, t, k)) continue;\n          double xv",
+     "double xv"),
+    ("bwd_db_halved", "if (db) db[c] += dz[t];", "if (db) db[c] += 0.5 * dz[t];"),
 ]
 
 
