@@ -9,6 +9,8 @@ that are not on a GPU, calls raise.
 Low level (same names as the C ABI):
     ccv_fwd(args, stream=None), ccv_fwd_check(args), ccv_fwd_plan(args),
     ccv_update(args, stream=None), ccv_update_check(args), ccv_update_plan(args),
+    ccv_bwd(args, stream=None), ccv_bwd_check(args), ccv_bwd_plan(args),
+    ccv_bwd_workspace_size(args),
     ccv_status_str(code), ccv_abi_version()
 High level (the full-sequence contract of Ch.4 "Dao interface and source map",
 section "Contract of the full-sequence interface"; and the update kernel of the
@@ -17,6 +19,11 @@ same page's section "Reading the source along the call chain"):
                       return_final_states=False, final_states_out=None,
                       activation=None)
     causal_conv1d_update(x, conv_state, weight, bias=None, activation=None)
+    causal_conv1d_bwd(x, weight, bias, dout, seq_idx=None, initial_states=None,
+                      dfinal_states=None, activation=None, ...)
+    causal_conv1d_fn(x, weight, bias=None, seq_idx=None, initial_states=None,
+                     return_final_states=False, final_states_out=None, activation=None)
+        (differentiable: a torch.autograd.Function over the forward and backward)
 """
 from __future__ import annotations
 
@@ -33,7 +40,7 @@ CALIB_LIB_PATH = os.path.join(_HERE, "libccv_calib.so")
 CCV_ABI_VERSION = 1
 CCV_F32, CCV_F16, CCV_BF16 = 0, 1, 2
 CCV_ACT_NONE, CCV_ACT_SILU = 0, 1
-CCV_PATH_NONE, CCV_PATH_CHANNEL_FIRST, CCV_PATH_CHANNEL_LAST, CCV_PATH_UPDATE = 0, 1, 2, 3
+CCV_PATH_NONE, CCV_PATH_CHANNEL_FIRST, CCV_PATH_CHANNEL_LAST, CCV_PATH_UPDATE, CCV_PATH_BACKWARD = 0, 1, 2, 3, 4
 STATUS = {
     0: "CCV_OK", -1: "CCV_E_NULL", -2: "CCV_E_SHAPE", -3: "CCV_E_KSIZE", -4: "CCV_E_DTYPE",
     -5: "CCV_E_LAYOUT", -6: "CCV_E_UNSUPPORTED", -7: "CCV_E_ALIAS", -8: "CCV_E_HIP",
@@ -84,6 +91,32 @@ class ccv_update_args_t(ctypes.Structure):
         self.struct_size = ctypes.sizeof(ccv_update_args_t)
 
 
+class ccv_bwd_args_t(ctypes.Structure):
+    """Mirror of ``ccv_bwd_args_t`` in include/ccv.h (field order and types)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_int64),
+        ("B", ctypes.c_int64), ("C", ctypes.c_int64), ("L", ctypes.c_int64),
+        ("K", ctypes.c_int32), ("activation", ctypes.c_int32),
+        ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("x_stride", _I64x3),
+        ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("seq_idx", ctypes.c_void_p),
+        ("initial_states", ctypes.c_void_p), ("init_stride", _I64x3),
+        ("dout", ctypes.c_void_p), ("dout_stride", _I64x3),
+        ("dfinal_states", ctypes.c_void_p), ("dfinal_stride", _I64x3),
+        ("dx", ctypes.c_void_p), ("dx_stride", _I64x3),
+        ("dweight", ctypes.c_void_p),
+        ("dbias", ctypes.c_void_p),
+        ("dinitial_states", ctypes.c_void_p), ("dinit_stride", _I64x3),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+    ]
+
+    def __init__(self, **kw):
+        super().__init__(**kw)
+        self.struct_size = ctypes.sizeof(ccv_bwd_args_t)
+
+
 class ccv_plan_t(ctypes.Structure):
     """Mirror of ``ccv_plan_t`` in include/ccv.h."""
     _fields_ = [
@@ -132,6 +165,15 @@ def lib() -> ctypes.CDLL:
         L.ccv_update_check.restype = ctypes.c_int
         L.ccv_update_plan.argtypes = [U, ctypes.POINTER(ccv_plan_t)]
         L.ccv_update_plan.restype = ctypes.c_int
+        G = ctypes.POINTER(ccv_bwd_args_t)
+        L.ccv_bwd.argtypes = [G, ctypes.c_void_p]
+        L.ccv_bwd.restype = ctypes.c_int
+        L.ccv_bwd_check.argtypes = [G]
+        L.ccv_bwd_check.restype = ctypes.c_int
+        L.ccv_bwd_plan.argtypes = [G, ctypes.POINTER(ccv_plan_t)]
+        L.ccv_bwd_plan.restype = ctypes.c_int
+        L.ccv_bwd_workspace_size.argtypes = [G]
+        L.ccv_bwd_workspace_size.restype = ctypes.c_int64
         L.ccv_status_str.argtypes = [ctypes.c_int]
         L.ccv_status_str.restype = ctypes.c_char_p
         L.ccv_abi_version.argtypes = []
@@ -183,6 +225,27 @@ def ccv_update_plan(args: ccv_update_args_t):
     p = ccv_plan_t()
     st = lib().ccv_update_plan(ctypes.byref(args), ctypes.byref(p))
     return st, p
+
+
+def ccv_bwd(args: ccv_bwd_args_t, stream=None) -> int:
+    """Enqueue the backward (two kernels) on `stream`; returns the status code."""
+    return lib().ccv_bwd(ctypes.byref(args), ctypes.c_void_p(_stream_handle(stream)))
+
+
+def ccv_bwd_check(args: ccv_bwd_args_t) -> int:
+    return lib().ccv_bwd_check(ctypes.byref(args))
+
+
+def ccv_bwd_plan(args: ccv_bwd_args_t):
+    """(status, ccv_plan_t) of a backward call, without touching the device."""
+    p = ccv_plan_t()
+    st = lib().ccv_bwd_plan(ctypes.byref(args), ctypes.byref(p))
+    return st, p
+
+
+def ccv_bwd_workspace_size(args: ccv_bwd_args_t) -> int:
+    """Workspace bytes the backward needs (>= 0), or a negative status."""
+    return lib().ccv_bwd_workspace_size(ctypes.byref(args))
 
 
 def ccv_status_str(status: int) -> str:
@@ -388,3 +451,135 @@ def update_plan_for(x, conv_state, weight, bias=None, activation=None) -> dict:
     st, p = ccv_update_plan(make_update_args(x3, weight.contiguous(), conv_state, out, bias, activation))
     _raise(st, "ccv_update")
     return p.as_dict()
+
+
+def make_bwd_args(x, weight, bias, dout, dx, dweight, dbias=None, seq_idx=None, initial_states=None,
+                  dfinal_states=None, dinitial_states=None, activation=None,
+                  workspace=None) -> ccv_bwd_args_t:
+    """Fill a ccv_bwd_args_t from tensors (no checks beyond dtype codes)."""
+    B, C, L = x.shape
+    a = ccv_bwd_args_t()
+    a.B, a.C, a.L = B, C, L
+    a.K = weight.shape[1]
+    a.activation = CCV_ACT_SILU if activation in ("silu", "swish") else CCV_ACT_NONE
+    a.x_dtype = DTYPE_CODE[x.dtype]
+    a.w_dtype = DTYPE_CODE[weight.dtype]
+    a.x, a.x_stride = _ptr(x), _strides3(x)
+    a.weight, a.bias, a.seq_idx = _ptr(weight), _ptr(bias), _ptr(seq_idx)
+    a.initial_states, a.init_stride = _ptr(initial_states), _strides3(initial_states)
+    a.dout, a.dout_stride = _ptr(dout), _strides3(dout)
+    a.dfinal_states, a.dfinal_stride = _ptr(dfinal_states), _strides3(dfinal_states)
+    a.dx, a.dx_stride = _ptr(dx), _strides3(dx)
+    a.dweight, a.dbias = _ptr(dweight), _ptr(dbias)
+    a.dinitial_states, a.dinit_stride = _ptr(dinitial_states), _strides3(dinitial_states)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return a
+
+
+def causal_conv1d_bwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                      dout: torch.Tensor, seq_idx: Optional[torch.Tensor] = None,
+                      initial_states: Optional[torch.Tensor] = None,
+                      dfinal_states: Optional[torch.Tensor] = None,
+                      activation: Optional[str] = None, dx: Optional[torch.Tensor] = None,
+                      return_dinitial_states: bool = False, want_dbias: Optional[bool] = None):
+    """Gradients of causal_conv1d_fwd on the GPU: (dx, dweight, dbias, dinitial_states).
+
+    dout [B, C, L] and dfinal_states [B, C, K-1] are in x's dtype; dx is allocated
+    in x's layout unless given (any strides); dweight [C, K] and dbias [C] come back
+    in the weight's dtype (accumulated in fp32); dbias is None unless a bias was
+    given (or want_dbias); dinitial_states [B, C, K-1] only with
+    return_dinitial_states (it needs initial_states).  The fp32 workspace for the
+    parameter sums is allocated here, through torch.
+    """
+    if activation not in (None, "silu", "swish"):
+        raise ValueError(f"activation must be None, 'silu' or 'swish', not {activation!r}")
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
+        raise ValueError("expected x [B, C, L] and weight [C, K]")
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor (there is no CPU path)")
+    B, C, L = x.shape
+    K = weight.shape[1]
+    for name, t in (("weight", weight), ("bias", bias), ("dout", dout), ("seq_idx", seq_idx),
+                    ("initial_states", initial_states), ("dfinal_states", dfinal_states), ("dx", dx)):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} must be on {x.device}")
+    if dout.dtype != x.dtype or tuple(dout.shape) != (B, C, L):
+        raise ValueError("dout must be [B, C, L] in x's dtype")
+    if dfinal_states is not None and (dfinal_states.dtype != x.dtype or tuple(dfinal_states.shape) != (B, C, K - 1)):
+        raise ValueError("dfinal_states must be [B, C, K-1] in x's dtype")
+    if initial_states is not None and (initial_states.dtype != x.dtype
+                                       or tuple(initial_states.shape) != (B, C, K - 1)):
+        raise ValueError("initial_states must be [B, C, K-1] in x's dtype")
+    if return_dinitial_states and initial_states is None:
+        raise ValueError("dinitial_states needs initial_states")
+    if seq_idx is not None:
+        if seq_idx.dtype != torch.int32 or tuple(seq_idx.shape) != (B, L):
+            raise ValueError("seq_idx must be int32 [B, L]")
+        seq_idx = seq_idx.contiguous()
+    weight = weight.contiguous()
+    if bias is not None:
+        if bias.dtype != weight.dtype:
+            raise ValueError("bias must have the weight's dtype")
+        bias = bias.contiguous()
+    if dx is None:
+        dx = empty_like_layout(x)
+    elif dx.dtype != x.dtype or tuple(dx.shape) != (B, C, L):
+        raise ValueError("dx must be [B, C, L] in x's dtype")
+    dweight = torch.empty(C, K, dtype=weight.dtype, device=x.device)
+    want_db = (bias is not None) if want_dbias is None else want_dbias
+    dbias = torch.empty(C, dtype=weight.dtype, device=x.device) if want_db else None
+    dinit = (torch.empty(B, K - 1, C, dtype=x.dtype, device=x.device).transpose(1, 2)
+             if return_dinitial_states else None)
+    args = make_bwd_args(x, weight, bias, dout, dx, dweight, dbias, seq_idx, initial_states,
+                         dfinal_states, dinit, activation)
+    ws = ccv_bwd_workspace_size(args)
+    _raise(int(ws) if ws < 0 else 0, "ccv_bwd")
+    workspace = torch.empty(max(int(ws), 16), dtype=torch.uint8, device=x.device)
+    args.workspace, args.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    with torch.cuda.device(x.device):
+        st = ccv_bwd(args)
+    _raise(st, "ccv_bwd")
+    return dx, dweight, dbias, dinit
+
+
+class _CausalConv1dFn(torch.autograd.Function):
+    """Forward and backward through the C ABI.  Saves x, weight, bias,
+    initial_states and seq_idx (Ch.4 "Dao interface and source map", section "How
+    autograd links forward and backward"); z is recomputed in the backward."""
+
+    @staticmethod
+    def forward(ctx, x, weight, bias, seq_idx, initial_states, return_final_states, final_states_out,
+                activation):
+        res = causal_conv1d_fwd(x, weight, bias, seq_idx, initial_states, return_final_states,
+                                final_states_out, activation)
+        ctx.save_for_backward(x, weight, bias, seq_idx, initial_states)
+        ctx.activation = activation
+        ctx.return_final_states = return_final_states
+        return res
+
+    @staticmethod
+    def backward(ctx, dout, *rest):
+        x, weight, bias, seq_idx, initial_states = ctx.saved_tensors
+        dfs = rest[0] if ctx.return_final_states and rest else None
+        if dout is None:
+            dout = torch.zeros_like(x)
+        dout = dout.to(x.dtype)
+        if dfs is not None:
+            dfs = dfs.to(x.dtype)
+        want_dinit = initial_states is not None and ctx.needs_input_grad[4]
+        dx, dw, db, dinit = causal_conv1d_bwd(
+            x, weight, bias, dout, seq_idx, initial_states, dfs, ctx.activation,
+            return_dinitial_states=want_dinit, want_dbias=bias is not None and ctx.needs_input_grad[2])
+        return dx, dw, db, None, dinit, None, None, None
+
+
+def causal_conv1d_fn(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                     seq_idx: Optional[torch.Tensor] = None,
+                     initial_states: Optional[torch.Tensor] = None, return_final_states: bool = False,
+                     final_states_out: Optional[torch.Tensor] = None, activation: Optional[str] = None):
+    """Differentiable causal depthwise conv1d (the full-sequence contract of
+    causal_conv1d_fwd, with gradients for x, weight, bias and initial_states through
+    causal_conv1d_bwd)."""
+    return _CausalConv1dFn.apply(x, weight, bias, seq_idx, initial_states, return_final_states,
+                                 final_states_out, activation)

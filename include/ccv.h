@@ -103,7 +103,8 @@ typedef struct ccv_fwd_args {
 /* Which kernel a call would launch and how (host-only; for tests and benches). */
 typedef enum {
   CCV_PATH_NONE = 0, CCV_PATH_CHANNEL_FIRST = 1, CCV_PATH_CHANNEL_LAST = 2,
-  CCV_PATH_UPDATE = 3      /* the update (decode) kernel; see ccv_update_plan */
+  CCV_PATH_UPDATE = 3,     /* the update (decode) kernel; see ccv_update_plan */
+  CCV_PATH_BACKWARD = 4    /* the backward kernels; see ccv_bwd_plan */
 } ccv_path_t;
 
 typedef struct ccv_plan {
@@ -194,6 +195,77 @@ int ccv_update_check(const ccv_update_args_t* args);
  * channels_per_item: rows per lane; grid, block, waves_per_group: the launch;
  * work_items: B*C rows; span: L; unroll: 1. */
 int ccv_update_plan(const ccv_update_args_t* args, ccv_plan_t* plan);
+
+/* ---- backward -----------------------------------------------------------------------
+ *
+ * The gradients of ccv_fwd (Ch.4 "Dao interface and source map", section "How
+ * autograd links forward and backward": the backward receives dout and, when the
+ * forward returned final states, dfinal_states; it returns dx, dweight, dbias and
+ * the gradient of initial_states; dweight and dbias are accumulated in fp32 and
+ * converted to the parameter dtype at the end; seq_idx has no gradient).  With z
+ * the pre-activation (recomputed, not stored) and X~ the extended input:
+ *
+ *   dz[b,c,t]   = dout[b,c,t] * act'(z[b,c,t])          (SiLU': s(z) (1 + z (1 - s(z))))
+ *   dX~[b,c,j]  = sum_k keep(t,k) w[c,k] dz[b,c,t] over t = j+K-1-k in [0, L)
+ *                 + dfinal_states[b,c,j-(L-K+1)]  when j >= L-K+1
+ *   dx[b,c,t]   = dX~[b,c,t];   dinitial_states[b,c,i] = dX~[b,c,i-(K-1)]
+ *   dweight[c,k] = sum_{b,t} keep(t,k) dz[b,c,t] X~[b,c,t-K+1+k];  dbias[c] = sum_{b,t} dz[b,c,t]
+ *
+ * Every sum is fp32; dx and dinitial_states are rounded once to x's dtype,
+ * dweight and dbias once to the weight dtype.  The parameter sums run in a fixed
+ * order (per time tile, then over tiles), so results repeat bit for bit.
+ * seq_idx together with initial_states, dfinal_states or dinitial_states is
+ * CCV_E_UNSUPPORTED, as in the forward.  Any element strides are accepted for x,
+ * dout, dx and the states; weight, bias, dweight, dbias are contiguous.  dx must
+ * not be x or dout; dinitial_states must not be initial_states (CCV_E_ALIAS).
+ *
+ * Workspace: the fp32 partial sums of dweight and dbias live in a caller-provided
+ * device buffer of ccv_bwd_workspace_size(args) bytes (16-byte aligned; its
+ * contents on entry do not matter).  It is CCV_E_NULL to pass none when that size
+ * is nonzero and CCV_E_SHAPE to pass fewer bytes. */
+typedef struct ccv_bwd_args {
+  int64_t struct_size;          /* = sizeof(ccv_bwd_args_t) */
+  int64_t B, C, L;              /* logical shape of x, dout, dx: [B, C, L] */
+  int32_t K;                    /* taps: 2, 3 or 4 */
+  int32_t activation;           /* ccv_act_t of the forward */
+  int32_t x_dtype;              /* of x, dout, dx, the states and their gradients */
+  int32_t w_dtype;              /* of weight, bias, dweight, dbias */
+  const void* x;                /* device, the forward's input */
+  int64_t x_stride[3];
+  const void* weight;           /* device, contiguous [C, K] */
+  const void* bias;             /* device [C] or NULL: the forward's bias (needed to recompute z) */
+  const int32_t* seq_idx;       /* device, contiguous int32 [B, L], or NULL */
+  const void* initial_states;   /* device [B, C, K-1] or NULL: the forward's history */
+  int64_t init_stride[3];
+  const void* dout;             /* device [B, C, L]: gradient of out */
+  int64_t dout_stride[3];
+  const void* dfinal_states;    /* device [B, C, K-1] or NULL: gradient of final_states */
+  int64_t dfinal_stride[3];
+  void* dx;                     /* device [B, C, L] */
+  int64_t dx_stride[3];
+  void* dweight;                /* device, contiguous [C, K] */
+  void* dbias;                  /* device [C] or NULL (not computed) */
+  void* dinitial_states;        /* device [B, C, K-1] or NULL; needs initial_states */
+  int64_t dinit_stride[3];
+  void* workspace;              /* device scratch, ccv_bwd_workspace_size bytes */
+  int64_t workspace_bytes;
+} ccv_bwd_args_t;
+
+/* Bytes of workspace ccv_bwd needs for `args` (>= 0), or a negative status when
+ * the arguments are invalid.  Host only. */
+int64_t ccv_bwd_workspace_size(const ccv_bwd_args_t* args);
+
+/* Enqueue the backward (two kernels, in order) on `hip_stream` and return without
+ * waiting.  Returns CCV_OK, a validation error (nothing enqueued) or CCV_E_HIP. */
+int ccv_bwd(const ccv_bwd_args_t* args, void* hip_stream);
+
+/* Validate `args` exactly as ccv_bwd does, without touching any device. */
+int ccv_bwd_check(const ccv_bwd_args_t* args);
+
+/* Describe the launch ccv_bwd would make (host only; `plan` may be NULL): path
+ * CCV_PATH_BACKWARD, span = time steps per tile, work_items = tiles x channels
+ * (one lane each), grid / block of the gradient kernel. */
+int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan);
 
 /* Static, NUL-terminated name of a status code ("CCV_OK", ...). */
 const char* ccv_status_str(int status);

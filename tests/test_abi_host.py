@@ -316,3 +316,98 @@ def test_update_plan_falls_back_to_element_path():
     p = uplan(uargs(C=60))
     assert p.elems_per_lane == 4 and p.grid == -(-2 * 60 // (256 * 4))
     assert uplan(uargs(L=0, x=None, weight=None, state=None, out=None)).path == ccv.CCV_PATH_NONE
+
+
+# ---- backward ----------------------------------------------------------------------
+
+DOUT, DX, DW, DB, DINIT, DFS, WS = (0x4000000 + 0x100000 * i for i in range(7))
+
+
+def bargs(B=2, C=64, L=1000, K=4, layout="cf", ws=True, **over):
+    a = ccv.ccv_bwd_args_t()
+    a.B, a.C, a.L, a.K = B, C, L, K
+    a.x_dtype = a.w_dtype = ccv.CCV_BF16
+    a.activation = ccv.CCV_ACT_SILU
+    st = (C * L, L, 1) if layout == "cf" else (L * C, 1, C)
+    a.x, a.dout, a.dx = X, DOUT, DX
+    a.x_stride = type(a.x_stride)(*st)
+    a.dout_stride = type(a.dout_stride)(*st)
+    a.dx_stride = type(a.dx_stride)(*st)
+    a.weight, a.dweight = W, DW
+    for k, v in over.items():
+        if k.endswith("stride"):
+            v = type(getattr(a, k))(*v)
+        setattr(a, k, v)
+    if ws:
+        a.workspace, a.workspace_bytes = WS, ccv.ccv_bwd_workspace_size(a)
+    return a
+
+
+def bcheck(a):
+    return ccv.STATUS[ccv.ccv_bwd_check(a)]
+
+
+def test_bwd_workspace_size_is_the_partial_sums():
+    a = bargs(B=3, C=100, L=1000, K=3, ws=False)
+    tiles = -(-1000 // 64)
+    assert ccv.ccv_bwd_workspace_size(a) == 3 * tiles * 100 * (3 + 1) * 4
+    assert ccv.ccv_bwd_workspace_size(bargs(B=2, C=5, L=0, ws=False)) == 2 * 1 * 5 * 5 * 4
+    assert ccv.ccv_bwd_workspace_size(bargs(B=0, ws=False)) == 0
+    assert ccv.ccv_bwd_workspace_size(bargs(K=5, ws=False)) == ccv.lib().ccv_bwd_check(bargs(K=5, ws=False))
+
+
+def test_bwd_valid_calls():
+    assert bcheck(bargs()) == "CCV_OK"
+    assert bcheck(bargs(layout="cl")) == "CCV_OK"
+    assert bcheck(bargs(bias=BIAS, dbias=DB, seq_idx=SEQ)) == "CCV_OK"
+    assert bcheck(bargs(initial_states=INIT, init_stride=(192, 1, 64), dfinal_states=DFS,
+                        dfinal_stride=(192, 3, 1), dinitial_states=DINIT,
+                        dinit_stride=(192, 1, 64))) == "CCV_OK"
+    # dx may be strided differently from x (any non-overlapping layout)
+    assert bcheck(bargs(dx_stride=(64 * 1000, 1, 64))) == "CCV_OK"
+
+
+def test_bwd_argument_errors():
+    a = bargs()
+    a.struct_size = 4
+    assert bcheck(a) == "CCV_E_ABI"
+    assert bcheck(bargs(K=1)) == "CCV_E_KSIZE"
+    assert bcheck(bargs(w_dtype=9)) == "CCV_E_DTYPE"
+    assert bcheck(bargs(activation=5)) == "CCV_E_UNSUPPORTED"
+    assert bcheck(bargs(seq_idx=SEQ, initial_states=INIT, init_stride=(192, 3, 1))) == "CCV_E_UNSUPPORTED"
+    assert bcheck(bargs(seq_idx=SEQ, dfinal_states=DFS, dfinal_stride=(192, 3, 1))) == "CCV_E_UNSUPPORTED"
+    assert bcheck(bargs(dinitial_states=DINIT, dinit_stride=(192, 3, 1))) == "CCV_E_UNSUPPORTED"
+    for name in ("x", "dout", "dx", "weight", "dweight"):
+        assert bcheck(bargs(**{name: None})) == "CCV_E_NULL", name
+    assert bcheck(bargs(dx=X)) == "CCV_E_ALIAS"
+    assert bcheck(bargs(dx=DOUT)) == "CCV_E_ALIAS"
+    assert bcheck(bargs(dweight=W)) == "CCV_E_ALIAS"
+    assert bcheck(bargs(initial_states=INIT, init_stride=(192, 3, 1), dinitial_states=INIT,
+                        dinit_stride=(192, 3, 1))) == "CCV_E_ALIAS"
+    assert bcheck(bargs(dx_stride=(64000, 1000, 0))) == "CCV_E_LAYOUT"     # dx overlaps itself
+    assert bcheck(bargs(x_stride=(64000, 1000, -1))) == "CCV_E_LAYOUT"
+
+
+def test_bwd_workspace_errors():
+    a = bargs(ws=False)
+    assert bcheck(a) == "CCV_E_NULL"
+    a.workspace, a.workspace_bytes = WS, ccv.ccv_bwd_workspace_size(a) - 4
+    assert bcheck(a) == "CCV_E_SHAPE"
+    a.workspace, a.workspace_bytes = WS + 4, ccv.ccv_bwd_workspace_size(a)
+    assert bcheck(a) == "CCV_E_LAYOUT"
+
+
+def test_bwd_empty_extents():
+    # no channels: nothing to do, no pointer needed
+    assert bcheck(bargs(C=0, x=None, dout=None, dx=None, weight=None, dweight=None, ws=False)) == "CCV_OK"
+    # no rows: dweight (and dbias) are still written (as zeros); x / dout / dx unused
+    a = bargs(B=0, x=None, dout=None, dx=None, ws=False)
+    assert bcheck(a) == "CCV_OK"
+    st, p = ccv.ccv_bwd_plan(a)
+    assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD and p.grid == 0
+
+
+def test_bwd_plan():
+    st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096))
+    assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD
+    assert p.span == 64 and p.work_items == 4 * 64 * 2048 and p.grid == 4 * 64 * 2048 // 256

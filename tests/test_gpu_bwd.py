@@ -1,0 +1,249 @@
+"""GPU parity of the backward through the C ABI, and of the autograd function.
+
+dx, dweight, dbias and d(initial_states) are compared with the oracle's fp64
+backward (the chain rule of the forward, pinned against torch autograd and
+finite differences) element by element.  The tolerance is the forward's, with
+the oracle's per-element error scale in place of S: for dx the sum of the
+magnitudes of its terms, each dz also carrying |dout| * S_z; for the parameter
+gradients, sums over B * L such terms in fp32, whose rounding grows with the
+tile length and the number of partial sums.  Invariants checked bit for bit:
+repeated runs, layout independence, packed = separate sequences for dx."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import causal_depthwise_conv1d_amd as ccv
+import workloads as wl
+from gpu_support import log, to_gpu_view
+from oracle import compare as ocmp
+from oracle.from_torch import bwd as oracle_bwd
+from oracle.from_torch import case, dtype_name, raw
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    ccv.lib()
+
+DTYPES = ["f32", "bf16", "f16"]
+KS = [2, 3, 4]
+DOUT_ID, DFS_ID = 5, 6
+TILE = 64
+
+
+def grad_inputs(w, layout, with_dfs, seed):
+    """dout [B, C, L] (channel-first or channel-last storage) and dfinal_states."""
+    B, C, L, K = w.B, w.C, w.L, w.K
+    g = wl.to_storage(wl.draw(B * C * L, seed, DOUT_ID, "normal", 1.0), w.x_dtype)
+    dout = g.reshape(B, C, L) if layout.startswith("cf") else g.reshape(B, L, C).transpose(1, 2)
+    dfs = None
+    if with_dfs:
+        dfs = wl.to_storage(wl.draw(B * C * (K - 1), seed, DFS_ID, "normal", 1.0), w.x_dtype).reshape(B, C, K - 1)
+    return dout, dfs
+
+
+def run_bwd(w, dout, dfs, want_dinit):
+    x = to_gpu_view(w.x_storage, w.x)
+    init = None if w.initial_states is None else to_gpu_view(w.init_storage, w.initial_states)
+    res = ccv.causal_conv1d_bwd(
+        x, w.weight.cuda(), None if w.bias is None else w.bias.cuda(), dout.cuda(),
+        None if w.seq_idx is None else w.seq_idx.cuda(), init, None if dfs is None else dfs.cuda(),
+        w.activation, return_dinitial_states=want_dinit)
+    torch.cuda.synchronize()
+    return [None if t is None else t.cpu().contiguous() for t in res]
+
+
+def param_terms(w):
+    """compare()'s K for the parameter gradients: (T + 32 + parts / 32 + K + 8) / 4
+    roundings of 2^-22 each cover the in-tile sum, the chunked sum of the partials
+    and the error of dz itself."""
+    parts = w.B * max(1, math.ceil(w.L / TILE))
+    return math.ceil((TILE + 32 + parts / 32 + w.K + 8) / 4)
+
+
+def check_bwd(w, dout, dfs, want_dinit, where):
+    dx, dw, db, dinit = run_bwd(w, dout, dfs, want_dinit)
+    c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
+    r = oracle_bwd(c, dout, dfs)
+    K = w.K
+    checks = [("dx", dx, r["dx"], r["ex"], K + 2)]
+    if want_dinit:
+        checks.append(("dinit", dinit, r["dinit"], r["einit"], K + 2))
+    pk = param_terms(w)
+    checks.append(("dweight", dw, r["dw"], r["ew"], pk))
+    if w.bias is not None:
+        checks.append(("dbias", db, r["db"], r["eb"], pk))
+    for name, got, ref, scale, kk in checks:
+        res = ocmp.compare(dtype_name(got), kk, raw(got), ref, scale)
+        if res["n_bad"]:
+            raise AssertionError(f"{where} {name}: " + ocmp.describe_failures(
+                res, ref, scale, raw(got), dtype_name(got), shape=tuple(got.shape)))
+    return dx, dw, db, dinit
+
+
+def build(B, C, L, K, dtype, layout, seed, w_dtype=None, seq=None, init=False, bias=True, act="silu"):
+    kw = {}
+    if layout == "cf_view":
+        kw = dict(layout="cf", c_pad=3, c_off=1, t_pad=13, t_off=5)
+    elif layout == "cl_view":
+        kw = dict(layout="cl", c_pad=8)
+    else:
+        kw = dict(layout=layout)
+    lengths = wl.packed_lengths(L, seq, 1, seed).tolist() if seq else None
+    return wl.make_case(B=B, C=C, L=L, K=K, x_dtype=dtype, w_dtype=w_dtype, bias=bias, init=init,
+                        seq_lengths=lengths, activation=act, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl", "cf_view", "cl_view"])
+@pytest.mark.parametrize("K", KS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_matches_oracle(dtype, K, layout):
+    cases = [  # L, C, B, features
+        (1, 7, 2, dict(bias=True, act="silu")),
+        (K - 1, 8, 1, dict(init=True, dfs=True, dinit=True)),
+        (63, 70, 2, dict(bias=True, act="silu", init=True, dfs=True, dinit=True)),
+        (64, 64, 1, dict(bias=False, act=None)),
+        (65, 130, 3, dict(bias=True, act="silu", seq=5)),
+        (300, 33, 2, dict(bias=True, act=None, init=True, dinit=True)),
+        (1000, 9, 1, dict(bias=True, act="silu", seq=17, w_dtype="f32")),
+    ]
+    for i, (L, C, B, f) in enumerate(cases):
+        seed = 3000 + 100 * K + i
+        w = build(B, C, L, K, dtype, layout, seed, w_dtype=f.get("w_dtype"), seq=f.get("seq"),
+                  init=f.get("init", False), bias=f.get("bias", True), act=f.get("act", "silu"))
+        dout, dfs = grad_inputs(w, layout, f.get("dfs", False), seed)
+        log(f"  bwd {dtype}/{w.w_dtype} K={K} {layout} L={L} C={C} B={B} {f}")
+        check_bwd(w, dout, dfs, f.get("dinit", False), f"[{dtype} K={K} {layout} L={L}]")
+
+
+def test_bwd_random_shapes():
+    g = np.random.default_rng(77)
+    for i in range(40):
+        K = int(g.integers(2, 5))
+        dtype = DTYPES[g.integers(0, 3)]
+        w_dtype = DTYPES[g.integers(0, 3)]
+        layout = ["cf", "cl", "cf_view", "cl_view"][g.integers(0, 4)]
+        B, C, L = int(g.integers(1, 4)), int(g.integers(1, 200)), int(g.integers(0, 700))
+        seq = int(g.integers(1, 9)) if (g.random() < 0.3 and L > 0) else None
+        init = seq is None and g.random() < 0.5
+        w = build(B, C, L, K, dtype, layout, 4000 + i, w_dtype=w_dtype, seq=seq, init=init,
+                  bias=bool(g.random() < 0.6), act=["silu", None][g.integers(0, 2)])
+        dout, dfs = grad_inputs(w, layout, seq is None and g.random() < 0.5, 4000 + i)
+        log(f"  random bwd {i}: {dtype}/{w_dtype} K={K} {layout} B={B} C={C} L={L} seq={seq} init={init}")
+        check_bwd(w, dout, dfs, init, f"[random {i}]")
+
+
+def test_bwd_zero_length_sequence():
+    """L = 0: dx is empty, d(initial_states) is dfinal_states passed through, and
+    dweight / dbias are zero."""
+    w = build(2, 12, 0, 4, "f32", "cf", 4500, init=True)
+    dout, dfs = grad_inputs(w, "cf", True, 4500)
+    dx, dw, db, dinit = check_bwd(w, dout, dfs, True, "[L=0]")
+    assert dx.shape == (2, 12, 0)
+    assert torch.equal(dinit, dfs) and not dw.any() and not db.any()
+
+
+def test_bwd_repeat_runs_bit_identical():
+    w = build(3, 256, 777, 4, "bf16", "cf", 4600, init=True)
+    dout, dfs = grad_inputs(w, "cf", True, 4600)
+    a = run_bwd(w, dout, dfs, True)
+    for _ in range(3):
+        b = run_bwd(w, dout, dfs, True)
+        for t0, t1 in zip(a, b):
+            assert torch.equal(t0.view(torch.int16), t1.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_layout_independent(dtype):
+    """The same logical problem stored channel-first and channel-last (x, dout and
+    dx) gives the same bits for every gradient: the arithmetic does not depend on
+    the strides."""
+    w = build(2, 72, 300, 4, dtype, "cf", 4700, init=True)
+    dout, dfs = grad_inputs(w, "cf", True, 4700)
+    x = w.x.cuda()
+    args = (w.weight.cuda(), w.bias.cuda())
+    init, dfs = w.initial_states.cuda(), dfs.cuda()
+
+    def cl(t):
+        return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+    res = []
+    for xv, gv in ((x, dout.cuda()), (cl(x), cl(dout.cuda()))):
+        out = ccv.causal_conv1d_bwd(xv, *args, gv, None, init, dfs, "silu", return_dinitial_states=True)
+        torch.cuda.synchronize()
+        assert out[0].stride() == xv.stride()                 # dx follows x's layout
+        res.append([t.cpu().contiguous() for t in out])
+    bits = torch.int32 if dtype == "f32" else torch.int16
+    for t0, t1 in zip(*res):
+        assert torch.equal(t0.view(bits), t1.view(bits))
+
+
+def test_bwd_packed_dx_equals_separate_runs():
+    """dx of a packed run with seq_idx equals dx of each sequence run alone, bit for
+    bit; dweight and dbias agree within the parameter tolerance of their sum."""
+    K, C = 4, 40
+    lengths = [3, 70, 1, 64, 129, 5]
+    L = sum(lengths)
+    w = wl.make_case(B=1, C=C, L=L, K=K, x_dtype="bf16", layout="cl", bias=True, activation="silu",
+                     seq_lengths=lengths, seed=4800)
+    dout, _ = grad_inputs(w, "cl", False, 4800)
+    dx, dw, db, _ = run_bwd(w, dout, None, False)
+    pos = 0
+    for n in lengths:
+        xp = torch.empty(1, C, n, dtype=w.x.dtype).copy_(w.x[:, :, pos:pos + n])   # fresh storage
+        part = wl.Workload(name="part", B=1, C=C, L=n, K=K, x_dtype="bf16", w_dtype="bf16",
+                           x_storage=xp, x=xp, weight=w.weight, bias=w.bias,
+                           seq_idx=None, init_storage=None, initial_states=None,
+                           return_final_states=False, activation="silu", layout="cf", seed=0)
+        dp = torch.empty(1, C, n, dtype=dout.dtype).copy_(dout[:, :, pos:pos + n])
+        pdx, _, _, _ = run_bwd(part, dp, None, False)
+        assert torch.equal(dx[:, :, pos:pos + n].view(torch.int16), pdx.view(torch.int16)), n
+        pos += n
+
+
+def test_bwd_workload_size_channel_first_bf16():
+    """The bench's channel-first bf16 shape (B=4, C=2048, L=4096, K=4, bias, SiLU):
+    every gradient element against the oracle."""
+    w = wl.workload(2)
+    dout, _ = grad_inputs(w, "cf", False, 1002)
+    check_bwd(w, dout, None, False, "[workload 2 shape]")
+
+
+def test_autograd_function_matches_oracle():
+    """causal_conv1d_fn: torch.autograd through the forward and backward kernels
+    gives the oracle's gradients for x, weight, bias and initial_states, and the
+    forward value of causal_conv1d_fwd."""
+    for dtype in ("f32", "bf16"):
+        w = build(2, 48, 150, 4, dtype, "cl", 4900, init=True)
+        dout, dfs = grad_inputs(w, "cl", True, 4900)
+        x = to_gpu_view(w.x_storage, w.x).detach().requires_grad_()
+        weight = w.weight.cuda().requires_grad_()
+        bias = w.bias.cuda().requires_grad_()
+        init = to_gpu_view(w.init_storage, w.initial_states).detach().requires_grad_()
+        out, fs = ccv.causal_conv1d_fn(x, weight, bias, None, init, True, None, "silu")
+        ref_out = ccv.causal_conv1d_fwd(x.detach(), weight.detach(), bias.detach(), initial_states=init.detach(),
+                                        activation="silu")
+        assert torch.equal(out.detach(), ref_out)
+        torch.autograd.backward([out, fs], [dout.cuda(), dfs.cuda()])
+        torch.cuda.synchronize()
+        c = case(w.x, w.weight, w.bias, None, w.initial_states, "silu")
+        r = oracle_bwd(c, dout, dfs)
+        pk = param_terms(w)
+        for name, got, ref, scale, kk in (("dx", x.grad, r["dx"], r["ex"], 6), ("dw", weight.grad, r["dw"], r["ew"], pk),
+                                          ("db", bias.grad, r["db"], r["eb"], pk),
+                                          ("dinit", init.grad, r["dinit"], r["einit"], 6)):
+            g = got.cpu().contiguous()
+            res = ocmp.compare(dtype_name(g), kk, raw(g), ref, scale)
+            assert res["n_bad"] == 0, (dtype, name, ocmp.describe_failures(res, ref, scale, raw(g), dtype_name(g)))
+
+
+def test_bwd_argument_errors_raise():
+    x = torch.zeros(2, 8, 16, device="cuda")
+    w = torch.zeros(8, 4, device="cuda")
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_bwd(x, w, None, x.half())                    # dout dtype
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_bwd(x, w, None, x, return_dinitial_states=True)   # no initial_states
+    with pytest.raises(ValueError):
+        ccv.causal_conv1d_bwd(x, w, None, x, dx=x)                     # dx is dout: alias
