@@ -42,6 +42,12 @@ KERNEL_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_cf.hip",
                   "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_api.cpp"]
+BWD_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_bwd.hip",
+               "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
+               "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
+               "causal_depthwise_conv1d_amd/csrc/ccv_bwd_launch.hpp",
+               "causal_depthwise_conv1d_amd/csrc/ccv_bwd_api.cpp"]
+BWD_METRIC = "causal conv1d bwd effective HBM GB/s and % of MI355X peak bandwidth"
 UPDATE_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_update.hip",
                   "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
@@ -97,8 +103,9 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--op", default="fwd", choices=["fwd", "update"],
-                    help="fwd: the forward on --workload (default); update: the decode step")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "update", "bwd"],
+                    help="fwd: the forward on --workload (default); update: the decode step; "
+                         "bwd: the backward on --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
@@ -124,6 +131,9 @@ def main():
 
     if args.op == "update":
         bench_update(args, dev, props)
+        return
+    if args.op == "bwd":
+        bench_bwd(args, dev, props)
         return
 
     t0 = time.time()
@@ -414,6 +424,170 @@ def bench_update(args, dev, props):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = update_cpu_baseline(w, nbytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bwd_bytes(w) -> int:
+    """Algorithmic bytes of one backward call: x and dout read once, dx written
+    once, the parameters read and their gradients written once, the states and
+    their gradients once.  The partial-sum workspace is overhead."""
+    es = w.x.element_size()
+    B, C, L, K = w.B, w.C, w.L, w.K
+    pb = w.weight.element_size()
+    n = 3 * B * C * L * es + 2 * C * K * pb
+    if w.bias is not None:
+        n += 2 * C * pb
+    if w.initial_states is not None:
+        n += 2 * B * C * (K - 1) * es
+    return n
+
+
+def bench_bwd(args, dev, props):
+    """The backward on the chosen workload's shape: one call checked against the
+    oracle, then W warm-up and K timed calls rotating over >= 1 GiB of (x, dout,
+    dx) sets."""
+    import ctypes
+
+    import torch
+
+    import causal_depthwise_conv1d_amd as ccv
+    import workloads as wl
+
+    w = wl.workload(args.workload)
+    B, C, L, K = w.B, w.C, w.L, w.K
+    es = w.x.element_size()
+    nbytes = bwd_bytes(w)
+    dout_cpu = wl.to_storage(wl.draw(B * C * L, w.seed, 5, "normal", 1.0), w.x_dtype).reshape(B, C, L)
+    set_bytes = 3 * B * C * L * es
+    nsets = max(2, math.ceil(ROTATION_BYTES / set_bytes))
+    if nsets * set_bytes > 0.5 * props.total_memory:
+        nsets = max(1, int(0.5 * props.total_memory // set_bytes))
+    weight = w.weight.to(dev)
+    bias = None if w.bias is None else w.bias.to(dev)
+    seq = None if w.seq_idx is None else w.seq_idx.to(dev)
+    init = None if w.initial_states is None else w.initial_states.to(dev)
+    dweight = torch.empty(C, K, dtype=weight.dtype, device=dev)
+    dbias = None if bias is None else torch.empty(C, dtype=weight.dtype, device=dev)
+    sets = []
+    workspace = None
+    for _ in range(nsets):
+        xs = w.x_storage.to(dev)
+        x = xs.as_strided(w.x.shape, w.x.stride(), w.x.storage_offset())
+        dout = ccv.empty_like_layout(x).copy_(dout_cpu.to(dev))      # the layout of out
+        dx = ccv.empty_like_layout(x)
+        a = ccv.make_bwd_args(x, weight, bias, dout, dx, dweight, dbias, seq, init, None, None, w.activation)
+        if workspace is None:
+            workspace = torch.empty(max(16, ccv.ccv_bwd_workspace_size(a)), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        sets.append((xs, dout, dx, a))
+    st, plan = ccv.ccv_bwd_plan(sets[0][3])
+    assert st == 0, ccv.ccv_status_str(st)
+    plan = plan.as_dict()
+    log(f"[bench] bwd: {nsets} buffer sets of {set_bytes / 1e6:.0f} MB; workspace "
+        f"{workspace.numel() / 1e6:.1f} MB; plan {plan}")
+
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    fn = ccv.lib().ccv_bwd
+    refs = [ctypes.byref(s[3]) for s in sets]
+
+    def step(i):
+        rc = fn(refs[i % nsets], sp)
+        if rc != 0:
+            raise RuntimeError(ccv.ccv_status_str(rc))
+
+    step(0)
+    torch.cuda.synchronize()
+    parity = bwd_parity(w, dout_cpu, sets[0][2], dweight, dbias)
+    log(f"[bench] bwd parity: {parity}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] bwd: {ms_per_step * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+    copy_gbps, empty_us = context_measurements(nbytes, dev, stream, min(args.steps, 200))
+
+    kernel_key = f"bwd_{w.x_dtype}_B{B}_C{C}_L{L}_K{K}"
+    sha = kernel_sources_sha256(BWD_SOURCES)
+    result = {
+        "metric": BWD_METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.notes.get("description"),
+            "B": B, "C": C, "L": L, "K": K,
+            "activation": w.activation,
+            "storage_dtype": w.x_dtype,
+            "algorithmic_bytes": nbytes,
+            "buffer_sets": nsets,
+            "kernel": kernel_key,
+            "plan": plan,
+        },
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "traffic": profile_traffic(kernel_key, sha),
+            "kernel": kernel_key,
+            "avg_launch_us": round(ms_per_step * 1e3, 3),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+        "parity": parity,
+        "context": {
+            "copy_same_bytes_GBps": round(copy_gbps, 1),
+            "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+            "empty_kernel_us": round(empty_us, 3),
+            "device": props.name,
+            "cu_count": props.multi_processor_count,
+            "kernel_sources_sha256": sha,
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias):
+    """One backward call against the oracle's fp64 gradients (every dx element,
+    every dweight / dbias element), with the tolerances of the GPU tests."""
+    from oracle import compare as ocmp
+    from oracle.from_torch import bwd, case, dtype_name, raw
+
+    c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
+    r = bwd(c, dout_cpu, None)
+    T = 32 if w.x_dtype == "f32" else 64              # time steps per backward tile
+    parts, levels = w.B * max(1, math.ceil(w.L / T)), 1
+    while parts > 32:                                  # levels of the fan-in-32 reduction tree
+        parts, levels = -(-parts // 32), levels + 1
+    pk = math.ceil((T + 32 * levels + w.K + 8) / 4)
+    out = {}
+    for name, got, ref, scale, kk in (("dx", dx_gpu, r["dx"], r["ex"], w.K + 2),
+                                      ("dweight", dweight, r["dw"], r["ew"], pk),
+                                      ("dbias", dbias, r["db"], r["eb"], pk)):
+        if got is None:
+            continue
+        g = got.cpu().contiguous()
+        res = ocmp.compare(dtype_name(g), kk, raw(g), ref, scale)
+        out[name] = {"n": res["n"], "out_of_tolerance": res["n_bad"], "max_ulp": res["max_ulp"],
+                     "max_rel": res["max_rel"]}
+    return out
 
 
 def update_parity(w, out_gpu, state_gpu):

@@ -17,10 +17,12 @@
 // channels, so a wave's accesses are coalesced when channels are unit-stride
 // and repeat over the same cache lines from step to step otherwise.
 //
-// Reduction kernel.  One lane per (tap or bias, channel) sums the partials of
-// all (b, tile) in a fixed order (chunks of kBwdChunk, then the chunk sums), so
-// dweight and dbias repeat bit for bit, and rounds once to the weight dtype
-// (the fp32-accumulate-then-convert of the section cited above).
+// Reduction kernel.  The partials of all (b, tile) are summed per (tap or bias,
+// channel) by a tree of fixed shape: each level adds groups of kBwdFanIn
+// consecutive rows in order, one lane per group and column, until one row is
+// left, which is rounded once to the weight dtype (the fp32-accumulate-then-
+// convert of the section cited above).  The shape depends only on the problem,
+// so dweight and dbias repeat bit for bit; a level reads coalesced rows.
 #include "ccv_bwd_launch.hpp"
 #include "ccv_device.hpp"
 
@@ -34,25 +36,18 @@ __device__ inline float silu_slope(float z) {
   return s * (1.0f + z * (1.0f - s));
 }
 
-template <class S, int K, bool SILU, bool SEQ>
-__global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
+// The walk of one lane over one tile (see the header comment), shared by both
+// kernels so that they compute the same bits.  `src` gives X~ at positions
+// >= t0 - K + 1 (history included), dout at positions >= t0, and takes dx.
+template <class S, int K, bool SILU, bool SEQ, class Src>
+__device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t t0, Src& src) {
   using raw = typename S::raw;
   constexpr int H = K - 1;
-  const int64_t id = (int64_t)blockIdx.x * kBwdBlock + threadIdx.x;
-  if (id >= a.lanes) return;
-  const int64_t bt = id / a.C;
-  const int64_t c = id - bt * a.C;
-  const int64_t b = bt / a.ntt;
-  const int64_t t0 = (bt - b * a.ntt) * a.T;
   const int64_t L = a.L;
   const int64_t t_end = t0 + a.T < L ? t0 + a.T : L;
-
   float w[K];
   load_params<K>(a.w, a.w_dtype, c * K, w);
   const float beta = a.bias ? load_param(a.bias, a.w_dtype, c) : 0.0f;
-  const raw* xr = static_cast<const raw*>(a.x) + b * a.x_sb + c * a.x_sc;
-  const raw* gr = static_cast<const raw*>(a.dout) + b * a.d_sb + c * a.d_sc;
-  raw* dxr = static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc;
   const int32_t* sr = SEQ ? a.seq + b * L : nullptr;
 
   // Slots 0 .. H-1 hold positions u-H .. u-1 before step u; slot H takes u.
@@ -61,12 +56,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < H; ++i) {
     const int64_t j = t0 - H + i;
-    if (j >= 0)
-      xw[i] = S::to_f(xr[j * a.x_sl]);
-    else if (a.init)
-      xw[i] = S::to_f(static_cast<const raw*>(a.init)[b * a.is_b + c * a.is_c + (j + H) * a.is_i]);
-    else
-      xw[i] = 0.0f;
+    xw[i] = src.x(j);
     idw[i] = (SEQ && j >= 0) ? sr[j] : 0;
     dzw[i] = 0.0f;                                 // dz left of the tile is never read
   }
@@ -78,7 +68,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
     float xu = 0.0f, dzu = 0.0f;
     int idu = 0;
     if (u < L) {
-      xu = S::to_f(xr[u * a.x_sl]);
+      xu = src.x(u);
       if constexpr (SEQ) idu = sr[u];
       bool keep[H];
       float z = beta;
@@ -88,7 +78,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
         if (keep[k]) z = __builtin_fmaf(w[k], xw[k], z);
       }
       z = __builtin_fmaf(w[H], xu, z);
-      const float go = S::to_f(gr[u * a.d_sl]);
+      const float go = src.g(u);
       dzu = SILU ? go * silu_slope(z) : go;
       if (u < t_end) {
 #pragma unroll
@@ -117,7 +107,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
       if (a.dfs && j >= L - H)
         acc += S::to_f(static_cast<const raw*>(a.dfs)[b * a.fs_b + c * a.fs_c + (j - (L - H)) * a.fs_i]);
       if (j >= 0)
-        dxr[j * a.g_sl] = S::from_f(acc);
+        src.put_dx(j, acc);
       else
         static_cast<raw*>(a.dinit)[b * a.di_b + c * a.di_c + (j + H) * a.di_i] = S::from_f(acc);
     }
@@ -129,10 +119,179 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
     }
   }
 
-  float* part = a.part + bt * (K + 1) * a.C + c;
+  float* part = a.part + ((b * a.ntt + t0 / a.T) * (K + 1)) * a.C + c;
 #pragma unroll
   for (int k = 0; k < K; ++k) part[k * a.C] = pw[k];
   part[K * a.C] = pb;
+}
+
+// Element path: strided global loads and stores (any layout).
+template <class S, int K>
+struct GlobalSrc {
+  using raw = typename S::raw;
+  const raw* xr;
+  const raw* gr;
+  raw* dxr;
+  const raw* init;          // the row's initial_states, or nullptr
+  int64_t x_sl, d_sl, g_sl, is_i;
+  __device__ float x(int64_t p) const {
+    if (p >= 0) return S::to_f(xr[p * x_sl]);
+    return init ? S::to_f(init[(p + K - 1) * is_i]) : 0.0f;
+  }
+  __device__ float g(int64_t p) const { return S::to_f(gr[p * d_sl]); }
+  __device__ void put_dx(int64_t j, float v) const { dxr[j * g_sl] = S::from_f(v); }
+};
+
+template <class S, int K, bool SILU, bool SEQ>
+__global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
+  using raw = typename S::raw;
+  const int64_t id = (int64_t)blockIdx.x * kBwdBlock + threadIdx.x;
+  if (id >= a.lanes) return;
+  const int64_t bt = id / a.C;
+  const int64_t c = id - bt * a.C;
+  const int64_t b = bt / a.ntt;
+  const int64_t t0 = (bt - b * a.ntt) * a.T;
+  GlobalSrc<S, K> src{static_cast<const raw*>(a.x) + b * a.x_sb + c * a.x_sc,
+                      static_cast<const raw*>(a.dout) + b * a.d_sb + c * a.d_sc,
+                      static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc,
+                      a.init ? static_cast<const raw*>(a.init) + b * a.is_b + c * a.is_c : nullptr,
+                      a.x_sl, a.d_sl, a.g_sl, a.is_i};
+  walk_tile<S, K, SILU, SEQ>(a, b, c, t0, src);
+}
+
+// LDS path: a wave stages its tile (64 channels x the T steps of the tile, with
+// V steps of margin on either side for the halos) with 16-byte loads along the
+// unit-stride dimension, walks it from LDS, and stores dx back with 16-byte
+// stores.  dx[j] is parked in the LDS slot of x[j], which the walk no longer
+// needs once dx[j] is final.  Channel-first tiles are stored channel-major with
+// an odd dword pitch (the walk's reads, one channel per lane, then fall in
+// distinct banks); channel-last tiles step-major, 64 channels to a step.
+template <class S>
+struct LdsGeom {
+  static constexpr int V = S::V;
+  static constexpr int T = 8 * V;                       // the tile length for this dtype
+  static constexpr int ES = sizeof(typename S::raw);
+  static constexpr int XN = T + 2 * V;                  // staged x positions: [t0 - V, t0 + T + V)
+  static constexpr int GN = T + V;                      // staged dout positions: [t0, t0 + T + V)
+  // channel-first pitches (elements), odd in dwords
+  static constexpr int XP = ((XN * ES / 4) | 1) * 4 / ES;
+  static constexpr int GP = ((GN * ES / 4) | 1) * 4 / ES;
+  static constexpr int CF_WORDS = 64 * (XP + GP) * ES / 4;
+  static constexpr int CL_WORDS = (XN + GN) * 64 * ES / 4;
+  static constexpr int WORDS = CF_WORDS > CL_WORDS ? CF_WORDS : CL_WORDS;
+};
+
+template <class S>
+struct LdsSrc {
+  using raw = typename S::raw;
+  raw* xs;                 // this lane's channel in the staged x tile, at position t0 - V
+  const raw* gs;           // ... in the staged dout tile, at position t0
+  int64_t t0;
+  int ps;                  // elements between consecutive positions
+  __device__ float x(int64_t p) const { return S::to_f(xs[(p - t0 + S::V) * ps]); }
+  __device__ float g(int64_t p) const { return S::to_f(gs[(p - t0) * ps]); }
+  __device__ void put_dx(int64_t j, float v) const { xs[(j - t0 + S::V) * ps] = S::from_f(v); }
+};
+
+__device__ inline void lds_put16(void* p, u32x4 v) {
+  uint32_t* d = static_cast<uint32_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = dword(v, i);
+}
+
+__device__ inline u32x4 lds_get16(const void* p) {
+  const uint32_t* d = static_cast<const uint32_t*>(p);
+  return u32x4{d[0], d[1], d[2], d[3]};
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool CL>
+__global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
+  using raw = typename S::raw;
+  using G = LdsGeom<S>;
+  constexpr int V = G::V, H = K - 1;
+  __shared__ uint32_t lds[G::WORDS];
+  raw* lx = reinterpret_cast<raw*>(lds);
+  raw* lg = lx + (CL ? G::XN * 64 : 64 * G::XP);
+
+  const int lane = threadIdx.x;
+  const int64_t ncg = (a.C + 63) / 64;
+  const int64_t item = blockIdx.x;
+  const int64_t bt = item / ncg;
+  const int64_t c0 = (item - bt * ncg) * 64;
+  const int64_t b = bt / a.ntt;
+  const int64_t t0 = (bt - b * a.ntt) * a.T;
+  const int64_t L = a.L, C = a.C;
+  const raw* xb = static_cast<const raw*>(a.x) + b * a.x_sb;
+  const raw* gb = static_cast<const raw*>(a.dout) + b * a.d_sb;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  // Stage x over [t0 - V, t0 + T + V) and dout over [t0, t0 + T + V); zeros outside
+  // [0, L) and past C (L and C are multiples of V on this path).
+  if constexpr (!CL) {
+    constexpr int NX = G::XN / V, NG = G::GN / V;
+    for (int q = lane; q < 64 * NX; q += 64) {
+      const int r = q / NX, k = q - r * NX;
+      const int64_t p = t0 - V + k * V;
+      u32x4 v = zero;
+      if (c0 + r < C && p >= 0 && p < L) v = load16(xb + (c0 + r) * a.x_sc + p);
+      lds_put16(lx + r * G::XP + k * V, v);
+    }
+    for (int q = lane; q < 64 * NG; q += 64) {
+      const int r = q / NG, k = q - r * NG;
+      const int64_t p = t0 + k * V;
+      u32x4 v = zero;
+      if (c0 + r < C && p < L) v = load16(gb + (c0 + r) * a.d_sc + p);
+      lds_put16(lg + r * G::GP + k * V, v);
+    }
+  } else {
+    constexpr int NS = 64 / V;                     // vectors per step
+    for (int q = lane; q < G::XN * NS; q += 64) {
+      const int st = q / NS, k = q - st * NS;
+      const int64_t p = t0 - V + st;
+      u32x4 v = zero;
+      if (c0 + k * V < C && p >= 0 && p < L) v = load16(xb + p * a.x_sl + c0 + k * V);
+      lds_put16(lx + st * 64 + k * V, v);
+    }
+    for (int q = lane; q < G::GN * NS; q += 64) {
+      const int st = q / NS, k = q - st * NS;
+      const int64_t p = t0 + st;
+      u32x4 v = zero;
+      if (c0 + k * V < C && p < L) v = load16(gb + p * a.d_sl + c0 + k * V);
+      lds_put16(lg + st * 64 + k * V, v);
+    }
+  }
+  const int64_t c = c0 + lane;
+  const int cs = CL ? 1 : G::XP, gcs = CL ? 1 : G::GP, ps = CL ? 64 : 1;
+  if (t0 == 0 && a.init && c < C) {                // the history left of t = 0
+#pragma unroll
+    for (int i = 0; i < H; ++i)
+      lx[lane * cs + (V - H + i) * ps] =
+          static_cast<const raw*>(a.init)[b * a.is_b + c * a.is_c + i * a.is_i];
+  }
+  __syncthreads();
+
+  if (c < C) {
+    LdsSrc<S> src{lx + lane * cs, lg + lane * gcs, t0, ps};
+    walk_tile<S, K, SILU, SEQ>(a, b, c, t0, src);
+  }
+  __syncthreads();
+
+  // dx over [t0, t_end) back to memory, 16 bytes at a time.
+  const int64_t t_end = t0 + a.T < L ? t0 + a.T : L;
+  const int nvt = (int)((t_end - t0) / V);
+  raw* db = static_cast<raw*>(a.dx) + b * a.g_sb;
+  if constexpr (!CL) {
+    for (int q = lane; q < 64 * nvt; q += 64) {
+      const int r = q / nvt, k = q - r * nvt;
+      if (c0 + r < C) store16(db + (c0 + r) * a.g_sc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
+    }
+  } else {
+    constexpr int NS = 64 / V;
+    for (int q = lane; q < (int)(t_end - t0) * NS; q += 64) {
+      const int st = q / NS, k = q - st * NS;
+      if (c0 + k * V < C) store16(db + (t0 + st) * a.g_sl + c0 + k * V, lds_get16(lx + (st + V) * 64 + k * V));
+    }
+  }
 }
 
 __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {
@@ -145,57 +304,71 @@ __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {
 }
 
 __global__ void __launch_bounds__(kBwdBlock) bwd_reduce_kernel(const BwdReduceArgs r) {
+  const int64_t width = (int64_t)(r.K + 1) * r.C;
   const int64_t id = (int64_t)blockIdx.x * kBwdBlock + threadIdx.x;
-  const int64_t slots = (int64_t)(r.K + 1) * r.C;
-  if (id >= slots) return;
-  const int64_t slot = id / r.C;
-  const int64_t c = id - slot * r.C;
-  if (slot == r.K && !r.db) return;
-  const float* p = r.part + slot * r.C + c;
-  const int64_t stride = (int64_t)(r.K + 1) * r.C;
-  float total = 0.0f;
-  for (int64_t p0 = 0; p0 < r.nparts; p0 += kBwdChunk) {
-    const int64_t p1 = p0 + kBwdChunk < r.nparts ? p0 + kBwdChunk : r.nparts;
-    float chunk = 0.0f;
-    for (int64_t q = p0; q < p1; ++q) chunk += p[q * stride];
-    total += chunk;
+  const int64_t groups = r.n_in > 0 ? (r.n_in + kBwdFanIn - 1) / kBwdFanIn : 1;   // no rows: zeros
+  if (id >= groups * width) return;
+  const int64_t g = id / width;
+  const int64_t s = id - g * width;
+  const int64_t q0 = g * kBwdFanIn;
+  const int64_t q1 = q0 + kBwdFanIn < r.n_in ? q0 + kBwdFanIn : r.n_in;
+  float acc = 0.0f;
+  for (int64_t q = q0; q < q1; ++q) acc += r.in[q * width + s];
+  if (!r.last) {
+    r.out[g * width + s] = acc;
+    return;
   }
+  const int64_t slot = s / r.C;
+  const int64_t c = s - slot * r.C;
   if (slot < r.K)
-    store_param(r.dw, r.w_dtype, c * r.K + slot, total);
-  else
-    store_param(r.db, r.w_dtype, c, total);
+    store_param(r.dw, r.w_dtype, c * r.K + slot, acc);
+  else if (r.db)
+    store_param(r.db, r.w_dtype, c, acc);
 }
 
 template <class S, int K, bool SILU, bool SEQ>
-int launch_one(const BwdArgs& a, uint32_t grid, void* st) {
+int launch_one(const BwdArgs& a, int path, uint32_t grid, void* st) {
   void* args[] = {const_cast<BwdArgs*>(&a)};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&bwd_kernel<S, K, SILU, SEQ>), dim3(grid),
-                              dim3(kBwdBlock), args, 0, static_cast<hipStream_t>(st));
+  const void* fn;
+  int block = 64;
+  if (path == kBwdPathLdsCf)
+    fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, false>);
+  else if (path == kBwdPathLdsCl)
+    fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, true>);
+  else {
+    fn = reinterpret_cast<const void*>(&bwd_kernel<S, K, SILU, SEQ>);
+    block = kBwdBlock;
+  }
+  return (int)hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, static_cast<hipStream_t>(st));
 }
 
 template <class S, int K>
-int launch_k(const BwdArgs& a, bool silu, bool seq, uint32_t grid, void* st) {
-  if (silu) return seq ? launch_one<S, K, true, true>(a, grid, st) : launch_one<S, K, true, false>(a, grid, st);
-  return seq ? launch_one<S, K, false, true>(a, grid, st) : launch_one<S, K, false, false>(a, grid, st);
+int launch_k(const BwdArgs& a, bool silu, bool seq, int path, uint32_t grid, void* st) {
+  if (silu)
+    return seq ? launch_one<S, K, true, true>(a, path, grid, st) : launch_one<S, K, true, false>(a, path, grid, st);
+  return seq ? launch_one<S, K, false, true>(a, path, grid, st) : launch_one<S, K, false, false>(a, path, grid, st);
 }
 
 template <class S>
-int launch_s(const BwdArgs& a, int K, bool silu, bool seq, uint32_t grid, void* st) {
+int launch_s(const BwdArgs& a, int K, bool silu, bool seq, int path, uint32_t grid, void* st) {
   switch (K) {
-    case 2: return launch_k<S, 2>(a, silu, seq, grid, st);
-    case 3: return launch_k<S, 3>(a, silu, seq, grid, st);
-    case 4: return launch_k<S, 4>(a, silu, seq, grid, st);
+    case 2: return launch_k<S, 2>(a, silu, seq, path, grid, st);
+    case 3: return launch_k<S, 3>(a, silu, seq, path, grid, st);
+    case 4: return launch_k<S, 4>(a, silu, seq, path, grid, st);
   }
   return (int)hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, uint32_t grid, void* stream) {
+int bwd_tile_steps(int dtype) { return dtype == CCV_DT_F32 ? LdsGeom<F32>::T : LdsGeom<BF16>::T; }
+
+int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, int path, uint32_t grid,
+               void* stream) {
   switch (dtype) {
-    case CCV_DT_F32: return launch_s<F32>(a, K, silu, seq, grid, stream);
-    case CCV_DT_F16: return launch_s<F16>(a, K, silu, seq, grid, stream);
-    case CCV_DT_BF16: return launch_s<BF16>(a, K, silu, seq, grid, stream);
+    case CCV_DT_F32: return launch_s<F32>(a, K, silu, seq, path, grid, stream);
+    case CCV_DT_F16: return launch_s<F16>(a, K, silu, seq, path, grid, stream);
+    case CCV_DT_BF16: return launch_s<BF16>(a, K, silu, seq, path, grid, stream);
   }
   return (int)hipErrorInvalidValue;
 }

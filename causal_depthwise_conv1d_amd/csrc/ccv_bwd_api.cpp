@@ -9,6 +9,7 @@
 //
 // Nothing here touches a device except ccv_bwd's two kernel launches.
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "ccv.h"
 #include "ccv_bwd_launch.hpp"
@@ -22,8 +23,28 @@ using namespace ccv::checks;
 struct BwdPlan {
   BwdArgs a;
   BwdReduceArgs r;
-  int64_t grid = 0, rgrid = 0, ws_bytes = 0;
+  int path = kBwdPathElement;
+  int64_t grid = 0, rgrid = 0, ws_bytes = 0, items = 0;
 };
+
+// Which gradient kernel applies (see kBwdPath* in ccv_bwd_launch.hpp).
+int choose_path(const ccv_bwd_args_t* a) {
+  const char* force = getenv("CCV_FORCE_SCALAR");
+  if (force && atoi(force) != 0) return kBwdPathElement;
+  const int es = elt_size(a->x_dtype);
+  const int V = 16 / es;
+  const int64_t B = a->B, C = a->C, L = a->L;
+  if (!aligned16(a->x) || !aligned16(a->dout) || !aligned16(a->dx)) return kBwdPathElement;
+  const int64_t* st[3] = {a->x_stride, a->dout_stride, a->dx_stride};
+  bool cf = L % V == 0, cl = C % V == 0;
+  for (const int64_t* s : st) {
+    cf = cf && s[2] == 1 && stride_ok16(B, s[0], es) && stride_ok16(C, s[1], es);
+    cl = cl && s[1] == 1 && stride_ok16(B, s[0], es) && stride_ok16(L, s[2], es);
+  }
+  if (cf) return kBwdPathLdsCf;
+  if (cl) return kBwdPathLdsCl;
+  return kBwdPathElement;
+}
 
 // Checks every argument and fills *p; the workspace fields are checked only when
 // `check_workspace` (ccv_bwd_workspace_size asks before there is one).
@@ -75,14 +96,17 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
 
   // One lane per (b, tile, c); a row with L = 0 still has one tile, which writes
   // d(initial_states) from dfinal_states.
-  const int64_t T = kBwdTile;
+  const int64_t T = bwd_tile_steps(a->x_dtype);
   const int64_t ntt = L > 0 ? (L + T - 1) / T : 1;
   int64_t nparts, lanes, ws;
   if (__builtin_mul_overflow(B, ntt, &nparts) || __builtin_mul_overflow(nparts, C, &lanes) ||
-      __builtin_mul_overflow(lanes, (int64_t)(K + 1) * 4, &ws))
+      __builtin_mul_overflow(nparts + bwd_reduce_rows(nparts), (int64_t)(K + 1) * C * 4, &ws))
     return CCV_E_SHAPE;
-  const int64_t grid = (lanes + kBwdBlock - 1) / kBwdBlock;
-  const int64_t rgrid = ((int64_t)(K + 1) * C + kBwdBlock - 1) / kBwdBlock;
+  const int path = rows ? choose_path(a) : kBwdPathElement;
+  const int64_t items = path == kBwdPathElement ? lanes : nparts * ((C + 63) / 64);
+  const int64_t grid = path == kBwdPathElement ? (lanes + kBwdBlock - 1) / kBwdBlock : items;
+  const int64_t groups = nparts > 0 ? (nparts + kBwdFanIn - 1) / kBwdFanIn : 1;   // B = 0 still writes zeros
+  const int64_t rgrid = (groups * (K + 1) * C + kBwdBlock - 1) / kBwdBlock;
   if (grid > INT32_MAX || rgrid > INT32_MAX) return CCV_E_SHAPE;
   if (check_workspace && ws > 0) {
     if (!a->workspace) return CCV_E_NULL;
@@ -128,14 +152,16 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   g.w_dtype = a->w_dtype;
 
   BwdReduceArgs& r = p->r;
-  r.part = g.part;
+  r.in = g.part;
   r.dw = a->dweight;
   r.db = a->dbias;
   r.C = C;
-  r.nparts = nparts;
+  r.n_in = nparts;
   r.K = K;
   r.w_dtype = a->w_dtype;
 
+  p->path = path;
+  p->items = items;
   p->grid = grid;
   p->rgrid = rgrid;
   p->ws_bytes = ws;
@@ -159,19 +185,20 @@ int ccv_bwd_check(const ccv_bwd_args_t* args) {
 
 int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan) {
   BwdPlan p;
-  const int st = validate(args, &p);
+  const int st = validate(args, &p, false);      // a plan is wanted before the workspace exists
   if (st != CCV_OK || !plan) return st;
   *plan = ccv_plan_t{};
+  const bool lds = p.path != kBwdPathElement;
   plan->path = p.grid || p.rgrid ? CCV_PATH_BACKWARD : CCV_PATH_NONE;
-  plan->vector = 0;
+  plan->vector = lds ? p.path : 0;
   plan->elems_per_lane = 1;
   plan->unroll = 1;
   plan->grid = p.grid;
-  plan->block = kBwdBlock;
-  plan->waves_per_group = kBwdBlock / 64;
-  plan->work_items = p.a.lanes;
+  plan->block = lds ? 64 : kBwdBlock;
+  plan->waves_per_group = lds ? 1 : kBwdBlock / 64;
+  plan->work_items = p.items;
   plan->span = p.a.T;
-  plan->channels_per_item = 1;
+  plan->channels_per_item = lds ? 64 : 1;
   return st;
 }
 
@@ -181,12 +208,26 @@ int ccv_bwd(const ccv_bwd_args_t* args, void* hip_stream) {
   if (st != CCV_OK) return st;
   if (p.grid > 0) {
     const int err = launch_bwd(p.a, args->x_dtype, args->K, args->activation == CCV_ACT_SILU,
-                               args->seq_idx != nullptr, (uint32_t)p.grid, hip_stream);
+                               args->seq_idx != nullptr, p.path, (uint32_t)p.grid, hip_stream);
     if (err != 0) return CCV_E_HIP;
   }
   if (p.rgrid > 0) {
-    const int err = launch_bwd_reduce(p.r, (uint32_t)p.rgrid, hip_stream);
-    if (err != 0) return CCV_E_HIP;
+    // Levels of the reduction tree, each reading the previous level's rows.
+    BwdReduceArgs r = p.r;
+    const int64_t width = (int64_t)(args->K + 1) * args->C;
+    float* next = p.a.part ? p.a.part + p.r.n_in * width : nullptr;
+    while (true) {
+      const int64_t groups = r.n_in > 0 ? (r.n_in + kBwdFanIn - 1) / kBwdFanIn : 1;
+      r.last = r.n_in <= kBwdFanIn;
+      r.out = r.last ? nullptr : next;
+      const int64_t grid = (groups * width + kBwdBlock - 1) / kBwdBlock;
+      const int err = launch_bwd_reduce(r, (uint32_t)(grid > 0 ? grid : 1), hip_stream);
+      if (err != 0) return CCV_E_HIP;
+      if (r.last) break;
+      r.in = next;
+      r.n_in = groups;
+      next += groups * width;
+    }
   }
   return CCV_OK;
 }

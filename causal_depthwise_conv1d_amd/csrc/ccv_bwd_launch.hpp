@@ -31,21 +31,45 @@ struct BwdArgs {
   int32_t w_dtype;
 };
 
-// Reduction kernel: one lane per (slot, c), slot < K + 1; sums the B * ntt
-// partials in a fixed order and writes dweight[c, slot] (slot < K) or dbias[c].
+// Reduction, one level: lane (g, s) with s < (K + 1) * C sums inputs
+// in[32 g .. 32 g + 31][s] in order (fewer in the last group) into out[g][s].
+// Levels repeat until one group is left; the last level instead rounds to the
+// weight dtype and writes dweight[c, slot] (slot < K) or dbias[c] (slot = K).
 struct BwdReduceArgs {
-  const float* part;
-  void* dw;                 // [C, K], w_dtype
-  void* db;                 // [C] or nullptr, w_dtype
-  int64_t C, nparts;
+  const float* in;          // [n_in][(K + 1) * C]
+  float* out;               // [ceil(n_in / 32)][(K + 1) * C], unused on the last level
+  void* dw;                 // [C, K], w_dtype (last level)
+  void* db;                 // [C] or nullptr, w_dtype (last level)
+  int64_t C, n_in;
   int32_t K, w_dtype;
+  int32_t last;
 };
 
-constexpr int kBwdBlock = 256;
-constexpr int kBwdTile = 64;        // T: time steps per lane
-constexpr int kBwdChunk = 32;       // partials summed per chunk in the reduction
+constexpr int kBwdBlock = 256;      // element path: lanes per workgroup
+constexpr int kBwdFanIn = 32;       // partial sums added per lane and level of the reduction
 
-int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, uint32_t grid, void* stream);
+// Gradient kernel variants: the element path (one lane per (b, tile, c), any
+// strides; grid = ceil(lanes / kBwdBlock)) and the LDS-staged paths (one 64-lane
+// workgroup per (b, tile, group of 64 channels); grid = B * ntt * ceil(C / 64)),
+// which need x, dout and dx unit-stride in the same dimension (time for CF,
+// channels for CL), 16-byte aligned bases and strides, and L (CF) or C (CL) a
+// multiple of 16 / element size.
+enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2 };
+
+// Time steps per tile T for a dtype (both paths use the same T, so their partial
+// sums, and so dweight and dbias, are identical).
+int bwd_tile_steps(int dtype);
+
+int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, int path, uint32_t grid,
+               void* stream);
 int launch_bwd_reduce(const BwdReduceArgs& r, uint32_t grid, void* stream);
+
+// Floats the reduction needs after the B * ntt partial rows: one row per group of
+// every level but the last.
+inline int64_t bwd_reduce_rows(int64_t nparts) {
+  int64_t rows = 0;
+  for (int64_t n = nparts; n > kBwdFanIn; n = (n + kBwdFanIn - 1) / kBwdFanIn) rows += (n + kBwdFanIn - 1) / kBwdFanIn;
+  return rows;
+}
 
 }  // namespace ccv

@@ -263,8 +263,13 @@ int ccv_bwd(const ccv_bwd_args_t* args, void* hip_stream);
 int ccv_bwd_check(const ccv_bwd_args_t* args);
 
 /* Describe the launch ccv_bwd would make (host only; `plan` may be NULL): path
- * CCV_PATH_BACKWARD, span = time steps per tile, work_items = tiles x channels
- * (one lane each), grid / block of the gradient kernel. */
+ * CCV_PATH_BACKWARD; vector 0 for the element path (one lane per (b, tile, c),
+ * any strides), 1 for the LDS-staged channel-first path, 2 for the LDS-staged
+ * channel-last path (x, dout and dx unit-stride in time, resp. channels, 16-byte
+ * aligned, L resp. C a multiple of 16 / element size); span = time steps per
+ * tile; channels_per_item = channels per work item; work_items, grid, block of
+ * the gradient kernel.  The workspace fields are not checked here, so a plan can
+ * be had before the workspace is allocated. */
 int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan);
 
 /* Static, NUL-terminated name of a status code ("CCV_OK", ...). */

@@ -348,10 +348,16 @@ def bcheck(a):
 
 
 def test_bwd_workspace_size_is_the_partial_sums():
+    # one fp32 row of (K + 1) * C partial sums per (b, tile), plus one row per group
+    # of 32 on every level of the reduction tree but the last
     a = bargs(B=3, C=100, L=1000, K=3, ws=False)
-    tiles = -(-1000 // 64)
-    assert ccv.ccv_bwd_workspace_size(a) == 3 * tiles * 100 * (3 + 1) * 4
+    parts = 3 * -(-1000 // 64)                       # 48 rows -> 2 groups -> 1
+    assert ccv.ccv_bwd_workspace_size(a) == (parts + 2) * 100 * (3 + 1) * 4
     assert ccv.ccv_bwd_workspace_size(bargs(B=2, C=5, L=0, ws=False)) == 2 * 1 * 5 * 5 * 4
+    a = bargs(B=2, C=128, L=1 << 20, K=3, ws=False)
+    a.x_dtype = ccv.CCV_F32
+    parts = 2 * (1 << 20) // 32                      # 65536 -> 2048 -> 64 -> 2 -> 1
+    assert ccv.ccv_bwd_workspace_size(a) == (parts + 2048 + 64 + 2) * 128 * 4 * 4
     assert ccv.ccv_bwd_workspace_size(bargs(B=0, ws=False)) == 0
     assert ccv.ccv_bwd_workspace_size(bargs(K=5, ws=False)) == ccv.lib().ccv_bwd_check(bargs(K=5, ws=False))
 
@@ -408,6 +414,21 @@ def test_bwd_empty_extents():
 
 
 def test_bwd_plan():
+    # aligned channel-first: the LDS-staged channel-first kernel, a 64-lane workgroup
+    # per (b, tile of 64 steps, group of 64 channels)
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096))
-    assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD
-    assert p.span == 64 and p.work_items == 4 * 64 * 2048 and p.grid == 4 * 64 * 2048 // 256
+    assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD and p.vector == 1
+    assert p.span == 64 and p.work_items == 4 * 64 * 32 and p.grid == p.work_items and p.block == 64
+    # aligned channel-last: the LDS-staged channel-last kernel
+    assert ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, layout="cl"))[1].vector == 2
+    # fp32 tiles are 32 steps (the same 16-byte vectors per lane)
+    a = bargs(B=1, C=64, L=100, ws=False)
+    a.x_dtype = ccv.CCV_F32
+    a.workspace, a.workspace_bytes = WS, ccv.ccv_bwd_workspace_size(a)
+    st, p = ccv.ccv_bwd_plan(a)
+    assert st == 0 and p.span == 32 and p.vector == 1
+    # unaligned or mixed layouts: the element kernel, one lane per (b, tile, c)
+    st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4095, x_stride=(2048 * 4095, 4095, 1),
+                                   dout_stride=(2048 * 4095, 4095, 1), dx_stride=(2048 * 4095, 4095, 1)))
+    assert st == 0 and p.vector == 0 and p.work_items == 4 * 64 * 2048 and p.grid == 4 * 64 * 2048 // 256
+    assert ccv.ccv_bwd_plan(bargs(dx_stride=(64 * 1000, 1, 64)))[1].vector == 0

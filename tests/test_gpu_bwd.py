@@ -29,7 +29,11 @@ if torch.cuda.is_available():
 DTYPES = ["f32", "bf16", "f16"]
 KS = [2, 3, 4]
 DOUT_ID, DFS_ID = 5, 6
-TILE = 64
+
+
+def tile_steps(dtype):
+    """Time steps per tile of the backward (8 vectors of 16 bytes)."""
+    return 32 if dtype == "f32" else 64
 
 
 def grad_inputs(w, layout, with_dfs, seed):
@@ -54,12 +58,20 @@ def run_bwd(w, dout, dfs, want_dinit):
     return [None if t is None else t.cpu().contiguous() for t in res]
 
 
+def reduction_levels(parts):
+    levels, n = 1, parts
+    while n > 32:
+        n, levels = -(-n // 32), levels + 1
+    return levels
+
+
 def param_terms(w):
-    """compare()'s K for the parameter gradients: (T + 32 + parts / 32 + K + 8) / 4
-    roundings of 2^-22 each cover the in-tile sum, the chunked sum of the partials
-    and the error of dz itself."""
-    parts = w.B * max(1, math.ceil(w.L / TILE))
-    return math.ceil((TILE + 32 + parts / 32 + w.K + 8) / 4)
+    """compare()'s K for the parameter gradients: (T + 32 * levels + K + 8) / 4
+    roundings of 2^-22 cover the in-tile sum, the levels of the fan-in-32
+    reduction tree over the partial sums, and the error of dz itself."""
+    T = tile_steps(w.x_dtype)
+    parts = w.B * max(1, math.ceil(w.L / T))
+    return math.ceil((T + 32 * reduction_levels(parts) + w.K + 8) / 4)
 
 
 def check_bwd(w, dout, dfs, want_dinit, where):
@@ -115,6 +127,33 @@ def test_bwd_matches_oracle(dtype, K, layout):
         dout, dfs = grad_inputs(w, layout, f.get("dfs", False), seed)
         log(f"  bwd {dtype}/{w.w_dtype} K={K} {layout} L={L} C={C} B={B} {f}")
         check_bwd(w, dout, dfs, f.get("dinit", False), f"[{dtype} K={K} {layout} L={L}]")
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_lds_path_equals_element_path(dtype, layout, monkeypatch):
+    """The LDS-staged kernels (chosen for aligned unit-stride layouts) and the
+    element kernel give the same bits for every gradient: a ragged last tile, a
+    partial group of 64 channels, history, dfinal_states and seq_idx."""
+    T = tile_steps(dtype)
+    for K in KS:
+        for f in (dict(init=True, dfs=True), dict(seq=7)):
+            B, C, L = 2, 136, 4 * T + 8
+            w = build(B, C, L, K, dtype, layout, 5100 + K, seq=f.get("seq"), init=f.get("init", False))
+            dout, dfs = grad_inputs(w, layout, f.get("dfs", False), 5100 + K)
+            res = []
+            for force, want in (("0", 1 if layout == "cf" else 2), ("1", 0)):
+                monkeypatch.setenv("CCV_FORCE_SCALAR", force)
+                x = to_gpu_view(w.x_storage, w.x)
+                args = ccv.make_bwd_args(x, w.weight.cuda(), w.bias.cuda(), dout.cuda(), ccv.empty_like_layout(x),
+                                         torch.empty(C, K, dtype=w.weight.dtype, device="cuda"))
+                st, plan = ccv.ccv_bwd_plan(args)
+                assert st == 0 and plan.vector == want, (force, plan.as_dict())
+                res.append(run_bwd(w, dout, dfs, bool(f.get("init"))))
+            bits = torch.int32 if dtype == "f32" else torch.int16
+            for name, t0, t1 in zip(("dx", "dweight", "dbias", "dinit"), *res):
+                if t0 is not None:
+                    assert torch.equal(t0.view(bits), t1.view(bits)), (K, f, name)
 
 
 def test_bwd_random_shapes():
