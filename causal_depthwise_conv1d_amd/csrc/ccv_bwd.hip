@@ -39,12 +39,15 @@ __device__ inline float silu_slope(float z) {
 // The walk of one lane over one tile (see the header comment), shared by both
 // kernels so that they compute the same bits.  `src` gives X~ at positions
 // >= t0 - K + 1 (history included), dout at positions >= t0, and takes dx.
-template <class S, int K, bool SILU, bool SEQ, class Src>
+// FULL (a tile of TT steps with t0 + TT + K - 1 <= L, not writing
+// d(initial_states)) fixes the trip count and every condition at compile time,
+// so the walk unrolls completely; the arithmetic is the same.
+template <class S, int K, bool SILU, bool SEQ, bool FULL, int TT, class Src>
 __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t t0, Src& src) {
   using raw = typename S::raw;
   constexpr int H = K - 1;
   const int64_t L = a.L;
-  const int64_t t_end = t0 + a.T < L ? t0 + a.T : L;
+  const int64_t t_end = FULL ? t0 + TT : (t0 + a.T < L ? t0 + a.T : L);
   float w[K];
   load_params<K>(a.w, a.w_dtype, c * K, w);
   const float beta = a.bias ? load_param(a.bias, a.w_dtype, c) : 0.0f;
@@ -64,10 +67,13 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
 #pragma unroll
   for (int k = 0; k < K; ++k) pw[k] = 0.0f;
 
-  for (int64_t u = t0; u < t_end + H; ++u) {
+  const int64_t n_steps = FULL ? TT + H : t_end + H - t0;
+#pragma unroll(FULL ? TT + H : 1)
+  for (int64_t i = 0; i < n_steps; ++i) {
+    const int64_t u = t0 + i;
     float xu = 0.0f, dzu = 0.0f;
     int idu = 0;
-    if (u < L) {
+    if (FULL || u < L) {
       xu = src.x(u);
       if constexpr (SEQ) idu = sr[u];
       bool keep[H];
@@ -80,7 +86,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
       z = __builtin_fmaf(w[H], xu, z);
       const float go = src.g(u);
       dzu = SILU ? go * silu_slope(z) : go;
-      if (u < t_end) {
+      if (FULL ? i < TT : u < t_end) {
 #pragma unroll
         for (int k = 0; k < H; ++k)
           if (keep[k]) pw[k] = __builtin_fmaf(dzu, xw[k], pw[k]);
@@ -94,17 +100,17 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
 
     // dX~ at j = u - H reads dz[j .. u] = slots 0 .. H.
     const int64_t j = u - H;
-    const bool to_dx = j >= t0;
-    const bool to_init = j < 0 && a.dinit != nullptr;
+    const bool to_dx = FULL ? i >= H : j >= t0;
+    const bool to_init = !FULL && j < 0 && a.dinit != nullptr;
     if (to_dx || to_init) {
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < K; ++k) {                // output t = j + H - k uses tap k on X~[j]
         const int64_t t = j + H - k;
-        const bool keep = t >= 0 && t < L && (!SEQ || idw[0] == idw[H - k]);
+        const bool keep = (FULL || (t >= 0 && t < L)) && (!SEQ || idw[0] == idw[H - k]);
         if (keep) acc = __builtin_fmaf(w[k], dzw[H - k], acc);
       }
-      if (a.dfs && j >= L - H)
+      if (!FULL && a.dfs && j >= L - H)
         acc += S::to_f(static_cast<const raw*>(a.dfs)[b * a.fs_b + c * a.fs_c + (j - (L - H)) * a.fs_i]);
       if (j >= 0)
         src.put_dx(j, acc);
@@ -156,7 +162,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
                       static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc,
                       a.init ? static_cast<const raw*>(a.init) + b * a.is_b + c * a.is_c : nullptr,
                       a.x_sl, a.d_sl, a.g_sl, a.is_i};
-  walk_tile<S, K, SILU, SEQ>(a, b, c, t0, src);
+  walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src);
 }
 
 // LDS path: a wave stages its tile (64 channels x the T steps of the tile, with
@@ -181,16 +187,15 @@ struct LdsGeom {
   static constexpr int WORDS = CF_WORDS > CL_WORDS ? CF_WORDS : CL_WORDS;
 };
 
-template <class S>
+template <class S, int PS>
 struct LdsSrc {
   using raw = typename S::raw;
   raw* xs;                 // this lane's channel in the staged x tile, at position t0 - V
   const raw* gs;           // ... in the staged dout tile, at position t0
-  int64_t t0;
-  int ps;                  // elements between consecutive positions
-  __device__ float x(int64_t p) const { return S::to_f(xs[(p - t0 + S::V) * ps]); }
-  __device__ float g(int64_t p) const { return S::to_f(gs[(p - t0) * ps]); }
-  __device__ void put_dx(int64_t j, float v) const { xs[(j - t0 + S::V) * ps] = S::from_f(v); }
+  int64_t t0;              // PS: elements between consecutive positions
+  __device__ float x(int64_t p) const { return S::to_f(xs[(p - t0 + S::V) * PS]); }
+  __device__ float g(int64_t p) const { return S::to_f(gs[(p - t0) * PS]); }
+  __device__ void put_dx(int64_t j, float v) const { xs[(j - t0 + S::V) * PS] = S::from_f(v); }
 };
 
 __device__ inline void lds_put16(void* p, u32x4 v) {
@@ -261,7 +266,7 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     }
   }
   const int64_t c = c0 + lane;
-  const int cs = CL ? 1 : G::XP, gcs = CL ? 1 : G::GP, ps = CL ? 64 : 1;
+  constexpr int cs = CL ? 1 : G::XP, gcs = CL ? 1 : G::GP, ps = CL ? 64 : 1;
   if (t0 == 0 && a.init && c < C) {                // the history left of t = 0
 #pragma unroll
     for (int i = 0; i < H; ++i)
@@ -271,8 +276,11 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   __syncthreads();
 
   if (c < C) {
-    LdsSrc<S> src{lx + lane * cs, lg + lane * gcs, t0, ps};
-    walk_tile<S, K, SILU, SEQ>(a, b, c, t0, src);
+    LdsSrc<S, ps> src{lx + lane * cs, lg + lane * gcs, t0};
+    if (t0 + G::T + H <= L && (t0 > 0 || !a.dinit))     // an interior tile
+      walk_tile<S, K, SILU, SEQ, true, G::T>(a, b, c, t0, src);
+    else
+      walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src);
   }
   __syncthreads();
 
