@@ -321,7 +321,15 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_reduce_kernel(const BwdReduceAr
   const int64_t q0 = g * kBwdFanIn;
   const int64_t q1 = q0 + kBwdFanIn < r.n_in ? q0 + kBwdFanIn : r.n_in;
   float acc = 0.0f;
-  for (int64_t q = q0; q < q1; ++q) acc += r.in[q * width + s];
+  if (q1 - q0 == kBwdFanIn) {                      // a whole group: all loads first, then the sum in order
+    float v[kBwdFanIn];
+#pragma unroll
+    for (int q = 0; q < kBwdFanIn; ++q) v[q] = r.in[(q0 + q) * width + s];
+#pragma unroll
+    for (int q = 0; q < kBwdFanIn; ++q) acc += v[q];
+  } else {
+    for (int64_t q = q0; q < q1; ++q) acc += r.in[q * width + s];
+  }
   if (!r.last) {
     r.out[g * width + s] = acc;
     return;
