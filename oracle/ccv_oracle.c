@@ -160,6 +160,38 @@ double ora_xt(const ora_problem_t* p, int64_t b, int64_t c, int64_t j) {
   return ora_decode(p->init, p->x_dtype, b * p->is[0] + c * p->is[1] + i * p->is[2]);
 }
 
+/* Sequence id of extended position j of row b: seq_idx[b, j] for j >= 0.  The
+ * history left of t = 0 is the history of the row's first sequence, so it carries
+ * seq_idx[b, 0]; without a history (or with L = 0) it has no id.  Returns 0 when
+ * the position has no id. */
+static int ora_pos_id(const ora_problem_t* p, int64_t b, int64_t j, int32_t* id) {
+  if (j >= 0) {
+    *id = p->seq[b * p->L + j];
+    return 1;
+  }
+  if (p->init == NULL || p->L == 0) return 0;
+  *id = p->seq[b * p->L];
+  return 1;
+}
+
+/* Whether term k of output t counts: always without seq_idx; with it, when its
+ * source position has the output's sequence id. */
+static int ora_keep(const ora_problem_t* p, int64_t b, int64_t t, int k) {
+  if (p->seq == NULL) return 1;
+  int32_t id;
+  if (!ora_pos_id(p, b, t - p->K + 1 + k, &id)) return 0;
+  return id == p->seq[b * p->L + t];
+}
+
+/* Whether extended position j survives into final_states: always without seq_idx;
+ * with it, final_states are the history of the row's last sequence, so a position
+ * of another sequence is zero there. */
+static int ora_final_kept(const ora_problem_t* p, int64_t b, int64_t j) {
+  if (p->seq == NULL || p->L == 0) return 1;
+  int32_t id;
+  return ora_pos_id(p, b, j, &id) && id == p->seq[b * p->L + p->L - 1];
+}
+
 int ora_point(const ora_problem_t* p, int64_t b, int64_t c, int64_t t,
               double* y, double* z, double* sabs) {
   if (b < 0 || b >= p->B || c < 0 || c >= p->C || t < 0 || t >= p->L) return -1;
@@ -172,10 +204,7 @@ int ora_point(const ora_problem_t* p, int64_t b, int64_t c, int64_t t,
   }
   for (int k = 0; k < K; ++k) {
     int64_t src = t - K + 1 + k;              /* w[c,K-1] meets the current step */
-    if (p->seq != NULL) {
-      if (src < 0) continue;                  /* no sequence id left of t = 0 */
-      if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;   /* dropped */
-    }
+    if (!ora_keep(p, b, t, k)) continue;      /* dropped */
     double term = ora_decode(p->w, p->w_dtype, c * K + k) * ora_xt(p, b, c, src);
     acc += term;
     s += fabs(term);
@@ -221,7 +250,9 @@ int ora_final_states(const ora_problem_t* p, void* fs) {
       for (int i = 0; i < K - 1; ++i) {
         int64_t j = p->L - K + 1 + i;         /* the last K-1 positions of X~ */
         char* dst = (char*)fs + ((b * p->C + c) * (K - 1) + i) * es;
-        if (j >= 0) {
+        if (!ora_final_kept(p, b, j)) {
+          memset(dst, 0, es);
+        } else if (j >= 0) {
           memcpy(dst, (const char*)p->x + (b * p->xs[0] + c * p->xs[1] + j * p->xs[2]) * es, es);
         } else if (p->init != NULL) {
           int64_t ii = j + K - 1;
@@ -249,10 +280,7 @@ int ora_point_f32(const ora_problem_t* p, int64_t b, int64_t c, int64_t t, float
   if (p->bias != NULL) acc = (float)ora_decode(p->bias, p->w_dtype, c);
   for (int k = 0; k < K; ++k) {
     int64_t src = t - K + 1 + k;
-    if (p->seq != NULL) {
-      if (src < 0) continue;
-      if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;
-    }
+    if (!ora_keep(p, b, t, k)) continue;
     float wv = (float)ora_decode(p->w, p->w_dtype, c * K + k);
     float xv = (float)ora_xt(p, b, c, src);
     acc = fmaf(wv, xv, acc);
@@ -276,14 +304,6 @@ int ora_points_f32(const ora_problem_t* p, int64_t n, const int64_t* idx, float*
 }
 
 /* ---- backward ------------------------------------------------------------------ */
-
-/* Whether term k of output t counts (the forward's mask). */
-static int ora_keep(const ora_problem_t* p, int64_t b, int64_t t, int k) {
-  if (p->seq == NULL) return 1;
-  int64_t src = t - p->K + 1 + k;
-  if (src < 0) return 0;
-  return p->seq[b * p->L + src] == p->seq[b * p->L + t];
-}
 
 int ora_bwd(const ora_problem_t* p, const ora_grad_t* g, double* dx, double* dinit,
             double* dw, double* db, double* ex, double* einit, double* ew, double* eb) {
@@ -329,7 +349,7 @@ int ora_bwd(const ora_problem_t* p, const ora_grad_t* g, double* dx, double* din
           acc += wk * dz[t];
           e += fabs(wk) * edz[t];
         }
-        if (g->dfs != NULL && j >= L - H) {
+        if (g->dfs != NULL && j >= L - H && ora_final_kept(p, b, j)) {
           int64_t i = j - (L - H);
           double v = ora_decode(g->dfs, p->x_dtype, b * g->fs[0] + c * g->fs[1] + i * g->fs[2]);
           acc += v;

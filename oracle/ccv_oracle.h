@@ -19,7 +19,11 @@
  * of boundary handled separately").  keep(t,k) is 1 without seq_idx; with it,
  * a term counts only when its source position s = t-K+1+k is >= 0 and
  * seq_idx[b,s] == seq_idx[b,t] (same section, the seq_idx paragraph); a term
- * that does not count is skipped, never multiplied by zero.
+ * that does not count is skipped, never multiplied by zero.  With seq_idx and
+ * initial_states together (a version limit of the pages' library, lifted here),
+ * the history is the history of the row's first sequence: a term reaching left of
+ * t = 0 counts when seq_idx[b,t] == seq_idx[b,0]; and final_states are the history
+ * of the row's last sequence: an entry from another sequence is zero.
  *
  * Strides are in elements: offset(b,c,t) = b*s_B + c*s_C + t*s_L (Ch.4,
  * section "Why one shape still has two layouts", the offset equation).

@@ -253,6 +253,45 @@ def pin_packing(ora):
                 pos += n
 
 
+def _fs_tensor(raw_fs, dt):
+    return (torch.from_numpy(raw_fs.copy()) if dt == "f32"
+            else torch.from_numpy(raw_fs.view(np.int16).copy()).view(DT[dt]))
+
+
+def pin_packed_chunking(ora):
+    """seq_idx together with states: a packed row split anywhere equals the whole
+    row when chunk 2's history is chunk 1's final states if its first sequence
+    continues chunk 1's last one, and zeros if it starts there.  That holds only
+    if the history counts for the row's first sequence and final states keep the
+    row's last sequence only.  Every output and final state, bit for bit."""
+    g = _gen(26)
+    for K in (2, 3, 4):
+        for dt in ("f32", "bf16"):
+            lengths = [3, 1, 6, 2, 9]
+            L, C, B = sum(lengths), 3, 2
+            x = torch.randn(B, C, L, generator=g).to(DT[dt])
+            w = torch.randn(C, K, generator=g).to(DT[dt])
+            bias = torch.randn(C, generator=g).to(DT[dt])
+            h = torch.randn(B, C, K - 1, generator=g).to(DT[dt])
+            ids = np.repeat(np.arange(len(lengths)), lengths)
+            seq = torch.tensor(np.stack([ids, ids[::-1] + 10]), dtype=torch.int32)
+            full = _cf_case(ora, x, w, bias, seq=seq, init=h, silu=True)
+            y_full, _ = full.fwd()
+            fs_full = full.final_states()
+            for L1 in range(1, L):
+                c1 = _cf_case(ora, x[:, :, :L1].contiguous(), w, bias, seq=seq[:, :L1].contiguous(), init=h,
+                              silu=True)
+                y1, _ = c1.fwd()
+                f1 = _fs_tensor(c1.final_states(), dt)
+                cont = (seq[:, L1] == seq[:, L1 - 1]).reshape(B, 1, 1)
+                h2 = torch.where(cont, f1, torch.zeros_like(f1))
+                c2 = _cf_case(ora, x[:, :, L1:].contiguous(), w, bias, seq=seq[:, L1:].contiguous(), init=h2,
+                              silu=True)
+                y2, _ = c2.fwd()
+                assert np.array_equal(np.concatenate([y1, y2], 2).view(np.uint64), y_full.view(np.uint64)), (K, dt, L1)
+                assert np.array_equal(c2.final_states(), fs_full), (K, dt, L1)
+
+
 def pin_mask_nan(ora):
     """A masked term is dropped, not multiplied by zero: a NaN in another sequence
     does not reach this one, while a NaN inside the window does."""
@@ -525,10 +564,8 @@ def _loss(ora, x, w, b, seq, init, silu, dout, dfs):
     c = _cf_case(ora, x, w, b, seq=seq, init=init, silu=silu)
     y, _ = c.fwd(want_sabs=False)
     loss = float(np.sum(y * dout.double().numpy()))
-    if dfs is not None:
-        K = w.shape[1]
-        xt = torch.cat([init if init is not None else torch.zeros(x.shape[0], x.shape[1], K - 1), x], 2)
-        loss += float((xt[:, :, xt.shape[2] - (K - 1):].double() * dfs.double()).sum())
+    if dfs is not None:                       # the oracle's final states (fp32 storage)
+        loss += float(np.sum(c.final_states().astype(np.float64) * dfs.double().numpy()))
     return loss
 
 
@@ -542,7 +579,8 @@ def pin_bwd_finite_differences(ora):
     def dyadic(*shape):
         return torch.randint(-256, 257, shape, generator=g).float() / 128.0
 
-    for K, L, seq, init in ((3, 9, [0, 0, 0, 1, 1, 2, 2, 2, 2], False), (4, 7, None, True)):
+    for K, L, seq, init in ((3, 9, [0, 0, 0, 1, 1, 2, 2, 2, 2], False), (4, 7, None, True),
+                            (4, 8, [5, 5, 6, 6, 6, 6, 6, 7], True), (3, 5, [1, 1, 1, 1, 1], True)):
         B, C = 1, 2
         x, w, b = dyadic(B, C, L), dyadic(C, K) / 2, dyadic(C)
         hist = dyadic(B, C, K - 1) if init else None
@@ -606,22 +644,32 @@ def pin_bwd_chunking(ora):
         B, C, L = 2, 3, 30
         x, w, b = dyadic(B, C, L), dyadic(C, K), dyadic(C)
         h, dout, dfs = dyadic(B, C, K - 1), dyadic(B, C, L), dyadic(B, C, K - 1)
-        full = _bwd(ora, x, w, b, init=h, dout=dout, dfs=dfs)
-        for L1 in sorted({1, K - 2, K - 1, K, 17} - {0}):
-            x1, x2 = x[:, :, :L1].contiguous(), x[:, :, L1:].contiguous()
-            f1 = torch.from_numpy(_cf_case(ora, x1, w, b, init=h).final_states().copy())
-            r2 = _bwd(ora, x2, w, b, init=f1, dout=dout[:, :, L1:].contiguous(), dfs=dfs)
-            d2 = torch.from_numpy(r2["dinit"]).float()
-            assert np.array_equal(d2.double().numpy(), r2["dinit"])       # exact in fp32
-            r1 = _bwd(ora, x1, w, b, init=h, dout=dout[:, :, :L1].contiguous(), dfs=d2)
-            assert np.array_equal(np.concatenate([r1["dx"], r2["dx"]], 2), full["dx"]), (K, L1)
-            assert np.array_equal(r1["dinit"], full["dinit"]), (K, L1)
-            assert np.array_equal(r1["dw"] + r2["dw"], full["dw"]), (K, L1)
-            assert np.array_equal(r1["db"] + r2["db"], full["db"]), (K, L1)
+        ids = np.repeat(np.arange(4), [5, 9, 1, 15])
+        for seq in (None, torch.tensor(np.stack([ids, ids[::-1] + 7]), dtype=torch.int32)):
+            full = _bwd(ora, x, w, b, seq=seq, init=h, dout=dout, dfs=dfs)
+            for L1 in sorted({1, K - 2, K - 1, K, 5, 14, 15, 17} - {0}):
+                x1, x2 = x[:, :, :L1].contiguous(), x[:, :, L1:].contiguous()
+                s1 = None if seq is None else seq[:, :L1].contiguous()
+                s2 = None if seq is None else seq[:, L1:].contiguous()
+                # chunk 2's history: chunk 1's final states, or zeros where a sequence starts at L1
+                cont = torch.ones(B, 1, 1, dtype=torch.bool) if seq is None else \
+                    (seq[:, L1] == seq[:, L1 - 1]).reshape(B, 1, 1)
+                f1 = torch.from_numpy(_cf_case(ora, x1, w, b, seq=s1, init=h).final_states().copy())
+                f1 = torch.where(cont, f1, torch.zeros_like(f1))
+                r2 = _bwd(ora, x2, w, b, seq=s2, init=f1, dout=dout[:, :, L1:].contiguous(), dfs=dfs)
+                d2 = torch.from_numpy(r2["dinit"]).float()
+                assert np.array_equal(d2.double().numpy(), r2["dinit"])       # exact in fp32
+                d2 = torch.where(cont, d2, torch.zeros_like(d2))
+                r1 = _bwd(ora, x1, w, b, seq=s1, init=h, dout=dout[:, :, :L1].contiguous(), dfs=d2)
+                where = (K, L1, seq is not None)
+                assert np.array_equal(np.concatenate([r1["dx"], r2["dx"]], 2), full["dx"]), where
+                assert np.array_equal(r1["dinit"], full["dinit"]), where
+                assert np.array_equal(r1["dw"] + r2["dw"], full["dw"]), where
+                assert np.array_equal(r1["db"] + r2["db"], full["db"]), where
 
 
 ALL_PINS = [pin_golden, pin_digits, pin_one_hot, pin_delta, pin_constant, pin_conv1d,
             pin_chunking, pin_packing, pin_mask_nan, pin_layout, pin_silu, pin_converters,
             pin_round_out, pin_f32_mode_exact_rational, pin_f32_mode_integers_are_exact,
             pin_f32_mode_error_bound, pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_packing,
-            pin_bwd_chunking]
+            pin_bwd_chunking, pin_packed_chunking]

@@ -22,11 +22,10 @@ MUTANTS = [
     ("silu_missing_z", "out = acc / (1.0 + exp(-acc));", "out = 1.0 / (1.0 + exp(-acc));"),
     ("bias_dropped", "acc = beta;", "acc = 0.0;"),
     ("history_reversed", "int64_t i = j + p->K - 1;\n  return", "int64_t i = -j - 1;\n  return"),
-    ("mask_never", "p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;   /*",
-     "p->seq[b * p->L + src] != p->seq[b * p->L + src]) continue;   /*"),
+    ("mask_never", "return id == p->seq[b * p->L + t];", "return id == id;"),
     ("mask_multiplies",
-     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) continue;   /*",
-     "if (p->seq[b * p->L + src] != p->seq[b * p->L + t]) { acc += 0.0 * ora_xt(p, b, c, src); continue; }   /*"),
+     "if (!ora_keep(p, b, t, k)) continue;      /* dropped */",
+     "if (!ora_keep(p, b, t, k)) { acc += 0.0 * ora_xt(p, b, c, src); continue; }"),
     ("final_off_by_one", "int64_t j = p->L - K + 1 + i;", "int64_t j = p->L - K + i;"),
     ("f16_exponent_bias", "ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
     ("bf16_ties_away", "(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
@@ -41,6 +40,10 @@ MUTANTS = [
     ("f32_bias_dropped", "if (p->bias != NULL) acc = (float)ora_decode(p->bias, p->w_dtype, c);", ""),
     ("f32_taps_reversed", "float wv = (float)ora_decode(p->w, p->w_dtype, c * K + k);",
      "float wv = (float)ora_decode(p->w, p->w_dtype, c * K + (K - 1 - k));"),
+    # seq_idx together with states
+    ("history_id_of_last_sequence", "*id = p->seq[b * p->L];", "*id = p->seq[b * p->L + p->L - 1];"),
+    ("history_never_counts_with_seq", "if (p->init == NULL || p->L == 0) return 0;", "return 0;"),
+    ("final_states_not_masked", "if (p->seq == NULL || p->L == 0) return 1;", "return 1;"),
     # the backward
     ("bwd_no_activation_slope", "dz[t] = go * slope;", "dz[t] = go;"),
     ("bwd_slope_sign", "slope = s * (1.0 + z * (1.0 - s));", "slope = s * (1.0 - z * (1.0 - s));"),
