@@ -339,8 +339,6 @@ def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
         raise ValueError(f"activation must be None, 'silu' or 'swish', not {activation!r}")
     if final_states_out is not None and not return_final_states:
         raise ValueError("final_states_out given but return_final_states is False")
-    if seq_idx is not None and (initial_states is not None or return_final_states):
-        raise ValueError("seq_idx cannot be combined with initial_states or final states")
     if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
         raise ValueError("expected x [B, C, L] and weight [C, K]")
     if not x.is_cuda:

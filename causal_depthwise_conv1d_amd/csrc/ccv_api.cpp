@@ -3,10 +3,11 @@
 // The checks follow the contract of Ch.4 "Dao interface and source map"
 // (section "Contract of the full-sequence interface", argument table; section
 // "Concrete limits of v1.5.0": K in {2,3,4}, three storage dtypes for x and
-// weight dispatched separately, bias in the weight dtype, states in x's dtype,
-// and no seq_idx together with initial or final states).  Two of that
-// version's limits are lifted because nothing in the arithmetic needs them:
-// states and seq_idx work with either layout, and channel-last needs no
+// weight dispatched separately, bias in the weight dtype, states in x's dtype).
+// That version's other limits are lifted, since the page calls them limits of
+// the version and not of the mathematics: states and seq_idx work with either
+// layout and with each other (the history is the row's first sequence's, the
+// final states the row's last sequence's), and channel-last needs no
 // multiple-of-8 alignment (an element-wise path serves unaligned views).
 //
 // Nothing here touches a device except ccv_fwd's single kernel launch.
@@ -76,7 +77,6 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
   if (a->K < 2 || a->K > 4) return CCV_E_KSIZE;
   if (a->x_dtype < 0 || a->x_dtype > 2 || a->w_dtype < 0 || a->w_dtype > 2) return CCV_E_DTYPE;
   if (a->activation != CCV_ACT_NONE && a->activation != CCV_ACT_SILU) return CCV_E_UNSUPPORTED;
-  if (a->seq_idx && (a->initial_states || a->final_states_out)) return CCV_E_UNSUPPORTED;
   for (int d = 0; d < 3; ++d) {
     if (a->x_stride[d] < 0 || a->out_stride[d] < 0) return CCV_E_LAYOUT;
     if (a->initial_states && a->init_stride[d] < 0) return CCV_E_LAYOUT;

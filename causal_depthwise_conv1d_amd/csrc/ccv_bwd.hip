@@ -52,6 +52,8 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
   load_params<K>(a.w, a.w_dtype, c * K, w);
   const float beta = a.bias ? load_param(a.bias, a.w_dtype, c) : 0.0f;
   const int32_t* sr = SEQ ? a.seq + b * L : nullptr;
+  const bool has_init = a.init != nullptr;       // with seq_idx: the history is the first sequence's
+  const int hist_id = (SEQ && has_init && L > 0) ? sr[0] : 0;
 
   // Slots 0 .. H-1 hold positions u-H .. u-1 before step u; slot H takes u.
   float xw[K], dzw[K];
@@ -60,7 +62,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
   for (int i = 0; i < H; ++i) {
     const int64_t j = t0 - H + i;
     xw[i] = src.x(j);
-    idw[i] = (SEQ && j >= 0) ? sr[j] : 0;
+    idw[i] = SEQ ? (j >= 0 ? sr[j] : hist_id) : 0;
     dzw[i] = 0.0f;                                 // dz left of the tile is never read
   }
   float pw[K], pb = 0.0f;
@@ -80,7 +82,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
       float z = beta;
 #pragma unroll
       for (int k = 0; k < H; ++k) {
-        keep[k] = !SEQ || (u - H + k >= 0 && idw[k] == idu);
+        keep[k] = !SEQ || ((u - H + k >= 0 || has_init) && idw[k] == idu);
         if (keep[k]) z = __builtin_fmaf(w[k], xw[k], z);
       }
       z = __builtin_fmaf(w[H], xu, z);
@@ -110,7 +112,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
         const bool keep = (FULL || (t >= 0 && t < L)) && (!SEQ || idw[0] == idw[H - k]);
         if (keep) acc = __builtin_fmaf(w[k], dzw[H - k], acc);
       }
-      if (!FULL && a.dfs && j >= L - H)
+      if (!FULL && a.dfs && j >= L - H && (!SEQ || L == 0 || idw[0] == sr[L - 1]))
         acc += S::to_f(static_cast<const raw*>(a.dfs)[b * a.fs_b + c * a.fs_c + (j - (L - H)) * a.fs_i]);
       if (j >= 0)
         src.put_dx(j, acc);

@@ -2,10 +2,9 @@
 // and the two launches (gradient kernel, then the fixed-order reduction of the
 // parameter gradients).  The operation and its contract are stated in ccv.h
 // beside ccv_bwd; the checks mirror ccv_fwd's (K in {2,3,4}, three storage
-// dtypes, bias in the weight dtype, states in x's dtype, no seq_idx together
-// with states: Ch.4 "Dao interface and source map", section "Concrete limits of
-// v1.5.0"), plus what the written gradients need: no aliasing with the inputs
-// and no self-overlapping layouts.
+// dtypes, bias in the weight dtype, states in x's dtype: Ch.4 "Dao interface
+// and source map", section "Concrete limits of v1.5.0"), plus what the written
+// gradients need: no aliasing with the inputs and no self-overlapping layouts.
 //
 // Nothing here touches a device except ccv_bwd's two kernel launches.
 #include <stdint.h>
@@ -55,7 +54,6 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   if (a->K < 2 || a->K > 4) return CCV_E_KSIZE;
   if (a->x_dtype < 0 || a->x_dtype > 2 || a->w_dtype < 0 || a->w_dtype > 2) return CCV_E_DTYPE;
   if (a->activation != CCV_ACT_NONE && a->activation != CCV_ACT_SILU) return CCV_E_UNSUPPORTED;
-  if (a->seq_idx && (a->initial_states || a->dfinal_states || a->dinitial_states)) return CCV_E_UNSUPPORTED;
   if (a->dinitial_states && !a->initial_states) return CCV_E_UNSUPPORTED;
   for (int d = 0; d < 3; ++d) {
     if (a->x_stride[d] < 0 || a->dout_stride[d] < 0 || a->dx_stride[d] < 0) return CCV_E_LAYOUT;

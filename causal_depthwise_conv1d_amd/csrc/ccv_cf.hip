@@ -90,8 +90,9 @@ __device__ inline void issue_segment(const CfArgs& a, const SegPos& p, bool vali
     const uintptr_t from_init = pick(m.init != nullptr, irow + (src + H) * m.is_i * ES, zero);
     const uintptr_t from_x = xrow + src * ES;
     q.hist[j] = gload<raw>(pick(valid, pick(src >= 0, from_x, from_init), zero));
-    if constexpr (SEQ)
-      q.hist_id[j] = gload<int32_t>(pick(valid && src >= 0, srow + src * 4, zero));
+    if constexpr (SEQ)                             // the history carries seq_idx[b, 0]
+      q.hist_id[j] = gload<int32_t>(pick(valid && src >= 0, srow + src * 4,
+                                         pick(valid && m.init != nullptr, srow, zero)));
     else
       q.hist_id[j] = 0;
   }
@@ -137,10 +138,11 @@ __device__ inline void stencil_vector(const float (&e)[S::V], const int (&id)[S:
 }
 
 template <int K, bool SEQ>
-__device__ inline void first_flags(int64_t t0, int lane, bool (&first_ok)[K - 1]) {
-  // With seq_idx a source left of t = 0 has no id and never counts.
+__device__ inline void first_flags(int64_t t0, int lane, bool has_init, bool (&first_ok)[K - 1]) {
+  // With seq_idx, a source left of t = 0 is the history of the row's first
+  // sequence (its id is seq_idx[b, 0]); without a history it never counts.
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) first_ok[j] = !(SEQ && lane == 0 && t0 - (K - 1) + j < 0);
+  for (int j = 0; j < K - 1; ++j) first_ok[j] = !(SEQ && !has_init && lane == 0 && t0 - (K - 1) + j < 0);
 }
 
 // Arithmetic and stores of a whole segment from its prefetched loads.
@@ -163,7 +165,7 @@ __device__ inline void compute_whole(const CfArgs& a, const SegPos& p, int lane,
     carry_id[j] = q.hist_id[j];
   }
   bool first_ok[H];
-  first_flags<K, SEQ>(p.t0, lane, first_ok);
+  first_flags<K, SEQ>(p.t0, lane, m.init != nullptr, first_ok);
   raw* __restrict__ ol = static_cast<raw*>(m.out) + p.b * a.o_sb + p.c * a.o_sc + p.t0 + lane * V;
 #pragma unroll
   for (int u = 0; u < kCfUnroll; ++u) {
@@ -205,10 +207,10 @@ __device__ inline void compute_partial(const CfArgs& a, const SegPos& p, int lan
     else if (m.init)
       carry[j] = S::to_f(static_cast<const raw*>(m.init)[p.b * m.is_b + p.c * m.is_c + (src + H) * m.is_i]);
     else carry[j] = 0.0f;
-    carry_id[j] = (SEQ && src >= 0) ? sr[src] : 0;
+    carry_id[j] = SEQ ? (src >= 0 ? sr[src] : (m.init ? sr[0] : 0)) : 0;
   }
   bool first_ok[H];
-  first_flags<K, SEQ>(p.t0, lane, first_ok);
+  first_flags<K, SEQ>(p.t0, lane, m.init != nullptr, first_ok);
 #pragma unroll
   for (int u = 0; u < kCfUnroll; ++u) {
     const int64_t te = p.t0 + (int64_t)(u * 64 + lane) * V;
@@ -228,7 +230,8 @@ __device__ inline void compute_partial(const CfArgs& a, const SegPos& p, int lan
 }
 
 // final_states of one row: the last K-1 extended inputs, bit for bit (Ch.5,
-// section "Three kinds of boundary handled separately").
+// section "Three kinds of boundary handled separately"); with seq_idx, those of
+// the row's last sequence only (others are zero).
 template <class S, int K>
 __device__ inline void final_states_row(const CfArgs& a, const SegPos& p, int lane) {
   constexpr int H = K - 1;
@@ -240,6 +243,7 @@ __device__ inline void final_states_row(const CfArgs& a, const SegPos& p, int la
   if (j >= 0) v = static_cast<const raw*>(m.x)[p.b * a.x_sb + p.c * a.x_sc + j];
   else if (m.init) v = static_cast<const raw*>(m.init)[p.b * m.is_b + p.c * m.is_c + (j + H) * m.is_i];
   else v = 0;
+  if (!final_kept(m.seq ? m.seq + p.b * m.L : nullptr, m.L, j, m.init != nullptr)) v = 0;
   static_cast<raw*>(m.fin)[p.b * m.fs_b + p.c * m.fs_c + lane * m.fs_i] = v;
 }
 

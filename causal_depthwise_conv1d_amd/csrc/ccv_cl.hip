@@ -96,8 +96,9 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
     const uintptr_t from_init = pick(m.init != nullptr, il + j * m.is_i * ES, zero);
     hv[j] = gload<u32x4>(pick(t0 >= H, from_x, from_init) + lx);
   }
+  // Ids of the U rows above the tile; at t = 0 the history's id is seq_idx[b, 0].
   u32x4 hid_v = {0u, 0u, 0u, 0u};
-  if constexpr (SEQ) hid_v = gload<u32x4>(pick(t0 >= U, sr + (t0 - U) * 4, zero));
+  if constexpr (SEQ) hid_v = gload<u32x4>(pick(t0 >= U, sr + (t0 - U) * 4, pick(m.init != nullptr, sr, zero)));
 
   // Row batches: A holds the current batch, B the next one.
   u32x4 ra[U], rb[U], ia = {0u, 0u, 0u, 0u}, ib = {0u, 0u, 0u, 0u};
@@ -127,13 +128,14 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
   float win[K][V];
 #pragma unroll
   for (int j = 0; j < H; ++j) S::unpack(hv[j], win[j + 1]);
-  // Ids of the window rows; rows left of t = 0 have none and never count.
+  // Ids of the window rows.  Rows left of t = 0 are the history of the row's first
+  // sequence (id seq_idx[b, 0]); without a history they never count.
   int wid[K];
   bool wok[K];
 #pragma unroll
   for (int j = 0; j < H; ++j) {
-    wid[j + 1] = SEQ ? __builtin_amdgcn_readfirstlane((int)dword(hid_v, U - H + j)) : 0;
-    wok[j + 1] = t0 - H + j >= 0;
+    wid[j + 1] = SEQ ? __builtin_amdgcn_readfirstlane((int)dword(hid_v, t0 >= U ? U - H + j : 0)) : 0;
+    wok[j + 1] = t0 - H + j >= 0 || m.init != nullptr;
   }
 
   auto compute = [&](int64_t t, const u32x4 (&r)[U], const u32x4& iv) {
@@ -246,8 +248,8 @@ __device__ inline void tile_general(const ClArgs& a, const TilePos& p, int lane)
       for (int i = 0; i < V; ++i)
         hist[j][i] = (ib && i < nch) ? S::to_f(ib[p.b * m.is_b + (c0 + i) * m.is_c + (src + H) * m.is_i]) : 0.0f;
     }
-    hok[j] = src >= 0;                               // rows left of t = 0 have no id
-    hid[j] = (SEQ && src >= 0) ? sr[src] : 0;
+    hok[j] = src >= 0 || ib != nullptr;              // the history: the first sequence's
+    hid[j] = SEQ ? (src >= 0 ? sr[src] : (ib ? sr[0] : 0)) : 0;
   }
 
   for (int64_t t = t0; t < t1; t += U) {
@@ -305,7 +307,7 @@ __device__ inline void tile_general(const ClArgs& a, const TilePos& p, int lane)
 
 // final_states of one (batch, channel group): the last K-1 extended inputs of the
 // lane's channels, bit for bit (Ch.5, section "Three kinds of boundary handled
-// separately").
+// separately"); with seq_idx, those of the row's last sequence only.
 template <class S, int K>
 __device__ inline void final_states_group(const ClArgs& a, int64_t b, int64_t cg, int lane) {
   constexpr int V = S::V;
@@ -326,6 +328,7 @@ __device__ inline void final_states_group(const ClArgs& a, int64_t b, int64_t cg
       if (src >= 0) v = xb[src * a.x_sl + i];
       else if (ib) v = ib[b * m.is_b + (c0 + i) * m.is_c + (src + H) * m.is_i];
       else v = 0;
+      if (!final_kept(m.seq ? m.seq + b * L : nullptr, L, src, ib != nullptr)) v = 0;
       fb[(c0 + i) * m.fs_c + j * m.fs_i] = v;
     }
   }

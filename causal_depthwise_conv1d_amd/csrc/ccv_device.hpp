@@ -165,6 +165,16 @@ __device__ inline uint32_t xcd_order(uint32_t g, uint32_t q, uint32_t r) {
   return x * q + (x < r ? x : r) + s;
 }
 
+// With seq_idx, final_states are the history of the row's last sequence: the
+// entry from extended position j survives when its sequence id (seq_idx[b, j], or
+// seq_idx[b, 0] for the history left of t = 0) is the id at t = L-1.  seq_row is
+// the row of seq_idx, or nullptr.
+__device__ inline bool final_kept(const int32_t* seq_row, int64_t L, int64_t j, bool has_init) {
+  if (!seq_row || L == 0) return true;
+  if (j < 0 && !has_init) return false;            // the zero history
+  return seq_row[j >= 0 ? j : 0] == seq_row[L - 1];
+}
+
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 __device__ inline void store16(void* p, u32x4 v) { *static_cast<u32x4*>(p) = v; }
 

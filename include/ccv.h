@@ -24,6 +24,14 @@
  *   - final_states_out[b,c,i] = X~[b,c,L-K+1+i], i = 0..K-2: the last K-1 conv
  *     inputs (not activations), copied bit for bit; correct for L < K-1 and L = 0
  *     (Ch.5, section "Three kinds of boundary handled separately").
+ *   - seq_idx together with states (a limit of the pages' library version, not
+ *     of the mathematics: Ch.4, section "Concrete limits of v1.5.0", lifted here):
+ *     initial_states is the history of the row's first sequence, so a term
+ *     reaching left of t = 0 counts when seq_idx[b,t] == seq_idx[b,0]; and
+ *     final_states is the history of the row's last sequence, so an entry from
+ *     another sequence is 0.  A packed row split anywhere then runs as two calls:
+ *     pass the first call's final_states as the second's initial_states where
+ *     the sequence continues across the split, zeros where one starts there.
  *
  * Layout: every tensor argument is a pointer plus element strides; the element
  * at (b,c,t) is at base + b*s_B + c*s_C + t*s_L elements (Ch.4, section "Why one
@@ -71,8 +79,8 @@ typedef enum {
   CCV_E_DTYPE = -4,       /* x_dtype or w_dtype not a ccv_dtype_t */
   CCV_E_LAYOUT = -5,      /* x (or out) has unit stride in neither time nor channels,
                              out's unit-stride dim differs from x's, or a stride < 0 */
-  CCV_E_UNSUPPORTED = -6, /* seq_idx together with initial_states or final_states_out,
-                             or an activation value outside ccv_act_t */
+  CCV_E_UNSUPPORTED = -6, /* an activation value outside ccv_act_t; in the backward,
+                             dinitial_states without initial_states */
   CCV_E_ALIAS = -7,       /* out == x, or final_states_out == initial_states */
   CCV_E_HIP = -8,         /* the HIP runtime refused the launch */
   CCV_E_INTERNAL = -9,    /* an unexpected internal condition */
@@ -213,9 +221,9 @@ int ccv_update_plan(const ccv_update_args_t* args, ccv_plan_t* plan);
  *
  * Every sum is fp32; dx and dinitial_states are rounded once to x's dtype,
  * dweight and dbias once to the weight dtype.  The parameter sums run in a fixed
- * order (per time tile, then over tiles), so results repeat bit for bit.
- * seq_idx together with initial_states, dfinal_states or dinitial_states is
- * CCV_E_UNSUPPORTED, as in the forward.  Any element strides are accepted for x,
+ * order (per time tile, then over tiles), so results repeat bit for bit.  With
+ * seq_idx, keep() and the history's sequence are the forward's, and
+ * dfinal_states reaches only the entries that final_states kept.  Any element strides are accepted for x,
  * dout, dx and the states; weight, bias, dweight, dbias are contiguous.  dx must
  * not be x or dout; dinitial_states must not be initial_states (CCV_E_ALIAS).
  *

@@ -104,9 +104,10 @@ def test_null_pointers():
     assert ccv.lib().ccv_fwd_check(None) == -1
 
 
-def test_forbidden_combinations():
-    assert check(args(seq_idx=SEQ, initial_states=INIT, init_stride=(192, 1, 64))) == "CCV_E_UNSUPPORTED"
-    assert check(args(seq_idx=SEQ, final_states_out=FIN, final_stride=(192, 1, 64))) == "CCV_E_UNSUPPORTED"
+def test_seq_idx_with_states_is_accepted():
+    # lifted version limit: the history is the first sequence's, final states the last's
+    assert check(args(seq_idx=SEQ, initial_states=INIT, init_stride=(192, 1, 64))) == "CCV_OK"
+    assert check(args(seq_idx=SEQ, final_states_out=FIN, final_stride=(192, 1, 64))) == "CCV_OK"
 
 
 def test_aliasing():
@@ -380,8 +381,8 @@ def test_bwd_argument_errors():
     assert bcheck(bargs(K=1)) == "CCV_E_KSIZE"
     assert bcheck(bargs(w_dtype=9)) == "CCV_E_DTYPE"
     assert bcheck(bargs(activation=5)) == "CCV_E_UNSUPPORTED"
-    assert bcheck(bargs(seq_idx=SEQ, initial_states=INIT, init_stride=(192, 3, 1))) == "CCV_E_UNSUPPORTED"
-    assert bcheck(bargs(seq_idx=SEQ, dfinal_states=DFS, dfinal_stride=(192, 3, 1))) == "CCV_E_UNSUPPORTED"
+    assert bcheck(bargs(seq_idx=SEQ, initial_states=INIT, init_stride=(192, 3, 1))) == "CCV_OK"
+    assert bcheck(bargs(seq_idx=SEQ, dfinal_states=DFS, dfinal_stride=(192, 3, 1))) == "CCV_OK"
     assert bcheck(bargs(dinitial_states=DINIT, dinit_stride=(192, 3, 1))) == "CCV_E_UNSUPPORTED"
     for name in ("x", "dout", "dx", "weight", "dweight"):
         assert bcheck(bargs(**{name: None})) == "CCV_E_NULL", name

@@ -102,7 +102,7 @@ def build(B, C, L, K, dtype, layout, seed, w_dtype=None, seq=None, init=False, b
         kw = dict(layout="cl", c_pad=8)
     else:
         kw = dict(layout=layout)
-    lengths = wl.packed_lengths(L, seq, 1, seed).tolist() if seq else None
+    lengths = wl.packed_lengths(L, min(seq, L), 1, seed).tolist() if (seq and L > 0) else None
     return wl.make_case(B=B, C=C, L=L, K=K, x_dtype=dtype, w_dtype=w_dtype, bias=bias, init=init,
                         seq_lengths=lengths, activation=act, seed=seed, **kw)
 
@@ -119,6 +119,9 @@ def test_bwd_matches_oracle(dtype, K, layout):
         (65, 130, 3, dict(bias=True, act="silu", seq=5)),
         (300, 33, 2, dict(bias=True, act=None, init=True, dinit=True)),
         (1000, 9, 1, dict(bias=True, act="silu", seq=17, w_dtype="f32")),
+        # seq_idx together with history, dfinal_states and d(initial_states)
+        (520, 64, 2, dict(bias=True, act="silu", seq=6, init=True, dfs=True, dinit=True)),
+        (K - 1, 8, 2, dict(seq=2, init=True, dfs=True, dinit=True)),
     ]
     for i, (L, C, B, f) in enumerate(cases):
         seed = 3000 + 100 * K + i
@@ -165,10 +168,10 @@ def test_bwd_random_shapes():
         layout = ["cf", "cl", "cf_view", "cl_view"][g.integers(0, 4)]
         B, C, L = int(g.integers(1, 4)), int(g.integers(1, 200)), int(g.integers(0, 700))
         seq = int(g.integers(1, 9)) if (g.random() < 0.3 and L > 0) else None
-        init = seq is None and g.random() < 0.5
+        init = g.random() < 0.5
         w = build(B, C, L, K, dtype, layout, 4000 + i, w_dtype=w_dtype, seq=seq, init=init,
                   bias=bool(g.random() < 0.6), act=["silu", None][g.integers(0, 2)])
-        dout, dfs = grad_inputs(w, layout, seq is None and g.random() < 0.5, 4000 + i)
+        dout, dfs = grad_inputs(w, layout, g.random() < 0.5, 4000 + i)
         log(f"  random bwd {i}: {dtype}/{w_dtype} K={K} {layout} B={B} C={C} L={L} seq={seq} init={init}")
         check_bwd(w, dout, dfs, init, f"[random {i}]")
 

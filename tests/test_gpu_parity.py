@@ -62,6 +62,9 @@ def matrix_cases(K):
         (513, 64, 1, dict(init=True, final=True, activation="silu")),
         (2049, 7, 2, dict(bias=True, activation="silu")),
         (4099, 72, 1, dict(bias=True, seq=40, activation=None)),
+        # seq_idx together with history and final states
+        (777, 72, 2, dict(bias=True, seq=6, init=True, final=True, activation="silu")),
+        (K - 1, 16, 2, dict(seq=2, init=True, final=True)),
     ]
 
 
@@ -156,9 +159,8 @@ def test_random_shapes():
         feats = dict(bias=bool(g.random() < 0.5), activation=["silu", "swish", None][g.integers(0, 3)])
         if use_seq:
             feats["seq"] = int(g.integers(1, 20))
-        else:
-            feats["init"] = bool(g.random() < 0.5)
-            feats["final"] = bool(g.random() < 0.5)
+        feats["init"] = bool(g.random() < 0.5)
+        feats["final"] = bool(g.random() < 0.5)
         w = build(L, C, B, K, dtype, layout, feats, seed=5000 + i, w_dtype=w_dtype)
         log(f"  random {i}: {dtype}/{w_dtype} K={K} {layout} B={B} C={C} L={L} {feats}")
         check_full(w, where=f"[random {i}]")
@@ -430,6 +432,35 @@ def test_noncontiguous_input_is_copied_and_reported():
     assert bits_equal(out.cpu(), ref.cpu())
 
 
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+def test_packed_rows_split_anywhere(layout):
+    """seq_idx with states: a packed row run in two calls, the second taking the
+    first's final states as history where its first sequence continues and zeros
+    where one starts, gives the one-call result bit for bit (outputs and final
+    states), for splits inside sequences and on their boundaries."""
+    K, C, B = 4, 72, 2
+    lengths = [130, 1, 70, 2, 97, 300, 24]
+    L = sum(lengths)
+    w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype="bf16", layout=layout, bias=True, init=True, final=True,
+                     activation="silu", seq_lengths=lengths, seed=6100)
+    kw = gpu_args(w)
+    full, fs_full = ccv.causal_conv1d_fwd(**kw)
+    seq = kw["seq_idx"]
+    starts = np.cumsum(lengths)[:-1]
+    for L1 in sorted({1, 64, 129, 130, 131, 200, 201, 202, int(starts[3]) + 1, 600, L - 1}):
+        x1, x2 = kw["x"][:, :, :L1], kw["x"][:, :, L1:]
+        o1, f1 = ccv.causal_conv1d_fwd(x1, kw["weight"], kw["bias"], seq[:, :L1].contiguous(),
+                                       kw["initial_states"], True, activation="silu")
+        cont = (seq[:, L1] == seq[:, L1 - 1]).reshape(B, 1, 1)
+        h2 = torch.where(cont, f1, torch.zeros_like(f1))
+        o2, f2 = ccv.causal_conv1d_fwd(x2, kw["weight"], kw["bias"], seq[:, L1:].contiguous(), h2, True,
+                                       activation="silu")
+        torch.cuda.synchronize()
+        assert bits_equal(torch.cat([o1, o2], 2).cpu(), full.cpu()), L1
+        assert bits_equal(f2.cpu(), fs_full.cpu()), L1
+    check_full(w, where=f"[packed with states {layout}]")
+
+
 def test_argument_errors_raise():
     x = torch.zeros(1, 4, 8, device="cuda")
     with pytest.raises(ValueError):
@@ -438,5 +469,4 @@ def test_argument_errors_raise():
         ccv.causal_conv1d_fwd(x, torch.zeros(4, 4, device="cuda"), activation="relu")
     with pytest.raises(ValueError):
         ccv.causal_conv1d_fwd(x, torch.zeros(4, 4, device="cuda"),
-                              seq_idx=torch.zeros(1, 8, dtype=torch.int32, device="cuda"),
-                              return_final_states=True)
+                              final_states_out=torch.zeros(1, 4, 3, device="cuda"))
