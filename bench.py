@@ -572,11 +572,12 @@ def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias):
 
     c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
     r = bwd(c, dout_cpu, None)
-    T = 32 if w.x_dtype == "f32" else 64              # time steps per backward tile
-    parts, levels = w.B * max(1, math.ceil(w.L / T)), 1
+    T = 32                                             # time steps per backward tile
+    tpi = 4 if (w.x.stride(1) == 1 or w.C <= 1) and not (w.x.stride(2) == 1 and w.L > 1) else 1
+    parts, levels = w.B * max(1, math.ceil(math.ceil(w.L / T) / tpi)), 1  # a row per tpi tiles
     while parts > 32:                                  # levels of the fan-in-32 reduction tree
         parts, levels = -(-parts // 32), levels + 1
-    pk = math.ceil((T + 32 * levels + w.K + 8) / 4)
+    pk = math.ceil((tpi * T + 32 * levels + w.K + 8) / 4)
     out = {}
     for name, got, ref, scale, kk in (("dx", dx_gpu, r["dx"], r["ex"], w.K + 2),
                                       ("dweight", dweight, r["dw"], r["ew"], pk),

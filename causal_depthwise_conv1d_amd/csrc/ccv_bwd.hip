@@ -43,7 +43,8 @@ __device__ inline float silu_slope(float z) {
 // d(initial_states)) fixes the trip count and every condition at compile time,
 // so the walk unrolls completely; the arithmetic is the same.
 template <class S, int K, bool SILU, bool SEQ, bool FULL, int TT, class Src>
-__device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t t0, Src& src) {
+__device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t t0, Src& src,
+                                 float (&pw)[K], float& pb) {
   using raw = typename S::raw;
   constexpr int H = K - 1;
   const int64_t L = a.L;
@@ -65,10 +66,6 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
     idw[i] = SEQ ? (j >= 0 ? sr[j] : hist_id) : 0;
     dzw[i] = 0.0f;                                 // dz left of the tile is never read
   }
-  float pw[K], pb = 0.0f;
-#pragma unroll
-  for (int k = 0; k < K; ++k) pw[k] = 0.0f;
-
   const int64_t n_steps = FULL ? TT + H : t_end + H - t0;
 #pragma unroll(FULL ? TT + H : 1)
   for (int64_t i = 0; i < n_steps; ++i) {
@@ -127,7 +124,13 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
     }
   }
 
-  float* part = a.part + ((b * a.ntt + t0 / a.T) * (K + 1)) * a.C + c;
+}
+
+// The lane's partial row: parameter gradients summed over its group of tiles.
+template <int K>
+__device__ inline void store_partials(const BwdArgs& a, int64_t b, int64_t g, int64_t c, const float (&pw)[K],
+                                      float pb) {
+  float* part = a.part + ((b * a.ngr + g) * (K + 1)) * a.C + c;
 #pragma unroll
   for (int k = 0; k < K; ++k) part[k * a.C] = pw[k];
   part[K * a.C] = pb;
@@ -155,29 +158,37 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
   using raw = typename S::raw;
   const int64_t id = (int64_t)blockIdx.x * kBwdBlock + threadIdx.x;
   if (id >= a.lanes) return;
-  const int64_t bt = id / a.C;
-  const int64_t c = id - bt * a.C;
-  const int64_t b = bt / a.ntt;
-  const int64_t t0 = (bt - b * a.ntt) * a.T;
+  const int64_t bg = id / a.C;
+  const int64_t c = id - bg * a.C;
+  const int64_t b = bg / a.ngr;
+  const int64_t g = bg - b * a.ngr;
   GlobalSrc<S, K> src{static_cast<const raw*>(a.x) + b * a.x_sb + c * a.x_sc,
                       static_cast<const raw*>(a.dout) + b * a.d_sb + c * a.d_sc,
                       static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc,
                       a.init ? static_cast<const raw*>(a.init) + b * a.is_b + c * a.is_c : nullptr,
                       a.x_sl, a.d_sl, a.g_sl, a.is_i};
-  walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src);
+  float pw[K], pb = 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) pw[k] = 0.0f;
+  const int64_t tt1 = (g + 1) * a.tpi < a.ntt ? (g + 1) * a.tpi : a.ntt;
+  for (int64_t tt = g * a.tpi; tt < tt1; ++tt)
+    walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, tt * a.T, src, pw, pb);
+  store_partials<K>(a, b, g, c, pw, pb);
 }
 
-// LDS path: a wave stages its tile (64 channels x the T steps of the tile, with
-// V steps of margin on either side for the halos) with 16-byte loads along the
-// unit-stride dimension, walks it from LDS, and stores dx back with 16-byte
-// stores.  dx[j] is parked in the LDS slot of x[j], which the walk no longer
+// LDS path: a wave takes a group of consecutive tiles of one (b, 64 channels);
+// for each it stages the tile (64 channels x the T steps, with V steps of margin
+// on either side for the halos) with 16-byte loads along the unit-stride
+// dimension, walks it from LDS, and stores dx back with 16-byte stores.  dx[j] is parked in the LDS slot of x[j], which the walk no longer
 // needs once dx[j] is final.  Channel-first tiles are stored channel-major with
 // an odd dword pitch (the walk's reads, one channel per lane, then fall in
 // distinct banks); channel-last tiles step-major, 64 channels to a step.
 template <class S>
 struct LdsGeom {
   static constexpr int V = S::V;
-  static constexpr int T = 8 * V;                       // the tile length for this dtype
+  // The tile length: 32 steps keeps a wave's LDS near 11 KB and its registers under
+  // 100, so about 13 waves fit on a CU; the K-1 step halo is recomputed per tile.
+  static constexpr int T = 32;
   static constexpr int ES = sizeof(typename S::raw);
   static constexpr int XN = T + 2 * V;                  // staged x positions: [t0 - V, t0 + T + V)
   static constexpr int GN = T + V;                      // staged dout positions: [t0, t0 + T + V)
@@ -223,85 +234,95 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   const int lane = threadIdx.x;
   const int64_t ncg = (a.C + 63) / 64;
   const int64_t item = blockIdx.x;
-  const int64_t bt = item / ncg;
-  const int64_t c0 = (item - bt * ncg) * 64;
-  const int64_t b = bt / a.ntt;
-  const int64_t t0 = (bt - b * a.ntt) * a.T;
+  const int64_t bg = item / ncg;
+  const int64_t c0 = (item - bg * ncg) * 64;
+  const int64_t b = bg / a.ngr;
+  const int64_t g = bg - b * a.ngr;
   const int64_t L = a.L, C = a.C;
   const raw* xb = static_cast<const raw*>(a.x) + b * a.x_sb;
   const raw* gb = static_cast<const raw*>(a.dout) + b * a.d_sb;
+  raw* db = static_cast<raw*>(a.dx) + b * a.g_sb;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-
-  // Stage x over [t0 - V, t0 + T + V) and dout over [t0, t0 + T + V); zeros outside
-  // [0, L) and past C (L and C are multiples of V on this path).
-  if constexpr (!CL) {
-    constexpr int NX = G::XN / V, NG = G::GN / V;
-    for (int q = lane; q < 64 * NX; q += 64) {
-      const int r = q / NX, k = q - r * NX;
-      const int64_t p = t0 - V + k * V;
-      u32x4 v = zero;
-      if (c0 + r < C && p >= 0 && p < L) v = load16(xb + (c0 + r) * a.x_sc + p);
-      lds_put16(lx + r * G::XP + k * V, v);
-    }
-    for (int q = lane; q < 64 * NG; q += 64) {
-      const int r = q / NG, k = q - r * NG;
-      const int64_t p = t0 + k * V;
-      u32x4 v = zero;
-      if (c0 + r < C && p < L) v = load16(gb + (c0 + r) * a.d_sc + p);
-      lds_put16(lg + r * G::GP + k * V, v);
-    }
-  } else {
-    constexpr int NS = 64 / V;                     // vectors per step
-    for (int q = lane; q < G::XN * NS; q += 64) {
-      const int st = q / NS, k = q - st * NS;
-      const int64_t p = t0 - V + st;
-      u32x4 v = zero;
-      if (c0 + k * V < C && p >= 0 && p < L) v = load16(xb + p * a.x_sl + c0 + k * V);
-      lds_put16(lx + st * 64 + k * V, v);
-    }
-    for (int q = lane; q < G::GN * NS; q += 64) {
-      const int st = q / NS, k = q - st * NS;
-      const int64_t p = t0 + st;
-      u32x4 v = zero;
-      if (c0 + k * V < C && p < L) v = load16(gb + p * a.d_sl + c0 + k * V);
-      lds_put16(lg + st * 64 + k * V, v);
-    }
-  }
   const int64_t c = c0 + lane;
   constexpr int cs = CL ? 1 : G::XP, gcs = CL ? 1 : G::GP, ps = CL ? 64 : 1;
-  if (t0 == 0 && a.init && c < C) {                // the history left of t = 0
+
+  float pw[K], pb = 0.0f;
 #pragma unroll
-    for (int i = 0; i < H; ++i)
-      lx[lane * cs + (V - H + i) * ps] =
-          static_cast<const raw*>(a.init)[b * a.is_b + c * a.is_c + i * a.is_i];
-  }
-  __syncthreads();
+  for (int k = 0; k < K; ++k) pw[k] = 0.0f;
+  const int64_t tt1 = (g + 1) * a.tpi < a.ntt ? (g + 1) * a.tpi : a.ntt;
+  for (int64_t tt = g * a.tpi; tt < tt1; ++tt) {
+    const int64_t t0 = tt * a.T;
+    __syncthreads();                               // the previous tile's dx has left LDS
 
-  if (c < C) {
-    LdsSrc<S, ps> src{lx + lane * cs, lg + lane * gcs, t0};
-    if (t0 + G::T + H <= L && (t0 > 0 || !a.dinit))     // an interior tile
-      walk_tile<S, K, SILU, SEQ, true, G::T>(a, b, c, t0, src);
-    else
-      walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src);
-  }
-  __syncthreads();
+    // Stage x over [t0 - V, t0 + T + V) and dout over [t0, t0 + T + V); zeros outside
+    // [0, L) and past C (L and C are multiples of V on this path).
+    if constexpr (!CL) {
+      constexpr int NX = G::XN / V, NG = G::GN / V;
+      for (int q = lane; q < 64 * NX; q += 64) {
+        const int r = q / NX, k = q - r * NX;
+        const int64_t p = t0 - V + k * V;
+        u32x4 v = zero;
+        if (c0 + r < C && p >= 0 && p < L) v = load16(xb + (c0 + r) * a.x_sc + p);
+        lds_put16(lx + r * G::XP + k * V, v);
+      }
+      for (int q = lane; q < 64 * NG; q += 64) {
+        const int r = q / NG, k = q - r * NG;
+        const int64_t p = t0 + k * V;
+        u32x4 v = zero;
+        if (c0 + r < C && p < L) v = load16(gb + (c0 + r) * a.d_sc + p);
+        lds_put16(lg + r * G::GP + k * V, v);
+      }
+    } else {
+      constexpr int NS = 64 / V;                   // vectors per step
+      for (int q = lane; q < G::XN * NS; q += 64) {
+        const int st = q / NS, k = q - st * NS;
+        const int64_t p = t0 - V + st;
+        u32x4 v = zero;
+        if (c0 + k * V < C && p >= 0 && p < L) v = load16(xb + p * a.x_sl + c0 + k * V);
+        lds_put16(lx + st * 64 + k * V, v);
+      }
+      for (int q = lane; q < G::GN * NS; q += 64) {
+        const int st = q / NS, k = q - st * NS;
+        const int64_t p = t0 + st;
+        u32x4 v = zero;
+        if (c0 + k * V < C && p < L) v = load16(gb + p * a.d_sl + c0 + k * V);
+        lds_put16(lg + st * 64 + k * V, v);
+      }
+    }
+    if (t0 == 0 && a.init && c < C) {              // the history left of t = 0
+#pragma unroll
+      for (int i = 0; i < H; ++i)
+        lx[lane * cs + (V - H + i) * ps] =
+            static_cast<const raw*>(a.init)[b * a.is_b + c * a.is_c + i * a.is_i];
+    }
+    __syncthreads();
 
-  // dx over [t0, t_end) back to memory, 16 bytes at a time.
-  const int64_t t_end = t0 + a.T < L ? t0 + a.T : L;
-  const int nvt = (int)((t_end - t0) / V);
-  raw* db = static_cast<raw*>(a.dx) + b * a.g_sb;
-  if constexpr (!CL) {
-    for (int q = lane; q < 64 * nvt; q += 64) {
-      const int r = q / nvt, k = q - r * nvt;
-      if (c0 + r < C) store16(db + (c0 + r) * a.g_sc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
+    if (c < C) {
+      LdsSrc<S, ps> src{lx + lane * cs, lg + lane * gcs, t0};
+      if (t0 + G::T + H <= L && (t0 > 0 || !a.dinit))   // an interior tile
+        walk_tile<S, K, SILU, SEQ, true, G::T>(a, b, c, t0, src, pw, pb);
+      else
+        walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src, pw, pb);
     }
-  } else {
-    constexpr int NS = 64 / V;
-    for (int q = lane; q < (int)(t_end - t0) * NS; q += 64) {
-      const int st = q / NS, k = q - st * NS;
-      if (c0 + k * V < C) store16(db + (t0 + st) * a.g_sl + c0 + k * V, lds_get16(lx + (st + V) * 64 + k * V));
+    __syncthreads();
+
+    // dx over [t0, t_end) back to memory, 16 bytes at a time.
+    const int64_t t_end = t0 + a.T < L ? t0 + a.T : L;
+    const int nvt = (int)((t_end - t0) / V);
+    if constexpr (!CL) {
+      for (int q = lane; q < 64 * nvt; q += 64) {
+        const int r = q / nvt, k = q - r * nvt;
+        if (c0 + r < C) store16(db + (c0 + r) * a.g_sc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
+      }
+    } else {
+      constexpr int NS = 64 / V;
+      for (int q = lane; q < (int)(t_end - t0) * NS; q += 64) {
+        const int st = q / NS, k = q - st * NS;
+        if (c0 + k * V < C) store16(db + (t0 + st) * a.g_sl + c0 + k * V, lds_get16(lx + (st + V) * 64 + k * V));
+      }
     }
   }
+  if (c < C) store_partials<K>(a, b, g, c, pw, pb);
 }
 
 __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {

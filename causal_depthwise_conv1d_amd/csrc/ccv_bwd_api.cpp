@@ -92,12 +92,15 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   int64_t bl;
   if (a->seq_idx && __builtin_mul_overflow(B, L, &bl)) return CCV_E_SHAPE;
 
-  // One lane per (b, tile, c); a row with L = 0 still has one tile, which writes
-  // d(initial_states) from dfinal_states.
+  // One lane per (b, group of kBwdTilesPerItem tiles, c); a row with L = 0 still
+  // has one tile, which writes d(initial_states) from dfinal_states.
   const int64_t T = bwd_tile_steps(a->x_dtype);
   const int64_t ntt = L > 0 ? (L + T - 1) / T : 1;
+  const bool channel_unit = (a->x_stride[1] == 1 || C <= 1) && !(a->x_stride[2] == 1 && L > 1);
+  const int64_t tpi = channel_unit ? kBwdTilesPerItem : 1;
+  const int64_t ngr = (ntt + tpi - 1) / tpi;
   int64_t nparts, lanes, ws;
-  if (__builtin_mul_overflow(B, ntt, &nparts) || __builtin_mul_overflow(nparts, C, &lanes) ||
+  if (__builtin_mul_overflow(B, ngr, &nparts) || __builtin_mul_overflow(nparts, C, &lanes) ||
       __builtin_mul_overflow(nparts + bwd_reduce_rows(nparts), (int64_t)(K + 1) * C * 4, &ws))
     return CCV_E_SHAPE;
   const int path = rows ? choose_path(a) : kBwdPathElement;
@@ -146,6 +149,8 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   g.di_i = a->dinit_stride[2];
   g.T = T;
   g.ntt = ntt;
+  g.tpi = tpi;
+  g.ngr = ngr;
   g.lanes = lanes;
   g.w_dtype = a->w_dtype;
 
@@ -190,7 +195,7 @@ int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan) {
   plan->path = p.grid || p.rgrid ? CCV_PATH_BACKWARD : CCV_PATH_NONE;
   plan->vector = lds ? p.path : 0;
   plan->elems_per_lane = 1;
-  plan->unroll = 1;
+  plan->unroll = (int32_t)p.a.tpi;
   plan->grid = p.grid;
   plan->block = lds ? 64 : kBwdBlock;
   plan->waves_per_group = lds ? 1 : kBwdBlock / 64;

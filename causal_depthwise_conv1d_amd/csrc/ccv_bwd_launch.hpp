@@ -6,9 +6,11 @@
 
 namespace ccv {
 
-// Gradient kernel: one lane per (b, c) row and time tile [tt * T, tt * T + T).
-// Lanes are numbered ((b * ntt + tt) * C + c), so a wave's lanes take consecutive
-// channels.  Strides are in elements.
+// Gradient kernel: one lane per (b, c) row and group of tpi consecutive time
+// tiles [tt * T, tt * T + T); the lane sums the parameter gradients of its whole
+// group and writes one partial row.  Lanes are numbered
+// ((b * ngr + g) * C + c), so a wave's lanes take consecutive channels.  Strides
+// are in elements.
 struct BwdArgs {
   const void* x;
   const void* w;            // [C, K] contiguous, w_dtype
@@ -19,7 +21,7 @@ struct BwdArgs {
   const void* dfs;          // [B, C, K-1] or nullptr
   void* dx;
   void* dinit;              // [B, C, K-1] or nullptr
-  float* part;              // [B * ntt][K + 1][C] fp32 partial sums (dw taps, then db)
+  float* part;              // [B * ngr][K + 1][C] fp32 partial sums (dw taps, then db)
   int64_t B, C, L;
   int64_t x_sb, x_sc, x_sl;
   int64_t d_sb, d_sc, d_sl;     // dout
@@ -27,7 +29,7 @@ struct BwdArgs {
   int64_t is_b, is_c, is_i;     // initial_states
   int64_t fs_b, fs_c, fs_i;     // dfinal_states
   int64_t di_b, di_c, di_i;     // dinitial_states
-  int64_t T, ntt, lanes;        // tile length, tiles per row, B * ntt * C
+  int64_t T, ntt, tpi, ngr, lanes;  // tile length, tiles per row, tiles per group, groups per row, B*ngr*C
   int32_t w_dtype;
 };
 
@@ -46,6 +48,11 @@ struct BwdReduceArgs {
 };
 
 constexpr int kBwdBlock = 256;      // element path: lanes per workgroup
+// Consecutive tiles summed into one partial row when x is unit-stride in channels
+// (a step of 64 channels is whole cache lines).  With unit stride in time a tile's
+// row segment is half a cache line, and the neighbouring tile is better run at
+// the same time by another wave than after this one: then one tile per row.
+constexpr int kBwdTilesPerItem = 4;
 constexpr int kBwdFanIn = 32;       // partial sums added per lane and level of the reduction
 
 // Gradient kernel variants: the element path (one lane per (b, tile, c), any
@@ -56,8 +63,8 @@ constexpr int kBwdFanIn = 32;       // partial sums added per lane and level of 
 // multiple of 16 / element size.
 enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2 };
 
-// Time steps per tile T for a dtype (both paths use the same T, so their partial
-// sums, and so dweight and dbias, are identical).
+// Time steps per tile T for a dtype (32 for all three; both paths use the same T,
+// so their partial sums, and so dweight and dbias, are identical).
 int bwd_tile_steps(int dtype);
 
 int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, int path, uint32_t grid,

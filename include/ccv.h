@@ -275,8 +275,10 @@ int ccv_bwd_check(const ccv_bwd_args_t* args);
  * any strides), 1 for the LDS-staged channel-first path, 2 for the LDS-staged
  * channel-last path (x, dout and dx unit-stride in time, resp. channels, 16-byte
  * aligned, L resp. C a multiple of 16 / element size); span = time steps per
- * tile; channels_per_item = channels per work item; work_items, grid, block of
- * the gradient kernel.  The workspace fields are not checked here, so a plan can
+ * tile; unroll = consecutive tiles per work item (summed into one partial row:
+ * 4 when x is unit-stride in channels, else 1);
+ * channels_per_item = channels per work item; work_items, grid, block of the
+ * gradient kernel.  The workspace fields are not checked here, so a plan can
  * be had before the workspace is allocated. */
 int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan);
 

@@ -351,9 +351,14 @@ def bcheck(a):
 def test_bwd_workspace_size_is_the_partial_sums():
     # one fp32 row of (K + 1) * C partial sums per (b, tile), plus one row per group
     # of 32 on every level of the reduction tree but the last
+    # channel-first: a row per tile of 32 steps
     a = bargs(B=3, C=100, L=1000, K=3, ws=False)
-    parts = 3 * -(-1000 // 64)                       # 48 rows -> 2 groups -> 1
-    assert ccv.ccv_bwd_workspace_size(a) == (parts + 2) * 100 * (3 + 1) * 4
+    parts = 3 * -(-1000 // 32)                       # 96 rows -> 3 groups -> 1
+    assert ccv.ccv_bwd_workspace_size(a) == (parts + 3) * 100 * (3 + 1) * 4
+    # channel-last: a row per group of 4 tiles
+    a = bargs(B=3, C=100, L=1000, K=3, layout="cl", ws=False)
+    parts = 3 * -(-(-(-1000 // 32)) // 4)            # 24 rows: one level
+    assert ccv.ccv_bwd_workspace_size(a) == parts * 100 * (3 + 1) * 4
     assert ccv.ccv_bwd_workspace_size(bargs(B=2, C=5, L=0, ws=False)) == 2 * 1 * 5 * 5 * 4
     a = bargs(B=2, C=128, L=1 << 20, K=3, ws=False)
     a.x_dtype = ccv.CCV_F32
@@ -416,13 +421,15 @@ def test_bwd_empty_extents():
 
 def test_bwd_plan():
     # aligned channel-first: the LDS-staged channel-first kernel, a 64-lane workgroup
-    # per (b, tile of 64 steps, group of 64 channels)
+    # per (b, tile of 32 steps, group of 64 channels)
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096))
     assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD and p.vector == 1
-    assert p.span == 64 and p.work_items == 4 * 64 * 32 and p.grid == p.work_items and p.block == 64
-    # aligned channel-last: the LDS-staged channel-last kernel
-    assert ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, layout="cl"))[1].vector == 2
-    # fp32 tiles are 32 steps (the same 16-byte vectors per lane)
+    assert p.span == 32 and p.unroll == 1
+    assert p.work_items == 4 * 128 * 32 and p.grid == p.work_items and p.block == 64
+    # aligned channel-last: the LDS-staged channel-last kernel, 4 tiles per work item
+    st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, layout="cl"))
+    assert st == 0 and p.vector == 2 and p.unroll == 4 and p.work_items == 4 * 32 * 32
+    # fp32 tiles are 32 steps too
     a = bargs(B=1, C=64, L=100, ws=False)
     a.x_dtype = ccv.CCV_F32
     a.workspace, a.workspace_bytes = WS, ccv.ccv_bwd_workspace_size(a)
@@ -431,5 +438,5 @@ def test_bwd_plan():
     # unaligned or mixed layouts: the element kernel, one lane per (b, tile, c)
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4095, x_stride=(2048 * 4095, 4095, 1),
                                    dout_stride=(2048 * 4095, 4095, 1), dx_stride=(2048 * 4095, 4095, 1)))
-    assert st == 0 and p.vector == 0 and p.work_items == 4 * 64 * 2048 and p.grid == 4 * 64 * 2048 // 256
+    assert st == 0 and p.vector == 0 and p.work_items == 4 * 128 * 2048 and p.grid == 4 * 128 * 2048 // 256
     assert ccv.ccv_bwd_plan(bargs(dx_stride=(64 * 1000, 1, 64)))[1].vector == 0
