@@ -67,7 +67,8 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
     dzw[i] = 0.0f;                                 // dz left of the tile is never read
   }
   const int64_t n_steps = FULL ? TT + H : t_end + H - t0;
-#pragma unroll(FULL ? TT + H : 1)
+  constexpr int kUnroll = FULL ? TT + H : 1;
+#pragma unroll kUnroll
   for (int64_t i = 0; i < n_steps; ++i) {
     const int64_t u = t0 + i;
     float xu = 0.0f, dzu = 0.0f;
@@ -111,7 +112,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
       }
       if (!FULL && a.dfs && j >= L - H && (!SEQ || L == 0 || idw[0] == sr[L - 1]))
         acc += S::to_f(static_cast<const raw*>(a.dfs)[b * a.fs_b + c * a.fs_c + (j - (L - H)) * a.fs_i]);
-      if (j >= 0)
+      if (FULL || j >= 0)                          // a whole tile never reaches left of t = 0
         src.put_dx(j, acc);
       else
         static_cast<raw*>(a.dinit)[b * a.di_b + c * a.di_c + (j + H) * a.di_i] = S::from_f(acc);
@@ -242,7 +243,7 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   const raw* xb = static_cast<const raw*>(a.x) + b * a.x_sb;
   const raw* gb = static_cast<const raw*>(a.dout) + b * a.d_sb;
   raw* db = static_cast<raw*>(a.dx) + b * a.g_sb;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const uintptr_t zero_src = reinterpret_cast<uintptr_t>(kZeroSrc);
   const int64_t c = c0 + lane;
   constexpr int cs = CL ? 1 : G::XP, gcs = CL ? 1 : G::GP, ps = CL ? 64 : 1;
 
@@ -255,39 +256,64 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     __syncthreads();                               // the previous tile's dx has left LDS
 
     // Stage x over [t0 - V, t0 + T + V) and dout over [t0, t0 + T + V); zeros outside
-    // [0, L) and past C (L and C are multiples of V on this path).
+    // [0, L) and past C (L and C are multiples of V on this path).  Every lane makes
+    // NX + NG 16-byte loads, all issued before the first LDS write (absent vectors
+    // load from the zero array), so the tile costs one memory latency, not one per
+    // load.  Channel-first: lane l reads channel c0 + l's run of steps (one base
+    // address per lane, constant offsets); channel-last: 64 / V consecutive lanes
+    // read one step's 64 channels.
+    constexpr int NX = G::XN / V, NG = G::GN / V, NS = 64 / V;
+    u32x4 vx[NX], vg[NG];
     if constexpr (!CL) {
-      constexpr int NX = G::XN / V, NG = G::GN / V;
-      for (int q = lane; q < 64 * NX; q += 64) {
-        const int r = q / NX, k = q - r * NX;
-        const int64_t p = t0 - V + k * V;
-        u32x4 v = zero;
-        if (c0 + r < C && p >= 0 && p < L) v = load16(xb + (c0 + r) * a.x_sc + p);
-        lds_put16(lx + r * G::XP + k * V, v);
+      // NX (NG) consecutive lanes read one channel's run, so each instruction covers
+      // whole runs of consecutive addresses.  The lane index passes through an empty
+      // asm statement per tile: otherwise the compiler keeps every load's row offset,
+      // LDS address and bounds in registers across the tile loop, which costs more
+      // waves than it saves.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int64_t xsc = a.x_sc, dsc = a.d_sc;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const int q = ln + 64 * i, r = q / NX;
+        const int64_t p = t0 - V + (q - r * NX) * V;
+        vx[i] = gload<u32x4>(pick(c0 + r < C && p >= 0 && p < L, reinterpret_cast<uintptr_t>(xb + (c0 + r) * xsc + p),
+                                  zero_src));
       }
-      for (int q = lane; q < 64 * NG; q += 64) {
-        const int r = q / NG, k = q - r * NG;
-        const int64_t p = t0 + k * V;
-        u32x4 v = zero;
-        if (c0 + r < C && p < L) v = load16(gb + (c0 + r) * a.d_sc + p);
-        lds_put16(lg + r * G::GP + k * V, v);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int q = ln + 64 * i, r = q / NG;
+        const int64_t p = t0 + (q - r * NG) * V;
+        vg[i] = gload<u32x4>(pick(c0 + r < C && p < L, reinterpret_cast<uintptr_t>(gb + (c0 + r) * dsc + p), zero_src));
+      }
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const int q = ln + 64 * i, r = q / NX;
+        lds_put16(lx + r * G::XP + (q - r * NX) * V, vx[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int q = ln + 64 * i, r = q / NG;
+        lds_put16(lg + r * G::GP + (q - r * NG) * V, vg[i]);
       }
     } else {
-      constexpr int NS = 64 / V;                   // vectors per step
-      for (int q = lane; q < G::XN * NS; q += 64) {
-        const int st = q / NS, k = q - st * NS;
-        const int64_t p = t0 - V + st;
-        u32x4 v = zero;
-        if (c0 + k * V < C && p >= 0 && p < L) v = load16(xb + p * a.x_sl + c0 + k * V);
-        lds_put16(lx + st * 64 + k * V, v);
+      const int64_t ck = c0 + (lane % NS) * V;     // this lane's first channel
+      const int s0 = lane / NS;                    // and step offset
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const int64_t p = t0 - V + s0 + i * (64 / NS);
+        vx[i] = gload<u32x4>(pick(ck < C && p >= 0 && p < L, reinterpret_cast<uintptr_t>(xb + p * a.x_sl + ck),
+                                  zero_src));
       }
-      for (int q = lane; q < G::GN * NS; q += 64) {
-        const int st = q / NS, k = q - st * NS;
-        const int64_t p = t0 + st;
-        u32x4 v = zero;
-        if (c0 + k * V < C && p < L) v = load16(gb + p * a.d_sl + c0 + k * V);
-        lds_put16(lg + st * 64 + k * V, v);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int64_t p = t0 + s0 + i * (64 / NS);
+        vg[i] = gload<u32x4>(pick(ck < C && p < L, reinterpret_cast<uintptr_t>(gb + p * a.d_sl + ck), zero_src));
       }
+#pragma unroll
+      for (int i = 0; i < NX; ++i) lds_put16(lx + (s0 + i * (64 / NS)) * 64 + (lane % NS) * V, vx[i]);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) lds_put16(lg + (s0 + i * (64 / NS)) * 64 + (lane % NS) * V, vg[i]);
     }
     if (t0 == 0 && a.init && c < C) {              // the history left of t = 0
 #pragma unroll
@@ -306,19 +332,41 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     }
     __syncthreads();
 
-    // dx over [t0, t_end) back to memory, 16 bytes at a time.
-    const int64_t t_end = t0 + a.T < L ? t0 + a.T : L;
-    const int nvt = (int)((t_end - t0) / V);
+    // dx over [t0, t_end) back to memory, 16 bytes at a time; a whole tile's stores
+    // unrolled.  Channel-first: lane l stores its own channel's run.
+    const int nst = (int)((t0 + a.T < L ? t0 + a.T : L) - t0);
     if constexpr (!CL) {
-      for (int q = lane; q < 64 * nvt; q += 64) {
-        const int r = q / nvt, k = q - r * nvt;
-        if (c0 + r < C) store16(db + (c0 + r) * a.g_sc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
+      int ln = lane;                               // recomputed per tile, as in the staging
+      asm volatile("" : "+v"(ln));
+      const int64_t gsc = a.g_sc;
+      const int nv = nst / V;                      // vectors per channel run
+      auto put = [&](int q) {
+        const int r = q / nv, k = q - r * nv;
+        if (c0 + r < C) store16(db + (c0 + r) * gsc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
+      };
+      if (nst == G::T) {
+#pragma unroll
+        for (int i = 0; i < G::T / V; ++i) {
+          const int q = ln + 64 * i, r = q / (G::T / V), k = q - r * (G::T / V);
+          if (c0 + r < C) store16(db + (c0 + r) * gsc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
+        }
+      } else {
+        for (int q = ln; q < 64 * nv; q += 64) put(q);
       }
     } else {
-      constexpr int NS = 64 / V;
-      for (int q = lane; q < (int)(t_end - t0) * NS; q += 64) {
-        const int st = q / NS, k = q - st * NS;
-        if (c0 + k * V < C) store16(db + (t0 + st) * a.g_sl + c0 + k * V, lds_get16(lx + (st + V) * 64 + k * V));
+      const int64_t ck = c0 + (lane % NS) * V;
+      const int s0 = lane / NS;
+      if (ck < C) {
+        if (nst == G::T) {
+#pragma unroll
+          for (int i = 0; i < G::T / V; ++i) {
+            const int st = s0 + i * (64 / NS);
+            store16(db + (t0 + st) * a.g_sl + ck, lds_get16(lx + (st + V) * 64 + (lane % NS) * V));
+          }
+        } else {
+          for (int st = s0; st < nst; st += 64 / NS)
+            store16(db + (t0 + st) * a.g_sl + ck, lds_get16(lx + (st + V) * 64 + (lane % NS) * V));
+        }
       }
     }
   }
