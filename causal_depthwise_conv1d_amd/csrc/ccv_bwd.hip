@@ -30,10 +30,12 @@ namespace ccv {
 namespace {
 
 // d silu(z) / dz = s (1 + z (1 - s)) with s = sigmoid(z), on the hardware exp2 and
-// rcp as the forward's SiLU.
+// rcp as the forward's SiLU; z (1 - s) = z - z s and s + s t are each one fused
+// multiply-add.
 __device__ inline float silu_slope(float z) {
   const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
-  return s * (1.0f + z * (1.0f - s));
+  const float t = __builtin_fmaf(-z, s, z);
+  return __builtin_fmaf(s, t, s);
 }
 
 // The walk of one lane over one tile (see the header comment), shared by both
@@ -44,14 +46,11 @@ __device__ inline float silu_slope(float z) {
 // so the walk unrolls completely; the arithmetic is the same.
 template <class S, int K, bool SILU, bool SEQ, bool FULL, int TT, class Src>
 __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t t0, Src& src,
-                                 float (&pw)[K], float& pb) {
+                                 const float (&w)[K], float beta, float (&pw)[K], float& pb) {
   using raw = typename S::raw;
   constexpr int H = K - 1;
   const int64_t L = a.L;
   const int64_t t_end = FULL ? t0 + TT : (t0 + a.T < L ? t0 + a.T : L);
-  float w[K];
-  load_params<K>(a.w, a.w_dtype, c * K, w);
-  const float beta = a.bias ? load_param(a.bias, a.w_dtype, c) : 0.0f;
   const int32_t* sr = SEQ ? a.seq + b * L : nullptr;
   const bool has_init = a.init != nullptr;       // with seq_idx: the history is the first sequence's
   const int hist_id = (SEQ && has_init && L > 0) ? sr[0] : 0;
@@ -168,27 +167,24 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
                       static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc,
                       a.init ? static_cast<const raw*>(a.init) + b * a.is_b + c * a.is_c : nullptr,
                       a.x_sl, a.d_sl, a.g_sl, a.is_i};
-  float pw[K], pb = 0.0f;
+  float w[K], pw[K], pb = 0.0f;
+  load_params<K>(a.w, a.w_dtype, c * K, w);
+  const float beta = a.bias ? load_param(a.bias, a.w_dtype, c) : 0.0f;
 #pragma unroll
   for (int k = 0; k < K; ++k) pw[k] = 0.0f;
   const int64_t tt1 = (g + 1) * a.tpi < a.ntt ? (g + 1) * a.tpi : a.ntt;
   for (int64_t tt = g * a.tpi; tt < tt1; ++tt)
-    walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, tt * a.T, src, pw, pb);
+    walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, tt * a.T, src, w, beta, pw, pb);
   store_partials<K>(a, b, g, c, pw, pb);
 }
 
-// LDS path: a wave takes a group of consecutive tiles of one (b, 64 channels);
-// for each it stages the tile (64 channels x the T steps, with V steps of margin
-// on either side for the halos) with 16-byte loads along the unit-stride
-// dimension, walks it from LDS, and stores dx back with 16-byte stores.  dx[j] is parked in the LDS slot of x[j], which the walk no longer
-// needs once dx[j] is final.  Channel-first tiles are stored channel-major with
-// an odd dword pitch (the walk's reads, one channel per lane, then fall in
-// distinct banks); channel-last tiles step-major, 64 channels to a step.
+// Geometry of the LDS path's tiles: 64 channels x T steps, staged with V steps of
+// margin on either side for the halos.
 template <class S>
 struct LdsGeom {
   static constexpr int V = S::V;
-  // The tile length: 32 steps keeps a wave's LDS near 11 KB and its registers under
-  // 100, so about 13 waves fit on a CU; the K-1 step halo is recomputed per tile.
+  // The tile length: 32 steps keeps a 16-bit tile's LDS near 11 KB, so about 14
+  // waves fit on a CU; the K-1 step halo is recomputed per tile.
   static constexpr int T = 32;
   static constexpr int ES = sizeof(typename S::raw);
   static constexpr int XN = T + 2 * V;                  // staged x positions: [t0 - V, t0 + T + V)
@@ -223,11 +219,97 @@ __device__ inline u32x4 lds_get16(const void* p) {
   return u32x4{d[0], d[1], d[2], d[3]};
 }
 
+// One tile's staged vectors: x over [t0 - V, t0 + T + V) and dout over
+// [t0, t0 + T + V), NX + NG 16-byte vectors per lane.
+template <class S>
+struct Staged {
+  static constexpr int NX = LdsGeom<S>::XN / S::V, NG = LdsGeom<S>::GN / S::V;
+  u32x4 x[NX], g[NG];
+};
+
+// Issues every load of tile t0 (absent vectors, outside [0, L) or past C, load
+// from the zero array; L and C are multiples of V on this path), with no wait.
+// Channel-first: NX (NG) consecutive lanes read one channel's run, so each
+// instruction covers whole runs of consecutive addresses.  Channel-last: 64 / V
+// consecutive lanes read one step's 64 channels.  `ln` is the lane index made
+// opaque to the compiler per tile, so that it recomputes the row offsets rather
+// than keeping one per load in registers for the whole kernel.
+template <class S, bool CL>
+__device__ inline void stage_issue(const BwdArgs& a, const typename S::raw* xb, const typename S::raw* gb,
+                                   int64_t c0, int64_t t0, int ln, Staged<S>& st) {
+  constexpr int V = S::V, NX = Staged<S>::NX, NG = Staged<S>::NG, NS = 64 / V;
+  const int64_t L = a.L, C = a.C;
+  const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
+  if constexpr (!CL) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int q = ln + 64 * i, r = q / NX;
+      const int64_t p = t0 - V + (q - r * NX) * V;
+      st.x[i] = gload<u32x4>(pick(c0 + r < C && p >= 0 && p < L,
+                                  reinterpret_cast<uintptr_t>(xb + (c0 + r) * a.x_sc + p), zero));
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int q = ln + 64 * i, r = q / NG;
+      const int64_t p = t0 + (q - r * NG) * V;
+      st.g[i] = gload<u32x4>(pick(c0 + r < C && p < L, reinterpret_cast<uintptr_t>(gb + (c0 + r) * a.d_sc + p), zero));
+    }
+  } else {
+    const int64_t ck = c0 + (ln % NS) * V;         // the lane's first channel
+    const int s0 = ln / NS;                        // and first step
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int64_t p = t0 - V + s0 + i * V;
+      st.x[i] = gload<u32x4>(pick(ck < C && p >= 0 && p < L, reinterpret_cast<uintptr_t>(xb + p * a.x_sl + ck), zero));
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int64_t p = t0 + s0 + i * V;
+      st.g[i] = gload<u32x4>(pick(ck < C && p < L, reinterpret_cast<uintptr_t>(gb + p * a.d_sl + ck), zero));
+    }
+  }
+}
+
+// Writes a tile's staged vectors to LDS (channel-first: channel-major rows of
+// pitch XP / GP; channel-last: step-major, 64 channels to a step).
+template <class S, bool CL>
+__device__ inline void stage_put(typename S::raw* lx, typename S::raw* lg, int ln, const Staged<S>& st) {
+  using G = LdsGeom<S>;
+  constexpr int V = S::V, NX = Staged<S>::NX, NG = Staged<S>::NG, NS = 64 / V;
+  if constexpr (!CL) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int q = ln + 64 * i, r = q / NX;
+      lds_put16(lx + r * G::XP + (q - r * NX) * V, st.x[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int q = ln + 64 * i, r = q / NG;
+      lds_put16(lg + r * G::GP + (q - r * NG) * V, st.g[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) lds_put16(lx + (ln / NS + i * V) * 64 + (ln % NS) * V, st.x[i]);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) lds_put16(lg + (ln / NS + i * V) * 64 + (ln % NS) * V, st.g[i]);
+  }
+}
+
+// LDS path: a wave takes a group of consecutive tiles of one (b, 64 channels).
+// Tile n's loads are issued before tile n-1's walk (software pipelining within
+// the wave; with seq_idx the walk itself reads ids from memory, and the hardware
+// waits for loads in issue order, so there each tile is loaded when its turn
+// comes).  A tile is written to LDS, walked from LDS, and its dx, parked in the
+// LDS slots of the x values that the walk no longer needs, is stored back with
+// 16-byte stores.  Channel-first tiles are channel-major with an odd dword pitch
+// (the walk's reads, one channel per lane, fall in distinct banks); channel-last
+// tiles step-major.
 template <class S, int K, bool SILU, bool SEQ, bool CL>
 __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   using raw = typename S::raw;
   using G = LdsGeom<S>;
-  constexpr int V = G::V, H = K - 1;
+  constexpr int V = G::V, H = K - 1, NS = 64 / V;
+  constexpr bool PREFETCH = !SEQ;
   __shared__ uint32_t lds[G::WORDS];
   raw* lx = reinterpret_cast<raw*>(lds);
   raw* lg = lx + (CL ? G::XN * 64 : 64 * G::XP);
@@ -243,133 +325,83 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   const raw* xb = static_cast<const raw*>(a.x) + b * a.x_sb;
   const raw* gb = static_cast<const raw*>(a.dout) + b * a.d_sb;
   raw* db = static_cast<raw*>(a.dx) + b * a.g_sb;
-  const uintptr_t zero_src = reinterpret_cast<uintptr_t>(kZeroSrc);
   const int64_t c = c0 + lane;
   constexpr int cs = CL ? 1 : G::XP, gcs = CL ? 1 : G::GP, ps = CL ? 64 : 1;
 
-  float pw[K], pb = 0.0f;
+  // Parameters first: they are the only loads the walk needs besides LDS.
+  float w[K], pw[K], pb = 0.0f;
+  load_params<K>(a.w, a.w_dtype, (c < C ? c : 0) * K, w);
+  const float beta = a.bias ? load_param(a.bias, a.w_dtype, c < C ? c : 0) : 0.0f;
 #pragma unroll
   for (int k = 0; k < K; ++k) pw[k] = 0.0f;
-  const int64_t tt1 = (g + 1) * a.tpi < a.ntt ? (g + 1) * a.tpi : a.ntt;
-  for (int64_t tt = g * a.tpi; tt < tt1; ++tt) {
-    const int64_t t0 = tt * a.T;
-    __syncthreads();                               // the previous tile's dx has left LDS
 
-    // Stage x over [t0 - V, t0 + T + V) and dout over [t0, t0 + T + V); zeros outside
-    // [0, L) and past C (L and C are multiples of V on this path).  Every lane makes
-    // NX + NG 16-byte loads, all issued before the first LDS write (absent vectors
-    // load from the zero array), so the tile costs one memory latency, not one per
-    // load.  Channel-first: lane l reads channel c0 + l's run of steps (one base
-    // address per lane, constant offsets); channel-last: 64 / V consecutive lanes
-    // read one step's 64 channels.
-    constexpr int NX = G::XN / V, NG = G::GN / V, NS = 64 / V;
-    u32x4 vx[NX], vg[NG];
-    if constexpr (!CL) {
-      // NX (NG) consecutive lanes read one channel's run, so each instruction covers
-      // whole runs of consecutive addresses.  The lane index passes through an empty
-      // asm statement per tile: otherwise the compiler keeps every load's row offset,
-      // LDS address and bounds in registers across the tile loop, which costs more
-      // waves than it saves.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int64_t xsc = a.x_sc, dsc = a.d_sc;
+  const int64_t tt0 = g * a.tpi;
+  const int64_t tt1 = (g + 1) * a.tpi < a.ntt ? (g + 1) * a.tpi : a.ntt;
+  Staged<S> st;
+  // dx of the previous tile, read out of LDS after its walk and stored after the
+  // next tile is in LDS: the hardware waits for loads in issue order, so stores
+  // issued just before the wait for the next tile's loads would be waited for too.
+  constexpr int ND = G::T / V;                     // dx vectors per lane and tile
+  u32x4 dxv[ND];
+  int64_t dx_t0 = -1;
+  int dx_n = 0;
+  auto store_dx = [&](int ln) {
 #pragma unroll
-      for (int i = 0; i < NX; ++i) {
-        const int q = ln + 64 * i, r = q / NX;
-        const int64_t p = t0 - V + (q - r * NX) * V;
-        vx[i] = gload<u32x4>(pick(c0 + r < C && p >= 0 && p < L, reinterpret_cast<uintptr_t>(xb + (c0 + r) * xsc + p),
-                                  zero_src));
+    for (int i = 0; i < ND; ++i) {
+      if constexpr (!CL) {
+        const int q = ln + 64 * i, r = q / ND, k = q - r * ND;
+        if (c0 + r < C && k * V < dx_n) store16(db + (c0 + r) * a.g_sc + dx_t0 + k * V, dxv[i]);
+      } else {
+        const int64_t ck = c0 + (ln % NS) * V;
+        const int s = ln / NS + i * V;
+        if (ck < C && s < dx_n) store16(db + (dx_t0 + s) * a.g_sl + ck, dxv[i]);
       }
-#pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        const int q = ln + 64 * i, r = q / NG;
-        const int64_t p = t0 + (q - r * NG) * V;
-        vg[i] = gload<u32x4>(pick(c0 + r < C && p < L, reinterpret_cast<uintptr_t>(gb + (c0 + r) * dsc + p), zero_src));
-      }
-#pragma unroll
-      for (int i = 0; i < NX; ++i) {
-        const int q = ln + 64 * i, r = q / NX;
-        lds_put16(lx + r * G::XP + (q - r * NX) * V, vx[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        const int q = ln + 64 * i, r = q / NG;
-        lds_put16(lg + r * G::GP + (q - r * NG) * V, vg[i]);
-      }
-    } else {
-      const int64_t ck = c0 + (lane % NS) * V;     // this lane's first channel
-      const int s0 = lane / NS;                    // and step offset
-#pragma unroll
-      for (int i = 0; i < NX; ++i) {
-        const int64_t p = t0 - V + s0 + i * (64 / NS);
-        vx[i] = gload<u32x4>(pick(ck < C && p >= 0 && p < L, reinterpret_cast<uintptr_t>(xb + p * a.x_sl + ck),
-                                  zero_src));
-      }
-#pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        const int64_t p = t0 + s0 + i * (64 / NS);
-        vg[i] = gload<u32x4>(pick(ck < C && p < L, reinterpret_cast<uintptr_t>(gb + p * a.d_sl + ck), zero_src));
-      }
-#pragma unroll
-      for (int i = 0; i < NX; ++i) lds_put16(lx + (s0 + i * (64 / NS)) * 64 + (lane % NS) * V, vx[i]);
-#pragma unroll
-      for (int i = 0; i < NG; ++i) lds_put16(lg + (s0 + i * (64 / NS)) * 64 + (lane % NS) * V, vg[i]);
     }
+  };
+
+  if constexpr (PREFETCH) stage_issue<S, CL>(a, xb, gb, c0, tt0 * a.T, lane, st);
+  for (int64_t tt = tt0; tt < tt1; ++tt) {
+    const int64_t t0 = tt * a.T;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if constexpr (!PREFETCH) stage_issue<S, CL>(a, xb, gb, c0, t0, ln, st);
+    __syncthreads();                               // the previous tile's dx has left LDS
+    stage_put<S, CL>(lx, lg, ln, st);
     if (t0 == 0 && a.init && c < C) {              // the history left of t = 0
 #pragma unroll
       for (int i = 0; i < H; ++i)
         lx[lane * cs + (V - H + i) * ps] =
             static_cast<const raw*>(a.init)[b * a.is_b + c * a.is_c + i * a.is_i];
     }
+    if (dx_t0 >= 0) store_dx(ln);
+    if constexpr (PREFETCH)
+      if (tt + 1 < tt1) stage_issue<S, CL>(a, xb, gb, c0, t0 + a.T, ln, st);
     __syncthreads();
 
     if (c < C) {
       LdsSrc<S, ps> src{lx + lane * cs, lg + lane * gcs, t0};
       if (t0 + G::T + H <= L && (t0 > 0 || !a.dinit))   // an interior tile
-        walk_tile<S, K, SILU, SEQ, true, G::T>(a, b, c, t0, src, pw, pb);
+        walk_tile<S, K, SILU, SEQ, true, G::T>(a, b, c, t0, src, w, beta, pw, pb);
       else
-        walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src, pw, pb);
+        walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src, w, beta, pw, pb);
     }
     __syncthreads();
 
-    // dx over [t0, t_end) back to memory, 16 bytes at a time; a whole tile's stores
-    // unrolled.  Channel-first: lane l stores its own channel's run.
-    const int nst = (int)((t0 + a.T < L ? t0 + a.T : L) - t0);
-    if constexpr (!CL) {
-      int ln = lane;                               // recomputed per tile, as in the staging
-      asm volatile("" : "+v"(ln));
-      const int64_t gsc = a.g_sc;
-      const int nv = nst / V;                      // vectors per channel run
-      auto put = [&](int q) {
-        const int r = q / nv, k = q - r * nv;
-        if (c0 + r < C) store16(db + (c0 + r) * gsc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
-      };
-      if (nst == G::T) {
+    // Read this tile's dx (the steps [t0, t0 + dx_n)) out of LDS, in the staging's
+    // lane mapping; vectors past dx_n are read but never stored.
 #pragma unroll
-        for (int i = 0; i < G::T / V; ++i) {
-          const int q = ln + 64 * i, r = q / (G::T / V), k = q - r * (G::T / V);
-          if (c0 + r < C) store16(db + (c0 + r) * gsc + t0 + k * V, lds_get16(lx + r * G::XP + (k + 1) * V));
-        }
+    for (int i = 0; i < ND; ++i) {
+      if constexpr (!CL) {
+        const int q = ln + 64 * i, r = q / ND, k = q - r * ND;
+        dxv[i] = lds_get16(lx + r * G::XP + (k + 1) * V);
       } else {
-        for (int q = ln; q < 64 * nv; q += 64) put(q);
-      }
-    } else {
-      const int64_t ck = c0 + (lane % NS) * V;
-      const int s0 = lane / NS;
-      if (ck < C) {
-        if (nst == G::T) {
-#pragma unroll
-          for (int i = 0; i < G::T / V; ++i) {
-            const int st = s0 + i * (64 / NS);
-            store16(db + (t0 + st) * a.g_sl + ck, lds_get16(lx + (st + V) * 64 + (lane % NS) * V));
-          }
-        } else {
-          for (int st = s0; st < nst; st += 64 / NS)
-            store16(db + (t0 + st) * a.g_sl + ck, lds_get16(lx + (st + V) * 64 + (lane % NS) * V));
-        }
+        dxv[i] = lds_get16(lx + (ln / NS + i * V + V) * 64 + (ln % NS) * V);
       }
     }
+    dx_t0 = t0;
+    dx_n = (int)((t0 + a.T < L ? t0 + a.T : L) - t0);
   }
+  if (dx_t0 >= 0) store_dx(lane);
   if (c < C) store_partials<K>(a, b, g, c, pw, pb);
 }
 
