@@ -263,13 +263,30 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
 
   // Phase 1: whole segments, two sets of loads in flight.  The next segment's
   // loads are issued before the current segment's arithmetic; the body is
-  // written twice so the sets swap roles without register copies.
+  // written twice so the sets swap roles without register copies.  Segment i is
+  // (row i / nfull, segment i % nfull), and row r is (b, c) = (r / C, r % C); the
+  // cursor steps by W segments with additions only, the quotients of W taken once.
   const int64_t nfull = VEC ? a.nfull : 0;
   const int64_t n1 = rows * nfull;
   if constexpr (VEC) if (w0 < n1) {
+    const int64_t drow = W / nfull, dseg = W - drow * nfull;
+    const int64_t db = drow / m.C, dc = drow - db * m.C;
+    const int64_t row0 = w0 / nfull;
+    int64_t seg = w0 - row0 * nfull, b = row0 / m.C, c = row0 - b * m.C;
+    auto advance = [&]() {
+      seg += dseg;
+      const int64_t carry = seg >= nfull ? 1 : 0;
+      seg -= carry * nfull;
+      c += dc + carry;                              // < 2C: at most one wrap
+      b += db;
+      if (c >= m.C) {
+        c -= m.C;
+        ++b;
+      }
+    };
     SegLoads<S, K, SEQ, WB> qa, qb;
     int64_t i = w0;
-    SegPos pa = row_pos(m, i / nfull, (i % nfull) * a.span), pb;
+    SegPos pa{b, c, seg * a.span}, pb;
     issue_segment<S, K, SEQ, WB>(a, pa, true, lane, qa);
     while (true) {
       const int64_t i1 = i + W;
@@ -277,7 +294,8 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
         compute_whole<S, K, SILU, SEQ, WB>(a, pa, lane, qa);
         break;
       }
-      pb = row_pos(m, i1 / nfull, (i1 % nfull) * a.span);
+      advance();
+      pb = SegPos{b, c, seg * a.span};
       issue_segment<S, K, SEQ, WB>(a, pb, true, lane, qb);
       compute_whole<S, K, SILU, SEQ, WB>(a, pa, lane, qa);
       const int64_t i2 = i1 + W;
@@ -285,7 +303,8 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
         compute_whole<S, K, SILU, SEQ, WB>(a, pb, lane, qb);
         break;
       }
-      pa = row_pos(m, i2 / nfull, (i2 % nfull) * a.span);
+      advance();
+      pa = SegPos{b, c, seg * a.span};
       issue_segment<S, K, SEQ, WB>(a, pa, true, lane, qa);
       compute_whole<S, K, SILU, SEQ, WB>(a, pb, lane, qb);
       i = i2;
