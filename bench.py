@@ -637,6 +637,7 @@ def cpu_baseline(w, out_gpu, nbytes, min_seconds):
     """The oracle as written (single-threaded fp64 loop) on this host's CPU, over
     the whole workload, repeated until at least `min_seconds` have passed; then the
     GPU output of this run compared with it at every output."""
+    import numpy as np
     import torch
 
     from oracle import compare as ocmp
@@ -654,6 +655,19 @@ def cpu_baseline(w, out_gpu, nbytes, min_seconds):
         passes += 1
     sec = t_total / passes
     log(f"[bench] cpu oracle: {passes} passes, {sec:.2f} s per pass")
+    # The same loop on all of this host's cores (context, not the baseline): rows of
+    # (b, c) split between threads, results bit-identical to the single thread.
+    from oracle import GCC_CMD
+    nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+    mt_passes, mt_total, ymt = 0, 0.0, None
+    while mt_passes == 0 or mt_total < min(min_seconds, 3.0):
+        t0 = time.perf_counter()
+        ymt, _ = c.fwd_threads(nthr)
+        round_out(w.x_dtype, ymt)
+        mt_total += time.perf_counter() - t0
+        mt_passes += 1
+    mt_sec = mt_total / mt_passes
+    log(f"[bench] cpu oracle on {nthr} threads: {mt_passes} passes, {mt_sec:.3f} s per pass")
     g = raw(out_gpu.cpu().contiguous())
     res = ocmp.compare(dtype_name(out_gpu), w.K, g, y, s)
     cpu_name = ""
@@ -675,6 +689,10 @@ def cpu_baseline(w, out_gpu, nbytes, min_seconds):
         "seconds_per_pass": round(sec, 3),
         "host_cpu": cpu_name,
         "host_threads_available": os.cpu_count(),
+        "compile_flags": " ".join(f for f in GCC_CMD[1:] if f.startswith("-") and f not in ("-o", "-shared")),
+        "all_cores": {"value": round(nbytes / mt_sec / 1e9, 4), "unit": "GB/s", "threads": nthr,
+                      "seconds_per_pass": round(mt_sec, 4), "passes": mt_passes,
+                      "bit_identical_to_one_thread": bool(np.array_equal(ymt.view(np.uint64), y.view(np.uint64)))},
         "parity": {"outputs": res["n"], "out_of_tolerance": res["n_bad"], "max_ulp": res["max_ulp"],
                    "max_rel": res["max_rel"], "floor_only": res["n_floor_only"],
                    "bit_equal": res["bit_equal"]},

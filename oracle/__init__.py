@@ -31,7 +31,7 @@ DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 _NP_STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16}
 
 GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-o", _SO, _SRC, "-lm"]
+           "-shared", "-Wall", "-Wextra", "-pthread", "-o", _SO, _SRC, "-lm"]
 
 
 class _Problem(ctypes.Structure):
@@ -68,6 +68,7 @@ def _load(path):
     i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
     L.ora_point.argtypes = [P, i64, i64, i64, dp, dp, dp]
     L.ora_fwd.argtypes = [P, vp, vp]
+    L.ora_fwd_threads.argtypes = [P, vp, vp, ctypes.c_int]
     L.ora_points.argtypes = [P, i64, vp, vp, vp]
     L.ora_final_states.argtypes = [P, vp]
     L.ora_bwd.argtypes = [P, ctypes.POINTER(_Grad)] + [vp] * 8
@@ -163,6 +164,17 @@ class Case:
         s = np.empty(n, dtype=np.float64) if want_sabs else None
         if lib().ora_fwd(ctypes.byref(self._p), y.ctypes.data, _ptr(s)) != 0:
             raise RuntimeError("ora_fwd failed")
+        shape = (self.B, self.C, self.L)
+        return y.reshape(shape), (None if s is None else s.reshape(shape))
+
+    def fwd_threads(self, nthreads: int, want_sabs: bool = True):
+        """fwd() on up to `nthreads` host threads (rows split between them); the
+        same outputs bit for bit."""
+        n = self.B * self.C * self.L
+        y = np.empty(n, dtype=np.float64)
+        s = np.empty(n, dtype=np.float64) if want_sabs else None
+        if lib().ora_fwd_threads(ctypes.byref(self._p), y.ctypes.data, _ptr(s), int(nthreads)) != 0:
+            raise RuntimeError("ora_fwd_threads failed")
         shape = (self.B, self.C, self.L)
         return y.reshape(shape), (None if s is None else s.reshape(shape))
 

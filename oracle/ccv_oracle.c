@@ -7,11 +7,16 @@
  * for the formula and its sources); there is no tiling, no reuse of partial
  * sums and no reordering of the terms.  Build: gcc -O2 -ffp-contract=off
  * (no fused multiply-add, no fast-math), so the fp64 arithmetic is exactly
- * what is written here.
+ * what is written here.  ora_fwd_threads runs the same per-output loop over
+ * disjoint ranges of (b, c) rows on several POSIX threads (for timing on all host
+ * cores); every output is still computed by the one function, so the results
+ * are the single-threaded ones bit for bit.
  */
+#define _POSIX_C_SOURCE 200809L
 #include "ccv_oracle.h"
 
 #include <math.h>
+#include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -217,17 +222,61 @@ int ora_point(const ora_problem_t* p, int64_t b, int64_t c, int64_t t,
   return 0;
 }
 
-int ora_fwd(const ora_problem_t* p, double* y, double* sabs) {
-  for (int64_t b = 0; b < p->B; ++b)
-    for (int64_t c = 0; c < p->C; ++c)
-      for (int64_t t = 0; t < p->L; ++t) {
-        int64_t o = (b * p->C + c) * p->L + t;
-        double yy, ss;
-        if (ora_point(p, b, c, t, &yy, NULL, &ss) != 0) return -1;
-        if (y) y[o] = yy;
-        if (sabs) sabs[o] = ss;
-      }
+/* Every output of rows r0 .. r1-1 (row r = b*C + c), in order. */
+static int ora_rows(const ora_problem_t* p, int64_t r0, int64_t r1, double* y, double* sabs) {
+  for (int64_t r = r0; r < r1; ++r) {
+    const int64_t b = r / p->C, c = r % p->C;
+    for (int64_t t = 0; t < p->L; ++t) {
+      int64_t o = r * p->L + t;
+      double yy, ss;
+      if (ora_point(p, b, c, t, &yy, NULL, &ss) != 0) return -1;
+      if (y) y[o] = yy;
+      if (sabs) sabs[o] = ss;
+    }
+  }
   return 0;
+}
+
+int ora_fwd(const ora_problem_t* p, double* y, double* sabs) {
+  return ora_rows(p, 0, p->B * p->C, y, sabs);
+}
+
+typedef struct {
+  const ora_problem_t* p;
+  double* y;
+  double* sabs;
+  int64_t r0, r1;
+  int status;
+} ora_rows_job;
+
+static void* ora_rows_thread(void* arg) {
+  ora_rows_job* j = (ora_rows_job*)arg;
+  j->status = ora_rows(j->p, j->r0, j->r1, j->y, j->sabs);
+  return NULL;
+}
+
+int ora_fwd_threads(const ora_problem_t* p, double* y, double* sabs, int nthreads) {
+  enum { MAX_THREADS = 256 };
+  const int64_t rows = p->B * p->C;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > MAX_THREADS) nthreads = MAX_THREADS;
+  if ((int64_t)nthreads > rows) nthreads = rows > 0 ? (int)rows : 1;
+  ora_rows_job jobs[MAX_THREADS];
+  pthread_t tid[MAX_THREADS];
+  int created[MAX_THREADS];
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (ora_rows_job){p, y, sabs, rows * i / nthreads, rows * (i + 1) / nthreads, 0};
+    /* range 0 runs on the calling thread, and so does any range whose thread fails to start */
+    created[i] = i > 0 && pthread_create(&tid[i], NULL, ora_rows_thread, &jobs[i]) == 0;
+  }
+  for (int i = 0; i < nthreads; ++i)
+    if (!created[i]) ora_rows_thread(&jobs[i]);
+  int status = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    if (created[i]) pthread_join(tid[i], NULL);
+    status |= jobs[i].status;
+  }
+  return status ? -1 : 0;
 }
 
 int ora_points(const ora_problem_t* p, int64_t n, const int64_t* idx,

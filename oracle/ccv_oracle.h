@@ -69,6 +69,11 @@ int ora_point(const ora_problem_t* p, int64_t b, int64_t c, int64_t t,
 /* All outputs, written to y[(b*C+c)*L+t] and sabs[...] (either may be NULL). */
 int ora_fwd(const ora_problem_t* p, double* y, double* sabs);
 
+/* The same outputs as ora_fwd, computed by the same per-output function on up to
+ * nthreads POSIX threads, each over a contiguous range of (b, c) rows: bit for bit
+ * the single-threaded result (for timing the oracle on all host cores). */
+int ora_fwd_threads(const ora_problem_t* p, double* y, double* sabs, int nthreads);
+
 /* n sampled outputs; idx holds n (b,c,t) triples. */
 int ora_points(const ora_problem_t* p, int64_t n, const int64_t* idx,
                double* y, double* sabs);
