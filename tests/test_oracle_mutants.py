@@ -1,8 +1,14 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU) and check that the
 pins catch every one of them.  Each mutant is the oracle's C source with one
-textual change, compiled with the same gcc line into a temporary directory."""
+textual change, compiled with the same gcc line into a temporary directory.
+
+A mutant runs the pins in an interpreter of its own: some mistakes (a swapped
+stride) read outside the input arrays, which may read garbage (a pin fails) or
+may leave the process's memory altogether; a mutant whose run dies that way is
+caught too, and cannot take the test session down with it."""
 import os
 import subprocess
+import sys
 
 import pytest
 
@@ -77,16 +83,34 @@ def test_unmutated_copy_passes(tmp_path):
             pin(oracle)
 
 
+_TESTS = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_TESTS)
+_RUN_PINS = """
+import sys
+sys.path[:0] = [{tests!r}, {root!r}]
+import oracle
+from oracle_pins import ALL_PINS
+caught = []
+with oracle.using_library({so!r}):
+    for pin in ALL_PINS:
+        try:
+            pin(oracle)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break                                  # one catch is enough
+print("CAUGHT:" + ",".join(caught))
+"""
+
+
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, name, old, new):
     text = open(SRC).read()
     assert text.count(old) == 1, f"mutation site for {name} not unique"
     so = _build(tmp_path, name, text.replace(old, new))
-    caught = []
-    with oracle.using_library(so):
-        for pin in ALL_PINS:
-            try:
-                pin(oracle)
-            except AssertionError:
-                caught.append(pin.__name__)
-    assert caught, f"no pin caught mutant {name}"
+    r = subprocess.run([sys.executable, "-c", _RUN_PINS.format(tests=_TESTS, root=_ROOT, so=so)],
+                       capture_output=True, text=True, timeout=900)
+    if r.returncode < 0:
+        return                                     # the mutant's run died on a signal: caught
+    assert r.returncode == 0, r.stderr[-2000:]     # any other error is the harness's, not a catch
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("CAUGHT:")]
+    assert lines and lines[-1] != "CAUGHT:", f"no pin caught mutant {name}"
