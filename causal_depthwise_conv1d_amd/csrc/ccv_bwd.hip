@@ -3,8 +3,9 @@
 // map", section "How autograd links forward and backward"; the formulas are
 // stated in ccv.h beside ccv_bwd).
 //
-// Gradient kernel.  One lane owns one (b, c) row and one tile of T time steps.
-// It walks u = t0 .. t_end + K - 2 once, with three register windows over the
+// Gradient kernel.  One lane owns one (b, c) row and a group of tpi consecutive
+// tiles of T time steps.  For each tile [t0, t_end) it walks
+// u = t0 .. t_end + K - 2 once, with three register windows over the
 // positions u-K+1 .. u: the extended input X~, the sequence ids, and dz.  At
 // each u < L it recomputes the pre-activation z[u] exactly as the forward does
 // (bias first, k ascending, fused multiply-adds) and forms dz[u] = dout[u] *
@@ -13,11 +14,12 @@
 // reads (dz[j .. j+K-1]), so dX~[j] is finished and stored: to dx when j lies in
 // the tile, to dinitial_states when j < 0 in the row's first tile.  Recomputing
 // z over the K-1 steps past the tile is the halo; nothing from the forward is
-// stored.  The lane's partial sums go to the workspace.  Lanes take consecutive
-// channels, so a wave's accesses are coalesced when channels are unit-stride
-// and repeat over the same cache lines from step to step otherwise.
+// stored.  The lane's partial sums over its group go to the workspace as one
+// row.  In the element kernel lanes take consecutive channels and read global
+// memory directly; in the LDS kernels a wave stages each tile of 64 channels in
+// LDS with 16-byte loads first (see bwd_lds_kernel).
 //
-// Reduction kernel.  The partials of all (b, tile) are summed per (tap or bias,
+// Reduction kernel.  The partials of all (b, tile group) are summed per (tap or bias,
 // channel) by a tree of fixed shape: each level adds groups of kBwdFanIn
 // consecutive rows in order, one lane per group and column, until one row is
 // left, which is rounded once to the weight dtype (the fp32-accumulate-then-

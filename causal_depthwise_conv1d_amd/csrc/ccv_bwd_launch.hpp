@@ -55,9 +55,9 @@ constexpr int kBwdBlock = 256;      // element path: lanes per workgroup
 constexpr int kBwdTilesPerItem = 4;
 constexpr int kBwdFanIn = 32;       // partial sums added per lane and level of the reduction
 
-// Gradient kernel variants: the element path (one lane per (b, tile, c), any
+// Gradient kernel variants: the element path (one lane per (b, tile group, c), any
 // strides; grid = ceil(lanes / kBwdBlock)) and the LDS-staged paths (one 64-lane
-// workgroup per (b, tile, group of 64 channels); grid = B * ntt * ceil(C / 64)),
+// workgroup per (b, tile group, 64 channels); grid = B * ngr * ceil(C / 64)),
 // which need x, dout and dx unit-stride in the same dimension (time for CF,
 // channels for CL), 16-byte aligned bases and strides, and L (CF) or C (CL) a
 // multiple of 16 / element size.
@@ -71,7 +71,7 @@ int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, int path
                void* stream);
 int launch_bwd_reduce(const BwdReduceArgs& r, uint32_t grid, void* stream);
 
-// Floats the reduction needs after the B * ntt partial rows: one row per group of
+// Rows the reduction needs after the B * ngr partial rows: one row per group of
 // every level but the last.
 inline int64_t bwd_reduce_rows(int64_t nparts) {
   int64_t rows = 0;

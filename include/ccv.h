@@ -221,7 +221,8 @@ int ccv_update_plan(const ccv_update_args_t* args, ccv_plan_t* plan);
  *
  * Every sum is fp32; dx and dinitial_states are rounded once to x's dtype,
  * dweight and dbias once to the weight dtype.  The parameter sums run in a fixed
- * order (per time tile, then over tiles), so results repeat bit for bit.  With
+ * order (within each group of consecutive time tiles of a row, then over the groups
+ * by a tree of fixed shape), so results repeat bit for bit.  With
  * seq_idx, keep() and the history's sequence are the forward's, and
  * dfinal_states reaches only the entries that final_states kept.  Any element strides are accepted for x,
  * dout, dx and the states; weight, bias, dweight, dbias are contiguous.  dx must
@@ -263,15 +264,15 @@ typedef struct ccv_bwd_args {
  * the arguments are invalid.  Host only. */
 int64_t ccv_bwd_workspace_size(const ccv_bwd_args_t* args);
 
-/* Enqueue the backward (two kernels, in order) on `hip_stream` and return without
- * waiting.  Returns CCV_OK, a validation error (nothing enqueued) or CCV_E_HIP. */
+/* Enqueue the backward (the gradient kernel, then one kernel per level of the
+ * reduction tree, in order) on `hip_stream` and return without waiting.  Returns CCV_OK, a validation error (nothing enqueued) or CCV_E_HIP. */
 int ccv_bwd(const ccv_bwd_args_t* args, void* hip_stream);
 
 /* Validate `args` exactly as ccv_bwd does, without touching any device. */
 int ccv_bwd_check(const ccv_bwd_args_t* args);
 
 /* Describe the launch ccv_bwd would make (host only; `plan` may be NULL): path
- * CCV_PATH_BACKWARD; vector 0 for the element path (one lane per (b, tile, c),
+ * CCV_PATH_BACKWARD; vector 0 for the element path (one lane per (b, tile group, c),
  * any strides), 1 for the LDS-staged channel-first path, 2 for the LDS-staged
  * channel-last path (x, dout and dx unit-stride in time, resp. channels, 16-byte
  * aligned, L resp. C a multiple of 16 / element size); span = time steps per
