@@ -416,35 +416,57 @@ __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {
     static_cast<uint16_t*>(p)[i] = F16::from_f(v);
 }
 
+// The in-order sum of rows q0 .. q1-1 of column s, from zero: a whole group's loads
+// are all issued before the additions.
+__device__ inline float sum_rows(const float* in, int64_t width, int64_t s, int64_t q0, int64_t q1) {
+  float acc = 0.0f;
+  if (q1 - q0 == kBwdFanIn) {
+    float v[kBwdFanIn];
+#pragma unroll
+    for (int q = 0; q < kBwdFanIn; ++q) v[q] = in[(q0 + q) * width + s];
+#pragma unroll
+    for (int q = 0; q < kBwdFanIn; ++q) acc += v[q];
+  } else {
+    for (int64_t q = q0; q < q1; ++q) acc += in[q * width + s];
+  }
+  return acc;
+}
+
 __global__ void __launch_bounds__(kBwdBlock) bwd_reduce_kernel(const BwdReduceArgs r) {
   const int64_t width = (int64_t)(r.K + 1) * r.C;
   const int64_t id = (int64_t)blockIdx.x * kBwdBlock + threadIdx.x;
-  const int64_t groups = r.n_in > 0 ? (r.n_in + kBwdFanIn - 1) / kBwdFanIn : 1;   // no rows: zeros
+  const int64_t groups = (r.n_in + kBwdFanIn - 1) / kBwdFanIn;
   if (id >= groups * width) return;
   const int64_t g = id / width;
   const int64_t s = id - g * width;
   const int64_t q0 = g * kBwdFanIn;
   const int64_t q1 = q0 + kBwdFanIn < r.n_in ? q0 + kBwdFanIn : r.n_in;
-  float acc = 0.0f;
-  if (q1 - q0 == kBwdFanIn) {                      // a whole group: all loads first, then the sum in order
-    float v[kBwdFanIn];
-#pragma unroll
-    for (int q = 0; q < kBwdFanIn; ++q) v[q] = r.in[(q0 + q) * width + s];
-#pragma unroll
-    for (int q = 0; q < kBwdFanIn; ++q) acc += v[q];
-  } else {
-    for (int64_t q = q0; q < q1; ++q) acc += r.in[q * width + s];
+  r.out[g * width + s] = sum_rows(r.in, width, s, q0, q1);
+}
+
+__global__ void __launch_bounds__(64 * kBwdFinalWaves) bwd_reduce_final_kernel(const BwdReduceArgs r) {
+  __shared__ float sums[kBwdFinalWaves][64];
+  const int64_t width = (int64_t)(r.K + 1) * r.C;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int64_t s = (int64_t)blockIdx.x * 64 + lane;
+  float acc = 0.0f;                                // no rows (B = 0): zeros
+  if (s < width) {
+    const int64_t q0 = (int64_t)wv * kBwdFanIn;
+    const int64_t q1 = q0 + kBwdFanIn < r.n_in ? q0 + kBwdFanIn : r.n_in;
+    acc = sum_rows(r.in, width, s, q0, q1);
   }
-  if (!r.last) {
-    r.out[g * width + s] = acc;
-    return;
-  }
+  sums[wv][lane] = acc;
+  __syncthreads();
+  if (wv != 0 || s >= width) return;
+  float tot = 0.0f;
+  for (int w = 0; w < nw; ++w) tot += sums[w][lane];
   const int64_t slot = s / r.C;
   const int64_t c = s - slot * r.C;
   if (slot < r.K)
-    store_param(r.dw, r.w_dtype, c * r.K + slot, acc);
+    store_param(r.dw, r.w_dtype, c * r.K + slot, tot);
   else if (r.db)
-    store_param(r.db, r.w_dtype, c, acc);
+    store_param(r.db, r.w_dtype, c, tot);
 }
 
 template <class S, int K, bool SILU, bool SEQ>
@@ -498,6 +520,13 @@ int launch_bwd_reduce(const BwdReduceArgs& r, uint32_t grid, void* stream) {
   void* args[] = {const_cast<BwdReduceArgs*>(&r)};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_kernel), dim3(grid), dim3(kBwdBlock),
                               args, 0, static_cast<hipStream_t>(stream));
+}
+
+int launch_bwd_reduce_final(const BwdReduceArgs& r, uint32_t grid, int waves, void* stream) {
+  if (waves < 1 || waves > kBwdFinalWaves) return (int)hipErrorInvalidValue;
+  void* args[] = {const_cast<BwdReduceArgs*>(&r)};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_final_kernel), dim3(grid),
+                              dim3(64 * waves), args, 0, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace ccv

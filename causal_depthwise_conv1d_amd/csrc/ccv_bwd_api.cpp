@@ -106,8 +106,13 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   const int path = rows ? choose_path(a) : kBwdPathElement;
   const int64_t items = path == kBwdPathElement ? lanes : nparts * ((C + 63) / 64);
   const int64_t grid = path == kBwdPathElement ? (lanes + kBwdBlock - 1) / kBwdBlock : items;
-  const int64_t groups = nparts > 0 ? (nparts + kBwdFanIn - 1) / kBwdFanIn : 1;   // B = 0 still writes zeros
-  const int64_t rgrid = (groups * (K + 1) * C + kBwdBlock - 1) / kBwdBlock;
+  // Reduction launches: level kernels while more rows are left than the final kernel
+  // takes (the first is the largest), then the final kernel, 64 columns per workgroup
+  // (it also runs for B = 0, to write zeros).
+  const int64_t width = (int64_t)(K + 1) * C;
+  const int64_t rgrid = nparts > (int64_t)kBwdFanIn * kBwdFinalWaves
+                            ? ((nparts + kBwdFanIn - 1) / kBwdFanIn * width + kBwdBlock - 1) / kBwdBlock
+                            : (width + 63) / 64;
   if (grid > INT32_MAX || rgrid > INT32_MAX) return CCV_E_SHAPE;
   if (check_workspace && ws > 0) {
     if (!a->workspace) return CCV_E_NULL;
@@ -215,22 +220,23 @@ int ccv_bwd(const ccv_bwd_args_t* args, void* hip_stream) {
     if (err != 0) return CCV_E_HIP;
   }
   if (p.rgrid > 0) {
-    // Levels of the reduction tree, each reading the previous level's rows.
+    // Levels of the reduction tree, each reading the previous level's rows, then the
+    // final kernel for the last two levels.
     BwdReduceArgs r = p.r;
     const int64_t width = (int64_t)(args->K + 1) * args->C;
     float* next = p.a.part ? p.a.part + p.r.n_in * width : nullptr;
-    while (true) {
-      const int64_t groups = r.n_in > 0 ? (r.n_in + kBwdFanIn - 1) / kBwdFanIn : 1;
-      r.last = r.n_in <= kBwdFanIn;
-      r.out = r.last ? nullptr : next;
+    while (r.n_in > (int64_t)kBwdFanIn * kBwdFinalWaves) {
+      const int64_t groups = (r.n_in + kBwdFanIn - 1) / kBwdFanIn;
+      r.out = next;
       const int64_t grid = (groups * width + kBwdBlock - 1) / kBwdBlock;
-      const int err = launch_bwd_reduce(r, (uint32_t)(grid > 0 ? grid : 1), hip_stream);
-      if (err != 0) return CCV_E_HIP;
-      if (r.last) break;
+      if (launch_bwd_reduce(r, (uint32_t)grid, hip_stream) != 0) return CCV_E_HIP;
       r.in = next;
       r.n_in = groups;
       next += groups * width;
     }
+    const int waves = r.n_in > 0 ? (int)((r.n_in + kBwdFanIn - 1) / kBwdFanIn) : 1;
+    const int64_t grid = (width + 63) / 64;
+    if (launch_bwd_reduce_final(r, (uint32_t)grid, waves, hip_stream) != 0) return CCV_E_HIP;
   }
   return CCV_OK;
 }

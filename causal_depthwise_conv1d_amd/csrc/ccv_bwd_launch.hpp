@@ -33,18 +33,22 @@ struct BwdArgs {
   int32_t w_dtype;
 };
 
-// Reduction, one level: lane (g, s) with s < (K + 1) * C sums inputs
-// in[32 g .. 32 g + 31][s] in order (fewer in the last group) into out[g][s].
-// Levels repeat until one group is left; the last level instead rounds to the
-// weight dtype and writes dweight[c, slot] (slot < K) or dbias[c] (slot = K).
+// Reduction over the partial rows, a tree of fixed shape: each level sums groups
+// of kBwdFanIn consecutive rows in order, starting from zero, until one row is
+// left.  A level kernel: lane (g, s) with s < (K + 1) * C sums
+// in[32 g .. 32 g + 31][s] (fewer in the last group) into out[g][s].  The final
+// kernel does the last two levels at once for n_in <= kBwdFanIn * kBwdFinalWaves
+// rows: a workgroup of ceil(n_in / 32) waves takes 64 columns, wave w sums rows
+// 32 w .. 32 w + 31, and one wave sums the wave sums in order, which is exactly
+// the arithmetic of the two levels; it rounds the result to the weight dtype and
+// writes dweight[c, slot] (slot < K) or dbias[c] (slot = K).
 struct BwdReduceArgs {
   const float* in;          // [n_in][(K + 1) * C]
-  float* out;               // [ceil(n_in / 32)][(K + 1) * C], unused on the last level
-  void* dw;                 // [C, K], w_dtype (last level)
-  void* db;                 // [C] or nullptr, w_dtype (last level)
+  float* out;               // [ceil(n_in / 32)][(K + 1) * C] (level kernel)
+  void* dw;                 // [C, K], w_dtype (final kernel)
+  void* db;                 // [C] or nullptr, w_dtype (final kernel)
   int64_t C, n_in;
   int32_t K, w_dtype;
-  int32_t last;
 };
 
 constexpr int kBwdBlock = 256;      // element path: lanes per workgroup
@@ -54,6 +58,7 @@ constexpr int kBwdBlock = 256;      // element path: lanes per workgroup
 // the same time by another wave than after this one: then one tile per row.
 constexpr int kBwdTilesPerItem = 4;
 constexpr int kBwdFanIn = 32;       // partial sums added per lane and level of the reduction
+constexpr int kBwdFinalWaves = 16;  // waves of the final reduction kernel's workgroups, at most
 
 // Gradient kernel variants: the element path (one lane per (b, tile group, c), any
 // strides; grid = ceil(lanes / kBwdBlock)) and the LDS-staged paths (one 64-lane
@@ -70,12 +75,16 @@ int bwd_tile_steps(int dtype);
 int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, int path, uint32_t grid,
                void* stream);
 int launch_bwd_reduce(const BwdReduceArgs& r, uint32_t grid, void* stream);
+int launch_bwd_reduce_final(const BwdReduceArgs& r, uint32_t grid, int waves, void* stream);
 
-// Rows the reduction needs after the B * ngr partial rows: one row per group of
-// every level but the last.
+// Rows the reduction needs after the B * ngr partial rows: the outputs of the
+// level kernels, which run while more rows are left than the final kernel takes.
 inline int64_t bwd_reduce_rows(int64_t nparts) {
   int64_t rows = 0;
-  for (int64_t n = nparts; n > kBwdFanIn; n = (n + kBwdFanIn - 1) / kBwdFanIn) rows += (n + kBwdFanIn - 1) / kBwdFanIn;
+  for (int64_t n = nparts; n > (int64_t)kBwdFanIn * kBwdFinalWaves;) {
+    n = (n + kBwdFanIn - 1) / kBwdFanIn;
+    rows += n;
+  }
   return rows;
 }
 

@@ -349,12 +349,13 @@ def bcheck(a):
 
 
 def test_bwd_workspace_size_is_the_partial_sums():
-    # one fp32 row of (K + 1) * C partial sums per (b, tile), plus one row per group
-    # of 32 on every level of the reduction tree but the last
+    # one fp32 row of (K + 1) * C partial sums per (b, tile group), plus the rows the
+    # level kernels of the reduction tree write while more than 512 rows are left (the
+    # final kernel sums up to 16 groups of 32 at once)
     # channel-first: a row per tile of 32 steps
     a = bargs(B=3, C=100, L=1000, K=3, ws=False)
-    parts = 3 * -(-1000 // 32)                       # 96 rows -> 3 groups -> 1
-    assert ccv.ccv_bwd_workspace_size(a) == (parts + 3) * 100 * (3 + 1) * 4
+    parts = 3 * -(-1000 // 32)                       # 96 rows: the final kernel alone
+    assert ccv.ccv_bwd_workspace_size(a) == parts * 100 * (3 + 1) * 4
     # channel-last: a row per group of 4 tiles
     a = bargs(B=3, C=100, L=1000, K=3, layout="cl", ws=False)
     parts = 3 * -(-(-(-1000 // 32)) // 4)            # 24 rows: one level
@@ -362,8 +363,12 @@ def test_bwd_workspace_size_is_the_partial_sums():
     assert ccv.ccv_bwd_workspace_size(bargs(B=2, C=5, L=0, ws=False)) == 2 * 1 * 5 * 5 * 4
     a = bargs(B=2, C=128, L=1 << 20, K=3, ws=False)
     a.x_dtype = ccv.CCV_F32
-    parts = 2 * (1 << 20) // 32                      # 65536 -> 2048 -> 64 -> 2 -> 1
-    assert ccv.ccv_bwd_workspace_size(a) == (parts + 2048 + 64 + 2) * 128 * 4 * 4
+    parts = 2 * (1 << 20) // 32                      # 65536 -> 2048 -> 64, then the final kernel
+    assert ccv.ccv_bwd_workspace_size(a) == (parts + 2048 + 64) * 128 * 4 * 4
+    a = bargs(B=1, C=8, L=512 * 32, K=2, ws=False)  # 512 rows: the final kernel alone
+    assert ccv.ccv_bwd_workspace_size(a) == 512 * 8 * 3 * 4
+    a = bargs(B=1, C=8, L=513 * 32, K=2, ws=False)  # 513 rows -> 17 -> final
+    assert ccv.ccv_bwd_workspace_size(a) == (513 + 17) * 8 * 3 * 4
     assert ccv.ccv_bwd_workspace_size(bargs(B=0, ws=False)) == 0
     assert ccv.ccv_bwd_workspace_size(bargs(K=5, ws=False)) == ccv.lib().ccv_bwd_check(bargs(K=5, ws=False))
 
