@@ -243,6 +243,25 @@ __device__ inline void stage_issue(const BwdArgs& a, const typename S::raw* xb, 
   const int64_t L = a.L, C = a.C;
   const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
   if constexpr (!CL) {
+    constexpr int ES = sizeof(typename S::raw);
+    if (a.off24 && c0 + 64 <= C && t0 >= V && t0 + LdsGeom<S>::T + V <= L) {
+      // An interior tile: every vector exists.  A wave-uniform base plus a 24-bit
+      // byte offset per lane (one multiply-add).
+      const uintptr_t xw = reinterpret_cast<uintptr_t>(xb + c0 * a.x_sc + (t0 - V));
+      const uintptr_t gw = reinterpret_cast<uintptr_t>(gb + c0 * a.d_sc + t0);
+      const uint32_t xs = (uint32_t)(a.x_sc * ES), gs = (uint32_t)(a.d_sc * ES);
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const uint32_t q = (uint32_t)ln + 64u * i, r = q / NX;
+        st.x[i] = gload<u32x4>(xw + (__umul24(r, xs) + (q - r * NX) * 16u));
+      }
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const uint32_t q = (uint32_t)ln + 64u * i, r = q / NG;
+        st.g[i] = gload<u32x4>(gw + (__umul24(r, gs) + (q - r * NG) * 16u));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int q = ln + 64 * i, r = q / NX;
@@ -311,7 +330,9 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   using raw = typename S::raw;
   using G = LdsGeom<S>;
   constexpr int V = G::V, H = K - 1, NS = 64 / V;
-  constexpr bool PREFETCH = !SEQ;
+  // Prefetch where a work item has several tiles (channel-last) and the walk reads
+  // nothing from memory (no seq_idx).
+  constexpr bool PREFETCH = !SEQ && CL;
   __shared__ uint32_t lds[G::WORDS];
   raw* lx = reinterpret_cast<raw*>(lds);
   raw* lg = lx + (CL ? G::XN * 64 : 64 * G::XP);
@@ -348,6 +369,18 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   int64_t dx_t0 = -1;
   int dx_n = 0;
   auto store_dx = [&](int ln) {
+    if constexpr (!CL) {
+      if (a.off24 && c0 + 64 <= C && dx_n == G::T) {   // as the interior staging
+        const uintptr_t dw = reinterpret_cast<uintptr_t>(db + c0 * a.g_sc + dx_t0);
+        const uint32_t ds = (uint32_t)(a.g_sc * sizeof(raw));
+#pragma unroll
+        for (int i = 0; i < ND; ++i) {
+          const uint32_t q = (uint32_t)ln + 64u * i, r = q / ND;
+          gstore16(dw + (__umul24(r, ds) + (q - r * ND) * 16u), dxv[i]);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       if constexpr (!CL) {
@@ -402,6 +435,10 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     }
     dx_t0 = t0;
     dx_n = (int)((t0 + a.T < L ? t0 + a.T : L) - t0);
+    if constexpr (!PREFETCH) {                     // no load in flight: store at once
+      store_dx(ln);
+      dx_t0 = -1;
+    }
   }
   if (dx_t0 >= 0) store_dx(lane);
   if (c < C) store_partials<K>(a, b, g, c, pw, pb);

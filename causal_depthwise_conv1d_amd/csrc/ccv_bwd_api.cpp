@@ -10,6 +10,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "ccv.h"
 #include "ccv_bwd_launch.hpp"
 #include "ccv_checks.hpp"
@@ -158,6 +160,7 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   g.ngr = ngr;
   g.lanes = lanes;
   g.w_dtype = a->w_dtype;
+  g.off24 = std::max({a->x_stride[1], a->dout_stride[1], a->dx_stride[1]}) < (int64_t)(1 << 24) / es;
 
   BwdReduceArgs& r = p->r;
   r.in = g.part;

@@ -31,6 +31,7 @@ struct BwdArgs {
   int64_t di_b, di_c, di_i;     // dinitial_states
   int64_t T, ntt, tpi, ngr, lanes;  // tile length, tiles per row, tiles per group, groups per row, B*ngr*C
   int32_t w_dtype;
+  int32_t off24;            // channel strides of x, dout and dx below 2^24 bytes (24-bit lane offsets)
 };
 
 // Reduction over the partial rows, a tree of fixed shape: each level sums groups
