@@ -216,6 +216,11 @@ __device__ inline void lds_put16(void* p, u32x4 v) {
   for (int i = 0; i < 4; ++i) d[i] = dword(v, i);
 }
 
+// A 16-byte store through a global-address-space pointer made from an integer address.
+__device__ inline void gstore16(uintptr_t addr, u32x4 v) {
+  *reinterpret_cast<u32x4 __attribute__((address_space(1)))*>(addr) = v;
+}
+
 __device__ inline u32x4 lds_get16(const void* p) {
   const uint32_t* d = static_cast<const uint32_t*>(p);
   return u32x4{d[0], d[1], d[2], d[3]};

@@ -201,9 +201,6 @@ __device__ inline T gload(uintptr_t addr) {
 __device__ inline u32x4 gload16_stream(uintptr_t addr) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 __attribute__((address_space(1)))*>(addr));
 }
-__device__ inline void gstore16(uintptr_t addr, u32x4 v) {
-  *reinterpret_cast<u32x4 __attribute__((address_space(1)))*>(addr) = v;
-}
 __device__ inline void gstore16_stream(uintptr_t addr, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4 __attribute__((address_space(1)))*>(addr));
 }
