@@ -183,6 +183,18 @@ def test_bwd_random_shapes():
         check_bwd(w, dout, dfs, init, f"[random {i}]")
 
 
+def test_bwd_reduction_with_level_kernels():
+    """More than 512 partial rows: level kernels of the reduction tree run before the
+    final kernel (2500 rows -> 79 -> the final kernel's 3 waves), with a partial
+    group of 64 channels."""
+    for dtype, act in (("f32", None), ("bf16", "silu")):
+        w = build(2, 72, 40000, 3, dtype, "cf", 4700, init=True, act=act)
+        assert w.B * -(-w.L // tile_steps(dtype)) == 2500
+        dout, dfs = grad_inputs(w, "cf", True, 4700)
+        log(f"  bwd level kernels {dtype}: B=2 C=72 L=40000 K=3")
+        check_bwd(w, dout, dfs, True, f"[levels {dtype}]")
+
+
 def test_bwd_zero_length_sequence():
     """L = 0: dx is empty, d(initial_states) is dfinal_states passed through, and
     dweight / dbias are zero."""
