@@ -199,6 +199,7 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {gbps:.0f} GB/s")
 
     copy_gbps, empty_us = context_measurements(nbytes, dev, stream, args.steps)
+    flushed = flushed_timing(step, dev, stream, nbytes)
 
     kernel_key = ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
         f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}"
@@ -246,8 +247,10 @@ def main():
             "copy_same_bytes_GBps": round(copy_gbps, 1),
             "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
             "empty_kernel_us": round(empty_us, 3),
+            "flushed_calls": flushed,
             "device": props.name,
             "cu_count": props.multi_processor_count,
+            "device_properties": device_properties(props),
             "kernel_sources_sha256": sha,
         },
     }
@@ -297,6 +300,50 @@ def context_measurements(nbytes, dev, stream, steps):
     empty_us = ev0.elapsed_time(ev1)  # ms for 1000 launches = us per launch
     log(f"[bench] copy of the same bytes: {copy_gbps:.0f} GB/s; empty kernel {empty_us:.2f} us")
     return copy_gbps, empty_us
+
+
+def flushed_timing(step, dev, stream, nbytes, iters=20):
+    """Single calls with the caches flushed before each (a 1 GiB copy, more than the
+    256 MB Infinity Cache and the L2s), each between its own pair of HIP events:
+    median, min and max over `iters` calls.  Context beside the back-to-back figure."""
+    import ctypes
+
+    import torch
+
+    import causal_depthwise_conv1d_amd as ccv
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    calib = ctypes.CDLL(ccv.CALIB_LIB_PATH)
+    calib.ccv_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    half = 512 << 20
+    src = torch.zeros(half, dtype=torch.uint8, device=dev)
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = []
+    for i in range(iters):
+        calib.ccv_calib_copy(dst.data_ptr(), src.data_ptr(), half, sp)
+        ev0.record(stream)
+        step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us.append(ev0.elapsed_time(ev1) * 1e3)
+    del src, dst
+    us.sort()
+    med = us[len(us) // 2] if len(us) % 2 else 0.5 * (us[len(us) // 2 - 1] + us[len(us) // 2])
+    log(f"[bench] flushed single calls: median {med:.2f} us (min {us[0]:.2f}, max {us[-1]:.2f})")
+    return {"iters": iters, "median_us": round(med, 3), "min_us": round(us[0], 3), "max_us": round(us[-1], 3),
+            "median_GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}
+
+
+def device_properties(props) -> dict:
+    """What the runtime reports about the GPU (names vary across torch builds)."""
+    out = {}
+    for name in ("gcnArchName", "total_memory", "multi_processor_count", "L2_cache_size",
+                 "max_threads_per_multi_processor", "warp_size", "regs_per_multiprocessor",
+                 "shared_memory_per_multiprocessor", "clock_rate", "memory_clock_rate", "memory_bus_width"):
+        v = getattr(props, name, None)
+        if isinstance(v, (int, float, str)):
+            out[name] = v
+    return out
 
 
 def update_bytes(w) -> int:
