@@ -252,6 +252,7 @@ def main():
             "cu_count": props.multi_processor_count,
             "device_properties": device_properties(props),
             "kernel_sources_sha256": sha,
+            "env_overrides": env_overrides(),
         },
     }
 
@@ -300,6 +301,13 @@ def context_measurements(nbytes, dev, stream, steps):
     empty_us = ev0.elapsed_time(ev1)  # ms for 1000 launches = us per launch
     log(f"[bench] copy of the same bytes: {copy_gbps:.0f} GB/s; empty kernel {empty_us:.2f} us")
     return copy_gbps, empty_us
+
+
+def env_overrides() -> dict:
+    """The library's tuning / ablation environment variables set for this run (none
+    in a default run; any set here change the launch the numbers come from)."""
+    names = ("CCV_CF_WAVES_PER_CU", "CCV_CL_WAVES_PER_CU", "CCV_CL_TILE_T", "CCV_CU_COUNT", "CCV_FORCE_SCALAR")
+    return {n: os.environ[n] for n in names if n in os.environ}
 
 
 def flushed_timing(step, dev, stream, nbytes, iters=20):
@@ -466,6 +474,7 @@ def bench_update(args, dev, props):
             "device": props.name,
             "cu_count": props.multi_processor_count,
             "kernel_sources_sha256": sha,
+            "env_overrides": env_overrides(),
         },
     }
     if not args.no_cpu_baseline:
@@ -606,6 +615,7 @@ def bench_bwd(args, dev, props):
             "device": props.name,
             "cu_count": props.multi_processor_count,
             "kernel_sources_sha256": sha,
+            "env_overrides": env_overrides(),
         },
     }
     print(json.dumps(result), flush=True)
