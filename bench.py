@@ -200,6 +200,7 @@ def main():
 
     copy_gbps, empty_us = context_measurements(nbytes, dev, stream, args.steps)
     flushed = flushed_timing(step, dev, stream, nbytes)
+    graph = graph_timing(fwd, arg_refs, nsets, nbytes)
 
     kernel_key = ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
         f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}"
@@ -248,6 +249,7 @@ def main():
             "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
             "empty_kernel_us": round(empty_us, 3),
             "flushed_calls": flushed,
+            "graph_replay": graph,
             "device": props.name,
             "cu_count": props.multi_processor_count,
             "device_properties": device_properties(props),
@@ -301,6 +303,35 @@ def context_measurements(nbytes, dev, stream, steps):
     empty_us = ev0.elapsed_time(ev1)  # ms for 1000 launches = us per launch
     log(f"[bench] copy of the same bytes: {copy_gbps:.0f} GB/s; empty kernel {empty_us:.2f} us")
     return copy_gbps, empty_us
+
+
+def graph_timing(fwd, arg_refs, nsets, nbytes, calls=100, reps=5):
+    """The same calls (rotating over the buffer sets) captured in one HIP graph of
+    `calls` launches and replayed `reps` times: time per call with the host's launch
+    cost taken out, which is what a launch-bound caller gets from a graph."""
+    import ctypes
+
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(calls):
+            rc = fwd(arg_refs[i % nsets], s)
+            if rc != 0:
+                raise RuntimeError(f"ccv_fwd returned {rc} while capturing")
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / (calls * reps)
+    del g
+    log(f"[bench] graph replay: {us:.2f} us per call ({calls} calls per graph)")
+    return {"calls_per_graph": calls, "replays": reps, "us_per_call": round(us, 3),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def env_overrides() -> dict:
