@@ -1,4 +1,5 @@
-"""The three calls captured in a HIP graph (torch.cuda.graph) and replayed.
+"""The three calls captured in a HIP graph (torch.cuda.graph) and replayed, and
+issued on concurrent streams.
 
 None of them clears memory with a memset or allocates inside the library: the
 forward and the update are one kernel each, the backward its gradient kernel and
@@ -132,3 +133,29 @@ def test_backward_graph_replays_equal_eager(layout):
         log(f"  backward graph {layout} replay {r}")
         for name, got, want in zip(("dx", "dweight", "dbias", "dinit"), outs, ref):
             assert torch.equal(bits(got), bits(want)), (r, name)
+
+
+def test_calls_on_concurrent_streams_equal_sequential():
+    """The library keeps no state between calls: forwards and backwards issued on two
+    streams at once give the bits they give one at a time."""
+    B, C, L, K = 2, 256, 2048, 4
+    w = rand((C, K), "bf16", 7600, 2, 0.5)
+    b = rand((C,), "bf16", 7600, 3, 0.3)
+    xs = [rand((B, C, L), "bf16", 7601 + i, 0) for i in range(4)]
+    douts = [rand((B, C, L), "bf16", 7611 + i, 4) for i in range(4)]
+    ref_f = [ccv.causal_conv1d_fwd(x, w, b, activation="silu") for x in xs]
+    ref_b = [ccv.causal_conv1d_bwd(x, w, b, d, activation="silu") for x, d in zip(xs, douts)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    got_f, got_b = [None] * 4, [None] * 4
+    for i in range(4):
+        with torch.cuda.stream(streams[i % 2]):
+            got_f[i] = ccv.causal_conv1d_fwd(xs[i], w, b, activation="silu")
+            got_b[i] = ccv.causal_conv1d_bwd(xs[i], w, b, douts[i], activation="silu")
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.equal(bits(got_f[i]), bits(ref_f[i])), i
+        for name, g_, r_ in zip(("dx", "dweight", "dbias"), got_b[i][:3], ref_b[i][:3]):
+            assert torch.equal(bits(g_), bits(r_)), (i, name)
