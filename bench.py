@@ -584,7 +584,7 @@ def bench_bwd(args, dev, props):
 
     step(0)
     torch.cuda.synchronize()
-    parity = bwd_parity(w, dout_cpu, sets[0][2], dweight, dbias)
+    parity = bwd_parity(w, dout_cpu, sets[0][2], dweight, dbias, plan)
     log(f"[bench] bwd parity: {parity}")
     for i in range(args.warmup):
         step(i)
@@ -652,20 +652,26 @@ def bench_bwd(args, dev, props):
     print(json.dumps(result), flush=True)
 
 
-def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias):
+def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias, plan):
     """One backward call against the oracle's fp64 gradients (every dx element,
-    every dweight / dbias element), with the tolerances of the GPU tests."""
+    every dweight / dbias element), with the tolerances of the GPU tests: for the
+    parameter gradients (n + 32 * levels + K + 8) / 4 roundings, n the terms of a
+    lane's in-order sum (the register-only channel-first path: span / 64 plus 6
+    butterfly levels; the others: tiles per partial row times the tile length)."""
     from oracle import compare as ocmp
     from oracle.from_torch import bwd, case, dtype_name, raw
 
     c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
     r = bwd(c, dout_cpu, None)
-    T = 32                                             # time steps per backward tile
-    tpi = 4 if (w.x.stride(1) == 1 or w.C <= 1) and not (w.x.stride(2) == 1 and w.L > 1) else 1
-    parts, levels = w.B * max(1, math.ceil(math.ceil(w.L / T) / tpi)), 1  # a row per tpi tiles
+    span, tpi = plan["span"], plan["unroll"]
+    if plan["vector"] == 3:
+        n, parts = span // 64 + 6, w.B * max(1, math.ceil(w.L / span))
+    else:
+        n, parts = tpi * span, w.B * max(1, math.ceil(math.ceil(w.L / span) / tpi))
+    levels = 1
     while parts > 32:                                  # levels of the fan-in-32 reduction tree
         parts, levels = -(-parts // 32), levels + 1
-    pk = math.ceil((tpi * T + 32 * levels + w.K + 8) / 4)
+    pk = math.ceil((n + 32 * levels + w.K + 8) / 4)
     out = {}
     for name, got, ref, scale, kk in (("dx", dx_gpu, r["dx"], r["ex"], w.K + 2),
                                       ("dweight", dweight, r["dw"], r["ew"], pk),

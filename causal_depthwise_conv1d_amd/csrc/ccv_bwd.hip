@@ -449,6 +449,301 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   if (c < C) store_partials<K>(a, b, g, c, pw, pb);
 }
 
+// ---- channel-first, registers only ------------------------------------------------
+//
+// For x, dout and dx unit-stride in time (16-byte aligned rows, L a multiple of V)
+// and no seq_idx.  The forward's channel-first layout of work: a segment is
+// 64 lanes x U vectors x V steps of one (b, c) row; lane l holds vectors
+// l, l + 64, ..., so every load and store moves 1 KB of consecutive addresses.
+// The K-1 inputs before a lane's vector come from lane l-1 (DPP shift right) or,
+// for lane 0, from lane 63 of the previous vector or the segment's history; z
+// and dz are recomputed per element exactly as in walk_tile.  dx needs the dz of
+// the K-1 steps after the element: from lane l+1 (DPP shift left), for lane 63
+// from lane 0 of the next vector, and for the segment's last vector from dz
+// recomputed over the K-1 steps past the segment.  So dx comes out with the same
+// bits as in the other paths.  The parameter gradients: each lane sums its
+// elements in step order, then a 64-lane xor butterfly (the same bits in every
+// lane) gives the segment's sum, written as one partial row per (b, segment).
+constexpr int kBwdRegUnroll = 4;                  // vectors per lane and segment
+
+// Lane l receives lane l+1's value; lane 63 receives `carry`.  DPP wave_shl:1.
+__device__ inline float shift_out(float carry, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, carry), __builtin_bit_cast(int, v), 0x130, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes; every lane ends with the same bits (partners add the same
+// two values).
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Everything one segment reads, loaded ahead of its arithmetic: the lane's x and
+// dout vectors, the vectors just past the segment, the K-1 inputs before it, the
+// channel's parameters (as the aligned dwords that hold them, so that the loads do
+// not depend on the weight dtype) and dfinal_states.  Absent data loads from the
+// zero array; nothing is converted until the arithmetic.
+template <class S, int K>
+struct RegLoads {
+  u32x4 xv[kBwdRegUnroll], gv[kBwdRegUnroll], hx, hg;
+  typename S::raw hist[K - 1], dfs[K - 1];
+  uint32_t w[K], bias;
+};
+
+struct RegPos {
+  int64_t b, c, seg;
+};
+
+template <class S, int K, bool EDGE>
+__device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, RegLoads<S, K>& q) {
+  using raw = typename S::raw;
+  constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U, ES = sizeof(raw);
+  const int64_t L = a.L;
+  const int64_t t0 = p.seg * SPAN, t1 = t0 + SPAN;
+  const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
+  const raw* xr = static_cast<const raw*>(a.x) + p.b * a.x_sb + p.c * a.x_sc;
+  const raw* gr = static_cast<const raw*>(a.dout) + p.b * a.d_sb + p.c * a.d_sc;
+  const uint32_t lo = (uint32_t)lane * (V * ES);
+  const uintptr_t xs = reinterpret_cast<uintptr_t>(xr + t0), gs = reinterpret_cast<uintptr_t>(gr + t0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t o = lo + (uint32_t)(u * 64 * V * ES);
+    if constexpr (EDGE) {
+      const bool ok = t0 + (int64_t)(u * 64 + lane) * V < L;
+      q.xv[u] = gload<u32x4>(pick(ok, xs + o, zero));
+      q.gv[u] = gload<u32x4>(pick(ok, gs + o, zero));
+    } else {                                       // every vector and the halo lie inside the row
+      q.xv[u] = gload<u32x4>(xs + o);
+      q.gv[u] = gload<u32x4>(gs + o);
+    }
+  }
+  if constexpr (EDGE) {
+    q.hx = gload<u32x4>(pick(t1 < L, reinterpret_cast<uintptr_t>(xr + t1), zero));
+    q.hg = gload<u32x4>(pick(t1 < L, reinterpret_cast<uintptr_t>(gr + t1), zero));
+  } else {
+    q.hx = gload<u32x4>(reinterpret_cast<uintptr_t>(xr + t1));
+    q.hg = gload<u32x4>(reinterpret_cast<uintptr_t>(gr + t1));
+  }
+  const uintptr_t ir = reinterpret_cast<uintptr_t>(static_cast<const raw*>(a.init) + p.b * a.is_b + p.c * a.is_c);
+  const uintptr_t fr = reinterpret_cast<uintptr_t>(static_cast<const raw*>(a.dfs) + p.b * a.fs_b + p.c * a.fs_c);
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const int64_t src = t0 - H + j;
+    const uintptr_t from_init = pick(a.init != nullptr, ir + (src + H) * a.is_i * ES, zero);
+    q.hist[j] = gload<raw>(pick(src >= 0, reinterpret_cast<uintptr_t>(xr + src), from_init));
+    q.dfs[j] = gload<raw>(pick(a.dfs != nullptr, fr + j * a.fs_i * ES, zero));
+  }
+  const int64_t wb = a.w_dtype == CCV_DT_F32 ? 4 : 2;
+  const uintptr_t wl = reinterpret_cast<uintptr_t>(a.w) + p.c * K * wb;
+#pragma unroll
+  for (int k = 0; k < K; ++k) q.w[k] = gload<uint32_t>((wl + k * wb) & ~(uintptr_t)3);
+  q.bias = gload<uint32_t>(pick(a.bias != nullptr, (reinterpret_cast<uintptr_t>(a.bias) + p.c * wb) & ~(uintptr_t)3, zero));
+}
+
+// A parameter from the aligned dword that holds it (element i of the array).
+__device__ inline float reg_param(uint32_t d, int dtype, int64_t i) {
+  if (dtype == CCV_DT_F32) return __builtin_bit_cast(float, d);
+  const uint32_t h = (i & 1) ? d >> 16 : d & 0xffffu;
+  return dtype == CCV_DT_BF16 ? __builtin_bit_cast(float, h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// The arithmetic and stores of one segment from its loads.  EDGE = false: the
+// segment's outputs and the K-1 steps past it lie inside the row
+// (t0 + span + K - 1 <= L), so no position needs a check and dfinal_states does not
+// reach it; EDGE = true: the row's last segment(s), every check in place.
+template <class S, int K, bool SILU, bool EDGE>
+__device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, const RegLoads<S, K>& q) {
+  using raw = typename S::raw;
+  constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U, ES = sizeof(raw);
+  const int64_t L = a.L;
+  const int64_t b = p.b, c = p.c, seg = p.seg;
+  const int64_t t0 = seg * SPAN, t1 = t0 + SPAN;
+  const uint32_t lo = (uint32_t)lane * (V * ES);
+  raw* dxr = static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc;
+  const bool has_dfs = EDGE && a.dfs != nullptr;
+
+  float w[K], hist[H], dfs[H];
+#pragma unroll
+  for (int k = 0; k < K; ++k) w[k] = reg_param(q.w[k], a.w_dtype, c * K + k);
+  const float beta = a.bias ? reg_param(q.bias, a.w_dtype, c) : 0.0f;
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    hist[j] = S::to_f(q.hist[j]);
+    dfs[j] = S::to_f(q.dfs[j]);
+  }
+
+  float pw[K], pb = 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) pw[k] = 0.0f;
+  float carry[H];                                  // X~ of the H steps before lane 0's vector
+#pragma unroll
+  for (int j = 0; j < H; ++j) carry[j] = hist[j];
+  float dzp[V], dz0[H];                            // dz of the previous vector; lane 0's first H of vector 0
+
+  // dx of vector u with dz d[] and the dz of the H steps after each lane's vector
+  // (next[]), stored when inside [0, L).
+  auto put_dx = [&](int u, const float (&d)[V], const float (&next)[H]) {
+    const int64_t base = t0 + (int64_t)(u * 64 + lane) * V;
+    float y[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {                // output t = base + i + H - k uses tap k
+        const int j = i + H - k;
+        const float dv = j < V ? d[j] : next[j - V];
+        if (!EDGE || base + i + H - k < L) acc = __builtin_fmaf(w[k], dv, acc);
+      }
+      if (has_dfs) {                               // the last H steps take dfinal_states
+        const int64_t t = base + i;
+#pragma unroll
+        for (int m = 0; m < H; ++m)
+          if (t == L - H + m) acc += dfs[m];
+      }
+      y[i] = acc;
+    }
+    const u32x4 pk = S::pack(y);
+    if (!EDGE || base < L)
+      store16(reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(dxr + t0) + lo + u * 64 * V * ES), pk);
+  };
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool ok = !EDGE || t0 + (int64_t)(u * 64 + lane) * V < L;
+    float e[V], g[V];
+    S::unpack(q.xv[u], e);
+    S::unpack(q.gv[u], g);
+    float h[H];
+#pragma unroll
+    for (int j = 0; j < H; ++j) h[j] = shift_in(carry[j], e[V - H + j]);
+#pragma unroll
+    for (int j = 0; j < H; ++j) carry[j] = lane63(e[V - H + j]);
+    float dz[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float xk[K];                                 // X~[t - H + k]
+#pragma unroll
+      for (int k = 0; k < K; ++k) xk[k] = i - H + k >= 0 ? e[i - H + k] : h[i + k];
+      float z = beta;
+#pragma unroll
+      for (int k = 0; k < K; ++k) z = __builtin_fmaf(w[k], xk[k], z);
+      const float d = SILU ? g[i] * silu_slope(z) : g[i];
+      dz[i] = ok ? d : 0.0f;
+      if (ok) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) pw[k] = __builtin_fmaf(dz[i], xk[k], pw[k]);
+        pb += dz[i];
+      }
+    }
+    if (u == 0) {
+#pragma unroll
+      for (int m = 0; m < H; ++m)
+        dz0[m] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dz[m]), 0));
+    }
+    if (u > 0) {
+      float next[H];
+#pragma unroll
+      for (int m = 0; m < H; ++m)
+        next[m] = shift_out(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dz[m]), 0)),
+                            dzp[m]);
+      put_dx(u - 1, dzp, next);
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) dzp[i] = dz[i];
+  }
+  // dz of the H steps past the segment (zero past L), for the last vector's lane 63.
+  {
+    float e[V], g[V];
+    S::unpack(q.hx, e);
+    S::unpack(q.hg, g);
+    float hz[H];
+#pragma unroll
+    for (int m = 0; m < H; ++m) {
+      float z = beta;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int j = m - H + k;                   // relative to t1
+        z = __builtin_fmaf(w[k], j >= 0 ? e[j] : carry[H + j], z);
+      }
+      const float d = SILU ? g[m] * silu_slope(z) : g[m];
+      hz[m] = !EDGE || t1 < L ? d : 0.0f;
+    }
+    float next[H];
+#pragma unroll
+    for (int m = 0; m < H; ++m) next[m] = shift_out(hz[m], dzp[m]);
+    put_dx(U - 1, dzp, next);
+  }
+
+  // d(initial_states): the history positions j = -H .. -1 of the row's first segment.
+  if (t0 == 0 && a.dinit && lane < H) {
+    const int j = lane - H;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int t = j + H - k;                     // < H: in lane 0's first vector
+      float dv = 0.0f;
+#pragma unroll
+      for (int m = 0; m < H; ++m) dv = t == m ? dz0[m] : dv;
+      if (t >= 0 && t < L) acc = __builtin_fmaf(w[k], dv, acc);
+    }
+    if (has_dfs) {
+#pragma unroll
+      for (int m = 0; m < H; ++m)
+        if (j == L - H + m) acc += dfs[m];
+    }
+    static_cast<raw*>(a.dinit)[b * a.di_b + c * a.di_c + (j + H) * a.di_i] = S::from_f(acc);
+  }
+
+  // The segment's parameter gradients: one partial row entry per (b, segment).
+  float sw[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) sw[k] = wave_sum(pw[k]);
+  const float sb = wave_sum(pb);
+  if (lane == 0) {
+    float* part = a.part + ((b * a.ngr + seg) * (K + 1)) * a.C + c;
+#pragma unroll
+    for (int k = 0; k < K; ++k) part[k * a.C] = sw[k];
+    part[K * a.C] = sb;
+  }
+}
+
+// One segment: its loads, then its arithmetic, in the interior or the edge form.
+template <class S, int K, bool SILU>
+__device__ inline void reg_segment(const BwdArgs& a, const RegPos& p, int lane) {
+  RegLoads<S, K> q;
+  if ((p.seg + 1) * (64 * kBwdRegUnroll * S::V) + K - 1 <= a.L) {
+    reg_issue<S, K, false>(a, p, lane, q);
+    reg_compute<S, K, SILU, false>(a, p, lane, q);
+  } else {
+    reg_issue<S, K, true>(a, p, lane, q);
+    reg_compute<S, K, SILU, true>(a, p, lane, q);
+  }
+}
+
+__device__ inline RegPos reg_pos(const BwdArgs& a, int64_t i) {
+  const int64_t row = i / a.ntt;
+  const int64_t b = row / a.C;
+  return RegPos{b, row - b * a.C, i - row * a.ntt};
+}
+
+// Work item i = segment (row i / nseg, segment i % nseg), row = b * C + c; wave w
+// of the W launched takes items w, w + W, ...  A segment's loads are issued
+// together and waited for once; other waves' arithmetic hides that latency.  (Also
+// issuing the next segment's loads before the current one's arithmetic needs about
+// 100 more registers, halves the waves per CU, and measured slower.)
+template <class S, int K, bool SILU>
+__global__ void __launch_bounds__(kBwdBlock) bwd_cf_reg_kernel(const BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t W = (int64_t)gridDim.x * (kBwdBlock / 64);
+  const int64_t items = a.B * a.C * a.ntt;
+  for (int64_t i = (int64_t)blockIdx.x * (kBwdBlock / 64) + wave; i < items; i += W) {
+    reg_segment<S, K, SILU>(a, reg_pos(a, i), lane);
+  }
+}
+
 __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {
   if (dtype == CCV_DT_F32)
     static_cast<float*>(p)[i] = v;
@@ -516,7 +811,13 @@ int launch_one(const BwdArgs& a, int path, uint32_t grid, void* st) {
   void* args[] = {const_cast<BwdArgs*>(&a)};
   const void* fn;
   int block = 64;
-  if (path == kBwdPathLdsCf)
+  if (path == kBwdPathRegCf) {
+    if constexpr (SEQ) return (int)hipErrorInvalidValue;   // the host never asks for it
+    else {
+      fn = reinterpret_cast<const void*>(&bwd_cf_reg_kernel<S, K, SILU>);
+      block = kBwdBlock;
+    }
+  } else if (path == kBwdPathLdsCf)
     fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, false>);
   else if (path == kBwdPathLdsCl)
     fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, true>);
@@ -547,6 +848,8 @@ int launch_s(const BwdArgs& a, int K, bool silu, bool seq, int path, uint32_t gr
 }  // namespace
 
 int bwd_tile_steps(int dtype) { return dtype == CCV_DT_F32 ? LdsGeom<F32>::T : LdsGeom<BF16>::T; }
+
+int bwd_reg_span(int dtype) { return 64 * kBwdRegUnroll * (dtype == CCV_DT_F32 ? F32::V : BF16::V); }
 
 int launch_bwd(const BwdArgs& a, int dtype, int K, bool silu, bool seq, int path, uint32_t grid,
                void* stream) {

@@ -42,10 +42,13 @@ int choose_path(const ccv_bwd_args_t* a) {
     cf = cf && s[2] == 1 && stride_ok16(B, s[0], es) && stride_ok16(C, s[1], es);
     cl = cl && s[1] == 1 && stride_ok16(B, s[0], es) && stride_ok16(L, s[2], es);
   }
-  if (cf) return kBwdPathLdsCf;
+  if (cf) return a->seq_idx ? kBwdPathLdsCf : kBwdPathRegCf;
   if (cl) return kBwdPathLdsCl;
   return kBwdPathElement;
 }
+
+// Resident waves per CU the register-only channel-first kernel is launched for.
+constexpr int kRegWavesPerCu = 16;
 
 // Checks every argument and fills *p; the workspace fields are checked only when
 // `check_workspace` (ccv_bwd_workspace_size asks before there is one).
@@ -94,20 +97,35 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   int64_t bl;
   if (a->seq_idx && __builtin_mul_overflow(B, L, &bl)) return CCV_E_SHAPE;
 
-  // One lane per (b, group of kBwdTilesPerItem tiles, c); a row with L = 0 still
-  // has one tile, which writes d(initial_states) from dfinal_states.
-  const int64_t T = bwd_tile_steps(a->x_dtype);
+  // Tiles of T steps (a row with L = 0 still has one, which writes d(initial_states)
+  // from dfinal_states), grouped tpi to a partial row: one lane per (b, group, c) on
+  // the element path, one wave per (b, group, 64 channels) on the LDS paths.  The
+  // register-only channel-first path: segments of its own span, one per partial row,
+  // one wave per (b, c, segment).
+  const int path = rows ? choose_path(a) : kBwdPathElement;
+  const bool reg = path == kBwdPathRegCf;
+  const int64_t T = reg ? bwd_reg_span(a->x_dtype) : bwd_tile_steps(a->x_dtype);
   const int64_t ntt = L > 0 ? (L + T - 1) / T : 1;
   const bool channel_unit = (a->x_stride[1] == 1 || C <= 1) && !(a->x_stride[2] == 1 && L > 1);
-  const int64_t tpi = channel_unit ? kBwdTilesPerItem : 1;
+  const int64_t tpi = channel_unit && !reg ? kBwdTilesPerItem : 1;
   const int64_t ngr = (ntt + tpi - 1) / tpi;
   int64_t nparts, lanes, ws;
   if (__builtin_mul_overflow(B, ngr, &nparts) || __builtin_mul_overflow(nparts, C, &lanes) ||
       __builtin_mul_overflow(nparts + bwd_reduce_rows(nparts), (int64_t)(K + 1) * C * 4, &ws))
     return CCV_E_SHAPE;
-  const int path = rows ? choose_path(a) : kBwdPathElement;
-  const int64_t items = path == kBwdPathElement ? lanes : nparts * ((C + 63) / 64);
-  const int64_t grid = path == kBwdPathElement ? (lanes + kBwdBlock - 1) / kBwdBlock : items;
+  const int64_t waves_per_group = kBwdBlock / 64;
+  int64_t items, grid;
+  if (path == kBwdPathElement) {
+    items = lanes;
+    grid = (lanes + kBwdBlock - 1) / kBwdBlock;
+  } else if (reg) {
+    items = lanes;                                  // B * C * segments
+    const int64_t cap = (int64_t)cu_count() * kRegWavesPerCu;
+    grid = ((items < cap ? items : cap) + waves_per_group - 1) / waves_per_group;
+  } else {
+    items = nparts * ((C + 63) / 64);
+    grid = items;
+  }
   // Reduction launches: level kernels while more rows are left than the final kernel
   // takes (the first is the largest), then the final kernel, 64 columns per workgroup
   // (it also runs for B = 0, to write zeros).
@@ -199,10 +217,10 @@ int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan) {
   const int st = validate(args, &p, false);      // a plan is wanted before the workspace exists
   if (st != CCV_OK || !plan) return st;
   *plan = ccv_plan_t{};
-  const bool lds = p.path != kBwdPathElement;
+  const bool lds = p.path == kBwdPathLdsCf || p.path == kBwdPathLdsCl;
   plan->path = p.grid || p.rgrid ? CCV_PATH_BACKWARD : CCV_PATH_NONE;
-  plan->vector = lds ? p.path : 0;
-  plan->elems_per_lane = 1;
+  plan->vector = p.path;
+  plan->elems_per_lane = p.path == kBwdPathRegCf ? 16 / elt_size(args->x_dtype) : 1;
   plan->unroll = (int32_t)p.a.tpi;
   plan->grid = p.grid;
   plan->block = lds ? 64 : kBwdBlock;

@@ -67,7 +67,13 @@ constexpr int kBwdFinalWaves = 16;  // waves of the final reduction kernel's wor
 // which need x, dout and dx unit-stride in the same dimension (time for CF,
 // channels for CL), 16-byte aligned bases and strides, and L (CF) or C (CL) a
 // multiple of 16 / element size.
-enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2 };
+enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2, kBwdPathRegCf = 3 };
+
+// The register-only channel-first path (no seq_idx; the layout conditions of the
+// LDS channel-first path): work items are segments of bwd_reg_span(dtype) steps of
+// one (b, c) row, numbered row-major; a partial row per (b, segment); a grid of
+// kBwdBlock-lane workgroups, each wave taking items w, w + waves, ...
+int bwd_reg_span(int dtype);
 
 // Time steps per tile T for a dtype (32 for all three; both paths use the same T,
 // so their partial sums, and so dweight and dbias, are identical).

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -13,6 +14,15 @@ namespace ccv {
 namespace checks {
 
 inline int elt_size(int dt) { return dt == CCV_F32 ? 4 : 2; }
+
+// Compute units of the GPU the launches go to.  Plans must not touch a device
+// (the checks run on machines without one), so this is a fixed property of the
+// target: MI355X has 256 CUs.  CCV_CU_COUNT overrides it for other parts.
+inline int cu_count() {
+  const char* v = getenv("CCV_CU_COUNT");
+  const int n = v && *v ? atoi(v) : 256;
+  return n > 0 ? n : 256;
+}
 
 // Largest element offset of an [n0, n1, n2] view with strides s (all >= 0), or
 // -1 when it does not fit in int64.

@@ -352,8 +352,16 @@ def test_bwd_workspace_size_is_the_partial_sums():
     # one fp32 row of (K + 1) * C partial sums per (b, tile group), plus the rows the
     # level kernels of the reduction tree write while more than 512 rows are left (the
     # final kernel sums up to 16 groups of 32 at once)
-    # channel-first: a row per tile of 32 steps
+    # channel-first without seq_idx: the register path, a row per segment of 2048
+    # (16-bit) or 1024 (fp32) steps
     a = bargs(B=3, C=100, L=1000, K=3, ws=False)
+    assert ccv.ccv_bwd_workspace_size(a) == 3 * 100 * (3 + 1) * 4
+    a = bargs(B=2, C=128, L=1 << 20, K=3, ws=False)
+    a.x_dtype = ccv.CCV_F32
+    parts = 2 * (1 << 20) // 1024                    # 2048 -> 64, then the final kernel
+    assert ccv.ccv_bwd_workspace_size(a) == (parts + 64) * 128 * 4 * 4
+    # channel-first with seq_idx: the LDS path, a row per tile of 32 steps
+    a = bargs(B=3, C=100, L=1000, K=3, ws=False, seq_idx=SEQ)
     parts = 3 * -(-1000 // 32)                       # 96 rows: the final kernel alone
     assert ccv.ccv_bwd_workspace_size(a) == parts * 100 * (3 + 1) * 4
     # channel-last: a row per group of 4 tiles
@@ -361,13 +369,9 @@ def test_bwd_workspace_size_is_the_partial_sums():
     parts = 3 * -(-(-(-1000 // 32)) // 4)            # 24 rows: one level
     assert ccv.ccv_bwd_workspace_size(a) == parts * 100 * (3 + 1) * 4
     assert ccv.ccv_bwd_workspace_size(bargs(B=2, C=5, L=0, ws=False)) == 2 * 1 * 5 * 5 * 4
-    a = bargs(B=2, C=128, L=1 << 20, K=3, ws=False)
-    a.x_dtype = ccv.CCV_F32
-    parts = 2 * (1 << 20) // 32                      # 65536 -> 2048 -> 64, then the final kernel
-    assert ccv.ccv_bwd_workspace_size(a) == (parts + 2048 + 64) * 128 * 4 * 4
-    a = bargs(B=1, C=8, L=512 * 32, K=2, ws=False)  # 512 rows: the final kernel alone
+    a = bargs(B=1, C=8, L=512 * 128, K=2, layout="cl", ws=False)   # 512 rows: the final kernel alone
     assert ccv.ccv_bwd_workspace_size(a) == 512 * 8 * 3 * 4
-    a = bargs(B=1, C=8, L=513 * 32, K=2, ws=False)  # 513 rows -> 17 -> final
+    a = bargs(B=1, C=8, L=513 * 128, K=2, layout="cl", ws=False)   # 513 rows -> 17 -> final
     assert ccv.ccv_bwd_workspace_size(a) == (513 + 17) * 8 * 3 * 4
     assert ccv.ccv_bwd_workspace_size(bargs(B=0, ws=False)) == 0
     assert ccv.ccv_bwd_workspace_size(bargs(K=5, ws=False)) == ccv.lib().ccv_bwd_check(bargs(K=5, ws=False))
@@ -425,19 +429,27 @@ def test_bwd_empty_extents():
 
 
 def test_bwd_plan():
-    # aligned channel-first: the LDS-staged channel-first kernel, a 64-lane workgroup
-    # per (b, tile of 32 steps, group of 64 channels)
+    # aligned channel-first without seq_idx: the register-only kernel, one wave per
+    # (b, c, segment of 2048 bf16 steps), 16 waves per CU in workgroups of 4
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096))
-    assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD and p.vector == 1
-    assert p.span == 32 and p.unroll == 1
+    assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD and p.vector == 3
+    assert p.span == 2048 and p.unroll == 1 and p.elems_per_lane == 8
+    assert p.work_items == 4 * 2048 * 2 and p.grid == 256 * 16 // 4 and p.block == 256
+    # with seq_idx: the LDS-staged channel-first kernel, a 64-lane workgroup per
+    # (b, tile of 32 steps, group of 64 channels)
+    st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, seq_idx=SEQ))
+    assert st == 0 and p.vector == 1 and p.span == 32 and p.unroll == 1
     assert p.work_items == 4 * 128 * 32 and p.grid == p.work_items and p.block == 64
     # aligned channel-last: the LDS-staged channel-last kernel, 4 tiles per work item
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, layout="cl"))
     assert st == 0 and p.vector == 2 and p.unroll == 4 and p.work_items == 4 * 32 * 32
-    # fp32 tiles are 32 steps too
+    # fp32: segments of 1024 steps on the register path, tiles of 32 on the LDS paths
     a = bargs(B=1, C=64, L=100, ws=False)
     a.x_dtype = ccv.CCV_F32
     a.workspace, a.workspace_bytes = WS, ccv.ccv_bwd_workspace_size(a)
+    st, p = ccv.ccv_bwd_plan(a)
+    assert st == 0 and p.span == 1024 and p.vector == 3 and p.work_items == 64 and p.grid == 16
+    a.seq_idx = SEQ
     st, p = ccv.ccv_bwd_plan(a)
     assert st == 0 and p.span == 32 and p.vector == 1
     # unaligned or mixed layouts: the element kernel, one lane per (b, tile, c)

@@ -65,31 +65,45 @@ def reduction_levels(parts):
     return levels
 
 
-def tiles_per_item(x):
-    """Tiles summed into one partial row: 4 when x is unit-stride in channels."""
-    B, C, L = x.shape
-    return 4 if (x.stride(1) == 1 or C <= 1) and not (x.stride(2) == 1 and L > 1) else 1
+def bwd_plan(x, weight, dout, seq=None):
+    """The launch ccv_bwd makes for these tensors (dx in x's layout)."""
+    C, K = weight.shape
+    args = ccv.make_bwd_args(x, weight, None, dout, ccv.empty_like_layout(x),
+                             torch.empty(C, K, dtype=weight.dtype, device="cuda"), seq_idx=seq)
+    st, plan = ccv.ccv_bwd_plan(args)
+    assert st == 0, st
+    return plan
 
 
-def param_terms(w, tpi=None):
-    """compare()'s K for the parameter gradients: (tpi T + 32 * levels + K + 8) / 4
-    roundings of 2^-22 cover a lane's sum over its tpi tiles, the levels of the
-    fan-in-32 reduction tree over the partial rows, and the error of dz."""
-    T = tile_steps(w.x_dtype)
-    tpi = tiles_per_item(w.x) if tpi is None else tpi
-    parts = w.B * max(1, math.ceil(math.ceil(w.L / T) / tpi))
-    return math.ceil((tpi * T + 32 * reduction_levels(parts) + w.K + 8) / 4)
+def param_terms_for(plan, B, L, K):
+    """compare()'s K for the parameter gradients: (n + 32 * levels + K + 8) / 4
+    roundings of 2^-22 cover a lane's in-order sum of n terms, the levels of the
+    fan-in-32 reduction tree over the partial rows, and the error of dz.  The
+    register-only channel-first path: n = its span / 64 elements plus 6 levels of
+    the lane butterfly, a partial row per segment; the other paths: n = the tiles
+    per partial row times the tile length."""
+    if plan.vector == 3:
+        n, parts = plan.span // 64 + 6, B * max(1, math.ceil(L / plan.span))
+    else:
+        n, parts = plan.unroll * plan.span, B * max(1, math.ceil(math.ceil(L / plan.span) / plan.unroll))
+    return math.ceil((n + 32 * reduction_levels(parts) + K + 8) / 4)
+
+
+def param_terms(w, plan):
+    return param_terms_for(plan, w.B, w.L, w.K)
 
 
 def check_bwd(w, dout, dfs, want_dinit, where):
     dx, dw, db, dinit = run_bwd(w, dout, dfs, want_dinit)
+    plan = bwd_plan(to_gpu_view(w.x_storage, w.x), w.weight.cuda(), dout.cuda(),
+                    None if w.seq_idx is None else w.seq_idx.cuda())
     c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
     r = oracle_bwd(c, dout, dfs)
     K = w.K
     checks = [("dx", dx, r["dx"], r["ex"], K + 2)]
     if want_dinit:
         checks.append(("dinit", dinit, r["dinit"], r["einit"], K + 2))
-    pk = param_terms(w)
+    pk = param_terms(w, plan)
     checks.append(("dweight", dw, r["dw"], r["ew"], pk))
     if w.bias is not None:
         checks.append(("dbias", db, r["db"], r["eb"], pk))
@@ -141,10 +155,13 @@ def test_bwd_matches_oracle(dtype, K, layout):
 
 @pytest.mark.parametrize("layout", ["cf", "cl"])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_bwd_lds_path_equals_element_path(dtype, layout, monkeypatch):
-    """The LDS-staged kernels (chosen for aligned unit-stride layouts) and the
-    element kernel give the same bits for every gradient: a ragged last tile, a
-    partial group of 64 channels, history, dfinal_states and seq_idx."""
+def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
+    """The kernels chosen for aligned unit-stride layouts against the element
+    kernel, with a ragged last tile, a partial group of 64 channels, history,
+    dfinal_states and seq_idx: dx and d(initial_states) have the same bits on every
+    path.  The LDS kernels (channel-last; channel-first with seq_idx) also give the
+    same dweight and dbias bits; the register-only channel-first kernel sums the
+    parameter gradients in another order, so there they meet the oracle's bound."""
     T = tile_steps(dtype)
     for K in KS:
         for f in (dict(init=True, dfs=True), dict(seq=7)):
@@ -152,18 +169,23 @@ def test_bwd_lds_path_equals_element_path(dtype, layout, monkeypatch):
             w = build(B, C, L, K, dtype, layout, 5100 + K, seq=f.get("seq"), init=f.get("init", False))
             dout, dfs = grad_inputs(w, layout, f.get("dfs", False), 5100 + K)
             res = []
-            for force, want in (("0", 1 if layout == "cf" else 2), ("1", 0)):
+            fast = (1 if f.get("seq") else 3) if layout == "cf" else 2
+            for force, want in (("0", fast), ("1", 0)):
                 monkeypatch.setenv("CCV_FORCE_SCALAR", force)
                 x = to_gpu_view(w.x_storage, w.x)
                 args = ccv.make_bwd_args(x, w.weight.cuda(), w.bias.cuda(), dout.cuda(), ccv.empty_like_layout(x),
-                                         torch.empty(C, K, dtype=w.weight.dtype, device="cuda"))
+                                         torch.empty(C, K, dtype=w.weight.dtype, device="cuda"),
+                                         seq_idx=None if w.seq_idx is None else w.seq_idx.cuda())
                 st, plan = ccv.ccv_bwd_plan(args)
                 assert st == 0 and plan.vector == want, (force, plan.as_dict())
                 res.append(run_bwd(w, dout, dfs, bool(f.get("init"))))
             bits = torch.int32 if dtype == "f32" else torch.int16
             for name, t0, t1 in zip(("dx", "dweight", "dbias", "dinit"), *res):
-                if t0 is not None:
+                if t0 is not None and (fast != 3 or name in ("dx", "dinit")):
                     assert torch.equal(t0.view(bits), t1.view(bits)), (K, f, name)
+            if fast == 3:
+                monkeypatch.setenv("CCV_FORCE_SCALAR", "0")
+                check_bwd(w, dout, dfs, bool(f.get("init")), f"[register path K={K}]")
 
 
 def test_bwd_random_shapes():
@@ -186,13 +208,17 @@ def test_bwd_random_shapes():
 def test_bwd_reduction_with_level_kernels():
     """More than 512 partial rows: level kernels of the reduction tree run before the
     final kernel (2500 rows -> 79 -> the final kernel's 3 waves), with a partial
-    group of 64 channels."""
+    group of 64 channels; and the register-only path with 2048 partial rows."""
     for dtype, act in (("f32", None), ("bf16", "silu")):
-        w = build(2, 72, 40000, 3, dtype, "cf", 4700, init=True, act=act)
+        w = build(2, 72, 40000, 3, dtype, "cf", 4700, init=True, act=act, seq=3)   # the LDS path
         assert w.B * -(-w.L // tile_steps(dtype)) == 2500
         dout, dfs = grad_inputs(w, "cf", True, 4700)
         log(f"  bwd level kernels {dtype}: B=2 C=72 L=40000 K=3")
         check_bwd(w, dout, dfs, True, f"[levels {dtype}]")
+    w = build(2, 72, 1024 * 1024, 3, "f32", "cf", 4710, init=True, act=None)   # 2 x 1024 segments
+    dout, dfs = grad_inputs(w, "cf", True, 4710)
+    log("  bwd register path, 2048 partial rows: B=2 C=72 L=1M K=3")
+    check_bwd(w, dout, dfs, True, "[levels register path]")
 
 
 def test_bwd_zero_length_sequence():
@@ -219,7 +245,7 @@ def test_bwd_repeat_runs_bit_identical():
 def test_bwd_layout_independent(dtype):
     """The same logical problem stored channel-first and channel-last (x, dout and
     dx): dx and d(initial_states) have the same bits (the per-element arithmetic
-    does not depend on the strides); dweight and dbias, summed over tiles grouped
+    does not depend on the strides); dweight and dbias, summed in a different order
     per layout, each meet the oracle's bound."""
     w = build(2, 72, 300, 4, dtype, "cf", 4700, init=True)
     dout, dfs = grad_inputs(w, "cf", True, 4700)
@@ -230,8 +256,9 @@ def test_bwd_layout_independent(dtype):
     def cl(t):
         return t.transpose(1, 2).contiguous().transpose(1, 2)
 
-    res = []
+    res, plans = [], []
     for xv, gv in ((x, dout.cuda()), (cl(x), cl(dout.cuda()))):
+        plans.append(bwd_plan(xv, args[0], gv))
         out = ccv.causal_conv1d_bwd(xv, *args, gv, None, init, dfs, "silu", return_dinitial_states=True)
         torch.cuda.synchronize()
         assert out[0].stride() == xv.stride()                 # dx follows x's layout
@@ -245,8 +272,8 @@ def test_bwd_layout_independent(dtype):
             assert torch.equal(t0.view(bits), t1.view(bits)), name
             continue
         ref, scale = (r["dw"], r["ew"]) if name == "dweight" else (r["db"], r["eb"])
-        for t, tpi in ((t0, 1), (t1, 4)):          # channel-first, channel-last grouping
-            res_c = ocmp.compare(dtype_name(t), param_terms(w, tpi), raw(t), ref, scale)
+        for t, plan in zip((t0, t1), plans):
+            res_c = ocmp.compare(dtype_name(t), param_terms(w, plan), raw(t), ref, scale)
             assert res_c["n_bad"] == 0, (name, ocmp.describe_failures(res_c, ref, scale, raw(t), dtype_name(t)))
 
 
@@ -300,7 +327,7 @@ def test_autograd_function_matches_oracle():
         torch.cuda.synchronize()
         c = case(w.x, w.weight, w.bias, None, w.initial_states, "silu")
         r = oracle_bwd(c, dout, dfs)
-        pk = param_terms(w)
+        pk = param_terms(w, bwd_plan(x.detach(), weight.detach(), dout.cuda()))
         for name, got, ref, scale, kk in (("dx", x.grad, r["dx"], r["ex"], 6), ("dw", weight.grad, r["dw"], r["ew"], pk),
                                           ("db", bias.grad, r["db"], r["eb"], pk),
                                           ("dinit", init.grad, r["dinit"], r["einit"], 6)):
