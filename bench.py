@@ -41,18 +41,21 @@ KERNEL_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_cf.hip",
                   "causal_depthwise_conv1d_amd/csrc/ccv_cl.hip",
                   "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
-                  "causal_depthwise_conv1d_amd/csrc/ccv_api.cpp"]
+                  "causal_depthwise_conv1d_amd/csrc/ccv_api.cpp",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_checks.hpp"]
 BWD_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_bwd.hip",
                "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
                "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
                "causal_depthwise_conv1d_amd/csrc/ccv_bwd_launch.hpp",
-               "causal_depthwise_conv1d_amd/csrc/ccv_bwd_api.cpp"]
+               "causal_depthwise_conv1d_amd/csrc/ccv_bwd_api.cpp",
+               "causal_depthwise_conv1d_amd/csrc/ccv_checks.hpp"]
 BWD_METRIC = "causal conv1d bwd effective HBM GB/s and % of MI355X peak bandwidth"
 UPDATE_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_update.hip",
                   "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
                   "causal_depthwise_conv1d_amd/csrc/ccv_update_launch.hpp",
-                  "causal_depthwise_conv1d_amd/csrc/ccv_update_api.cpp"]
+                  "causal_depthwise_conv1d_amd/csrc/ccv_update_api.cpp",
+                  "causal_depthwise_conv1d_amd/csrc/ccv_checks.hpp"]
 
 
 def log(msg):

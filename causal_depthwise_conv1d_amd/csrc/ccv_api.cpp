@@ -15,11 +15,13 @@
 #include <stdlib.h>
 
 #include "ccv.h"
+#include "ccv_checks.hpp"
 #include "ccv_launch.hpp"
 
 namespace {
 
 using namespace ccv;
+using namespace ccv::checks;
 
 struct Plan {
   ccv_plan_t pub;
@@ -28,44 +30,10 @@ struct Plan {
   ClArgs cl;
 };
 
-inline int elt_size(int dt) { return dt == CCV_F32 ? 4 : 2; }
-
-// Largest element offset of a [n0, n1, n2] view with strides s (all >= 0), or -1
-// when it does not fit in int64.
-int64_t max_offset(int64_t n0, int64_t n1, int64_t n2, const int64_t s[3]) {
-  int64_t total = 0;
-  const int64_t n[3] = {n0, n1, n2};
-  for (int d = 0; d < 3; ++d) {
-    if (n[d] <= 1) continue;
-    int64_t p;
-    if (__builtin_mul_overflow(n[d] - 1, s[d], &p)) return -1;
-    if (__builtin_add_overflow(total, p, &total)) return -1;
-  }
-  return total;
-}
-
-bool fits_bytes(int64_t max_off, int es) {
-  int64_t bytes;
-  return max_off >= 0 && !__builtin_mul_overflow(max_off + 1, (int64_t)es, &bytes);
-}
-
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-// The element stride of a dimension keeps 16-byte alignment (or is never used).
-bool stride_ok16(int64_t n, int64_t s, int es) { return n <= 1 || ((s * es) & 15) == 0; }
-
 int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
   return atoi(v);
-}
-
-// Compute units of the GPU the launches go to.  The plan must not touch a device
-// (ccv_fwd_check runs on machines without one), so this is a fixed property of the
-// target: MI355X has 256 CUs.  CCV_CU_COUNT overrides it for other parts.
-int cu_count() {
-  const int n = env_int("CCV_CU_COUNT", 256);
-  return n > 0 ? n : 256;
 }
 
 // Checks every argument and fills *plan (never NULL) with the launch to make.
@@ -108,11 +76,12 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
   else return CCV_E_LAYOUT;
 
   const int es = elt_size(a->x_dtype);
-  const int64_t xo = max_offset(B, C, L, a->x_stride);
+  const int64_t nx[3] = {B, C, L}, ns[3] = {B, C, K - 1};
+  const int64_t xo = max_offset(nx, a->x_stride);
   if (!fits_bytes(xo, es)) return CCV_E_SHAPE;
-  if (want_out && !fits_bytes(max_offset(B, C, L, a->out_stride), es)) return CCV_E_SHAPE;
-  if (a->initial_states && !fits_bytes(max_offset(B, C, K - 1, a->init_stride), es)) return CCV_E_SHAPE;
-  if (a->final_states_out && !fits_bytes(max_offset(B, C, K - 1, a->final_stride), es)) return CCV_E_SHAPE;
+  if (want_out && !fits_bytes(max_offset(nx, a->out_stride), es)) return CCV_E_SHAPE;
+  if (a->initial_states && !fits_bytes(max_offset(ns, a->init_stride), es)) return CCV_E_SHAPE;
+  if (a->final_states_out && !fits_bytes(max_offset(ns, a->final_stride), es)) return CCV_E_SHAPE;
   int64_t bl;
   if (a->seq_idx && __builtin_mul_overflow(B, L, &bl)) return CCV_E_SHAPE;
 

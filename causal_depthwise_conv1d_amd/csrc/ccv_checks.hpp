@@ -1,6 +1,6 @@
-// ccv_checks.hpp -- host-side argument checks shared by the update and backward
-// entry points: element sizes, offset overflow, alignment and self-overlap of
-// strided views.  Host only, no HIP.
+// ccv_checks.hpp -- host-side argument checks shared by the forward, update and
+// backward entry points: element sizes, offset overflow, alignment and
+// self-overlap of strided views, and the target's CU count.  Host only, no HIP.
 #pragma once
 
 #include <stdint.h>
