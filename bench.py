@@ -659,8 +659,9 @@ def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias, plan):
     """One backward call against the oracle's fp64 gradients (every dx element,
     every dweight / dbias element), with the tolerances of the GPU tests: for the
     parameter gradients (n + 32 * levels + K + 8) / 4 roundings, n the terms of a
-    lane's in-order sum (the register-only channel-first path: span / 64 plus 6
-    butterfly levels; the others: tiles per partial row times the tile length)."""
+    lane's in-order sum (the register-only channel-first path: span / 64 plus the 7
+    additions of the 64-lane sum; the others: tiles per partial row times the tile
+    length)."""
     from oracle import compare as ocmp
     from oracle.from_torch import bwd, case, dtype_name, raw
 
@@ -668,7 +669,7 @@ def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias, plan):
     r = bwd(c, dout_cpu, None)
     span, tpi = plan["span"], plan["unroll"]
     if plan["vector"] == 3:
-        n, parts = span // 64 + 6, w.B * max(1, math.ceil(w.L / span))
+        n, parts = span // 64 + 7, w.B * max(1, math.ceil(w.L / span))
     else:
         n, parts = tpi * span, w.B * max(1, math.ceil(math.ceil(w.L / span) / tpi))
     levels = 1

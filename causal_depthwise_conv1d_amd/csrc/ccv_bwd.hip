@@ -17,7 +17,9 @@
 // stored.  The lane's partial sums over its group go to the workspace as one
 // row.  In the element kernel lanes take consecutive channels and read global
 // memory directly; in the LDS kernels a wave stages each tile of 64 channels in
-// LDS with 16-byte loads first (see bwd_lds_kernel).
+// LDS with 16-byte loads first (see bwd_lds_kernel).  For channel-first data
+// without seq_idx a third kernel keeps everything in registers: 64-lane segments
+// of one row with the halos passed between lanes (see bwd_cf_reg_kernel).
 //
 // Reduction kernel.  The partials of all (b, tile group) are summed per (tap or bias,
 // channel) by a tree of fixed shape: each level adds groups of kBwdFanIn
@@ -216,11 +218,6 @@ __device__ inline void lds_put16(void* p, u32x4 v) {
   for (int i = 0; i < 4; ++i) d[i] = dword(v, i);
 }
 
-// A 16-byte store through a global-address-space pointer made from an integer address.
-__device__ inline void gstore16(uintptr_t addr, u32x4 v) {
-  *reinterpret_cast<u32x4 __attribute__((address_space(1)))*>(addr) = v;
-}
-
 __device__ inline u32x4 lds_get16(const void* p) {
   const uint32_t* d = static_cast<const uint32_t*>(p);
   return u32x4{d[0], d[1], d[2], d[3]};
@@ -258,12 +255,12 @@ __device__ inline void stage_issue(const BwdArgs& a, const typename S::raw* xb, 
 #pragma unroll
       for (int i = 0; i < NX; ++i) {
         const uint32_t q = (uint32_t)ln + 64u * i, r = q / NX;
-        st.x[i] = gload<u32x4>(xw + (__umul24(r, xs) + (q - r * NX) * 16u));
+        st.x[i] = gload16_stream(xw + (__umul24(r, xs) + (q - r * NX) * 16u));
       }
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const uint32_t q = (uint32_t)ln + 64u * i, r = q / NG;
-        st.g[i] = gload<u32x4>(gw + (__umul24(r, gs) + (q - r * NG) * 16u));
+        st.g[i] = gload16_stream(gw + (__umul24(r, gs) + (q - r * NG) * 16u));
       }
       return;
     }
@@ -381,7 +378,7 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < ND; ++i) {
           const uint32_t q = (uint32_t)ln + 64u * i, r = q / ND;
-          gstore16(dw + (__umul24(r, ds) + (q - r * ND) * 16u), dxv[i]);
+          gstore16_stream(dw + (__umul24(r, ds) + (q - r * ND) * 16u), dxv[i]);
         }
         return;
       }
@@ -390,11 +387,11 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     for (int i = 0; i < ND; ++i) {
       if constexpr (!CL) {
         const int q = ln + 64 * i, r = q / ND, k = q - r * ND;
-        if (c0 + r < C && k * V < dx_n) store16(db + (c0 + r) * a.g_sc + dx_t0 + k * V, dxv[i]);
+        if (c0 + r < C && k * V < dx_n) store16_stream(db + (c0 + r) * a.g_sc + dx_t0 + k * V, dxv[i]);
       } else {
         const int64_t ck = c0 + (ln % NS) * V;
         const int s = ln / NS + i * V;
-        if (ck < C && s < dx_n) store16(db + (dx_t0 + s) * a.g_sl + ck, dxv[i]);
+        if (ck < C && s < dx_n) store16_stream(db + (dx_t0 + s) * a.g_sl + ck, dxv[i]);
       }
     }
   };
@@ -462,8 +459,13 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
 // from lane 0 of the next vector, and for the segment's last vector from dz
 // recomputed over the K-1 steps past the segment.  So dx comes out with the same
 // bits as in the other paths.  The parameter gradients: each lane sums its
-// elements in step order, then a 64-lane xor butterfly (the same bits in every
-// lane) gives the segment's sum, written as one partial row per (b, segment).
+// elements in step order, then a fixed-order 64-lane sum over DPP lane patterns
+// (wave_sum) gives the segment's sum in lane 0, written as one partial row per
+// (b, segment).
+// x and dout vectors and dx are touched once and use streaming (non-temporal)
+// accesses, as do the LDS kernels' interior staging loads and dx stores; the
+// vectors just past a segment, which the next segment reads again, are ordinary
+// loads.
 constexpr int kBwdRegUnroll = 4;                  // vectors per lane and segment
 
 // Lane l receives lane l+1's value; lane 63 receives `carry`.  DPP wave_shl:1.
@@ -472,12 +474,29 @@ __device__ inline float shift_out(float carry, float v) {
       __builtin_bit_cast(int, carry), __builtin_bit_cast(int, v), 0x130, 0xf, 0xf, false));
 }
 
-// Sum over the 64 lanes; every lane ends with the same bits (partners add the same
-// two values).
+// v plus the value of lane p(i) for the DPP lane pattern CTRL (row_mask and
+// bank_mask full: every lane reads a lane of its own row).
+template <int CTRL>
+__device__ inline float dpp_pair_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes in a fixed order, valid in lane 0.  Within each row of 16
+// lanes: swap neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), then
+// the half-row and row mirrors, each of which pairs a lane with one holding the
+// sum of the other quad / half; partners add the same two values, so after the
+// four steps every lane of a row holds the row's sum with the same bits.  Lane 0
+// then adds the sums of rows 1, 2 and 3 in that order.
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v = dpp_pair_add<0xB1>(v);
+  v = dpp_pair_add<0x4E>(v);
+  v = dpp_pair_add<0x141>(v);
+  v = dpp_pair_add<0x140>(v);
+  const int bits = __builtin_bit_cast(int, v);
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 48));
+  return ((v + r1) + r2) + r3;
 }
 
 // Everything one segment reads, loaded ahead of its arithmetic: the lane's x and
@@ -496,9 +515,15 @@ struct RegPos {
   int64_t b, c, seg;
 };
 
-template <class S, int K, bool EDGE>
+// Where a segment lies in its row: inside with the K-1 steps past it
+// (t0 + span + K - 1 <= L), ending exactly at L (every vector inside, nothing
+// past it), or anything else (the row's last, partial segment).
+enum { kSegInner = 0, kSegLast = 1, kSegEdge = 2 };
+
+template <class S, int K, int MODE>
 __device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, RegLoads<S, K>& q) {
   using raw = typename S::raw;
+  constexpr bool EDGE = MODE == kSegEdge;
   constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U, ES = sizeof(raw);
   const int64_t L = a.L;
   const int64_t t0 = p.seg * SPAN, t1 = t0 + SPAN;
@@ -512,16 +537,18 @@ __device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, Re
     const uint32_t o = lo + (uint32_t)(u * 64 * V * ES);
     if constexpr (EDGE) {
       const bool ok = t0 + (int64_t)(u * 64 + lane) * V < L;
-      q.xv[u] = gload<u32x4>(pick(ok, xs + o, zero));
-      q.gv[u] = gload<u32x4>(pick(ok, gs + o, zero));
+      q.xv[u] = gload16_stream(pick(ok, xs + o, zero));
+      q.gv[u] = gload16_stream(pick(ok, gs + o, zero));
     } else {                                       // every vector and the halo lie inside the row
-      q.xv[u] = gload<u32x4>(xs + o);
-      q.gv[u] = gload<u32x4>(gs + o);
+      q.xv[u] = gload16_stream(xs + o);
+      q.gv[u] = gload16_stream(gs + o);
     }
   }
   if constexpr (EDGE) {
     q.hx = gload<u32x4>(pick(t1 < L, reinterpret_cast<uintptr_t>(xr + t1), zero));
     q.hg = gload<u32x4>(pick(t1 < L, reinterpret_cast<uintptr_t>(gr + t1), zero));
+  } else if constexpr (MODE == kSegLast) {
+    q.hx = q.hg = u32x4{0u, 0u, 0u, 0u};         // nothing past L; not read
   } else {
     q.hx = gload<u32x4>(reinterpret_cast<uintptr_t>(xr + t1));
     q.hg = gload<u32x4>(reinterpret_cast<uintptr_t>(gr + t1));
@@ -549,13 +576,15 @@ __device__ inline float reg_param(uint32_t d, int dtype, int64_t i) {
   return dtype == CCV_DT_BF16 ? __builtin_bit_cast(float, h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// The arithmetic and stores of one segment from its loads.  EDGE = false: the
-// segment's outputs and the K-1 steps past it lie inside the row
-// (t0 + span + K - 1 <= L), so no position needs a check and dfinal_states does not
-// reach it; EDGE = true: the row's last segment(s), every check in place.
-template <class S, int K, bool SILU, bool EDGE>
+// The arithmetic and stores of one segment from its loads.  kSegInner: no
+// position needs a check and dfinal_states does not reach the segment.  kSegLast:
+// no position needs a check, but lane 63 of the last vector holds the row's last
+// H steps: it skips the taps that would read dz past L and adds dfinal_states,
+// exactly as the checked form does.  kSegEdge: every check in place.
+template <class S, int K, bool SILU, int MODE>
 __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, const RegLoads<S, K>& q) {
   using raw = typename S::raw;
+  constexpr bool EDGE = MODE == kSegEdge, LAST = MODE == kSegLast;
   constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U, ES = sizeof(raw);
   const int64_t L = a.L;
   const int64_t b = p.b, c = p.c, seg = p.seg;
@@ -563,6 +592,8 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
   const uint32_t lo = (uint32_t)lane * (V * ES);
   raw* dxr = static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc;
   const bool has_dfs = EDGE && a.dfs != nullptr;
+  const bool tail = LAST && lane == 63;            // the row's last H steps, in the last vector
+  const bool tail_dfs = tail && a.dfs != nullptr;
 
   float w[K], hist[H], dfs[H];
 #pragma unroll
@@ -586,6 +617,7 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
   // (next[]), stored when inside [0, L).
   auto put_dx = [&](int u, const float (&d)[V], const float (&next)[H]) {
     const int64_t base = t0 + (int64_t)(u * 64 + lane) * V;
+    const bool skip_next = LAST && u == U - 1 && tail;
     float y[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -594,7 +626,12 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
       for (int k = 0; k < K; ++k) {                // output t = base + i + H - k uses tap k
         const int j = i + H - k;
         const float dv = j < V ? d[j] : next[j - V];
-        if (!EDGE || base + i + H - k < L) acc = __builtin_fmaf(w[k], dv, acc);
+        if (j >= V && LAST) {
+          const float f = __builtin_fmaf(w[k], dv, acc);
+          acc = skip_next ? acc : f;
+        } else if (!EDGE || base + i + H - k < L) {
+          acc = __builtin_fmaf(w[k], dv, acc);
+        }
       }
       if (has_dfs) {                               // the last H steps take dfinal_states
         const int64_t t = base + i;
@@ -602,11 +639,14 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
         for (int m = 0; m < H; ++m)
           if (t == L - H + m) acc += dfs[m];
       }
+      if (LAST && u == U - 1 && i >= V - H) {
+        if (tail_dfs) acc += dfs[i - (V - H)];
+      }
       y[i] = acc;
     }
     const u32x4 pk = S::pack(y);
     if (!EDGE || base < L)
-      store16(reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(dxr + t0) + lo + u * 64 * V * ES), pk);
+      store16_stream(reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(dxr + t0) + lo + u * 64 * V * ES), pk);
   };
 
 #pragma unroll
@@ -654,7 +694,13 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
     for (int i = 0; i < V; ++i) dzp[i] = dz[i];
   }
   // dz of the H steps past the segment (zero past L), for the last vector's lane 63.
-  {
+  if constexpr (LAST) {
+    const float none[H] = {};
+    float next[H];
+#pragma unroll
+    for (int m = 0; m < H; ++m) next[m] = shift_out(none[m], dzp[m]);
+    put_dx(U - 1, dzp, next);
+  } else {
     float e[V], g[V];
     S::unpack(q.hx, e);
     S::unpack(q.hg, g);
@@ -709,16 +755,20 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
   }
 }
 
-// One segment: its loads, then its arithmetic, in the interior or the edge form.
+// One segment: its loads, then its arithmetic, in the form for where it lies.
 template <class S, int K, bool SILU>
 __device__ inline void reg_segment(const BwdArgs& a, const RegPos& p, int lane) {
   RegLoads<S, K> q;
-  if ((p.seg + 1) * (64 * kBwdRegUnroll * S::V) + K - 1 <= a.L) {
-    reg_issue<S, K, false>(a, p, lane, q);
-    reg_compute<S, K, SILU, false>(a, p, lane, q);
+  const int64_t t1 = (p.seg + 1) * (64 * kBwdRegUnroll * S::V);
+  if (t1 + K - 1 <= a.L) {
+    reg_issue<S, K, kSegInner>(a, p, lane, q);
+    reg_compute<S, K, SILU, kSegInner>(a, p, lane, q);
+  } else if (t1 == a.L) {
+    reg_issue<S, K, kSegLast>(a, p, lane, q);
+    reg_compute<S, K, SILU, kSegLast>(a, p, lane, q);
   } else {
-    reg_issue<S, K, true>(a, p, lane, q);
-    reg_compute<S, K, SILU, true>(a, p, lane, q);
+    reg_issue<S, K, kSegEdge>(a, p, lane, q);
+    reg_compute<S, K, SILU, kSegEdge>(a, p, lane, q);
   }
 }
 
@@ -728,20 +778,19 @@ __device__ inline RegPos reg_pos(const BwdArgs& a, int64_t i) {
   return RegPos{b, row - b * a.C, i - row * a.ntt};
 }
 
-// Work item i = segment (row i / nseg, segment i % nseg), row = b * C + c; wave w
-// of the W launched takes items w, w + W, ...  A segment's loads are issued
-// together and waited for once; other waves' arithmetic hides that latency.  (Also
-// issuing the next segment's loads before the current one's arithmetic needs about
-// 100 more registers, halves the waves per CU, and measured slower.)
+// Work item i = segment (row i / nseg, segment i % nseg), row = b * C + c, one
+// wave per item: the hardware keeps as many waves resident as the registers allow
+// and starts the next as one ends.  A segment's loads are issued together and
+// waited for once; other waves' arithmetic hides that latency.  (Issuing the next
+// segment's loads before the current one's arithmetic, in a wave that loops over
+// items, needs about 100 more registers, halves the waves per CU, and measured
+// slower; so did a fixed grid of 16 resident waves per CU looping over items.)
 template <class S, int K, bool SILU>
 __global__ void __launch_bounds__(kBwdBlock) bwd_cf_reg_kernel(const BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t W = (int64_t)gridDim.x * (kBwdBlock / 64);
-  const int64_t items = a.B * a.C * a.ntt;
-  for (int64_t i = (int64_t)blockIdx.x * (kBwdBlock / 64) + wave; i < items; i += W) {
-    reg_segment<S, K, SILU>(a, reg_pos(a, i), lane);
-  }
+  const int64_t i = (int64_t)blockIdx.x * (kBwdBlock / 64) + wave;
+  if (i < a.B * a.C * a.ntt) reg_segment<S, K, SILU>(a, reg_pos(a, i), lane);
 }
 
 __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {

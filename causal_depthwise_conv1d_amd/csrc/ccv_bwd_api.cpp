@@ -47,9 +47,6 @@ int choose_path(const ccv_bwd_args_t* a) {
   return kBwdPathElement;
 }
 
-// Resident waves per CU the register-only channel-first kernel is launched for.
-constexpr int kRegWavesPerCu = 16;
-
 // Checks every argument and fills *p; the workspace fields are checked only when
 // `check_workspace` (ccv_bwd_workspace_size asks before there is one).
 int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
@@ -119,9 +116,8 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
     items = lanes;
     grid = (lanes + kBwdBlock - 1) / kBwdBlock;
   } else if (reg) {
-    items = lanes;                                  // B * C * segments
-    const int64_t cap = (int64_t)cu_count() * kRegWavesPerCu;
-    grid = ((items < cap ? items : cap) + waves_per_group - 1) / waves_per_group;
+    items = lanes;                                  // B * C * segments, one wave each
+    grid = (items + waves_per_group - 1) / waves_per_group;
   } else {
     items = nparts * ((C + 63) / 64);
     grid = items;

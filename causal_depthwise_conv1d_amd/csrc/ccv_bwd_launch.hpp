@@ -72,7 +72,7 @@ enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2, kBwdPathRegCf 
 // The register-only channel-first path (no seq_idx; the layout conditions of the
 // LDS channel-first path): work items are segments of bwd_reg_span(dtype) steps of
 // one (b, c) row, numbered row-major; a partial row per (b, segment); a grid of
-// kBwdBlock-lane workgroups, each wave taking items w, w + waves, ...
+// kBwdBlock-lane workgroups, one wave per item.
 int bwd_reg_span(int dtype);
 
 // Time steps per tile T for a dtype (32 for all three; both paths use the same T,

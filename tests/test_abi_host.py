@@ -430,11 +430,11 @@ def test_bwd_empty_extents():
 
 def test_bwd_plan():
     # aligned channel-first without seq_idx: the register-only kernel, one wave per
-    # (b, c, segment of 2048 bf16 steps), 16 waves per CU in workgroups of 4
+    # (b, c, segment of 2048 bf16 steps), in workgroups of 4
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096))
     assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD and p.vector == 3
     assert p.span == 2048 and p.unroll == 1 and p.elems_per_lane == 8
-    assert p.work_items == 4 * 2048 * 2 and p.grid == 256 * 16 // 4 and p.block == 256
+    assert p.work_items == 4 * 2048 * 2 and p.grid == 4 * 2048 * 2 // 4 and p.block == 256
     # with seq_idx: the LDS-staged channel-first kernel, a 64-lane workgroup per
     # (b, tile of 32 steps, group of 64 channels)
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, seq_idx=SEQ))

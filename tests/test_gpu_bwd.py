@@ -79,11 +79,11 @@ def param_terms_for(plan, B, L, K):
     """compare()'s K for the parameter gradients: (n + 32 * levels + K + 8) / 4
     roundings of 2^-22 cover a lane's in-order sum of n terms, the levels of the
     fan-in-32 reduction tree over the partial rows, and the error of dz.  The
-    register-only channel-first path: n = its span / 64 elements plus 6 levels of
-    the lane butterfly, a partial row per segment; the other paths: n = the tiles
+    register-only channel-first path: n = its span / 64 elements plus the 7 additions of
+    the 64-lane sum, a partial row per segment; the other paths: n = the tiles
     per partial row times the tile length."""
     if plan.vector == 3:
-        n, parts = plan.span // 64 + 6, B * max(1, math.ceil(L / plan.span))
+        n, parts = plan.span // 64 + 7, B * max(1, math.ceil(L / plan.span))
     else:
         n, parts = plan.unroll * plan.span, B * max(1, math.ceil(math.ceil(L / plan.span) / plan.unroll))
     return math.ceil((n + 32 * reduction_levels(parts) + K + 8) / 4)
@@ -158,34 +158,41 @@ def test_bwd_matches_oracle(dtype, K, layout):
 def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
     """The kernels chosen for aligned unit-stride layouts against the element
     kernel, with a ragged last tile, a partial group of 64 channels, history,
-    dfinal_states and seq_idx: dx and d(initial_states) have the same bits on every
+    dfinal_states and seq_idx, and (register path) rows that end inside a segment or
+    exactly at a segment's end: dx and d(initial_states) have the same bits on every
     path.  The LDS kernels (channel-last; channel-first with seq_idx) also give the
     same dweight and dbias bits; the register-only channel-first kernel sums the
     parameter gradients in another order, so there they meet the oracle's bound."""
     T = tile_steps(dtype)
+    span = 64 * 4 * (4 if dtype == "f32" else 8)        # the register path's segment
     for K in KS:
         for f in (dict(init=True, dfs=True), dict(seq=7)):
-            B, C, L = 2, 136, 4 * T + 8
-            w = build(B, C, L, K, dtype, layout, 5100 + K, seq=f.get("seq"), init=f.get("init", False))
-            dout, dfs = grad_inputs(w, layout, f.get("dfs", False), 5100 + K)
-            res = []
-            fast = (1 if f.get("seq") else 3) if layout == "cf" else 2
-            for force, want in (("0", fast), ("1", 0)):
-                monkeypatch.setenv("CCV_FORCE_SCALAR", force)
-                x = to_gpu_view(w.x_storage, w.x)
-                args = ccv.make_bwd_args(x, w.weight.cuda(), w.bias.cuda(), dout.cuda(), ccv.empty_like_layout(x),
-                                         torch.empty(C, K, dtype=w.weight.dtype, device="cuda"),
-                                         seq_idx=None if w.seq_idx is None else w.seq_idx.cuda())
-                st, plan = ccv.ccv_bwd_plan(args)
-                assert st == 0 and plan.vector == want, (force, plan.as_dict())
-                res.append(run_bwd(w, dout, dfs, bool(f.get("init"))))
-            bits = torch.int32 if dtype == "f32" else torch.int16
-            for name, t0, t1 in zip(("dx", "dweight", "dbias", "dinit"), *res):
-                if t0 is not None and (fast != 3 or name in ("dx", "dinit")):
-                    assert torch.equal(t0.view(bits), t1.view(bits)), (K, f, name)
-            if fast == 3:
-                monkeypatch.setenv("CCV_FORCE_SCALAR", "0")
-                check_bwd(w, dout, dfs, bool(f.get("init")), f"[register path K={K}]")
+            # the register path: one partial segment; one segment ending at L; an inner
+            # segment then one ending at L; an inner segment then a partial one
+            Ls = [4 * T + 8] + ([span, 2 * span, span + 40] if layout == "cf" and not f.get("seq") else [])
+            for L in Ls:
+                B, C = 2, 136
+                log(f"  bwd fast vs element {dtype} {layout} K={K} L={L} {f}")
+                w = build(B, C, L, K, dtype, layout, 5100 + K, seq=f.get("seq"), init=f.get("init", False))
+                dout, dfs = grad_inputs(w, layout, f.get("dfs", False), 5100 + K)
+                res = []
+                fast = (1 if f.get("seq") else 3) if layout == "cf" else 2
+                for force, want in (("0", fast), ("1", 0)):
+                    monkeypatch.setenv("CCV_FORCE_SCALAR", force)
+                    x = to_gpu_view(w.x_storage, w.x)
+                    args = ccv.make_bwd_args(x, w.weight.cuda(), w.bias.cuda(), dout.cuda(), ccv.empty_like_layout(x),
+                                             torch.empty(C, K, dtype=w.weight.dtype, device="cuda"),
+                                             seq_idx=None if w.seq_idx is None else w.seq_idx.cuda())
+                    st, plan = ccv.ccv_bwd_plan(args)
+                    assert st == 0 and plan.vector == want, (force, plan.as_dict())
+                    res.append(run_bwd(w, dout, dfs, bool(f.get("init"))))
+                bits = torch.int32 if dtype == "f32" else torch.int16
+                for name, t0, t1 in zip(("dx", "dweight", "dbias", "dinit"), *res):
+                    if t0 is not None and (fast != 3 or name in ("dx", "dinit")):
+                        assert torch.equal(t0.view(bits), t1.view(bits)), (K, L, f, name)
+                if fast == 3:
+                    monkeypatch.setenv("CCV_FORCE_SCALAR", "0")
+                    check_bwd(w, dout, dfs, bool(f.get("init")), f"[register path K={K} L={L}]")
 
 
 def test_bwd_random_shapes():
