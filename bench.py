@@ -401,9 +401,10 @@ def update_bytes(w) -> int:
 
 
 def bench_update(args, dev, props):
-    """The update (decode) call on the decode workload: one parity-checked call,
-    then W warm-up and K timed calls rotating over >= 1 GiB of (x, state, out)
-    sets, so every call reads its inputs from HBM."""
+    """The update (decode) call on the decode workload: a first call whose output
+    and new state the cpu_baseline leg checks against the oracle, then W warm-up
+    and K timed calls rotating over >= 1 GiB of (x, state, out) sets, so every call
+    reads its inputs from HBM."""
     import ctypes
 
     import torch
@@ -435,13 +436,13 @@ def bench_update(args, dev, props):
     upd = ccv.lib().ccv_update
     refs = [ctypes.byref(s[3]) for s in sets]
 
-    # One call checked against the oracle before the states start to move.
+    # The first call's output and new state, kept for the check against the oracle
+    # in the cpu_baseline leg (before the states start to move).
     rc = upd(refs[0], sp)
     if rc != 0:
         raise RuntimeError(ccv.ccv_status_str(rc))
     torch.cuda.synchronize()
-    parity = update_parity(w, sets[0][2], sets[0][1])
-    log(f"[bench] update parity: {parity}")
+    first_out, first_state = sets[0][2].cpu(), sets[0][1].cpu()
 
     def step(i):
         rc = upd(refs[i % nsets], sp)
@@ -500,7 +501,6 @@ def bench_update(args, dev, props):
             "avg_launch_us": round(ms_per_step * 1e3, 3),
             "algorithmic_bytes_per_launch": nbytes,
         },
-        "parity": parity,
         "context": {
             "copy_same_bytes_GBps": round(copy_gbps, 1),
             "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
@@ -512,7 +512,7 @@ def bench_update(args, dev, props):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = update_cpu_baseline(w, nbytes, args.cpu_seconds)
+        result["cpu_baseline"] = update_cpu_baseline(w, nbytes, args.cpu_seconds, first_out, first_state)
     print(json.dumps(result), flush=True)
 
 
@@ -532,9 +532,9 @@ def bwd_bytes(w) -> int:
 
 
 def bench_bwd(args, dev, props):
-    """The backward on the chosen workload's shape: one call checked against the
-    oracle, then W warm-up and K timed calls rotating over >= 1 GiB of (x, dout,
-    dx) sets."""
+    """The backward on the chosen workload's shape: a first call whose gradients
+    the cpu_baseline leg checks against the oracle, then W warm-up and K timed
+    calls rotating over >= 1 GiB of (x, dout, dx) sets."""
     import ctypes
 
     import torch
@@ -585,10 +585,11 @@ def bench_bwd(args, dev, props):
         if rc != 0:
             raise RuntimeError(ccv.ccv_status_str(rc))
 
+    # The first call's gradients, kept for the check against the oracle in the
+    # cpu_baseline leg.
     step(0)
     torch.cuda.synchronize()
-    parity = bwd_parity(w, dout_cpu, sets[0][2], dweight, dbias, plan)
-    log(f"[bench] bwd parity: {parity}")
+    first = (sets[0][2].cpu(), dweight.cpu(), None if dbias is None else dbias.cpu())
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -641,7 +642,6 @@ def bench_bwd(args, dev, props):
             "avg_launch_us": round(ms_per_step * 1e3, 3),
             "algorithmic_bytes_per_launch": nbytes,
         },
-        "parity": parity,
         "context": {
             "copy_same_bytes_GBps": round(copy_gbps, 1),
             "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
@@ -652,21 +652,21 @@ def bench_bwd(args, dev, props):
             "env_overrides": env_overrides(),
         },
     }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = bwd_cpu_baseline(w, dout_cpu, nbytes, args.cpu_seconds, first, plan)
     print(json.dumps(result), flush=True)
 
 
-def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias, plan):
-    """One backward call against the oracle's fp64 gradients (every dx element,
-    every dweight / dbias element), with the tolerances of the GPU tests: for the
+def bwd_parity(w, r, first, plan):
+    """The first backward call's gradients against the oracle's fp64 result r (every
+    dx, dweight and dbias element), with the tolerances of the GPU tests: for the
     parameter gradients (n + 32 * levels + K + 8) / 4 roundings, n the terms of a
     lane's in-order sum (the register-only channel-first path: span / 64 plus the 7
     additions of the 64-lane sum; the others: tiles per partial row times the tile
     length)."""
     from oracle import compare as ocmp
-    from oracle.from_torch import bwd, case, dtype_name, raw
+    from oracle.from_torch import dtype_name, raw
 
-    c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
-    r = bwd(c, dout_cpu, None)
     span, tpi = plan["span"], plan["unroll"]
     if plan["vector"] == 3:
         n, parts = span // 64 + 7, w.B * max(1, math.ceil(w.L / span))
@@ -676,17 +676,42 @@ def bwd_parity(w, dout_cpu, dx_gpu, dweight, dbias, plan):
     while parts > 32:                                  # levels of the fan-in-32 reduction tree
         parts, levels = -(-parts // 32), levels + 1
     pk = math.ceil((n + 32 * levels + w.K + 8) / 4)
+    dx, dweight, dbias = first
     out = {}
-    for name, got, ref, scale, kk in (("dx", dx_gpu, r["dx"], r["ex"], w.K + 2),
+    for name, got, ref, scale, kk in (("dx", dx, r["dx"], r["ex"], w.K + 2),
                                       ("dweight", dweight, r["dw"], r["ew"], pk),
                                       ("dbias", dbias, r["db"], r["eb"], pk)):
         if got is None:
             continue
-        g = got.cpu().contiguous()
+        g = got.contiguous()
         res = ocmp.compare(dtype_name(g), kk, raw(g), ref, scale)
         out[name] = {"n": res["n"], "out_of_tolerance": res["n_bad"], "max_ulp": res["max_ulp"],
                      "max_rel": res["max_rel"]}
     return out
+
+
+def bwd_cpu_baseline(w, dout_cpu, nbytes, min_seconds, first, plan):
+    """The oracle's backward as written (single-threaded fp64 loops: dx, dweight,
+    dbias and their error scales) on this host's CPU over the whole workload,
+    repeated until at least `min_seconds` have passed; then the first GPU call's
+    gradients checked against it."""
+    from oracle.from_torch import bwd, case
+
+    c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
+    passes, t_total, r = 0, 0.0, None
+    while passes == 0 or t_total < min_seconds:
+        t0 = time.perf_counter()
+        r = bwd(c, dout_cpu, None)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    sec = t_total / passes
+    log(f"[bench] cpu oracle bwd: {passes} passes, {sec:.2f} s per pass")
+    parity = bwd_parity(w, r, first, plan)
+    log(f"[bench] bwd parity: {parity}")
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload ({w.B * w.C * w.L} elements), {passes} pass(es) of the "
+                      "single-threaded fp64 oracle backward (dx, dweight, dbias and their error scales)",
+            "seconds_per_pass": round(sec, 3), "parity": parity}
 
 
 def update_parity(w, out_gpu, state_gpu):
@@ -709,9 +734,10 @@ def update_parity(w, out_gpu, state_gpu):
             "state_bit_exact": bool(np.array_equal(got.view(bits), want.view(bits)))}
 
 
-def update_cpu_baseline(w, nbytes, min_seconds):
+def update_cpu_baseline(w, nbytes, min_seconds, first_out, first_state):
     """The oracle as written for one update call (its forward with the state as
-    initial states, plus the final states), repeated for at least `min_seconds`."""
+    initial states, plus the final states), repeated for at least `min_seconds`;
+    then the first GPU call's output and new state checked against it."""
     from oracle import round_out
     from oracle.from_torch import case
 
@@ -725,10 +751,12 @@ def update_cpu_baseline(w, nbytes, min_seconds):
         t_total += time.perf_counter() - t0
         passes += 1
     sec = t_total / passes
+    parity = update_parity(w, first_out, first_state)
+    log(f"[bench] update parity: {parity}")
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole decode call ({w.B * w.C} rows), {passes} passes of the single-threaded "
                       "fp64 oracle incl. rounding and the new state",
-            "seconds_per_pass": round(sec, 4)}
+            "seconds_per_pass": round(sec, 4), "parity": parity}
 
 
 def cpu_baseline(w, out_gpu, nbytes, min_seconds):
