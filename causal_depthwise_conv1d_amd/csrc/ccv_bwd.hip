@@ -341,7 +341,10 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
 
   const int lane = threadIdx.x;
   const int64_t ncg = (a.C + 63) / 64;
-  const int64_t item = blockIdx.x;
+  // Channel-last: each XCD takes one contiguous range of items (neighbouring channel
+  // groups of the same rows, and the next tile group's halo rows), as in the
+  // channel-last forward; channel-first keeps the hardware's round-robin order.
+  const int64_t item = CL ? xcd_order(blockIdx.x, gridDim.x >> 3, gridDim.x & 7) : blockIdx.x;
   const int64_t bg = item / ncg;
   const int64_t c0 = (item - bg * ncg) * 64;
   const int64_t b = bg / a.ngr;
