@@ -44,7 +44,9 @@ __device__ inline float silu_slope(float z) {
 
 // The walk of one lane over one tile (see the header comment), shared by both
 // kernels so that they compute the same bits.  `src` gives X~ at positions
-// >= t0 - K + 1 (history included), dout at positions >= t0, and takes dx.
+// >= t0 - K + 1 (history included), dout at positions >= t0, the sequence id at
+// positions in [0, L) from t0 - K + 1 to t0 + T + K - 2 (and at 0 when t0 = 0),
+// and takes dx.
 // FULL (a tile of TT steps with t0 + TT + K - 1 <= L, not writing
 // d(initial_states)) fixes the trip count and every condition at compile time,
 // so the walk unrolls completely; the arithmetic is the same.
@@ -55,9 +57,8 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
   constexpr int H = K - 1;
   const int64_t L = a.L;
   const int64_t t_end = FULL ? t0 + TT : (t0 + a.T < L ? t0 + a.T : L);
-  const int32_t* sr = SEQ ? a.seq + b * L : nullptr;
   const bool has_init = a.init != nullptr;       // with seq_idx: the history is the first sequence's
-  const int hist_id = (SEQ && has_init && L > 0) ? sr[0] : 0;
+  const int hist_id = (SEQ && has_init && L > 0 && t0 < H) ? src.id(0) : 0;   // read left of t = 0 only
 
   // Slots 0 .. H-1 hold positions u-H .. u-1 before step u; slot H takes u.
   float xw[K], dzw[K];
@@ -66,7 +67,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
   for (int i = 0; i < H; ++i) {
     const int64_t j = t0 - H + i;
     xw[i] = src.x(j);
-    idw[i] = SEQ ? (j >= 0 ? sr[j] : hist_id) : 0;
+    idw[i] = SEQ ? (j >= 0 ? src.id(j) : hist_id) : 0;
     dzw[i] = 0.0f;                                 // dz left of the tile is never read
   }
   const int64_t n_steps = FULL ? TT + H : t_end + H - t0;
@@ -78,7 +79,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
     int idu = 0;
     if (FULL || u < L) {
       xu = src.x(u);
-      if constexpr (SEQ) idu = sr[u];
+      if constexpr (SEQ) idu = src.id(u);
       bool keep[H];
       float z = beta;
 #pragma unroll
@@ -113,7 +114,7 @@ __device__ inline void walk_tile(const BwdArgs& a, int64_t b, int64_t c, int64_t
         const bool keep = (FULL || (t >= 0 && t < L)) && (!SEQ || idw[0] == idw[H - k]);
         if (keep) acc = __builtin_fmaf(w[k], dzw[H - k], acc);
       }
-      if (!FULL && a.dfs && j >= L - H && (!SEQ || L == 0 || idw[0] == sr[L - 1]))
+      if (!FULL && a.dfs && j >= L - H && (!SEQ || L == 0 || idw[0] == src.id(L - 1)))
         acc += S::to_f(static_cast<const raw*>(a.dfs)[b * a.fs_b + c * a.fs_c + (j - (L - H)) * a.fs_i]);
       if (FULL || j >= 0)                          // a whole tile never reaches left of t = 0
         src.put_dx(j, acc);
@@ -148,6 +149,7 @@ struct GlobalSrc {
   const raw* gr;
   raw* dxr;
   const raw* init;          // the row's initial_states, or nullptr
+  const int32_t* sr;        // the row of seq_idx, or nullptr
   int64_t x_sl, d_sl, g_sl, is_i;
   __device__ float x(int64_t p) const {
     if (p >= 0) return S::to_f(xr[p * x_sl]);
@@ -155,6 +157,7 @@ struct GlobalSrc {
   }
   __device__ float g(int64_t p) const { return S::to_f(gr[p * d_sl]); }
   __device__ void put_dx(int64_t j, float v) const { dxr[j * g_sl] = S::from_f(v); }
+  __device__ int id(int64_t p) const { return sr[p]; }
 };
 
 template <class S, int K, bool SILU, bool SEQ>
@@ -170,7 +173,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_kernel(const BwdArgs a) {
                       static_cast<const raw*>(a.dout) + b * a.d_sb + c * a.d_sc,
                       static_cast<raw*>(a.dx) + b * a.g_sb + c * a.g_sc,
                       a.init ? static_cast<const raw*>(a.init) + b * a.is_b + c * a.is_c : nullptr,
-                      a.x_sl, a.d_sl, a.g_sl, a.is_i};
+                      SEQ ? a.seq + b * a.L : nullptr, a.x_sl, a.d_sl, a.g_sl, a.is_i};
   float w[K], pw[K], pb = 0.0f;
   load_params<K>(a.w, a.w_dtype, c * K, w);
   const float beta = a.bias ? load_param(a.bias, a.w_dtype, c) : 0.0f;
@@ -206,10 +209,14 @@ struct LdsSrc {
   using raw = typename S::raw;
   raw* xs;                 // this lane's channel in the staged x tile, at position t0 - V
   const raw* gs;           // ... in the staged dout tile, at position t0
+  const int32_t* ids;      // the staged sequence ids, at position t0 - V (with seq_idx)
   int64_t t0;              // PS: elements between consecutive positions
   __device__ float x(int64_t p) const { return S::to_f(xs[(p - t0 + S::V) * PS]); }
   __device__ float g(int64_t p) const { return S::to_f(gs[(p - t0) * PS]); }
   __device__ void put_dx(int64_t j, float v) const { xs[(j - t0 + S::V) * PS] = S::from_f(v); }
+  // All lanes of the workgroup share (b, t): the id is wave-uniform, so the masks
+  // built from it are scalar.
+  __device__ int id(int64_t p) const { return __builtin_amdgcn_readfirstlane(ids[p - t0 + S::V]); }
 };
 
 __device__ inline void lds_put16(void* p, u32x4 v) {
@@ -224,11 +231,13 @@ __device__ inline u32x4 lds_get16(const void* p) {
 }
 
 // One tile's staged vectors: x over [t0 - V, t0 + T + V) and dout over
-// [t0, t0 + T + V), NX + NG 16-byte vectors per lane.
+// [t0, t0 + T + V), NX + NG 16-byte vectors per lane; with seq_idx also the ids
+// over [t0 - V, t0 + T + V), one per lane (XN <= 64).
 template <class S>
 struct Staged {
   static constexpr int NX = LdsGeom<S>::XN / S::V, NG = LdsGeom<S>::GN / S::V;
   u32x4 x[NX], g[NG];
+  int32_t id;
 };
 
 // Issues every load of tile t0 (absent vectors, outside [0, L) or past C, load
@@ -238,12 +247,16 @@ struct Staged {
 // consecutive lanes read one step's 64 channels.  `ln` is the lane index made
 // opaque to the compiler per tile, so that it recomputes the row offsets rather
 // than keeping one per load in registers for the whole kernel.
-template <class S, bool CL>
+template <class S, bool CL, bool SEQ>
 __device__ inline void stage_issue(const BwdArgs& a, const typename S::raw* xb, const typename S::raw* gb,
-                                   int64_t c0, int64_t t0, int ln, Staged<S>& st) {
+                                   const int32_t* sr, int64_t c0, int64_t t0, int ln, Staged<S>& st) {
   constexpr int V = S::V, NX = Staged<S>::NX, NG = Staged<S>::NG, NS = 64 / V;
   const int64_t L = a.L, C = a.C;
   const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
+  if constexpr (SEQ) {                             // the ids first: the walk reads them from LDS
+    const int64_t p = t0 - V + ln;
+    st.id = gload<int32_t>(pick(ln < LdsGeom<S>::XN && p >= 0 && p < L, reinterpret_cast<uintptr_t>(sr + p), zero));
+  }
   if constexpr (!CL) {
     constexpr int ES = sizeof(typename S::raw);
     if (a.off24 && c0 + 64 <= C && t0 >= V && t0 + LdsGeom<S>::T + V <= L) {
@@ -295,10 +308,13 @@ __device__ inline void stage_issue(const BwdArgs& a, const typename S::raw* xb, 
 
 // Writes a tile's staged vectors to LDS (channel-first: channel-major rows of
 // pitch XP / GP; channel-last: step-major, 64 channels to a step).
-template <class S, bool CL>
-__device__ inline void stage_put(typename S::raw* lx, typename S::raw* lg, int ln, const Staged<S>& st) {
+template <class S, bool CL, bool SEQ>
+__device__ inline void stage_put(typename S::raw* lx, typename S::raw* lg, int32_t* lids, int ln,
+                                 const Staged<S>& st) {
   using G = LdsGeom<S>;
   constexpr int V = S::V, NX = Staged<S>::NX, NG = Staged<S>::NG, NS = 64 / V;
+  if constexpr (SEQ)
+    if (ln < G::XN) lids[ln] = st.id;
   if constexpr (!CL) {
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
@@ -320,9 +336,9 @@ __device__ inline void stage_put(typename S::raw* lx, typename S::raw* lg, int l
 
 // LDS path: a wave takes a group of consecutive tiles of one (b, 64 channels).
 // Tile n's loads are issued before tile n-1's walk (software pipelining within
-// the wave; with seq_idx the walk itself reads ids from memory, and the hardware
-// waits for loads in issue order, so there each tile is loaded when its turn
-// comes).  A tile is written to LDS, walked from LDS, and its dx, parked in the
+// the wave; the walk reads nothing from global memory except dfinal_states in a
+// row's last tile, which has no successor in flight: the sequence ids are staged
+// in LDS with the tile).  A tile is written to LDS, walked from LDS, and its dx, parked in the
 // LDS slots of the x values that the walk no longer needs, is stored back with
 // 16-byte stores.  Channel-first tiles are channel-major with an odd dword pitch
 // (the walk's reads, one channel per lane, fall in distinct banks); channel-last
@@ -332,12 +348,12 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   using raw = typename S::raw;
   using G = LdsGeom<S>;
   constexpr int V = G::V, H = K - 1, NS = 64 / V;
-  // Prefetch where a work item has several tiles (channel-last) and the walk reads
-  // nothing from memory (no seq_idx).
-  constexpr bool PREFETCH = !SEQ && CL;
-  __shared__ uint32_t lds[G::WORDS];
+  // Prefetch where a work item has several tiles (channel-last).
+  constexpr bool PREFETCH = CL;
+  __shared__ uint32_t lds[G::WORDS + (SEQ ? 64 : 0)];
   raw* lx = reinterpret_cast<raw*>(lds);
   raw* lg = lx + (CL ? G::XN * 64 : 64 * G::XP);
+  int32_t* lids = reinterpret_cast<int32_t*>(lds + G::WORDS);
 
   const int lane = threadIdx.x;
   const int64_t ncg = (a.C + 63) / 64;
@@ -399,14 +415,15 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     }
   };
 
-  if constexpr (PREFETCH) stage_issue<S, CL>(a, xb, gb, c0, tt0 * a.T, lane, st);
+  const int32_t* sr = SEQ ? a.seq + b * L : nullptr;
+  if constexpr (PREFETCH) stage_issue<S, CL, SEQ>(a, xb, gb, sr, c0, tt0 * a.T, lane, st);
   for (int64_t tt = tt0; tt < tt1; ++tt) {
     const int64_t t0 = tt * a.T;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    if constexpr (!PREFETCH) stage_issue<S, CL>(a, xb, gb, c0, t0, ln, st);
+    if constexpr (!PREFETCH) stage_issue<S, CL, SEQ>(a, xb, gb, sr, c0, t0, ln, st);
     __syncthreads();                               // the previous tile's dx has left LDS
-    stage_put<S, CL>(lx, lg, ln, st);
+    stage_put<S, CL, SEQ>(lx, lg, lids, ln, st);
     if (t0 == 0 && a.init && c < C) {              // the history left of t = 0
 #pragma unroll
       for (int i = 0; i < H; ++i)
@@ -415,11 +432,11 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     }
     if (dx_t0 >= 0) store_dx(ln);
     if constexpr (PREFETCH)
-      if (tt + 1 < tt1) stage_issue<S, CL>(a, xb, gb, c0, t0 + a.T, ln, st);
+      if (tt + 1 < tt1) stage_issue<S, CL, SEQ>(a, xb, gb, sr, c0, t0 + a.T, ln, st);
     __syncthreads();
 
     if (c < C) {
-      LdsSrc<S, ps> src{lx + lane * cs, lg + lane * gcs, t0};
+      LdsSrc<S, ps> src{lx + lane * cs, lg + lane * gcs, lids, t0};
       if (t0 + G::T + H <= L && (t0 > 0 || !a.dinit))   // an interior tile
         walk_tile<S, K, SILU, SEQ, true, G::T>(a, b, c, t0, src, w, beta, pw, pb);
       else
