@@ -212,6 +212,30 @@ def test_bwd_random_shapes():
         check_bwd(w, dout, dfs, init, f"[random {i}]")
 
 
+def test_bwd_random_long_rows():
+    """Rows long enough for several segments of the register-only channel-first
+    kernel (2048 steps for 16-bit data, 1024 for fp32) and several tile groups of
+    the channel-last kernels: lengths that end inside a segment, exactly at a
+    segment's end, or just past one, in every layout, with and without seq_idx."""
+    g = np.random.default_rng(78)
+    for i in range(16):
+        K = int(g.integers(2, 5))
+        dtype = DTYPES[g.integers(0, 3)]
+        span = 64 * 4 * (4 if dtype == "f32" else 8)
+        V = 4 if dtype == "f32" else 8
+        L = [span * int(g.integers(1, 3)), span * int(g.integers(1, 3)) + V * int(g.integers(1, 4)),
+             int(g.integers(1, 5000))][i % 3]
+        layout = ["cf", "cl", "cf_view", "cl_view"][g.integers(0, 4)]
+        B, C = int(g.integers(1, 4)), int(g.integers(1, 100))
+        seq = int(g.integers(1, 9)) if g.random() < 0.3 else None
+        init = g.random() < 0.5
+        w = build(B, C, L, K, dtype, layout, 4100 + i, seq=seq, init=init, bias=bool(g.random() < 0.6),
+                  act=["silu", None][g.integers(0, 2)])
+        dout, dfs = grad_inputs(w, layout, g.random() < 0.5, 4100 + i)
+        log(f"  random long bwd {i}: {dtype} K={K} {layout} B={B} C={C} L={L} seq={seq} init={init}")
+        check_bwd(w, dout, dfs, init, f"[random long {i}]")
+
+
 def test_bwd_reduction_with_level_kernels():
     """More than 512 partial rows: level kernels of the reduction tree run before the
     final kernel (2500 rows -> 79 -> the final kernel's 3 waves), with a partial
