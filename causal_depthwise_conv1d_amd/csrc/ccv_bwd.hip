@@ -435,12 +435,30 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
       if (tt + 1 < tt1) stage_issue<S, CL, SEQ>(a, xb, gb, sr, c0, t0 + a.T, ln, st);
     __syncthreads();
 
+    // With seq_idx, a tile right of the history whose rows t0-H .. t0+T+H-1 (those
+    // inside [0, L)) all carry one id keeps every term, so the unmasked walk gives
+    // the same bits (every mask and the dfinal_states condition read true).
+    bool one_seq = false;
+    if constexpr (SEQ) {
+      const int64_t p = t0 - V + lane;             // the lane's staged position
+      const int64_t hi = t0 + G::T + H < L ? t0 + G::T + H : L;
+      const int ref = lids[V];                     // the id at t0
+      const bool same = lane >= G::XN || p < t0 - H || p >= hi || lids[lane] == ref;
+      one_seq = t0 >= H && t0 < L && __all(same);
+    }
     if (c < C) {
       LdsSrc<S, ps> src{lx + lane * cs, lg + lane * gcs, lids, t0};
-      if (t0 + G::T + H <= L && (t0 > 0 || !a.dinit))   // an interior tile
+      const bool inner = t0 + G::T + H <= L && (t0 > 0 || !a.dinit);   // an interior tile
+      if (SEQ && one_seq) {
+        if (inner)
+          walk_tile<S, K, SILU, false, true, G::T>(a, b, c, t0, src, w, beta, pw, pb);
+        else
+          walk_tile<S, K, SILU, false, false, 0>(a, b, c, t0, src, w, beta, pw, pb);
+      } else if (inner) {
         walk_tile<S, K, SILU, SEQ, true, G::T>(a, b, c, t0, src, w, beta, pw, pb);
-      else
+      } else {
         walk_tile<S, K, SILU, SEQ, false, 0>(a, b, c, t0, src, w, beta, pw, pb);
+      }
     }
     __syncthreads();
 
