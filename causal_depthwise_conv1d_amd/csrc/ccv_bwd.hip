@@ -201,7 +201,6 @@ struct LdsGeom {
   static constexpr int GP = ((GN * ES / 4) | 1) * 4 / ES;
   static constexpr int CF_WORDS = 64 * (XP + GP) * ES / 4;
   static constexpr int CL_WORDS = (XN + GN) * 64 * ES / 4;
-  static constexpr int WORDS = CF_WORDS > CL_WORDS ? CF_WORDS : CL_WORDS;
 };
 
 template <class S, int PS>
@@ -350,10 +349,11 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   constexpr int V = G::V, H = K - 1, NS = 64 / V;
   // Prefetch where a work item has several tiles (channel-last).
   constexpr bool PREFETCH = CL;
-  __shared__ uint32_t lds[G::WORDS + (SEQ ? 64 : 0)];
+  constexpr int WORDS = CL ? G::CL_WORDS : G::CF_WORDS;   // LDS per wave bounds the waves per CU
+  __shared__ uint32_t lds[WORDS + (SEQ ? 64 : 0)];
   raw* lx = reinterpret_cast<raw*>(lds);
   raw* lg = lx + (CL ? G::XN * 64 : 64 * G::XP);
-  int32_t* lids = reinterpret_cast<int32_t*>(lds + G::WORDS);
+  int32_t* lids = reinterpret_cast<int32_t*>(lds + WORDS);
 
   const int lane = threadIdx.x;
   const int64_t ncg = (a.C + 63) / 64;
