@@ -135,6 +135,34 @@ def test_backward_graph_replays_equal_eager(layout):
             assert torch.equal(bits(got), bits(want)), (r, name)
 
 
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+def test_backward_graph_with_packed_sequences(layout):
+    """seq_idx on the LDS kernels (ids staged with each tile; long sequences, so many
+    tiles take the unmasked walk): replays equal eager calls bit for bit."""
+    B, C, L, K = 2, 200, 4096, 4
+    w = rand((C, K), "bf16", 7700, 2, 0.5)
+    b = rand((C,), "bf16", 7700, 3, 0.3)
+    seq = wl.seq_idx_from_lengths(wl.packed_lengths(L, 5, 64, 7701), B).cuda()
+
+    def fresh(seed):
+        if layout == "cf":
+            return rand((B, C, L), "bf16", seed, 0), rand((B, C, L), "bf16", seed, 4)
+        return (rand((B, L, C), "bf16", seed, 0).transpose(1, 2), rand((B, L, C), "bf16", seed, 4).transpose(1, 2))
+
+    x, dout = fresh(7702)
+    g, outs = capture(lambda: ccv.causal_conv1d_bwd(x, w, b, dout, seq_idx=seq, activation="silu"))
+    for r in range(REPLAYS):
+        nx, ndout = fresh(7800 + r)
+        x.copy_(nx)
+        dout.copy_(ndout)
+        ref = ccv.causal_conv1d_bwd(nx, w, b, ndout, seq_idx=seq, activation="silu")
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"  backward graph with seq_idx {layout} replay {r}")
+        for name, got, want in zip(("dx", "dweight", "dbias"), outs, ref):
+            assert torch.equal(bits(got), bits(want)), (r, name)
+
+
 def test_calls_on_concurrent_streams_equal_sequential():
     """The library keeps no state between calls: forwards and backwards issued on two
     streams at once give the bits they give one at a time."""
