@@ -55,7 +55,9 @@ __device__ inline void put_elems(const typename S::raw (&r)[N], u32x4* v) {
 // c .. c+V-1 of batch row b.  With x and out unit-stride in channels, the state
 // stored [B, C, K-1] contiguously and the weights in x's dtype, the lane's x and
 // out of one step, its bias, its K*V weights and its (K-1)*V history values are
-// whole aligned vectors: K-1 + K + 2 loads and K stores cover V rows.
+// whole aligned vectors: K-1 + K + 2 loads and K stores cover V rows.  x and out
+// are touched once and use streaming (non-temporal) accesses; the state, which the
+// next decode step reads again, uses ordinary ones.
 template <class S, int K, bool SILU>
 __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
   using raw = typename S::raw;
@@ -84,7 +86,7 @@ __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
   const raw* xr = static_cast<const raw*>(a.x) + b * a.x_sb + c;
   raw* orow = static_cast<raw*>(a.out) + b * a.o_sb + c;
   for (int64_t t = 0; t < a.L; ++t) {
-    u32x4 xv[1] = {load16(xr + t * a.x_sl)};
+    u32x4 xv[1] = {load16_stream(xr + t * a.x_sl)};
     float y[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -98,7 +100,7 @@ __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
       for (int i = 0; i + 1 < H; ++i) hist[j][i] = hist[j][i + 1];
       hist[j][H - 1] = xe;
     }
-    store16(orow + t * a.o_sl, S::pack(y));
+    store16_stream(orow + t * a.o_sl, S::pack(y));
   }
 
   raw flat[V * H];
