@@ -508,6 +508,49 @@ def pin_f32_mode_error_bound(ora):
             assert np.array_equal(case.points_f32(idx), case.fwd_f32()[idx[:, 0], idx[:, 1], idx[:, 2]])
 
 
+def pin_points(ora):
+    """The sampled entry (the fp64 values at a list of (b, c, t) triples, used for the
+    large workloads) returns exactly what the whole-array call returns at those
+    triples: y and sabs bit for bit, with seq_idx and a history, on a strided
+    channel-last view of a wider buffer, for all three storage dtypes.  The triples
+    are random plus every boundary (first and last step, batch, channel), and no
+    dimension sizes agree, so a permuted index reads another output."""
+    g = _gen(23)
+    B, C, L, K = 3, 5, 37, 4
+    for dt, wdt in (("f32", "f32"), ("bf16", "bf16"), ("f16", "f32")):
+        x = torch.randn(B, L, C + 4, generator=g).to(DT[dt])          # [B, L, C + 4] parent
+        w = (torch.randn(C, K, generator=g) * 0.5).to(DT[wdt])
+        bias = torch.randn(C, generator=g).to(DT[wdt])
+        init = torch.randn(B, C, K - 1, generator=g).to(DT[dt])
+        seq = torch.tensor([[0] * 9 + [4] * 20 + [2] * 8, [1] * 37, [3] * 2 + [5] * 35],
+                           dtype=torch.int32)
+        case = ora.Case(B=B, C=C, L=L, K=K, x=_raw(x), x_off=2, x_dtype=dt,
+                        x_strides=(L * (C + 4), 1, C + 4), w=_raw(w), w_dtype=wdt,
+                        bias=_raw(bias), seq=seq.numpy(), init=_raw(init),
+                        init_strides=init.stride(), silu=True)
+        y, s = case.fwd()
+        rng = np.random.default_rng(24)
+        rand = np.stack([rng.integers(0, B, 200), rng.integers(0, C, 200),
+                         rng.integers(0, L, 200)], 1)
+        edge = np.array([[b, c, t] for b in (0, B - 1) for c in (0, C - 1)
+                         for t in (0, 1, K - 2, K - 1, 8, 9, 28, 29, L - 1)])
+        idx = np.concatenate([rand, edge])
+        try:
+            py, ps = case.points(idx)
+        except IndexError:
+            raise AssertionError(f"{dt}: an in-range index was refused")
+        want_y = y[idx[:, 0], idx[:, 1], idx[:, 2]]
+        want_s = s[idx[:, 0], idx[:, 1], idx[:, 2]]
+        assert np.array_equal(py.view(np.uint64), want_y.view(np.uint64)), dt
+        assert np.array_equal(ps.view(np.uint64), want_s.view(np.uint64)), dt
+        for bad in ([B, 0, 0], [0, C, 0], [0, 0, L], [-1, 0, 0], [0, 0, -1]):
+            try:
+                case.points(np.array([bad]))
+            except IndexError:
+                continue
+            raise AssertionError(f"index {bad} out of range was accepted")
+
+
 # ---- backward -------------------------------------------------------------------------
 
 def _bwd(ora, x, w, b=None, seq=None, init=None, silu=False, dout=None, dfs=None):
@@ -672,4 +715,4 @@ ALL_PINS = [pin_golden, pin_digits, pin_one_hot, pin_delta, pin_constant, pin_co
             pin_chunking, pin_packing, pin_mask_nan, pin_layout, pin_silu, pin_converters,
             pin_round_out, pin_f32_mode_exact_rational, pin_f32_mode_integers_are_exact,
             pin_f32_mode_error_bound, pin_bwd_autograd, pin_bwd_finite_differences, pin_bwd_packing,
-            pin_bwd_chunking, pin_packed_chunking]
+            pin_bwd_chunking, pin_packed_chunking, pin_points]

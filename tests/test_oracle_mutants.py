@@ -50,6 +50,12 @@ MUTANTS = [
     ("history_id_of_last_sequence", "*id = p->seq[b * p->L];", "*id = p->seq[b * p->L + p->L - 1];"),
     ("history_never_counts_with_seq", "if (p->init == NULL || p->L == 0) return 0;", "return 0;"),
     ("final_states_not_masked", "if (p->seq == NULL || p->L == 0) return 1;", "return 1;"),
+    # the sampled entry
+    ("points_index_order", "ora_point(p, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], &yy, NULL, &ss)",
+     "ora_point(p, idx[3 * i + 1], idx[3 * i], idx[3 * i + 2], &yy, NULL, &ss)"),
+    ("points_time_channel_swapped", "ora_point(p, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], &yy, NULL, &ss)",
+     "ora_point(p, idx[3 * i], idx[3 * i + 2], idx[3 * i + 1], &yy, NULL, &ss)"),
+    ("points_sabs_as_y", "if (y) y[i] = yy;", "if (y) y[i] = ss;"),
     # the backward
     ("bwd_no_activation_slope", "dz[t] = go * slope;", "dz[t] = go;"),
     ("bwd_slope_sign", "slope = s * (1.0 + z * (1.0 - s));", "slope = s * (1.0 - z * (1.0 - s));"),
