@@ -53,6 +53,8 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
 
   const int64_t B = a->B, C = a->C, L = a->L;
   const int K = a->K;
+  int64_t rows;
+  if (__builtin_mul_overflow(B, C, &rows)) return CCV_E_SHAPE;
   const bool want_out = B > 0 && C > 0 && L > 0;
   const bool want_fin = B > 0 && C > 0 && a->final_states_out != nullptr;
   *plan = Plan{};
@@ -62,6 +64,8 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
   if (want_out && (!a->x || !a->weight || !a->out)) return CCV_E_NULL;
   if (want_out && a->out == a->x) return CCV_E_ALIAS;
   if (a->final_states_out && a->initial_states && a->final_states_out == a->initial_states) return CCV_E_ALIAS;
+  if (want_fin && (a->final_states_out == a->x || (want_out && a->final_states_out == a->out)))
+    return CCV_E_ALIAS;
 
   // Kernel choice by the unit-stride dimension of x (Ch.4, section "Why one shape
   // still has two layouts"); out must be unit-stride in the same dimension.  The
@@ -84,6 +88,10 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
   if (a->final_states_out && !fits_bytes(max_offset(ns, a->final_stride), es)) return CCV_E_SHAPE;
   int64_t bl;
   if (a->seq_idx && __builtin_mul_overflow(B, L, &bl)) return CCV_E_SHAPE;
+  // Waves write out and final_states_out concurrently, each element once: a
+  // layout that maps two logical elements to one address would race.
+  if (want_out && !non_overlapping(nx, a->out_stride)) return CCV_E_LAYOUT;
+  if (want_fin && !non_overlapping(ns, a->final_stride)) return CCV_E_LAYOUT;
 
   const int V = 16 / es;
   Common m{};
@@ -120,7 +128,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
     if (a->seq_idx) vec = vec && aligned16(a->seq_idx) && (B <= 1 || (L & 3) == 0);
     vec = vec && !force_scalar;
     c.nfull = vec ? L / c.span : 0;
-    if (__builtin_mul_overflow(B * C, c.nseg, &nwork)) return CCV_E_SHAPE;
+    if (__builtin_mul_overflow(rows, c.nseg, &nwork)) return CCV_E_SHAPE;
     // Waves launched.  Arithmetic-heavy calls (16-bit storage packs twice the
     // outputs into each byte; SiLU adds two transcendentals per output) run a grid
     // of 16 waves per CU, each walking its segments with the next one's loads in
@@ -148,7 +156,8 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
     c.tile = tile;
     c.ntt = L > 0 ? (L + tile - 1) / tile : 1;
     c.ncg = (C + 64 * V - 1) / (64 * V);
-    if (__builtin_mul_overflow(B * c.ncg, c.ntt, &nwork)) return CCV_E_SHAPE;
+    int64_t bcg;
+    if (__builtin_mul_overflow(B, c.ncg, &bcg) || __builtin_mul_overflow(bcg, c.ntt, &nwork)) return CCV_E_SHAPE;
     bool vec = aligned16(a->x) && stride_ok16(B, c.x_sb, es) && stride_ok16(L, c.x_sl, es);
     if (want_out) vec = vec && aligned16(a->out) && stride_ok16(B, c.o_sb, es) && stride_ok16(L, c.o_sl, es);
     P.vector = vec && !force_scalar;

@@ -78,10 +78,12 @@ typedef enum {
   CCV_E_KSIZE = -3,       /* K not in {2,3,4} */
   CCV_E_DTYPE = -4,       /* x_dtype or w_dtype not a ccv_dtype_t */
   CCV_E_LAYOUT = -5,      /* x (or out) has unit stride in neither time nor channels,
-                             out's unit-stride dim differs from x's, or a stride < 0 */
+                             out's unit-stride dim differs from x's, a stride < 0, or the
+                             layout of out or final_states_out maps two elements to one
+                             address */
   CCV_E_UNSUPPORTED = -6, /* an activation value outside ccv_act_t; in the backward,
                              dinitial_states without initial_states */
-  CCV_E_ALIAS = -7,       /* out == x, or final_states_out == initial_states */
+  CCV_E_ALIAS = -7,       /* out == x, or final_states_out is x, out or initial_states */
   CCV_E_HIP = -8,         /* the HIP runtime refused the launch */
   CCV_E_INTERNAL = -9,    /* an unexpected internal condition */
   CCV_E_ABI = -10         /* struct_size does not match this library's struct */

@@ -18,9 +18,12 @@ match exactly.  Every output is checked; nothing is reduced to a norm.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
-from . import decode, round_out
+from . import decode, lib, round_out
 
 _MBITS = {"bf16": 7, "f16": 10}
 _BIAS = {"bf16": 127, "f16": 15}
@@ -32,12 +35,26 @@ def _ord16(bits: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
+def _ulp_table(dtype: str) -> np.ndarray:
+    """ulp of the 16-bit format for each value of its exponent field (subnormals and
+    zero share the smallest normal exponent's spacing)."""
+    m = _MBITS[dtype]
+    e = np.maximum(np.arange(1 << (15 - m), dtype=np.int64), 1)
+    return np.ldexp(1.0, e - _BIAS[dtype] - m)
+
+
+_ULP_TABLES = {d: _ulp_table(d) for d in _MBITS}
+
+
 def ulp16(dtype: str, bits: np.ndarray) -> np.ndarray:
     """Spacing of the 16-bit format at each value (its exponent's ulp)."""
     m = _MBITS[dtype]
-    e = (bits.astype(np.int64) >> m) & ((1 << (15 - m)) - 1)
-    e = np.maximum(e, 1)
-    return np.ldexp(1.0, (e - _BIAS[dtype] - m).astype(np.int64))
+    e = (np.asarray(bits, dtype=np.uint16) >> m) & ((1 << (15 - m)) - 1)
+    return _ULP_TABLES[dtype][e]
+
+
+_CHUNK = 1 << 20
+_THREADS = min(16, len(os.sched_getaffinity(0)))
 
 
 def compare(dtype: str, K: int, g_raw: np.ndarray, y: np.ndarray, sabs: np.ndarray) -> dict:
@@ -46,16 +63,45 @@ def compare(dtype: str, K: int, g_raw: np.ndarray, y: np.ndarray, sabs: np.ndarr
     Returns a dict with ``bad`` (boolean mask of failures), ``n``, ``n_bad``,
     ``max_rel`` (max |g - o| / |o| over finite nonzero o), ``max_ulp`` (16-bit),
     ``n_floor_only`` (passed only through the S term) and ``bit_equal`` (count of
-    outputs equal to the rounded oracle value)."""
+    outputs equal to the rounded oracle value).  Large inputs are checked in
+    chunks on several host threads; every element gets the same test either way."""
     y = np.asarray(y, dtype=np.float64).reshape(-1)
     s = np.asarray(sabs, dtype=np.float64).reshape(-1)
     g_raw = np.ascontiguousarray(g_raw).reshape(-1)
+    n = y.size
+    bad = np.zeros(n, dtype=bool)
+    bounds = [(lo, min(n, lo + _CHUNK)) for lo in range(0, n, _CHUNK)]
+    lib()                                          # load (or build) before any thread uses it
+
+    def one(lo_hi):
+        lo, hi = lo_hi
+        return _compare_chunk(dtype, K, g_raw[lo:hi], y[lo:hi], s[lo:hi], bad[lo:hi])
+
+    if len(bounds) > 1 and _THREADS > 1:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            parts = list(ex.map(one, bounds))
+    else:
+        parts = [one(b) for b in bounds]
+    ulps = [p["max_ulp"] for p in parts if p["max_ulp"] is not None]
+    return {
+        "bad": bad,
+        "n": int(n),
+        "n_bad": sum(p["n_bad"] for p in parts),
+        "max_rel": max([p["max_rel"] for p in parts], default=0.0),
+        "max_ulp": None if dtype == "f32" else max(ulps, default=0),
+        "n_floor_only": sum(p["n_floor_only"] for p in parts),
+        "bit_equal": sum(p["bit_equal"] for p in parts),
+    }
+
+
+def _compare_chunk(dtype: str, K: int, g_raw, y, s, bad) -> dict:
+    """compare() on one slice; writes the slice's failures into `bad` (a view)."""
     floor = K * 2.0 ** -22 * s
     o_raw = round_out(dtype, y)
     g = decode(dtype, g_raw)
     o = decode(dtype, o_raw)
     nan_g, nan_y = np.isnan(g), np.isnan(y)
-    bad = nan_g != nan_y
+    bad[:] = nan_g != nan_y
     both = ~nan_g & ~nan_y
     with np.errstate(invalid="ignore", over="ignore"):
         exact = g == o
@@ -75,8 +121,6 @@ def compare(dtype: str, K: int, g_raw: np.ndarray, y: np.ndarray, sabs: np.ndarr
         fin = both & np.isfinite(o) & (o != 0) & np.isfinite(g)
         rel = np.abs(g[fin] - o[fin]) / np.abs(o[fin])
     return {
-        "bad": bad,
-        "n": int(y.size),
         "n_bad": int(bad.sum()),
         "max_rel": float(rel.max()) if rel.size else 0.0,
         "max_ulp": max_ulp,

@@ -116,6 +116,32 @@ def test_aliasing():
                       final_stride=(192, 1, 64))) == "CCV_E_ALIAS"
 
 
+def test_final_states_aliasing_x_or_out():
+    fs = dict(final_states_out=X, final_stride=(192, 1, 64))
+    assert check(args(**fs)) == "CCV_E_ALIAS"
+    fs["final_states_out"] = OUT
+    assert check(args(**fs)) == "CCV_E_ALIAS"
+    # with L = 0 nothing of out is written, so only x is compared
+    assert check(args(L=0, out=FIN, final_states_out=FIN, final_stride=(192, 1, 64))) == "CCV_OK"
+
+
+def test_written_layouts_must_not_overlap():
+    # out with a zero stride, or time steps landing on the next channel's elements
+    assert check(args(out_stride=(64000, 0, 1))) == "CCV_E_LAYOUT"
+    assert check(args(out_stride=(64000, 500, 1))) == "CCV_E_LAYOUT"
+    assert check(args(layout="cl", out_stride=(64000, 1, 32))) == "CCV_E_LAYOUT"
+    # final states whose entries of two channels coincide
+    assert check(args(final_states_out=FIN, final_stride=(192, 0, 64))) == "CCV_E_LAYOUT"
+    assert check(args(final_states_out=FIN, final_stride=(192, 2, 1))) == "CCV_E_LAYOUT"
+    # a padded pitch is fine
+    assert check(args(out_stride=(70000, 1024, 1))) == "CCV_OK"
+
+
+def test_batch_times_channels_overflow():
+    # zero batch and channel strides keep every offset small, but B*C overflows int64
+    assert check(args(B=2**40, C=2**30, L=4, x_stride=(0, 0, 1))) == "CCV_E_SHAPE"
+
+
 def test_layouts():
     # neither time nor channels unit-stride: the caller must copy
     assert check(args(x_stride=(64 * 1000 * 2, 2000, 2))) == "CCV_E_LAYOUT"

@@ -1,13 +1,16 @@
 """The five named workloads at their full sizes, in the launch configuration the
 bench times (default plan, torch's current stream).
 
-The small channel-first workload and the channel-first bf16 workload are compared
-with the oracle at every output.  The three large ones are compared at sampled
-outputs the oracle computes one by one (uniform random positions plus every
-wave-segment / time-tile boundary, sequence boundary and sequence start/end),
-over the whole time axis of a slice of channels (channels are independent, so a
-channel slice is an exact sub-problem), and by properties that hold at any size
-(every output finite; final states bit-exact in full)."""
+Every output of every workload is compared with the oracle.  The large ones are
+checked in pieces of (batch, channel range): channels are independent, so such a
+piece is an exact sub-problem, which the oracle runs on all host cores.  On top
+of that: sampled outputs the oracle computes one by one (uniform random
+positions plus every wave-segment / time-tile boundary, sequence boundary and
+sequence start/end), properties that hold at any size (every output finite;
+final states bit-exact in full) and, without an activation, bit-identity with
+the oracle's binary32 chain.  Outputs that pass only through the summation-error
+floor of the tolerance are counted and bounded."""
+import os
 import time
 
 import numpy as np
@@ -16,7 +19,7 @@ import torch
 
 import causal_depthwise_conv1d_amd as ccv
 import workloads as wl
-from gpu_support import assert_close, assert_final_states, gpu_args, log, oracle_case
+from gpu_support import assert_final_states, gpu_args, log, oracle_case
 from oracle import compare as ocmp
 from oracle.from_torch import case, dtype_name, raw
 
@@ -60,21 +63,51 @@ def sampled_check(w, out_gpu, extra_t=None, n_random=200_000, seed=0):
     return res
 
 
-def channel_slice_check(w, kw, out_gpu, c0, c1, b=0):
-    """Every output of channels [c0, c1) of batch b against the oracle run on the
-    same sub-problem."""
-    x = w.x[b:b + 1, c0:c1]
-    init = None if w.initial_states is None else w.initial_states[b:b + 1, c0:c1]
-    seq = None if w.seq_idx is None else w.seq_idx[b:b + 1]
-    sub = case(x, w.weight[c0:c1], None if w.bias is None else w.bias[c0:c1], seq, init, w.activation)
+ORACLE_THREADS = min(16, len(os.sched_getaffinity(0)))
+
+# Outputs allowed to pass only through the K * 2^-22 * S floor (a cancellation far
+# below the terms' magnitudes).  None for 16-bit outputs: an fp32 fused
+# multiply-add chain rounded to bf16 / fp16 stays within two ulps of the format on
+# all 268 million outputs of these workloads (checked on the CPU with the oracle's
+# binary32 mode).  For fp32 outputs rel 1e-5 is only ~170 fp32 roundings of the
+# result, and that same emulation leaves 0.095% (small workload, SiLU) and 0.076%
+# (long workload) of outputs to the floor; the bound is three times that.
+FLOOR_ONLY_FRACTION = {"bf16": 0.0, "f16": 0.0, "f32": 3e-3}
+
+
+def full_check(w, out_gpu, pieces):
+    """Every output against the oracle, one (b, c0, c1) piece at a time; returns the
+    summed comparison figures.  `pieces` must cover [0, B) x [0, C)."""
+    covered = np.zeros((w.B, w.C), dtype=np.int32)
+    tot = {"n": 0, "n_bad": 0, "n_floor_only": 0, "bit_equal": 0, "max_ulp": 0, "max_rel": 0.0}
     t0 = time.time()
-    y, s = sub.fwd()
-    log(f"  oracle: channel slice [{c0},{c1}) x {w.L} steps in {time.time() - t0:.1f}s")
-    g = out_gpu[b:b + 1, c0:c1].cpu().contiguous()
-    res = ocmp.compare(dtype_name(g), w.K, raw(g), y, s)
-    if res["n_bad"]:
-        raise AssertionError(ocmp.describe_failures(res, y, s, raw(g), dtype_name(g), shape=tuple(g.shape)))
-    return res
+    for b, c0, c1 in pieces:
+        covered[b, c0:c1] += 1
+        sub = case(w.x[b:b + 1, c0:c1], w.weight[c0:c1], None if w.bias is None else w.bias[c0:c1],
+                   None if w.seq_idx is None else w.seq_idx[b:b + 1],
+                   None if w.initial_states is None else w.initial_states[b:b + 1, c0:c1], w.activation)
+        y, s = sub.fwd_threads(ORACLE_THREADS)
+        g = out_gpu[b:b + 1, c0:c1].cpu().contiguous()
+        res = ocmp.compare(dtype_name(g), w.K, raw(g), y, s)
+        if res["n_bad"]:
+            raise AssertionError(f"batch {b} channels [{c0},{c1}): " + ocmp.describe_failures(
+                res, y, s, raw(g), dtype_name(g), shape=tuple(g.shape)))
+        for k in ("n", "n_bad", "n_floor_only", "bit_equal"):
+            tot[k] += res[k]
+        tot["max_ulp"] = max(tot["max_ulp"], res["max_ulp"] or 0)
+        tot["max_rel"] = max(tot["max_rel"], res["max_rel"])
+    assert (covered == 1).all(), "the pieces must cover every (b, c) row once"
+    assert tot["n"] == w.B * w.C * w.L
+    log(f"  full check: {tot['n']} outputs in {time.time() - t0:.1f}s on {ORACLE_THREADS} threads: "
+        f"{tot['n_bad']} out of tolerance, max ulp {tot['max_ulp']}, max rel {tot['max_rel']:.2e}, "
+        f"floor-only {tot['n_floor_only']}, bit-equal {tot['bit_equal']}")
+    limit = FLOOR_ONLY_FRACTION[w.x_dtype] * tot["n"]
+    assert tot["n_floor_only"] <= limit, f"{tot['n_floor_only']} floor-only outputs (limit {limit:.0f})"
+    return tot
+
+
+def pieces_of(w, channels):
+    return [(b, c0, min(w.C, c0 + channels)) for b in range(w.B) for c0 in range(0, w.C, channels)]
 
 
 def fma_chain_check(w, out_gpu, extra_t, c0, c1, n_random=200_000, seed=1):
@@ -105,21 +138,14 @@ def test_workload_1_small_channel_first_all_outputs():
     w = wl.workload(1)
     kw, plan, out, _ = run(w)
     assert plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST and plan["vector"] == 1
-    y, s = oracle_case(w).fwd()
-    res = assert_close(w, out.cpu().contiguous(), y, s)
-    log(f"  workload 1: {res['n']} outputs, max rel {res['max_rel']:.2e}, floor-only {res['n_floor_only']}")
+    full_check(w, out, pieces_of(w, w.C))
 
 
 def test_workload_2_channel_first_bf16_all_outputs():
     w = wl.workload(2)
     kw, plan, out, _ = run(w)
     assert plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST and plan["vector"] == 1
-    t0 = time.time()
-    y, s = oracle_case(w).fwd()
-    log(f"  oracle: all {y.size} outputs in {time.time() - t0:.1f}s")
-    res = assert_close(w, out.cpu().contiguous(), y, s)
-    log(f"  workload 2: max ulp {res['max_ulp']}, floor-only {res['n_floor_only']}, "
-        f"bit-equal {res['bit_equal']}/{res['n']}")
+    full_check(w, out, pieces_of(w, w.C))
 
 
 def test_workload_3_channel_last_view_with_states():
@@ -132,8 +158,7 @@ def test_workload_3_channel_last_view_with_states():
     assert bool(torch.isfinite(out).all()), "an output read outside the view"
     assert_final_states(w, fs.cpu().contiguous())
     sampled_check(w, out, boundary_times(w.L, plan["span"], w.K))
-    channel_slice_check(w, kw, out, 0, 64, b=0)
-    channel_slice_check(w, kw, out, 4096 - 40, 4096, b=7)
+    full_check(w, out, pieces_of(w, 2048))
 
 
 def test_workload_4_packed_varlen_fp16():
@@ -148,8 +173,7 @@ def test_workload_4_packed_varlen_fp16():
         extra |= set(range(max(0, s0 - 4), min(w.L, s0 + 4)))
     assert bool(torch.isfinite(out).all())
     sampled_check(w, out, np.array(sorted(extra)))
-    channel_slice_check(w, kw, out, 0, 16)
-    channel_slice_check(w, kw, out, 2560 - 16, 2560)
+    full_check(w, out, pieces_of(w, 256))
 
 
 def test_workload_5_long_sequence_channel_first():
@@ -164,6 +188,5 @@ def test_workload_5_long_sequence_channel_first():
     assert bool(torch.isfinite(out).all())
     assert_final_states(w, fs.cpu().contiguous())
     sampled_check(w, out, boundary_times(w.L, plan["span"], w.K))
-    channel_slice_check(w, kw, out, 0, 2, b=0)
-    channel_slice_check(w, kw, out, 126, 128, b=1)
+    full_check(w, out, pieces_of(w, 16))
     fma_chain_check(w, out, boundary_times(w.L, plan["span"], w.K), 40, 41)
