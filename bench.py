@@ -1,23 +1,32 @@
 """Bench: effective HBM bandwidth of the causal depthwise conv1d forward on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
 One step is one forward call (validation, dispatch, one kernel) over one batch of
-synthetic input already resident in HBM.  The default workload is the
-channel-first bf16 call B=4, C=2048, L=4096, K=4 with bias and SiLU.  Its
-134 MB working set would fit in the 256 MB Infinity Cache, so the timed steps
-rotate over enough separate input/output buffer sets (>= 1 GiB in total) that
-every step reads inputs that have left the caches.
+synthetic input already resident in HBM.  By default every one of the five
+named workloads is measured, and the printed line's headline is the largest one
+(workload 5: fp32, B=2, C=128, L=1048576, K=3, carried states, 2.15 GB per call);
+--workload N measures one workload and makes it the headline.
+
+Timing, per workload: W warm-up and then exactly K timed calls, each preceded by
+an untimed cache flush (a 1 GiB copy, then a 1 GiB read-only sweep, so the 256 MB
+Infinity Cache and the L2s hold clean lines of other data) and bracketed by its
+own pair of HIP events on the stream the kernel is launched on.  The headline
+value is the median; the roofline object uses the mean (the average launch
+duration).  Beside it, as context: K back-to-back calls rotating over >= 1 GiB of
+buffer sets, the same calls replayed from a HIP graph, a streaming copy kernel
+moving the same number of bytes, and the empty-kernel launch floor.
 
 Effective bandwidth = algorithmic bytes / time, where the algorithmic bytes count
 x read once, out written once, and weight, bias, seq_idx and the states once each
-(halo re-reads are not counted).  Time comes from HIP events recorded on the
-stream the kernels are launched on, around exactly K steps.
+(halo re-reads are not counted).
 
-Printed: one JSON line with the metric, a "roofline" object for the forward
-kernel (against MI355X's 8 TB/s HBM), and a "cpu_baseline" object (the CPU oracle
-timed on this host over the same workload, and the element-wise parity of this
-run's GPU output against it).
+Printed: one JSON line with the metric, a "roofline" object for the headline
+kernel (against MI355X's 8 TB/s HBM), a "cpu_baseline" object (the CPU oracle
+timed on this host, on one thread over a bounded sample and on all cores over the
+whole workload, and the element-wise parity of this run's GPU output against it
+at every output), and under context.per_workload the same figures for every
+other measured workload.
 """
 from __future__ import annotations
 
@@ -100,48 +109,154 @@ def profile_traffic(kernel_key: str, sha: str):
     return int(m_tr.group(1))
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--op", default="fwd", choices=["fwd", "update", "bwd"],
-                    help="fwd: the forward on --workload (default); update: the decode step; "
-                         "bwd: the backward on --workload")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="minimum CPU time spent timing the oracle")
-    args = ap.parse_args()
+HEADLINE_WORKLOAD = 5           # the largest single-GPU workload (2,147,489,280 bytes per call)
+FLUSH_BYTES = 1 << 30
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the op needs no communication: batch or channel shards run independently)",
-              file=sys.stderr)
-        sys.exit(2)
 
-    import numpy as np
+class Calib:
+    """The measurement helpers of libccv_calib.so (copy, read-only sweep, empty
+    kernel) and the buffers of the cache flush."""
+
+    def __init__(self, dev):
+        import ctypes
+
+        import torch
+
+        import causal_depthwise_conv1d_amd as ccv
+        c = ctypes.CDLL(ccv.CALIB_LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        c.ccv_calib_copy_ex.argtypes = [vp, vp, i64, i32, i32, vp]
+        c.ccv_calib_copy.argtypes = [vp, vp, i64, vp]
+        c.ccv_calib_read.argtypes = [vp, i64, ctypes.c_uint32, vp, vp]
+        c.ccv_calib_empty.argtypes = [vp]
+        self.lib = c
+        self.dev = dev
+        half = FLUSH_BYTES // 2
+        self.fsrc = torch.zeros(half, dtype=torch.uint8, device=dev)
+        self.fdst = torch.empty(half, dtype=torch.uint8, device=dev)
+        self.fread = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(64, dtype=torch.int32, device=dev)
+
+    def flush(self, sp):
+        """Write 512 MB, then read 1 GiB of other data: what the caches hold after
+        this is clean and unrelated to the next call."""
+        rc = self.lib.ccv_calib_copy(self.fdst.data_ptr(), self.fsrc.data_ptr(), self.fsrc.numel(), sp)
+        rc = rc or self.lib.ccv_calib_read(self.fread.data_ptr(), self.fread.numel(), 0x9E3779B9,
+                                           self.sink.data_ptr(), sp)
+        if rc != 0:
+            raise RuntimeError(f"cache flush failed ({rc})")
+
+
+def timed_calls(step, warmup, steps, calib, stream):
+    """W flushed warm-up calls, then exactly K flushed calls, each between its own
+    HIP events on `stream`; returns the K per-call times in microseconds."""
+    import ctypes
+
+    import torch
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for i in range(warmup):
+        calib.flush(sp)
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        calib.flush(sp)
+        a.record(stream)
+        step(warmup + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def back_to_back(step, steps, stream):
+    """K calls in a row (the caller rotates buffer sets): microseconds per call."""
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / steps
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def gbps(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
+
+
+def copy_ceiling(nbytes, dev, stream, calib, steps):
+    """A streaming copy that reads and writes nbytes / 2 each (rotated over >= 1 GiB
+    of buffers), in three forms: non-temporal with 16 waves per CU walking 4 KB
+    chunks, non-temporal with one wave per chunk, and ordinary accesses with one
+    wave per chunk.  Returns the fastest, with all three."""
+    import ctypes
+
+    import torch
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    half = max(16, (nbytes // 2) // 16 * 16)
+    csets = max(2, math.ceil(ROTATION_BYTES / (2 * half)))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.zeros(half, dtype=torch.uint8, device=dev))
+            for _ in range(csets)]
+    forms = {"nt_16_waves_per_cu": (16, 1), "nt_wave_per_chunk": (0, 1), "plain_wave_per_chunk": (0, 0)}
+    res = {}
+    for name, (wpc, nt) in forms.items():
+        def step(i, wpc=wpc, nt=nt):
+            d, s_ = bufs[i % csets]
+            if calib.lib.ccv_calib_copy_ex(d.data_ptr(), s_.data_ptr(), half, wpc, nt, sp) != 0:
+                raise RuntimeError("copy failed")
+        us = back_to_back(step, steps, stream)
+        res[name] = round(gbps(2 * half, us), 1)
+    del bufs
+    best = max(res, key=res.get)
+    return {"GBps": res[best], "frac": round(res[best] / PEAK_HBM_GBPS, 4), "form": best, "forms": res}
+
+
+def empty_floor(stream, calib):
+    """Device time per launch of an empty kernel over 1000 back-to-back launches."""
+    import ctypes
+
+    import torch
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(50):
+        calib.lib.ccv_calib_empty(sp)
+    ev0.record(stream)
+    for _ in range(1000):
+        calib.lib.ccv_calib_empty(sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1)           # ms for 1000 launches = us per launch
+
+
+def kernel_key_of(w, plan):
+    import causal_depthwise_conv1d_amd as ccv
+    return ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
+        f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}"
+
+
+def measure_forward(n, args, dev, props, calib):
+    """GPU half of one workload's record: flushed timed calls, back-to-back calls,
+    graph replay and the copy ceiling; returns (record, workload, host copy of out,
+    host copy of final_states or None)."""
+    import ctypes
+
     import torch
 
     import causal_depthwise_conv1d_amd as ccv
     import workloads as wl
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    ccv.lib()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    props = torch.cuda.get_device_properties(dev)
-
-    if args.op == "update":
-        bench_update(args, dev, props)
-        return
-    if args.op == "bwd":
-        bench_bwd(args, dev, props)
-        return
-
     t0 = time.time()
-    w = wl.workload(args.workload)
-    log(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s")
+    w = wl.workload(n)
+    log(f"[bench] workload {n} {w.name}: generated in {time.time() - t0:.1f}s")
     nbytes = algorithmic_bytes(w)
     set_bytes = 2 * w.x.numel() * w.x.element_size()
     if w.x_storage.numel() > w.x.numel():
@@ -159,7 +274,7 @@ def main():
         init = w.init_storage.to(dev).as_strided(w.initial_states.shape, w.initial_states.stride(),
                                                  w.initial_states.storage_offset())
     sets = []
-    for i in range(nsets):
+    for _ in range(nsets):
         xs = w.x_storage.to(dev)
         x = xs.as_strided(w.x.shape, w.x.stride(), w.x.storage_offset())
         out = ccv.empty_like_layout(x)
@@ -173,139 +288,174 @@ def main():
     log(f"[bench] {nsets} buffer sets of {set_bytes / 1e6:.0f} MB; plan {plan}")
 
     stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
     fwd = ccv.lib().ccv_fwd
-    import ctypes
     arg_refs = [ctypes.byref(s[4]) for s in sets]
-    sp = ctypes.c_void_p(sptr)
+    sp = ctypes.c_void_p(stream.cuda_stream)
 
     def step(i):
         rc = fwd(arg_refs[i % nsets], sp)
         if rc != 0:
             raise RuntimeError(ccv.ccv_status_str(rc))
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
+    # The timed region: every call reads x from HBM with clean, unrelated caches.
+    us = timed_calls(lambda i: step(0), args.warmup, args.steps, calib, stream)
+    med, mean = median(us), sum(us) / len(us)
+    rec = {
+        "workload": w.name,
+        "description": w.notes.get("description"),
+        "B": w.B, "C": w.C, "L": w.L, "K": w.K,
+        "x_strides": list(w.x.stride()),
+        "activation": w.activation,
+        "storage_dtype": w.x_dtype,
+        "algorithmic_bytes": nbytes,
+        "kernel": kernel_key_of(w, plan),
+        "plan": plan,
+        "flushed_calls": {"calls": len(us), "median_us": round(med, 3), "mean_us": round(mean, 3),
+                          "min_us": round(min(us), 3), "max_us": round(max(us), 3),
+                          "median_GBps": round(gbps(nbytes, med), 1),
+                          "median_frac": round(gbps(nbytes, med) / PEAK_HBM_GBPS, 4),
+                          "mean_GBps": round(gbps(nbytes, mean), 1)},
+    }
+    log(f"[bench] flushed calls: median {med:.2f} us ({gbps(nbytes, med):.0f} GB/s), mean {mean:.2f} us, "
+        f"min {min(us):.2f}, max {max(us):.2f}")
+    out_host = sets[0][2].cpu()
+    fs_host = None if sets[0][3] is None else sets[0][3].cpu()
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    ms_per_step = total_ms / args.steps
-    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
-    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step, {gbps:.0f} GB/s")
-
-    copy_gbps, empty_us = context_measurements(nbytes, dev, stream, args.steps)
-    flushed = flushed_timing(step, dev, stream, nbytes)
-    graph = graph_timing(fwd, arg_refs, nsets, nbytes)
-
-    kernel_key = ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
-        f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}"
+    if not args.timed_only:
+        b2b = back_to_back(step, args.steps, stream)
+        rec["back_to_back"] = {"calls": args.steps, "buffer_sets": nsets, "us_per_call": round(b2b, 3),
+                               "GBps": round(gbps(nbytes, b2b), 1),
+                               "frac": round(gbps(nbytes, b2b) / PEAK_HBM_GBPS, 4)}
+        log(f"[bench] back-to-back: {b2b:.2f} us per call, {gbps(nbytes, b2b):.0f} GB/s")
+        rec["graph_replay"] = graph_timing(fwd, arg_refs, nsets, nbytes)
+        rec["copy_same_bytes"] = copy_ceiling(nbytes, dev, stream, calib, args.steps)
+        log(f"[bench] copy of the same bytes: {rec['copy_same_bytes']}")
     sha = kernel_sources_sha256()
-    traffic = profile_traffic(kernel_key, sha)
+    traffic = profile_traffic(rec["kernel"], sha)
+    rec["traffic_bytes"] = traffic
+    rec["traffic_ratio"] = None if traffic is None else round(traffic / nbytes, 4)
+    del sets, arg_refs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, w, out_host, fs_host
 
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=0, choices=[0, 1, 2, 3, 4, 5],
+                    help="0 (default): all five, headline on workload 5; N: only workload N")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "update", "bwd"],
+                    help="fwd: the forward (default); update: the decode step; "
+                         "bwd: the backward on --workload (default 2)")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="only the warm-up and timed calls (for profiling): no back-to-back, graph or copy runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="minimum time spent timing the one-thread oracle, per workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the op needs no communication: batch or channel shards run independently)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_depthwise_conv1d_amd as ccv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ccv.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    if args.op == "update":
+        args.workload = 0
+        bench_update(args, dev, props)
+        return
+    if args.op == "bwd":
+        args.workload = args.workload or 2
+        bench_bwd(args, dev, props)
+        return
+
+    calib = Calib(dev)
+    stream = torch.cuda.current_stream()
+    floor_us = empty_floor(stream, calib)
+    log(f"[bench] empty kernel: {floor_us:.2f} us per launch")
+    ns = [args.workload] if args.workload else [1, 2, 3, 4, 5]
+    head = args.workload or HEADLINE_WORKLOAD
+    records = {}
+    for n in ns:
+        rec, w, out_host, fs_host = measure_forward(n, args, dev, props, calib)
+        if not args.no_cpu_baseline:
+            rec["oracle"] = oracle_leg(w, out_host, fs_host, rec["algorithmic_bytes"], args.cpu_seconds)
+        records[n] = rec
+        del w, out_host, fs_host
+
+    r = records[head]
+    fl = r["flushed_calls"]
+    med_us, mean_us = fl["median_us"], fl["mean_us"]
+    value = gbps(r["algorithmic_bytes"], med_us)
+    achieved = gbps(r["algorithmic_bytes"], mean_us)
     result = {
         "metric": METRIC,
-        "value": round(gbps, 1),
+        "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(med_us * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "description": w.notes.get("description"),
-            "B": w.B, "C": w.C, "L": w.L, "K": w.K,
-            "x_strides": list(w.x.stride()),
-            "activation": w.activation,
-            "storage_dtype": w.x_dtype,
-            "algorithmic_bytes": nbytes,
-            "buffer_sets": nsets,
-            "kernel": kernel_key,
-            "plan": plan,
-        },
-        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "config": {k: r[k] for k in ("workload", "description", "B", "C", "L", "K", "x_strides", "activation",
+                                     "storage_dtype", "algorithmic_bytes", "kernel", "plan")},
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "timing": "value: algorithmic bytes / median of the K flushed single calls (HIP events on the "
+                  "launch stream); roofline.achieved: the same bytes / their mean",
         "roofline": {
             "bound": "hbm",
-            "achieved": round(gbps, 1),
+            "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
-            "frac": round(gbps / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
-            "kernel": kernel_key,
-            "avg_launch_us": round(ms_per_step * 1e3, 3),
-            "algorithmic_bytes_per_launch": nbytes,
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": r["traffic_bytes"],
+            "kernel": r["kernel"],
+            "avg_launch_us": mean_us,
+            "algorithmic_bytes_per_launch": r["algorithmic_bytes"],
         },
         "context": {
-            "copy_same_bytes_GBps": round(copy_gbps, 1),
-            "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
-            "empty_kernel_us": round(empty_us, 3),
-            "flushed_calls": flushed,
-            "graph_replay": graph,
+            "headline_record": {k: v for k, v in r.items() if k != "oracle"},
+            "per_workload": {str(n): v for n, v in records.items() if n != head},
+            "empty_kernel_us": round(floor_us, 3),
             "device": props.name,
             "cu_count": props.multi_processor_count,
             "device_properties": device_properties(props),
-            "kernel_sources_sha256": sha,
+            "kernel_sources_sha256": kernel_sources_sha256(),
             "env_overrides": env_overrides(),
         },
     }
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, sets[0][2], nbytes, args.cpu_seconds)
-
+    if "oracle" in r:
+        o = r["oracle"]
+        result["cpu_baseline"] = dict(o["one_thread"], all_cores=o["all_cores"], parity=o["parity"],
+                                      host_cpu=o["host_cpu"], compile_flags=o["compile_flags"])
     print(json.dumps(result), flush=True)
 
 
 def context_measurements(nbytes, dev, stream, steps):
-    """Context on the same GPU: a plain copy kernel moving the same bytes (half read,
-    half written, rotated over >= 1 GiB), and the launch floor of an empty kernel."""
-    import ctypes
-
-    import torch
-
-    import causal_depthwise_conv1d_amd as ccv
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    calib = ctypes.CDLL(ccv.CALIB_LIB_PATH)
-    calib.ccv_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    calib.ccv_calib_empty.argtypes = [ctypes.c_void_p]
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    half = (nbytes // 2) // 16 * 16
-    csets = max(2, math.ceil(ROTATION_BYTES / (2 * half)))
-    bufs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.zeros(half, dtype=torch.uint8, device=dev))
-            for _ in range(csets)]
-    for i in range(20):
-        d, s_ = bufs[i % csets]
-        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
-    ev0.record(stream)
-    for i in range(steps):
-        d, s_ = bufs[i % csets]
-        calib.ccv_calib_copy(d.data_ptr(), s_.data_ptr(), half, sp)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = ev0.elapsed_time(ev1) / steps
-    copy_gbps = 2 * half / (copy_ms * 1e-3) / 1e9
-    del bufs
-    for _ in range(50):
-        calib.ccv_calib_empty(sp)
-    ev0.record(stream)
-    for _ in range(1000):
-        calib.ccv_calib_empty(sp)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    empty_us = ev0.elapsed_time(ev1)  # ms for 1000 launches = us per launch
-    log(f"[bench] copy of the same bytes: {copy_gbps:.0f} GB/s; empty kernel {empty_us:.2f} us")
-    return copy_gbps, empty_us
+    """The copy ceiling and the empty-kernel floor, for the update and backward
+    lines: (best copy GB/s, empty kernel us)."""
+    calib = Calib(dev)
+    c = copy_ceiling(nbytes, dev, stream, calib, steps)
+    floor_us = empty_floor(stream, calib)
+    log(f"[bench] copy of the same bytes: {c['GBps']:.0f} GB/s ({c['form']}); empty kernel {floor_us:.2f} us")
+    return c["GBps"], floor_us
 
 
 def graph_timing(fwd, arg_refs, nsets, nbytes, calls=100, reps=5):
@@ -342,38 +492,6 @@ def env_overrides() -> dict:
     in a default run; any set here change the launch the numbers come from)."""
     names = ("CCV_CF_WAVES_PER_CU", "CCV_CL_WAVES_PER_CU", "CCV_CL_TILE_T", "CCV_CU_COUNT", "CCV_FORCE_SCALAR")
     return {n: os.environ[n] for n in names if n in os.environ}
-
-
-def flushed_timing(step, dev, stream, nbytes, iters=20):
-    """Single calls with the caches flushed before each (a 1 GiB copy, more than the
-    256 MB Infinity Cache and the L2s), each between its own pair of HIP events:
-    median, min and max over `iters` calls.  Context beside the back-to-back figure."""
-    import ctypes
-
-    import torch
-
-    import causal_depthwise_conv1d_amd as ccv
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    calib = ctypes.CDLL(ccv.CALIB_LIB_PATH)
-    calib.ccv_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    half = 512 << 20
-    src = torch.zeros(half, dtype=torch.uint8, device=dev)
-    dst = torch.empty(half, dtype=torch.uint8, device=dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    us = []
-    for i in range(iters):
-        calib.ccv_calib_copy(dst.data_ptr(), src.data_ptr(), half, sp)
-        ev0.record(stream)
-        step(i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        us.append(ev0.elapsed_time(ev1) * 1e3)
-    del src, dst
-    us.sort()
-    med = us[len(us) // 2] if len(us) % 2 else 0.5 * (us[len(us) // 2 - 1] + us[len(us) // 2])
-    log(f"[bench] flushed single calls: median {med:.2f} us (min {us[0]:.2f}, max {us[-1]:.2f})")
-    return {"iters": iters, "median_us": round(med, 3), "min_us": round(us[0], 3), "max_us": round(us[-1], 3),
-            "median_GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}
 
 
 def device_properties(props) -> dict:
@@ -759,70 +877,111 @@ def update_cpu_baseline(w, nbytes, min_seconds, first_out, first_state):
             "seconds_per_pass": round(sec, 4), "parity": parity}
 
 
-def cpu_baseline(w, out_gpu, nbytes, min_seconds):
-    """The oracle as written (single-threaded fp64 loop) on this host's CPU, over
-    the whole workload, repeated until at least `min_seconds` have passed; then the
-    GPU output of this run compared with it at every output."""
-    import numpy as np
-    import torch
-
-    from oracle import compare as ocmp
-    from oracle import round_out
-    from oracle.from_torch import case, dtype_name, raw
-
-    c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
-    passes, t_total = 0, 0.0
-    y = s = None
-    while passes == 0 or t_total < min_seconds:
-        t0 = time.perf_counter()
-        y, s = c.fwd()
-        round_out(w.x_dtype, y)
-        t_total += time.perf_counter() - t0
-        passes += 1
-    sec = t_total / passes
-    log(f"[bench] cpu oracle: {passes} passes, {sec:.2f} s per pass")
-    # The same loop on all of this host's cores (context, not the baseline): rows of
-    # (b, c) split between threads, results bit-identical to the single thread.
-    from oracle import GCC_CMD
-    nthr = max(1, min(16, len(os.sched_getaffinity(0))))
-    mt_passes, mt_total, ymt = 0, 0.0, None
-    while mt_passes == 0 or mt_total < min(min_seconds, 3.0):
-        t0 = time.perf_counter()
-        ymt, _ = c.fwd_threads(nthr)
-        round_out(w.x_dtype, ymt)
-        mt_total += time.perf_counter() - t0
-        mt_passes += 1
-    mt_sec = mt_total / mt_passes
-    log(f"[bench] cpu oracle on {nthr} threads: {mt_passes} passes, {mt_sec:.3f} s per pass")
-    g = raw(out_gpu.cpu().contiguous())
-    res = ocmp.compare(dtype_name(out_gpu), w.K, g, y, s)
-    cpu_name = ""
+def host_cpu_name() -> str:
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu_name = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {
-        "value": round(nbytes / sec / 1e9, 4),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"the whole workload ({w.B * w.C * w.L} outputs), {passes} pass(es) of the "
-                  "single-threaded fp64 oracle incl. rounding to the output dtype",
-        "seconds_per_pass": round(sec, 3),
-        "host_cpu": cpu_name,
-        "host_threads_available": os.cpu_count(),
-        "compile_flags": " ".join(f for f in GCC_CMD[1:] if f.startswith("-") and f not in ("-o", "-shared")),
-        "all_cores": {"value": round(nbytes / mt_sec / 1e9, 4), "unit": "GB/s", "threads": nthr,
-                      "seconds_per_pass": round(mt_sec, 4), "passes": mt_passes,
-                      "bit_identical_to_one_thread": bool(np.array_equal(ymt.view(np.uint64), y.view(np.uint64)))},
-        "parity": {"outputs": res["n"], "out_of_tolerance": res["n_bad"], "max_ulp": res["max_ulp"],
-                   "max_rel": res["max_rel"], "floor_only": res["n_floor_only"],
-                   "bit_equal": res["bit_equal"]},
-    }
+    return ""
+
+
+def oracle_pieces(w, max_outputs):
+    """(b, c0, c1) pieces of at most max_outputs outputs (at least one channel)
+    that together cover the workload once; channels are independent, so each
+    piece is an exact sub-problem."""
+    ch = max(1, min(w.C, max_outputs // max(1, w.L)))
+    return [(b, c0, min(w.C, c0 + ch)) for b in range(w.B) for c0 in range(0, w.C, ch)]
+
+
+def sub_case(w, b, c0, c1):
+    from oracle.from_torch import case
+    return case(w.x[b:b + 1, c0:c1], w.weight[c0:c1], None if w.bias is None else w.bias[c0:c1],
+                None if w.seq_idx is None else w.seq_idx[b:b + 1],
+                None if w.initial_states is None else w.initial_states[b:b + 1, c0:c1], w.activation)
+
+
+def oracle_leg(w, out_host, fs_host, nbytes, min_seconds):
+    """The oracle as written on this host's CPU.
+
+    One thread (the baseline): the plain fp64 loop, rounding included, over a
+    bounded sample -- the whole workload when it has at most 2^25 outputs,
+    otherwise its first (b, channel range) piece of at most 2^25 outputs --
+    repeated until at least `min_seconds` have passed; GB/s = the sample's share
+    of the algorithmic bytes / time.
+
+    All cores (context): the same per-output function on up to 16 threads over
+    the whole workload, piece by piece; every output of this run's GPU result is
+    compared with it at the stated tolerances, and the final states bit for bit."""
+    import numpy as np
+
+    from oracle import GCC_CMD, round_out
+    from oracle import compare as ocmp
+    from oracle.from_torch import dtype_name, raw
+
+    total = w.B * w.C * w.L
+    pieces = oracle_pieces(w, 1 << 25)
+    b, c0, c1 = pieces[0]
+    sample = sub_case(w, b, c0, c1)
+    n_sample = (c1 - c0) * w.L
+    passes, t_total, y1 = 0, 0.0, None
+    while passes == 0 or t_total < min_seconds:
+        t0 = time.perf_counter()
+        y1, _ = sample.fwd()
+        round_out(w.x_dtype, y1)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    sec = t_total / passes
+    share = n_sample / total
+    log(f"[bench] cpu oracle, one thread: {n_sample} outputs, {passes} passes, {sec:.3f} s per pass")
+    one = {"value": round(nbytes * share / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": (f"batch {b}, channels [{c0},{c1}) x {w.L} steps = {n_sample} of {total} outputs "
+                      f"({100 * share:.1f}%), {passes} pass(es) of the single-threaded fp64 oracle incl. "
+                      "rounding to the output dtype; GB/s scaled by that share of the algorithmic bytes"),
+           "seconds_per_pass": round(sec, 4),
+           "seconds_whole_workload_est": round(sec / share, 3)}
+
+    nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+    out_c = out_host.contiguous()
+    t_oracle, t_check = 0.0, 0.0
+    tot = {"outputs": 0, "out_of_tolerance": 0, "max_ulp": 0, "max_rel": 0.0, "floor_only": 0, "bit_equal": 0}
+    same_as_one_thread = None
+    for (b, c0, c1) in pieces:
+        c = sub_case(w, b, c0, c1)
+        t0 = time.perf_counter()
+        y, s = c.fwd_threads(nthr)
+        round_out(w.x_dtype, y)
+        t_oracle += time.perf_counter() - t0
+        if same_as_one_thread is None:
+            same_as_one_thread = bool(np.array_equal(y.view(np.uint64), y1.view(np.uint64)))
+        t0 = time.perf_counter()
+        g = out_c[b:b + 1, c0:c1].contiguous()
+        res = ocmp.compare(dtype_name(g), w.K, raw(g), y, s)
+        t_check += time.perf_counter() - t0
+        tot["outputs"] += res["n"]
+        tot["out_of_tolerance"] += res["n_bad"]
+        tot["floor_only"] += res["n_floor_only"]
+        tot["bit_equal"] += res["bit_equal"]
+        tot["max_ulp"] = max(tot["max_ulp"], res["max_ulp"] or 0)
+        tot["max_rel"] = max(tot["max_rel"], res["max_rel"])
+    if w.x_dtype == "f32":
+        tot["max_ulp"] = None
+    if fs_host is not None:
+        from oracle.from_torch import case
+        want = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation).final_states()
+        got = raw(fs_host.contiguous())
+        bits = np.uint32 if got.dtype == np.float32 else np.uint16
+        tot["final_states_bit_exact"] = bool(np.array_equal(got.view(bits), want.view(bits)))
+    log(f"[bench] cpu oracle on {nthr} threads: whole workload in {t_oracle:.2f} s; parity {tot} "
+        f"(checked in {t_check:.1f} s)")
+    allc = {"value": round(nbytes / t_oracle / 1e9, 4), "unit": "GB/s", "threads": nthr,
+            "seconds_whole_workload": round(t_oracle, 3), "pieces": len(pieces),
+            "first_piece_bit_identical_to_one_thread": same_as_one_thread}
+    return {"one_thread": one, "all_cores": allc, "parity": tot, "host_cpu": host_cpu_name(),
+            "host_threads_available": os.cpu_count(),
+            "compile_flags": " ".join(f for f in GCC_CMD[1:] if f.startswith("-") and f not in ("-o", "-shared"))}
 
 
 if __name__ == "__main__":

@@ -68,3 +68,32 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True,
                        timeout=300)
     assert r.returncode != 0 and "one GPU" in r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("i", [1, 3, 5])
+def test_oracle_pieces_cover_every_row_once(i):
+    import numpy as np
+    w = wl.workload(i, L_override=4096 if i != 1 else None)
+    seen = np.zeros((w.B, w.C), dtype=int)
+    for b, c0, c1 in bench.oracle_pieces(w, 1 << 16):
+        assert c1 > c0 and (c1 - c0) * w.L <= max(1 << 16, w.L)
+        seen[b, c0:c1] += 1
+    assert (seen == 1).all()
+
+
+def test_oracle_leg_accounting_on_the_small_workload():
+    """The oracle leg on a result that is the oracle's own rounded output: every
+    output counted once, none out of tolerance, all bit-equal, and the one-thread
+    sample scaled to the whole workload's bytes."""
+    import torch
+
+    from oracle import round_out
+    from oracle.from_torch import case
+    w = wl.workload(1)
+    y, _ = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation).fwd()
+    out = torch.from_numpy(round_out("f32", y))
+    r = bench.oracle_leg(w, out, None, bench.algorithmic_bytes(w), 0.01)
+    p = r["parity"]
+    assert p["outputs"] == p["bit_equal"] == 64 * 2048 and p["out_of_tolerance"] == 0
+    assert r["one_thread"]["cores"] == 1 and "2048" in r["one_thread"]["sample"]
+    assert r["all_cores"]["first_piece_bit_identical_to_one_thread"]
