@@ -266,9 +266,19 @@ def _strides3(t: Optional[torch.Tensor]):
     return _I64x3(*(t.stride() if t is not None else (0, 0, 0)))
 
 
+def _contiguous_ids(seq_idx):
+    """The C ABI reads seq_idx as a contiguous [B, L] array: refuse any other layout
+    (a view with other strides would be read as different ids)."""
+    if seq_idx is not None and not seq_idx.is_contiguous():
+        raise ValueError("seq_idx must be contiguous [B, L] for the C ABI; call .contiguous() first")
+    return seq_idx
+
+
 def make_args(x, weight, out, bias=None, seq_idx=None, initial_states=None,
               final_states_out=None, activation=None) -> ccv_fwd_args_t:
-    """Fill a ccv_fwd_args_t from tensors (no checks beyond dtype codes)."""
+    """Fill a ccv_fwd_args_t from tensors (no checks beyond dtype codes and a
+    contiguous seq_idx)."""
+    _contiguous_ids(seq_idx)
     B, C, L = x.shape
     a = ccv_fwd_args_t()
     a.B, a.C, a.L = B, C, L
@@ -454,7 +464,9 @@ def update_plan_for(x, conv_state, weight, bias=None, activation=None) -> dict:
 def make_bwd_args(x, weight, bias, dout, dx, dweight, dbias=None, seq_idx=None, initial_states=None,
                   dfinal_states=None, dinitial_states=None, activation=None,
                   workspace=None) -> ccv_bwd_args_t:
-    """Fill a ccv_bwd_args_t from tensors (no checks beyond dtype codes)."""
+    """Fill a ccv_bwd_args_t from tensors (no checks beyond dtype codes and a
+    contiguous seq_idx)."""
+    _contiguous_ids(seq_idx)
     B, C, L = x.shape
     a = ccv_bwd_args_t()
     a.B, a.C, a.L = B, C, L

@@ -483,3 +483,21 @@ def test_bwd_plan():
                                    dout_stride=(2048 * 4095, 4095, 1), dx_stride=(2048 * 4095, 4095, 1)))
     assert st == 0 and p.vector == 0 and p.work_items == 4 * 128 * 2048 and p.grid == 4 * 128 * 2048 // 256
     assert ccv.ccv_bwd_plan(bargs(dx_stride=(64 * 1000, 1, 64)))[1].vector == 0
+
+
+def test_binding_refuses_non_contiguous_seq_idx():
+    """The C ABI reads seq_idx as a contiguous [B, L] array, so the binding's argument
+    builders refuse a view with other strides instead of passing its pointer on."""
+    import torch
+
+    import workloads as wl
+    ids = wl.seq_idx_from_lengths([3, 5], 2)
+    assert ids.is_contiguous() and ids.stride() == (8, 1)
+    x = torch.zeros(2, 4, 8)
+    wt = torch.zeros(4, 4)
+    bad = torch.zeros(8, 2, dtype=torch.int32).t()
+    with pytest.raises(ValueError, match="contiguous"):
+        ccv.make_args(x, wt, x.clone(), seq_idx=bad)
+    with pytest.raises(ValueError, match="contiguous"):
+        ccv.make_bwd_args(x, wt, None, x, x.clone(), wt.clone(), seq_idx=bad)
+    ccv.make_args(x, wt, x.clone(), seq_idx=bad.contiguous())

@@ -75,18 +75,29 @@ def bwd_plan(x, weight, dout, seq=None):
     return plan
 
 
+# The most roundings' worth the parameter-gradient tolerance may grant, fixed by
+# the tests rather than by the kernels' plans: a kernel change that lengthens a
+# lane's in-order sum (longer tiles, more tiles per partial row, a deeper tree)
+# past it fails here instead of silently widening the tolerance.  The current
+# plans need at most 59 (channel-last: 4 tiles of 32 steps per partial row, three
+# tree levels).
+PARAM_TERMS_CAP = 64
+
+
 def param_terms_for(plan, B, L, K):
     """compare()'s K for the parameter gradients: (n + 32 * levels + K + 8) / 4
     roundings of 2^-22 cover a lane's in-order sum of n terms, the levels of the
     fan-in-32 reduction tree over the partial rows, and the error of dz.  The
     register-only channel-first path: n = its span / 64 elements plus the 7 additions of
     the 64-lane sum, a partial row per segment; the other paths: n = the tiles
-    per partial row times the tile length."""
+    per partial row times the tile length.  Never more than PARAM_TERMS_CAP."""
     if plan.vector == 3:
         n, parts = plan.span // 64 + 7, B * max(1, math.ceil(L / plan.span))
     else:
         n, parts = plan.unroll * plan.span, B * max(1, math.ceil(math.ceil(L / plan.span) / plan.unroll))
-    return math.ceil((n + 32 * reduction_levels(parts) + K + 8) / 4)
+    k = math.ceil((n + 32 * reduction_levels(parts) + K + 8) / 4)
+    assert k <= PARAM_TERMS_CAP, f"the plan's parameter sums need {k} > {PARAM_TERMS_CAP} roundings' worth"
+    return k
 
 
 def param_terms(w, plan):

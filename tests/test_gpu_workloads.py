@@ -66,13 +66,16 @@ def sampled_check(w, out_gpu, extra_t=None, n_random=200_000, seed=0):
 ORACLE_THREADS = min(16, len(os.sched_getaffinity(0)))
 
 # Outputs allowed to pass only through the K * 2^-22 * S floor (a cancellation far
-# below the terms' magnitudes).  None for 16-bit outputs: an fp32 fused
-# multiply-add chain rounded to bf16 / fp16 stays within two ulps of the format on
-# all 268 million outputs of these workloads (checked on the CPU with the oracle's
-# binary32 mode).  For fp32 outputs rel 1e-5 is only ~170 fp32 roundings of the
-# result, and that same emulation leaves 0.095% (small workload, SiLU) and 0.076%
-# (long workload) of outputs to the floor; the bound is three times that.
-FLOOR_ONLY_FRACTION = {"bf16": 0.0, "f16": 0.0, "f32": 3e-3}
+# below the terms' magnitudes).  For 16-bit outputs that needs |y| below about
+# K * 2^-16 * S and fp32 roundings that did not cancel: the GPU leaves 1 of the 268
+# million outputs of the strided bf16 workload to the floor (64 ulps at a value
+# near zero), none of the others; an emulation with the oracle's binary32 chain
+# gives none on the CPU.  The bound, 1e-7 of the outputs, still fails any
+# systematic error by orders of magnitude.  For fp32 outputs rel 1e-5 is only ~170
+# fp32 roundings of the result, and the emulation leaves 0.095% (small workload,
+# SiLU) and 0.076% (long workload) of outputs to the floor; the bound is three
+# times that.
+FLOOR_ONLY_FRACTION = {"bf16": 1e-7, "f16": 1e-7, "f32": 3e-3}
 
 
 def full_check(w, out_gpu, pieces):
