@@ -96,8 +96,8 @@ def packed_lengths(total: int, nseq: int, min_len: int, seed: int) -> np.ndarray
 
 def seq_idx_from_lengths(lengths, B: int = 1) -> torch.Tensor:
     ids = np.repeat(np.arange(len(lengths), dtype=np.int32), np.asarray(lengths))
-    # C order: a plain copy of the broadcast view would keep the batch axis fastest
-    return torch.from_numpy(np.ascontiguousarray(np.broadcast_to(ids, (B, ids.size))))
+    # a C-order copy: a plain copy of the broadcast view would keep the batch axis fastest
+    return torch.from_numpy(np.array(np.broadcast_to(ids, (B, ids.size)), order="C"))
 
 
 @dataclass
