@@ -44,8 +44,9 @@ CCV_PATH_NONE, CCV_PATH_CHANNEL_FIRST, CCV_PATH_CHANNEL_LAST, CCV_PATH_UPDATE, C
 STATUS = {
     0: "CCV_OK", -1: "CCV_E_NULL", -2: "CCV_E_SHAPE", -3: "CCV_E_KSIZE", -4: "CCV_E_DTYPE",
     -5: "CCV_E_LAYOUT", -6: "CCV_E_UNSUPPORTED", -7: "CCV_E_ALIAS", -8: "CCV_E_HIP",
-    -9: "CCV_E_INTERNAL", -10: "CCV_E_ABI",
+    -9: "CCV_E_INTERNAL", -10: "CCV_E_ABI", -11: "CCV_E_SCRATCH",
 }
+CCV_BWD_STATIC_SCRATCH_BYTES = 64 << 20
 DTYPE_CODE = {torch.float32: CCV_F32, torch.float16: CCV_F16, torch.bfloat16: CCV_BF16}
 
 _I64x3 = ctypes.c_int64 * 3
@@ -172,6 +173,8 @@ def lib() -> ctypes.CDLL:
         L.ccv_bwd_check.restype = ctypes.c_int
         L.ccv_bwd_plan.argtypes = [G, ctypes.POINTER(ccv_plan_t)]
         L.ccv_bwd_plan.restype = ctypes.c_int
+        L.ccv_bwd_static.argtypes = [G, ctypes.c_void_p]
+        L.ccv_bwd_static.restype = ctypes.c_int
         L.ccv_bwd_workspace_size.argtypes = [G]
         L.ccv_bwd_workspace_size.restype = ctypes.c_int64
         L.ccv_status_str.argtypes = [ctypes.c_int]
@@ -230,6 +233,12 @@ def ccv_update_plan(args: ccv_update_args_t):
 def ccv_bwd(args: ccv_bwd_args_t, stream=None) -> int:
     """Enqueue the backward (two kernels) on `stream`; returns the status code."""
     return lib().ccv_bwd(ctypes.byref(args), ctypes.c_void_p(_stream_handle(stream)))
+
+
+def ccv_bwd_static(args: ccv_bwd_args_t, stream=None) -> int:
+    """ccv_bwd with the partial sums in the library's fixed device array (no
+    workspace, nothing allocated)."""
+    return lib().ccv_bwd_static(ctypes.byref(args), ctypes.c_void_p(_stream_handle(stream)))
 
 
 def ccv_bwd_check(args: ccv_bwd_args_t) -> int:

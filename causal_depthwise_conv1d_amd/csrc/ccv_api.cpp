@@ -234,6 +234,7 @@ const char* ccv_status_str(int s) {
     case CCV_E_HIP: return "CCV_E_HIP";
     case CCV_E_INTERNAL: return "CCV_E_INTERNAL";
     case CCV_E_ABI: return "CCV_E_ABI";
+    case CCV_E_SCRATCH: return "CCV_E_SCRATCH";
   }
   return "CCV_E_UNKNOWN";
 }

@@ -86,7 +86,9 @@ typedef enum {
   CCV_E_ALIAS = -7,       /* out == x, or final_states_out is x, out or initial_states */
   CCV_E_HIP = -8,         /* the HIP runtime refused the launch */
   CCV_E_INTERNAL = -9,    /* an unexpected internal condition */
-  CCV_E_ABI = -10         /* struct_size does not match this library's struct */
+  CCV_E_ABI = -10,        /* struct_size does not match this library's struct */
+  CCV_E_SCRATCH = -11     /* ccv_bwd_static: the call needs more partial-sum space than
+                             the library's fixed array (CCV_BWD_STATIC_SCRATCH_BYTES) */
 } ccv_status_t;
 
 /* All arguments of one forward call.  Strides are in elements. */
@@ -287,6 +289,30 @@ int ccv_bwd_check(const ccv_bwd_args_t* args);
  * gradient kernel.  The workspace fields are not checked here, so a plan can
  * be had before the workspace is allocated. */
 int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan);
+
+/* ---- backward without allocation --------------------------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  ccv_bwd_static is ccv_bwd
+ * with the fp32 partial sums in a fixed device array of the library instead of the
+ * caller's workspace; the caller still passes (and owns) every input and output,
+ * and args->workspace / workspace_bytes are ignored.  Same kernels, same launches,
+ * same results bit for bit.
+ *
+ * The array holds CCV_BWD_STATIC_SCRATCH_BYTES (64 MiB, enough for every call
+ * whose ccv_bwd_workspace_size is at most that: e.g. bf16 [8, 4096, 8192] needs
+ * 40 MiB); a call that needs more returns CCV_E_SCRATCH and enqueues nothing.
+ * Each GPU the library runs on holds its own array from the first call there until
+ * the process ends.  The call allocates nothing (no hipMalloc, no hipFree); its
+ * first call on a device looks up that device's array address once.  The stream
+ * (NULL = the null stream of the current device) must belong to the current device,
+ * else CCV_E_UNSUPPORTED.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (on different streams, or from several host
+ * threads without ordering) race on it and give wrong parameter gradients; calls
+ * ordered on one stream are fine.  Nothing in the array needs clearing between
+ * calls (each call writes every partial sum it reads).  Other errors as ccv_bwd. */
+#define CCV_BWD_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+int ccv_bwd_static(const ccv_bwd_args_t* args, void* hip_stream);
 
 /* Static, NUL-terminated name of a status code ("CCV_OK", ...). */
 const char* ccv_status_str(int status);

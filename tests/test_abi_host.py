@@ -485,6 +485,23 @@ def test_bwd_plan():
     assert ccv.ccv_bwd_plan(bargs(dx_stride=(64 * 1000, 1, 64)))[1].vector == 0
 
 
+def test_bwd_static_refuses_calls_beyond_its_scratch():
+    """ccv_bwd_static checks the partial-sum space it needs against its fixed array
+    before touching any device."""
+    a = ccv.ccv_bwd_args_t()
+    a.B, a.C, a.L, a.K = 16, 8192, 8192, 4
+    a.x_dtype = a.w_dtype = ccv.CCV_BF16
+    a.x, a.dout, a.dx, a.weight, a.dweight = X, OUT, FIN, W, BIAS
+    for f in ("x_stride", "dout_stride", "dx_stride"):
+        setattr(a, f, type(getattr(a, f))(8192 * 8192, 1, 8192))
+    assert ccv.ccv_bwd_workspace_size(a) > ccv.CCV_BWD_STATIC_SCRATCH_BYTES == 64 << 20
+    static = ccv.lib().ccv_bwd_static
+    assert ccv.STATUS[static(ctypes.byref(a), None)] == "CCV_E_SCRATCH"
+    assert ccv.STATUS[static(None, None)] == "CCV_E_NULL"
+    a.dx = X                                           # argument errors come first, as in ccv_bwd
+    assert ccv.STATUS[static(ctypes.byref(a), None)] == "CCV_E_ALIAS"
+
+
 def test_binding_refuses_non_contiguous_seq_idx():
     """The C ABI reads seq_idx as a contiguous [B, L] array, so the binding's argument
     builders refuse a view with other strides instead of passing its pointer on."""
