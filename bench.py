@@ -240,7 +240,7 @@ def empty_floor(stream, calib):
 def kernel_key_of(w, plan):
     import causal_depthwise_conv1d_amd as ccv
     return ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
-        f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}"
+        f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}" + ("" if w.w_dtype == w.x_dtype else f"_w{w.w_dtype}")
 
 
 def measure_forward(n, args, dev, props, calib):
@@ -256,6 +256,12 @@ def measure_forward(n, args, dev, props, calib):
 
     t0 = time.time()
     w = wl.workload(n)
+    if args.w_dtype and args.w_dtype != w.w_dtype:
+        # the same weight values stored in another dtype (exact when widening)
+        w.weight = w.weight.to(wl.TORCH_DTYPES[args.w_dtype])
+        w.bias = None if w.bias is None else w.bias.to(wl.TORCH_DTYPES[args.w_dtype])
+        w.w_dtype = args.w_dtype
+        w.name += f"_w{args.w_dtype}"
     log(f"[bench] workload {n} {w.name}: generated in {time.time() - t0:.1f}s")
     nbytes = algorithmic_bytes(w)
     set_bytes = 2 * w.x.numel() * w.x.element_size()
@@ -307,6 +313,7 @@ def measure_forward(n, args, dev, props, calib):
         "x_strides": list(w.x.stride()),
         "activation": w.activation,
         "storage_dtype": w.x_dtype,
+        "weight_dtype": w.w_dtype,
         "algorithmic_bytes": nbytes,
         "kernel": kernel_key_of(w, plan),
         "plan": plan,
@@ -350,6 +357,9 @@ def main():
     ap.add_argument("--op", default="fwd", choices=["fwd", "update", "bwd"],
                     help="fwd: the forward (default); update: the decode step; "
                          "bwd: the backward on --workload (default 2)")
+    ap.add_argument("--w-dtype", default=None, choices=["f32", "bf16", "f16"],
+                    help="store the workload's weights and bias in this dtype instead (same values "
+                         "when widening): a mixed x / weight dtype call")
     ap.add_argument("--timed-only", action="store_true",
                     help="only the warm-up and timed calls (for profiling): no back-to-back, graph or copy runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -415,7 +425,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {k: r[k] for k in ("workload", "description", "B", "C", "L", "K", "x_strides", "activation",
-                                     "storage_dtype", "algorithmic_bytes", "kernel", "plan")},
+                                     "storage_dtype", "weight_dtype", "algorithmic_bytes", "kernel", "plan")},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "timing": "value: algorithmic bytes / median of the K flushed single calls (HIP events on the "
                   "launch stream); roofline.achieved: the same bytes / their mean",

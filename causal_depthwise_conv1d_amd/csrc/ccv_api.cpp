@@ -173,7 +173,11 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
     const int64_t cap = wpc > 0 ? (int64_t)cu_count() * wpc : nwork;
     c.nwaves = nwork < cap ? nwork : cap;
     if (c.nwaves < 1) c.nwaves = 1;
-    P.unroll = kClUnroll;
+    // Whole tiles of whole channel vectors take the straight-line path when all of
+    // their loads can be vectors; then two row batches are in flight per lane.
+    const bool straight = P.vector && c.vec_par && tile % kClUnroll == 0 &&
+                          (!a->initial_states || c.vec_init) && (!a->seq_idx || c.vec_seq);
+    P.unroll = straight ? 2 * kClUnroll : kClUnroll;
     P.span = tile;
     P.channels_per_item = 64 * V;
   }

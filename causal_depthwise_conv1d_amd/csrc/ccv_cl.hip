@@ -64,8 +64,8 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
   constexpr int U = kClUnroll;
   constexpr int H = K - 1;
   constexpr int ES = sizeof(typename S::raw);
-  constexpr int NWV = V * K * WB / 16;               // weight vectors per lane
-  constexpr int NBV = V * WB / 16;                   // bias vectors per lane
+  constexpr int NWB = V * K * WB;                    // bytes of a lane's weights
+  constexpr int NBB = V * WB;                        // bytes of a lane's biases
   static_assert(U == 4 && U >= H, "a row batch is 4 rows and covers the history");
   const Common& m = a.m;
   const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
@@ -79,15 +79,11 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
 
   // Parameters and history first: waiting for them later leaves the row batches
   // issued after them in flight.
-  u32x4 wv[NWV], bv[NBV];
+  uint32_t wv[NWB / 4], bv[NBB / 4];
   const uintptr_t wl = reinterpret_cast<uintptr_t>(m.w) + cbase * K * WB;
-  const uint32_t lw = (uint32_t)lane * (V * K * WB);
-#pragma unroll
-  for (int q = 0; q < NWV; ++q) wv[q] = gload<u32x4>(wl + q * 16 + lw);
+  load_param_block<NWB>(wl + (uint32_t)lane * NWB, wv);
   const uintptr_t bl = pick(m.bias != nullptr, reinterpret_cast<uintptr_t>(m.bias) + cbase * WB, zero);
-  const uint32_t lb = (uint32_t)lane * (V * WB);
-#pragma unroll
-  for (int q = 0; q < NBV; ++q) bv[q] = gload<u32x4>(bl + q * 16 + lb);
+  load_param_block<NBB>(bl + (uint32_t)lane * NBB, bv);
   u32x4 hv[H];
   const uintptr_t il = reinterpret_cast<uintptr_t>(m.init) + (p.b * m.is_b + cbase) * ES;
 #pragma unroll
@@ -115,14 +111,9 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
   for (int i = 0; i < V; ++i) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int f = i * K + k;                       // element of the lane's weight block
-      const uint32_t r = WB == 4 ? dword(wv[f / 4], f % 4)
-                                 : (dword(wv[f / 8], (f / 2) % 4) >> (16 * (f % 2))) & 0xffffu;
-      w[i][k] = param_f32<WB>(r, m.w_dtype);
+      w[i][k] = param_f32<WB>(block_param_raw<WB>(wv, i * K + k), m.w_dtype);
     }
-    const uint32_t r = WB == 4 ? dword(bv[i / 4], i % 4)
-                               : (dword(bv[i / 8], (i / 2) % 4) >> (16 * (i % 2))) & 0xffffu;
-    beta[i] = param_f32<WB>(r, m.w_dtype);
+    beta[i] = param_f32<WB>(block_param_raw<WB>(bv, i), m.w_dtype);
   }
   // Sliding window of the last K rows as fp32: win[0] is the oldest.
   float win[K][V];
@@ -344,14 +335,11 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
   const int64_t w0 = (int64_t)g * kWavesPerGroup + wave;
   if (w0 >= a.nwaves) return;                       // whole wave leaves together
   const int64_t W = a.nwaves;
-  // The straight-line path exists when a lane's weight and bias blocks are whole
-  // 16-byte vectors.
-  constexpr bool kFastShape = (V * K * WB) % 16 == 0 && (V * WB) % 16 == 0;
 
   if (m.L > 0) {
     for (int64_t it = w0; it < m.nwork; it += W) {
       const TilePos p = tile_pos(a, it);
-      if constexpr (VEC && kFastShape) {
+      if constexpr (VEC) {
         const int64_t t0 = p.tt * a.tile;
         const bool fast = a.vec_par && (a.tile % kClUnroll) == 0 && (p.cg + 1) * (64 * V) <= m.C &&
                           t0 + a.tile <= m.L &&

@@ -11,6 +11,7 @@
 namespace ccv {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -214,6 +215,37 @@ template <int WB>
 __device__ inline uint32_t load_param_raw(uintptr_t addr) {
   if constexpr (WB == 4) return gload<uint32_t>(addr);
   else return gload<uint16_t>(addr);
+}
+
+// A lane's block of NB bytes of consecutive parameters (its V channels' weights or
+// biases), as dwords: 16-byte loads when NB is a multiple of 16 (the block then
+// starts 16-byte aligned), else 8-byte loads (fp32 data with 16-bit parameters:
+// blocks of 8 or 24 bytes, starting 8-byte aligned).
+template <int NB>
+__device__ inline void load_param_block(uintptr_t p, uint32_t (&d)[NB / 4]) {
+  static_assert(NB % 8 == 0, "parameter blocks are whole 8-byte units");
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const u32x4 v = gload<u32x4>(p + 16 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[4 * i + j] = dword(v, j);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB / 8; ++i) {
+      const u32x2 v = gload<u32x2>(p + 8 * i);
+      d[2 * i] = v[0];
+      d[2 * i + 1] = v[1];
+    }
+  }
+}
+
+// Raw parameter e of a block loaded by load_param_block (WB bytes each).
+template <int WB, int ND>
+__device__ inline uint32_t block_param_raw(const uint32_t (&d)[ND], int e) {
+  if constexpr (WB == 4) return d[e];
+  else return (d[e / 2] >> (16 * (e % 2))) & 0xffffu;
 }
 
 template <int WB>

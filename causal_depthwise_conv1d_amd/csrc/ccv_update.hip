@@ -52,22 +52,24 @@ __device__ inline void put_elems(const typename S::raw (&r)[N], u32x4* v) {
 }
 
 // The 16-byte path: a lane owns V = 16 / sizeof(raw) consecutive channels
-// c .. c+V-1 of batch row b.  With x and out unit-stride in channels, the state
-// stored [B, C, K-1] contiguously and the weights in x's dtype, the lane's x and
-// out of one step, its bias, its K*V weights and its (K-1)*V history values are
-// whole aligned vectors: K-1 + K + 2 loads and K stores cover V rows.  x and out
-// are touched once and use streaming (non-temporal) accesses; the state, which the
-// next decode step reads again, uses ordinary ones.
-template <class S, int K, bool SILU>
+// c .. c+V-1 of batch row b.  With x and out unit-stride in channels and the state
+// stored [B, C, K-1] contiguously, the lane's x and out of one step and its (K-1)*V
+// history values are whole aligned vectors, and its K*V weights and V biases (WB
+// bytes each, any of the three dtypes) whole 16- or 8-byte blocks: for bf16 with
+// bf16 weights, K-1 + K + 2 loads and K stores cover V rows.  x and out are touched
+// once and use streaming (non-temporal) accesses; the state, which the next decode
+// step reads again, uses ordinary ones.
+template <class S, int K, bool SILU, int WB>
 __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
   using raw = typename S::raw;
   constexpr int V = S::V;
   constexpr int H = K - 1;
-  const raw* wp = static_cast<const raw*>(a.w) + c * K;
-  u32x4 wv[K], bv[1], hv[H];
-#pragma unroll
-  for (int i = 0; i < K; ++i) wv[i] = load16(wp + i * V);
-  bv[0] = a.bias ? load16(static_cast<const raw*>(a.bias) + c) : u32x4{0u, 0u, 0u, 0u};
+  constexpr int NWB = V * K * WB, NBB = V * WB;    // bytes of the lane's weights, biases
+  uint32_t wv[NWB / 4], bv[NBB / 4];
+  load_param_block<NWB>(reinterpret_cast<uintptr_t>(a.w) + c * K * WB, wv);
+  load_param_block<NBB>(pick(a.bias != nullptr, reinterpret_cast<uintptr_t>(a.bias) + c * WB,
+                             reinterpret_cast<uintptr_t>(kZeroSrc)), bv);
+  u32x4 hv[H];
   raw* sp = static_cast<raw*>(a.state) + b * a.s_sb + c * H;
 #pragma unroll
   for (int i = 0; i < H; ++i) hv[i] = load16(sp + i * V);
@@ -76,9 +78,9 @@ __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
   raw hist[V][H];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
-    beta[j] = S::to_f(get_elem<S>(bv, j));
+    beta[j] = param_f32<WB>(block_param_raw<WB>(bv, j), a.w_dtype);
 #pragma unroll
-    for (int k = 0; k < K; ++k) w[j][k] = S::to_f(get_elem<S>(wv, j * K + k));
+    for (int k = 0; k < K; ++k) w[j][k] = param_f32<WB>(block_param_raw<WB>(wv, j * K + k), a.w_dtype);
 #pragma unroll
     for (int i = 0; i < H; ++i) hist[j][i] = get_elem<S>(hv, j * H + i);
   }
@@ -113,7 +115,7 @@ __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
   for (int i = 0; i < H; ++i) store16(sp + i * V, hv[i]);
 }
 
-template <class S, int K, bool SILU, bool VEC>
+template <class S, int K, bool SILU, bool VEC, int WB>
 __global__ void __launch_bounds__(kUpdateBlock) update_kernel(const UpdArgs a) {
   if constexpr (VEC) {
     constexpr int V = S::V;
@@ -129,7 +131,7 @@ __global__ void __launch_bounds__(kUpdateBlock) update_kernel(const UpdArgs a) {
       c -= q * a.C;
     }
     // C is a multiple of V, so a lane has all V of its rows or none.
-    if (first + (int64_t)lane * V < a.rows) update_rows_vec<S, K, SILU>(a, b, c);
+    if (first + (int64_t)lane * V < a.rows) update_rows_vec<S, K, SILU, WB>(a, b, c);
     return;
   }
   using raw = typename S::raw;
@@ -206,12 +208,16 @@ __global__ void __launch_bounds__(kUpdateBlock) update_kernel(const UpdArgs a) {
 template <class S, int K>
 int launch_k(const UpdArgs& a, bool silu, bool vec, uint32_t grid, void* st) {
   const void* fn;
-  if (vec)
-    fn = silu ? reinterpret_cast<const void*>(&update_kernel<S, K, true, true>)
-              : reinterpret_cast<const void*>(&update_kernel<S, K, false, true>);
+  const bool w4 = a.w_dtype == CCV_DT_F32;        // the 16-byte path's weight width
+  if (vec && w4)
+    fn = silu ? reinterpret_cast<const void*>(&update_kernel<S, K, true, true, 4>)
+              : reinterpret_cast<const void*>(&update_kernel<S, K, false, true, 4>);
+  else if (vec)
+    fn = silu ? reinterpret_cast<const void*>(&update_kernel<S, K, true, true, 2>)
+              : reinterpret_cast<const void*>(&update_kernel<S, K, false, true, 2>);
   else
-    fn = silu ? reinterpret_cast<const void*>(&update_kernel<S, K, true, false>)
-              : reinterpret_cast<const void*>(&update_kernel<S, K, false, false>);
+    fn = silu ? reinterpret_cast<const void*>(&update_kernel<S, K, true, false, 0>)
+              : reinterpret_cast<const void*>(&update_kernel<S, K, false, false, 0>);
   void* args[] = {const_cast<UpdArgs*>(&a)};
   return (int)hipLaunchKernel(fn, dim3(grid), dim3(kUpdateBlock), args, 0, static_cast<hipStream_t>(st));
 }

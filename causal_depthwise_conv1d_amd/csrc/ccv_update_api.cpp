@@ -25,7 +25,7 @@ bool vector_path(const ccv_update_args_t* a) {
   const int V = 16 / es;
   const int64_t B = a->B, C = a->C, L = a->L, H = a->K - 1;
   if (getenv("CCV_FORCE_SCALAR") && atoi(getenv("CCV_FORCE_SCALAR")) != 0) return false;
-  if (a->w_dtype != a->x_dtype || C % V != 0) return false;
+  if (C % V != 0) return false;
   if (!aligned16(a->weight) || (a->bias && !aligned16(a->bias))) return false;
   const bool x_ok = (a->x_stride[1] == 1 || C <= 1) && aligned16(a->x) &&
                     stride_ok16(B, a->x_stride[0], es) && stride_ok16(L, a->x_stride[2], es);

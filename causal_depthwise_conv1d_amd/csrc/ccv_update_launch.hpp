@@ -27,9 +27,10 @@ constexpr int kUpdateBlock = 256;          // 4 waves
 constexpr int kUpdateRowsPerLane = 4;      // R
 
 // Launch one instance; returns a hipError_t value (0 = success).  vec selects the
-// 16-byte path, which needs: weight and bias in x's dtype; C a multiple of V; x and
-// out unit-stride in channels; the state stored [B, C, K-1] contiguously (s_i = 1,
-// s_c = K-1); every base pointer and every used stride 16-byte aligned.
+// 16-byte path, which needs: C a multiple of V; x and out unit-stride in channels;
+// the state stored [B, C, K-1] contiguously (s_i = 1, s_c = K-1); every base
+// pointer and every used stride 16-byte aligned.  Weight and bias may take any of
+// the three dtypes.
 int launch_update(const UpdArgs& a, int dtype, int K, bool silu, bool vec, uint32_t grid, void* stream);
 
 }  // namespace ccv

@@ -123,7 +123,10 @@ typedef struct ccv_plan {
   int32_t path;            /* ccv_path_t; NONE when there is nothing to compute or write */
   int32_t vector;          /* 1: 16-byte loads and stores; 0: element loads and stores */
   int32_t elems_per_lane;  /* elements one lane holds per 16-byte vector (16 / element size) */
-  int32_t unroll;          /* vectors (channel-first) or time rows (channel-last) in flight per lane */
+  int32_t unroll;          /* vectors (channel-first) or time rows (channel-last) in flight per
+                              lane; channel-last: 8 when whole tiles take the straight-line
+                              path (the row batch being computed and the next one; weights,
+                              bias, history rows and seq_idx ids as vectors), 4 otherwise */
   int64_t grid;            /* workgroups launched */
   int32_t block;           /* threads per workgroup */
   int32_t waves_per_group; /* independent wave work items per workgroup */
@@ -201,9 +204,9 @@ int ccv_update_check(const ccv_update_args_t* args);
 /* Validate and describe the launch ccv_update would make, without touching any
  * device (`plan` may be NULL): path CCV_PATH_UPDATE (NONE when nothing is
  * enqueued); vector 1 when each lane moves whole 16-byte vectors of V = 16 /
- * element size consecutive channels (weight and bias in x's dtype, C a multiple
- * of V, x and out unit-stride in channels, the state stored [B, C, K-1]
- * contiguously, all 16-byte aligned), else 0; elems_per_lane and
+ * element size consecutive channels (C a multiple of V, x and out unit-stride in
+ * channels, the state stored [B, C, K-1] contiguously, all 16-byte aligned;
+ * weight and bias of any dtype), else 0; elems_per_lane and
  * channels_per_item: rows per lane; grid, block, waves_per_group: the launch;
  * work_items: B*C rows; span: L; unroll: 1. */
 int ccv_update_plan(const ccv_update_args_t* args, ccv_plan_t* plan);

@@ -336,7 +336,8 @@ def test_update_plan_takes_16_byte_path_on_standard_layouts():
 def test_update_plan_falls_back_to_element_path():
     assert uplan(uargs(state_layout="bic")).vector == 0            # channels-fastest state
     assert uplan(uargs(C=60)).vector == 0                          # C not a multiple of 8
-    assert uplan(uargs(w_dtype=ccv.CCV_F32)).vector == 0           # weights in another dtype
+    assert uplan(uargs(w_dtype=ccv.CCV_F32)).vector == 1           # weights of another dtype are fine
+    assert uplan(uargs(w_dtype=ccv.CCV_F32, weight=W + 4)).vector == 0  # but not unaligned ones
     assert uplan(uargs(x=X + 2)).vector == 0                       # x not 16-byte aligned
     assert uplan(uargs(bias=BIAS + 2)).vector == 0
     assert uplan(uargs(L=3, x_stride=(192, 3, 1), out_stride=(192, 3, 1))).vector == 0
@@ -518,3 +519,23 @@ def test_binding_refuses_non_contiguous_seq_idx():
     with pytest.raises(ValueError, match="contiguous"):
         ccv.make_bwd_args(x, wt, None, x, x.clone(), wt.clone(), seq_idx=bad)
     ccv.make_args(x, wt, x.clone(), seq_idx=bad.contiguous())
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_every_dtype_pair_takes_the_vector_paths(K):
+    """Aligned channel-last calls take the straight-line tile path (two row batches in
+    flight) and aligned decode calls the 16-byte update path for every pair of x and
+    weight dtypes."""
+    codes = (ccv.CCV_F32, ccv.CCV_F16, ccv.CCV_BF16)
+    for xd in codes:
+        for wd in codes:
+            a = args(K=K, layout="cl", x_dtype=xd, w_dtype=wd, bias=BIAS,
+                     initial_states=INIT, init_stride=(64 * (K - 1), 1, 64))
+            st, p = ccv.ccv_fwd_plan(a)
+            assert st == 0 and p.path == ccv.CCV_PATH_CHANNEL_LAST and p.vector == 1 and p.unroll == 8, (xd, wd)
+            u = uargs(K=K, x_dtype=xd, w_dtype=wd)
+            st, p = ccv.ccv_update_plan(u)
+            assert st == 0 and p.vector == 1, (xd, wd)
+    # an unaligned weight pointer sends whole tiles to the element path
+    st, p = ccv.ccv_fwd_plan(args(layout="cl", weight=W + 2))
+    assert st == 0 and p.vector == 1 and p.unroll == 4

@@ -192,6 +192,24 @@ def test_mixed_weight_dtypes(dtype):
             check_full(w, where=f"[x {dtype} w {wd} {layout}]")
 
 
+@pytest.mark.parametrize("K", [3, 4])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_mixed_weight_dtypes_take_the_straight_line_tiles(dtype, K):
+    """Channel-last whole tiles of whole channel groups run the straight-line path for
+    every pair of x and weight dtypes (the plan reports two row batches in flight),
+    including fp32 x with 16-bit weights, whose per-lane weight and bias blocks are
+    8 or 24 bytes, and agree with the oracle."""
+    for wd in DTYPES:
+        w = wl.make_case(B=2, C=1024, L=300, K=K, x_dtype=dtype, w_dtype=wd, layout="cl",
+                         bias=True, init=True, final=True, activation="silu", seed=78 + K)
+        kw = gpu_args(w)
+        plan = ccv.plan_for(x=kw["x"], weight=kw["weight"], bias=kw["bias"],
+                            initial_states=kw["initial_states"], activation="silu")
+        assert plan["path"] == ccv.CCV_PATH_CHANNEL_LAST and plan["vector"] == 1 and plan["unroll"] == 8, plan
+        log(f"  x {dtype} w {wd} K={K}: straight-line tiles")
+        check_full(w, where=f"[x {dtype} w {wd} K={K} cl]")
+
+
 @pytest.mark.parametrize("layout", ["cf", "cl"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_down_convert_rounds_to_nearest_even(dtype, layout):

@@ -114,15 +114,32 @@ def test_update_matches_oracle(dtype, K):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_update_vector_path_takes_any_weight_dtype(dtype):
+    """The 16-byte path with weights and bias of each other dtype (16- or 8-byte
+    parameter blocks per lane) against the oracle."""
+    for K in KS:
+        for wd in DTYPES:
+            for i, (B, C, L, xl, bias, act) in enumerate(((4, 256, 1, "2d", True, "silu"),
+                                                          (2, 512, 3, "cl", False, None))):
+                seed = 940 + 10 * K + i
+                x = x_view(B, C, L, dtype, xl, seed)
+                st = state_view(B, C, K - 1, dtype, "bci", seed)
+                w, b = params(C, K, wd, bias, seed)
+                assert ccv.update_plan_for(x, st, w, b, act)["vector"] == 1, (K, wd, i)
+                log(f"  update {dtype}/{wd} K={K} B={B} C={C} L={L}: 16-byte path")
+                check_update(x, st, w, b, act, f"[{dtype} w {wd} K={K} case {i}]")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_update_vector_path_equals_element_path(dtype, monkeypatch):
     """The 16-byte path and the element path give the same bits (out and new state)."""
     for K in KS:
-        for L, xl in ((1, "2d"), (4, "cl")):
+        for L, xl, wd in ((1, "2d", dtype), (4, "cl", dtype), (2, "cl", "f32" if dtype != "f32" else "bf16")):
             B, C = 3, 1024
             seed = 960 + K + L
             x = x_view(B, C, L, dtype, xl, seed)
             st0 = state_view(B, C, K - 1, dtype, "bci", seed)
-            w, b = params(C, K, dtype, True, seed)
+            w, b = params(C, K, wd, True, seed)
             res = []
             for force in ("0", "1"):
                 monkeypatch.setenv("CCV_FORCE_SCALAR", force)
