@@ -153,6 +153,10 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
     // 4855 at 64 rows) and the packed fp16 call (5027 vs 4998).
     int tile = env_int("CCV_CL_TILE_T", 32);
     if (tile < kClUnroll) tile = kClUnroll;
+    // CCV_CL_LDS=1: whole tiles staged through LDS, kClLdsRows rows each (measured
+    // against the register path; not the default).
+    c.lds = env_int("CCV_CL_LDS", 0) != 0;
+    if (c.lds) tile = kClLdsRows;
     c.tile = tile;
     c.ntt = L > 0 ? (L + tile - 1) / tile : 1;
     c.ncg = (C + 64 * V - 1) / (64 * V);
@@ -177,7 +181,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
     // their loads can be vectors; then two row batches are in flight per lane.
     const bool straight = P.vector && c.vec_par && tile % kClUnroll == 0 &&
                           (!a->initial_states || c.vec_init) && (!a->seq_idx || c.vec_seq);
-    P.unroll = straight ? 2 * kClUnroll : kClUnroll;
+    P.unroll = straight ? (c.lds ? kClLdsRows : 2 * kClUnroll) : kClUnroll;
     P.span = tile;
     P.channels_per_item = 64 * V;
   }

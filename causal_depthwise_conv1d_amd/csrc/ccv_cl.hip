@@ -58,8 +58,19 @@ __device__ inline void row_stencil(const float (&w)[S::V][K], const float (&beta
 
 // Addresses are a wave-uniform base plus this lane's 32-bit offset, so the loads
 // and stores use the scalar-base addressing mode.
-template <class S, int K, bool SILU, bool SEQ, int WB>
-__device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
+//
+// Two ways to keep rows in flight.  Registers (LDSM false): each next batch
+// of U rows is loaded into registers before the current batch's arithmetic.  LDS
+// (LDSM; rows = this wave's region of kClLdsRows x 1 KB, the tile that long): every row
+// of the tile goes straight from global memory into LDS with 16-byte
+// global-to-LDS loads, one 1 KB row per instruction, before any arithmetic; each
+// lane then reads its own 16 bytes of each row back.  The rows then take no
+// registers while in flight, so more waves fit on a CU; the arithmetic is the
+// same, term for term.
+typedef u32x4 __attribute__((address_space(3))) lds_u32x4;
+
+template <class S, int K, bool SILU, bool SEQ, int WB, bool LDSM>
+__device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane, lds_u32x4* rows) {
   constexpr int V = S::V;
   constexpr int U = kClUnroll;
   constexpr int H = K - 1;
@@ -103,7 +114,21 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
     for (int u = 0; u < U; ++u) r[u] = gload16_stream(xb + (t + u) * xs + lx);
     if constexpr (SEQ) iv = gload<u32x4>(sr + t * 4);
   };
-  issue(t0, ra, ia);
+  constexpr int NLB = kClLdsRows / U;               // row batches of an LDS tile
+  if constexpr (LDSM) {
+#pragma unroll
+    for (int r = 0; r < kClLdsRows; ++r)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xb + (t0 + r) * xs + lx),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(rows + r * 64),
+                                       16, 0, 0);
+    // The tile's ids after its rows: lane i < kClLdsRows brings the id of row t0 + i.
+    if constexpr (SEQ)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(pick(lane < kClLdsRows, sr + (t0 + lane) * 4, zero)),
+          reinterpret_cast<__attribute__((address_space(3))) void*>(rows + kClLdsRows * 64), 4, 0, 0);
+  } else {
+    issue(t0, ra, ia);
+  }
 
   // Convert parameters and history (waits for them only).
   float w[V][K], beta[V];
@@ -169,6 +194,16 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane) {
     }
   };
 
+  if constexpr (LDSM) {
+#pragma unroll 1
+    for (int j = 0; j < NLB; ++j) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) ra[u] = rows[(j * U + u) * 64 + lane];
+      if constexpr (SEQ) ia = rows[kClLdsRows * 64 + j];   // 4 ids, the same for every lane
+      compute(t0 + j * U, ra, ia);
+    }
+    return;
+  }
   const int64_t nb = a.tile / U;
   int64_t j = 0;
   while (true) {
@@ -325,8 +360,8 @@ __device__ inline void final_states_group(const ClArgs& a, int64_t b, int64_t cg
   }
 }
 
-template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
-__global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
+template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB, bool LDSM>
+__device__ inline void cl_fwd_body(const ClArgs& a, lds_u32x4* rows) {
   constexpr int V = S::V;
   const Common& m = a.m;
   const int lane = threadIdx.x & 63;
@@ -345,7 +380,7 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
                           t0 + a.tile <= m.L &&
                           (t0 >= K - 1 || m.init == nullptr || a.vec_init) && (!SEQ || a.vec_seq);
         if (fast) {
-          tile_fast<S, K, SILU, SEQ, WB>(a, p, lane);
+          tile_fast<S, K, SILU, SEQ, WB, LDSM>(a, p, lane, LDSM ? rows + wave * (kClLdsRows * 64 + 16) : rows);
           continue;
         }
       }
@@ -359,11 +394,26 @@ __global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
 }
 
 template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
+__global__ void __launch_bounds__(256) cl_fwd_kernel(const ClArgs a) {
+  cl_fwd_body<S, K, SILU, SEQ, VEC, WB, false>(a, nullptr);
+}
+
+// The same work with whole tiles staged through LDS (tiles of kClLdsRows rows):
+// per wave kClLdsRows KB of rows and 256 bytes of ids.
+constexpr int kClLdsWaveVecs = kClLdsRows * 64 + 16;
+
+template <class S, int K, bool SILU, bool SEQ, int WB>
+__global__ void __launch_bounds__(256) cl_fwd_lds_kernel(const ClArgs a) {
+  __shared__ u32x4 rows[kWavesPerGroup * kClLdsWaveVecs];
+  cl_fwd_body<S, K, SILU, SEQ, true, WB, true>(a, (lds_u32x4*)rows);
+}
+
+template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
 static int launch_one(const ClArgs& a, uint32_t grid, void* stream) {
   void* args[] = {const_cast<ClArgs*>(&a)};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cl_fwd_kernel<S, K, SILU, SEQ, VEC, WB>),
-                              dim3(grid), dim3(64 * kWavesPerGroup), args, 0,
-                              static_cast<hipStream_t>(stream));
+  const void* fn = VEC && a.lds ? reinterpret_cast<const void*>(&cl_fwd_lds_kernel<S, K, SILU, SEQ, WB>)
+                                : reinterpret_cast<const void*>(&cl_fwd_kernel<S, K, SILU, SEQ, VEC, WB>);
+  return (int)hipLaunchKernel(fn, dim3(grid), dim3(64 * kWavesPerGroup), args, 0, static_cast<hipStream_t>(stream));
 }
 
 template <class S, int K, bool SILU, bool SEQ, bool VEC>

@@ -56,6 +56,7 @@ struct ClArgs {
   int32_t vec_init;  // initial_states rows load as aligned 16-byte channel vectors
   int32_t vec_seq;   // seq_idx rows load as aligned 16-byte vectors of 4 ids
   int32_t vec_par;   // weight and bias blocks of a lane load as aligned 16-byte vectors
+  int32_t lds;       // whole tiles staged through LDS (tile == kClLdsRows)
 };
 
 // Launch one kernel instance; returns a hipError_t value (0 = success).
@@ -69,5 +70,6 @@ int launch_cl(const ClArgs& a, int dtype, int K, bool silu, bool seq, bool vec,
 constexpr int kWavesPerGroup = 4;
 constexpr int kCfUnroll = 4;     // 16-byte vectors per lane per segment
 constexpr int kClUnroll = 4;     // time rows loaded ahead per lane
+constexpr int kClLdsRows = 16;   // rows of a tile staged through LDS
 
 }  // namespace ccv

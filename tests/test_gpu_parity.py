@@ -210,6 +210,33 @@ def test_mixed_weight_dtypes_take_the_straight_line_tiles(dtype, K):
         check_full(w, where=f"[x {dtype} w {wd} K={K} cl]")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lds_staged_tiles_equal_register_tiles(dtype, monkeypatch):
+    """Channel-last tiles staged through LDS (CCV_CL_LDS=1: 16-row tiles whose rows
+    go straight from global memory into LDS) give the register path's bits, with
+    bias, SiLU, seq_idx, history and final states, ragged time tails and a partial
+    channel group, and agree with the oracle."""
+    cases = [(2, 1024, 300, 4, dict(bias=True, init=True, final=True, activation="silu")),
+             (1, 600, 777, 3, dict(bias=True, seq=9, activation="silu")),
+             (2, 520, 96, 2, dict(bias=False, seq=3, init=True, final=True, activation=None))]
+    for i, (B, C, L, K, feats) in enumerate(cases):
+        w = build(L, C, B, K, dtype, "cl", feats, seed=4300 + i)
+        res = []
+        for lds in ("0", "1"):
+            monkeypatch.setenv("CCV_CL_LDS", lds)
+            kw = gpu_args(w)
+            plan = ccv.plan_for(x=kw["x"], weight=kw["weight"], bias=kw["bias"], seq_idx=kw["seq_idx"],
+                                initial_states=kw["initial_states"], activation=kw["activation"])
+            assert plan["span"] == (16 if lds == "1" else 32), plan
+            assert plan["unroll"] == (16 if lds == "1" else 8), plan
+            res.append(run_gpu(w))
+        log(f"  LDS tiles {dtype} B={B} C={C} L={L} K={K} {feats}")
+        assert bits_equal(res[0][0], res[1][0]), (i, "out")
+        if w.return_final_states:
+            assert bits_equal(res[0][1], res[1][1]), (i, "final states")
+        check_full(w, where=f"[LDS tiles {dtype} case {i}]")
+
+
 @pytest.mark.parametrize("layout", ["cf", "cl"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_down_convert_rounds_to_nearest_even(dtype, layout):
