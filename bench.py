@@ -46,12 +46,13 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, decimal GB/s
 ROTATION_BYTES = 1 << 30        # >= 4x the 256 MB Infinity Cache
 METRIC = "causal conv1d fwd effective HBM GB/s and % of MI355X peak bandwidth"
 UPDATE_METRIC = "causal conv1d update (decode) effective HBM GB/s and % of MI355X peak bandwidth"
-KERNEL_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_cf.hip",
-                  "causal_depthwise_conv1d_amd/csrc/ccv_cl.hip",
-                  "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
-                  "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
-                  "causal_depthwise_conv1d_amd/csrc/ccv_api.cpp",
-                  "causal_depthwise_conv1d_amd/csrc/ccv_checks.hpp"]
+FWD_SHARED = ["causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
+              "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
+              "causal_depthwise_conv1d_amd/csrc/ccv_api.cpp",
+              "causal_depthwise_conv1d_amd/csrc/ccv_checks.hpp"]
+CF_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_cf.hip"] + FWD_SHARED
+CL_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_cl.hip"] + FWD_SHARED
+KERNEL_SOURCES = CF_SOURCES[:1] + CL_SOURCES
 BWD_SOURCES = ["causal_depthwise_conv1d_amd/csrc/ccv_bwd.hip",
                "causal_depthwise_conv1d_amd/csrc/ccv_device.hpp",
                "causal_depthwise_conv1d_amd/csrc/ccv_launch.hpp",
@@ -337,7 +338,9 @@ def measure_forward(n, args, dev, props, calib):
         rec["graph_replay"] = graph_timing(fwd, arg_refs, nsets, nbytes)
         rec["copy_same_bytes"] = copy_ceiling(nbytes, dev, stream, calib, args.steps)
         log(f"[bench] copy of the same bytes: {rec['copy_same_bytes']}")
-    sha = kernel_sources_sha256()
+    # the sources of this record's kernel: a profile stays valid while they are unchanged
+    sha = kernel_sources_sha256(CF_SOURCES if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else CL_SOURCES)
+    rec["kernel_sources_sha256"] = sha
     traffic = profile_traffic(rec["kernel"], sha)
     rec["traffic_bytes"] = traffic
     rec["traffic_ratio"] = None if traffic is None else round(traffic / nbytes, 4)
