@@ -363,6 +363,8 @@ def main():
     ap.add_argument("--w-dtype", default=None, choices=["f32", "bf16", "f16"],
                     help="store the workload's weights and bias in this dtype instead (same values "
                          "when widening): a mixed x / weight dtype call")
+    ap.add_argument("--seqs", type=int, default=0,
+                    help="--op bwd: pack each row with this many sequences (seq_idx)")
     ap.add_argument("--timed-only", action="store_true",
                     help="only the warm-up and timed calls (for profiling): no back-to-back, graph or copy runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -649,12 +651,14 @@ def bench_update(args, dev, props):
 
 def bwd_bytes(w) -> int:
     """Algorithmic bytes of one backward call: x and dout read once, dx written
-    once, the parameters read and their gradients written once, the states and
-    their gradients once.  The partial-sum workspace is overhead."""
+    once, the parameters read and their gradients written once, seq_idx read once,
+    the states and their gradients once.  The partial-sum workspace is overhead."""
     es = w.x.element_size()
     B, C, L, K = w.B, w.C, w.L, w.K
     pb = w.weight.element_size()
     n = 3 * B * C * L * es + 2 * C * K * pb
+    if w.seq_idx is not None:
+        n += B * L * 4
     if w.bias is not None:
         n += 2 * C * pb
     if w.initial_states is not None:
@@ -674,6 +678,10 @@ def bench_bwd(args, dev, props):
     import workloads as wl
 
     w = wl.workload(args.workload)
+    if args.seqs:
+        # the same rows packed with that many sequences (uniform lengths, at least 64 steps)
+        w.seq_idx = wl.seq_idx_from_lengths(wl.packed_lengths(w.L, args.seqs, 64, w.seed), w.B)
+        w.name += f"_seq{args.seqs}"
     B, C, L, K = w.B, w.C, w.L, w.K
     es = w.x.element_size()
     nbytes = bwd_bytes(w)

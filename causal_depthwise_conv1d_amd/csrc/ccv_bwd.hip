@@ -486,8 +486,8 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
 
 // ---- channel-first, registers only ------------------------------------------------
 //
-// For x, dout and dx unit-stride in time (16-byte aligned rows, L a multiple of V)
-// and no seq_idx.  The forward's channel-first layout of work: a segment is
+// For x, dout and dx unit-stride in time (16-byte aligned rows, L a multiple of V).
+// The forward's channel-first layout of work: a segment is
 // 64 lanes x U vectors x V steps of one (b, c) row; lane l holds vectors
 // l, l + 64, ..., so every load and store moves 1 KB of consecutive addresses.
 // The K-1 inputs before a lane's vector come from lane l-1 (DPP shift right) or,
@@ -499,7 +499,10 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
 // bits as in the other paths.  The parameter gradients: each lane sums its
 // elements in step order, then a fixed-order 64-lane sum over DPP lane patterns
 // (wave_sum) gives the segment's sum in lane 0, written as one partial row per
-// (b, segment).
+// (b, segment).  With seq_idx each lane also loads the ids of its elements, and
+// the ids before and after its vector travel with x and dz: the same keep() as
+// the walk's decides every term of z, of dx and of the parameter sums, and which
+// dfinal_states entries and history taps count.
 // x and dout vectors and dx are touched once and use streaming (non-temporal)
 // accesses, as do the LDS kernels' interior staging loads and dx stores; the
 // vectors just past a segment, which the next segment reads again, are ordinary
@@ -542,12 +545,30 @@ __device__ inline float wave_sum(float v) {
 // channel's parameters (as the aligned dwords that hold them, so that the loads do
 // not depend on the weight dtype) and dfinal_states.  Absent data loads from the
 // zero array; nothing is converted until the arithmetic.
-template <class S, int K>
+template <class S, int K, bool SEQ>
 struct RegLoads {
   u32x4 xv[kBwdRegUnroll], gv[kBwdRegUnroll], hx, hg;
   typename S::raw hist[K - 1], dfs[K - 1];
   uint32_t w[K], bias;
+  // with seq_idx: the ids of each vector's elements and of the V steps past the
+  // segment, the ids of the K-1 steps before it (seq_idx[b, 0] for the history left
+  // of t = 0), and the row's first and last ids
+  u32x4 iv[SEQ ? kBwdRegUnroll : 1][S::V / 4], hi[S::V / 4];
+  int32_t hist_id[K - 1], first_id, last_id;
 };
+
+// Ids as ints from the vectors that hold them.
+template <int V>
+__device__ inline void unpack_ids(const u32x4 (&v)[V / 4], int (&id)[V]) {
+#pragma unroll
+  for (int r = 0; r < V / 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id[4 * r + i] = (int)dword(v[r], i);
+}
+
+__device__ inline int shift_out(int carry, int v) {
+  return __builtin_amdgcn_update_dpp(carry, v, 0x130, 0xf, 0xf, false);
+}
 
 struct RegPos {
   int64_t b, c, seg;
@@ -558,8 +579,8 @@ struct RegPos {
 // past it), or anything else (the row's last, partial segment).
 enum { kSegInner = 0, kSegLast = 1, kSegEdge = 2 };
 
-template <class S, int K, int MODE>
-__device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, RegLoads<S, K>& q) {
+template <class S, int K, bool SEQ, int MODE>
+__device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, RegLoads<S, K, SEQ>& q) {
   using raw = typename S::raw;
   constexpr bool EDGE = MODE == kSegEdge;
   constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U, ES = sizeof(raw);
@@ -600,6 +621,26 @@ __device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, Re
     q.hist[j] = gload<raw>(pick(src >= 0, reinterpret_cast<uintptr_t>(xr + src), from_init));
     q.dfs[j] = gload<raw>(pick(a.dfs != nullptr, fr + j * a.fs_i * ES, zero));
   }
+  if constexpr (SEQ) {
+    const uintptr_t sr = reinterpret_cast<uintptr_t>(a.seq + p.b * L);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + (int64_t)(u * 64 + lane) * V;
+      const uintptr_t at = pick(!EDGE || t < L, sr + t * 4, zero);
+#pragma unroll
+      for (int r = 0; r < V / 4; ++r) q.iv[u][r] = gload<u32x4>(at + (EDGE && t >= L ? 0 : r * 16));
+    }
+    const uintptr_t ah = pick(MODE != kSegLast && t1 < L, sr + t1 * 4, zero);
+#pragma unroll
+    for (int r = 0; r < V / 4; ++r) q.hi[r] = gload<u32x4>(ah + (MODE != kSegLast && t1 < L ? r * 16 : 0));
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const int64_t src = t0 - H + j;              // the history carries seq_idx[b, 0]
+      q.hist_id[j] = gload<int32_t>(pick(src >= 0, sr + src * 4, pick(a.init != nullptr, sr, zero)));
+    }
+    q.first_id = gload<int32_t>(sr);
+    q.last_id = gload<int32_t>(sr + (L - 1) * 4);
+  }
   const int64_t wb = a.w_dtype == CCV_DT_F32 ? 4 : 2;
   const uintptr_t wl = reinterpret_cast<uintptr_t>(a.w) + p.c * K * wb;
 #pragma unroll
@@ -619,8 +660,8 @@ __device__ inline float reg_param(uint32_t d, int dtype, int64_t i) {
 // no position needs a check, but lane 63 of the last vector holds the row's last
 // H steps: it skips the taps that would read dz past L and adds dfinal_states,
 // exactly as the checked form does.  kSegEdge: every check in place.
-template <class S, int K, bool SILU, int MODE>
-__device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, const RegLoads<S, K>& q) {
+template <class S, int K, bool SILU, bool SEQ, int MODE>
+__device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, const RegLoads<S, K, SEQ>& q) {
   using raw = typename S::raw;
   constexpr bool EDGE = MODE == kSegEdge, LAST = MODE == kSegLast;
   constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U, ES = sizeof(raw);
@@ -647,13 +688,20 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
 #pragma unroll
   for (int k = 0; k < K; ++k) pw[k] = 0.0f;
   float carry[H];                                  // X~ of the H steps before lane 0's vector
+  int carry_id[H];                                 // and their ids
 #pragma unroll
-  for (int j = 0; j < H; ++j) carry[j] = hist[j];
+  for (int j = 0; j < H; ++j) {
+    carry[j] = hist[j];
+    carry_id[j] = SEQ ? q.hist_id[j] : 0;
+  }
   float dzp[V], dz0[H];                            // dz of the previous vector; lane 0's first H of vector 0
+  int idp[V], id0[H];                              // their ids
 
-  // dx of vector u with dz d[] and the dz of the H steps after each lane's vector
-  // (next[]), stored when inside [0, L).
-  auto put_dx = [&](int u, const float (&d)[V], const float (&next)[H]) {
+  // dx of vector u with dz d[] (ids di[]) and the dz of the H steps after each
+  // lane's vector (next[], ids nid[]), stored when inside [0, L).  With seq_idx an
+  // output's tap counts when its id is the element's.
+  auto put_dx = [&](int u, const float (&d)[V], const int (&di)[V], const float (&next)[H],
+                    const int (&nid)[H]) {
     const int64_t base = t0 + (int64_t)(u * 64 + lane) * V;
     const bool skip_next = LAST && u == U - 1 && tail;
     float y[V];
@@ -664,21 +712,24 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
       for (int k = 0; k < K; ++k) {                // output t = base + i + H - k uses tap k
         const int j = i + H - k;
         const float dv = j < V ? d[j] : next[j - V];
+        const bool same = !SEQ || (j < V ? di[j] : nid[j - V]) == di[i];
         if (j >= V && LAST) {
           const float f = __builtin_fmaf(w[k], dv, acc);
-          acc = skip_next ? acc : f;
+          acc = skip_next || !same ? acc : f;
         } else if (!EDGE || base + i + H - k < L) {
-          acc = __builtin_fmaf(w[k], dv, acc);
+          const float f = __builtin_fmaf(w[k], dv, acc);
+          acc = same ? f : acc;
         }
       }
+      const bool fin_kept = !SEQ || di[i] == q.last_id;   // final_states keep the last sequence's steps
       if (has_dfs) {                               // the last H steps take dfinal_states
         const int64_t t = base + i;
 #pragma unroll
         for (int m = 0; m < H; ++m)
-          if (t == L - H + m) acc += dfs[m];
+          if (t == L - H + m && fin_kept) acc += dfs[m];
       }
       if (LAST && u == U - 1 && i >= V - H) {
-        if (tail_dfs) acc += dfs[i - (V - H)];
+        if (tail_dfs && fin_kept) acc += dfs[i - (V - H)];
       }
       y[i] = acc;
     }
@@ -687,61 +738,101 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
       store16_stream(reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(dxr + t0) + lo + u * 64 * V * ES), pk);
   };
 
+  // Lane 0 of the row's first vector: whether each of the H history steps before
+  // it has an id (without a history, steps left of t = 0 have none and never count).
+  const bool lead = lane == 0 && t0 == 0 && a.init == nullptr;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool ok = !EDGE || t0 + (int64_t)(u * 64 + lane) * V < L;
     float e[V], g[V];
     S::unpack(q.xv[u], e);
     S::unpack(q.gv[u], g);
+    int id[V], hid[H];
+    if constexpr (SEQ) unpack_ids<V>(q.iv[u], id);
     float h[H];
 #pragma unroll
-    for (int j = 0; j < H; ++j) h[j] = shift_in(carry[j], e[V - H + j]);
+    for (int j = 0; j < H; ++j) {
+      h[j] = shift_in(carry[j], e[V - H + j]);
+      if constexpr (SEQ) hid[j] = shift_in(carry_id[j], id[V - H + j]);
+    }
 #pragma unroll
-    for (int j = 0; j < H; ++j) carry[j] = lane63(e[V - H + j]);
+    for (int j = 0; j < H; ++j) {
+      carry[j] = lane63(e[V - H + j]);
+      if constexpr (SEQ) carry_id[j] = lane63(id[V - H + j]);
+    }
     float dz[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       float xk[K];                                 // X~[t - H + k]
+      bool keep[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) xk[k] = i - H + k >= 0 ? e[i - H + k] : h[i + k];
+      for (int k = 0; k < K; ++k) {
+        const int j = i - H + k;
+        xk[k] = j >= 0 ? e[j] : h[i + k];
+        if constexpr (SEQ)
+          keep[k] = j >= 0 ? id[j] == id[i] : !(lead && u == 0) && hid[i + k] == id[i];
+        else
+          keep[k] = true;
+      }
       float z = beta;
 #pragma unroll
-      for (int k = 0; k < K; ++k) z = __builtin_fmaf(w[k], xk[k], z);
+      for (int k = 0; k < K; ++k) {
+        const float f = __builtin_fmaf(w[k], xk[k], z);
+        z = keep[k] ? f : z;
+      }
       const float d = SILU ? g[i] * silu_slope(z) : g[i];
       dz[i] = ok ? d : 0.0f;
       if (ok) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) pw[k] = __builtin_fmaf(dz[i], xk[k], pw[k]);
+        for (int k = 0; k < K; ++k) {
+          const float f = __builtin_fmaf(dz[i], xk[k], pw[k]);
+          pw[k] = keep[k] ? f : pw[k];
+        }
         pb += dz[i];
       }
     }
     if (u == 0) {
 #pragma unroll
-      for (int m = 0; m < H; ++m)
+      for (int m = 0; m < H; ++m) {
         dz0[m] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dz[m]), 0));
+        id0[m] = SEQ ? __builtin_amdgcn_readlane(id[m], 0) : 0;
+      }
     }
     if (u > 0) {
       float next[H];
+      int nid[H];
 #pragma unroll
-      for (int m = 0; m < H; ++m)
+      for (int m = 0; m < H; ++m) {
         next[m] = shift_out(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dz[m]), 0)),
                             dzp[m]);
-      put_dx(u - 1, dzp, next);
+        nid[m] = SEQ ? shift_out(__builtin_amdgcn_readlane(id[m], 0), idp[m]) : 0;
+      }
+      put_dx(u - 1, dzp, idp, next, nid);
     }
 #pragma unroll
-    for (int i = 0; i < V; ++i) dzp[i] = dz[i];
+    for (int i = 0; i < V; ++i) {
+      dzp[i] = dz[i];
+      idp[i] = SEQ ? id[i] : 0;
+    }
   }
   // dz of the H steps past the segment (zero past L), for the last vector's lane 63.
   if constexpr (LAST) {
     const float none[H] = {};
+    const int none_id[H] = {};
     float next[H];
+    int nid[H];
 #pragma unroll
-    for (int m = 0; m < H; ++m) next[m] = shift_out(none[m], dzp[m]);
-    put_dx(U - 1, dzp, next);
+    for (int m = 0; m < H; ++m) {
+      next[m] = shift_out(none[m], dzp[m]);
+      nid[m] = SEQ ? shift_out(none_id[m], idp[m]) : 0;
+    }
+    put_dx(U - 1, dzp, idp, next, nid);
   } else {
     float e[V], g[V];
     S::unpack(q.hx, e);
     S::unpack(q.hg, g);
+    int ida[V];                                    // ids of the steps past the segment
+    if constexpr (SEQ) unpack_ids<V>(q.hi, ida);
     float hz[H];
 #pragma unroll
     for (int m = 0; m < H; ++m) {
@@ -749,18 +840,24 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int j = m - H + k;                   // relative to t1
-        z = __builtin_fmaf(w[k], j >= 0 ? e[j] : carry[H + j], z);
+        const float f = __builtin_fmaf(w[k], j >= 0 ? e[j] : carry[H + j], z);
+        z = !SEQ || (j >= 0 ? ida[j] : carry_id[H + j]) == ida[m] ? f : z;
       }
       const float d = SILU ? g[m] * silu_slope(z) : g[m];
       hz[m] = !EDGE || t1 < L ? d : 0.0f;
     }
     float next[H];
+    int nid[H];
 #pragma unroll
-    for (int m = 0; m < H; ++m) next[m] = shift_out(hz[m], dzp[m]);
-    put_dx(U - 1, dzp, next);
+    for (int m = 0; m < H; ++m) {
+      next[m] = shift_out(hz[m], dzp[m]);
+      nid[m] = SEQ ? shift_out(ida[m], idp[m]) : 0;
+    }
+    put_dx(U - 1, dzp, idp, next, nid);
   }
 
-  // d(initial_states): the history positions j = -H .. -1 of the row's first segment.
+  // d(initial_states): the history positions j = -H .. -1 of the row's first
+  // segment; with seq_idx the history is the first sequence's (id seq_idx[b, 0]).
   if (t0 == 0 && a.dinit && lane < H) {
     const int j = lane - H;
     float acc = 0.0f;
@@ -768,11 +865,15 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
     for (int k = 0; k < K; ++k) {
       const int t = j + H - k;                     // < H: in lane 0's first vector
       float dv = 0.0f;
+      int tid = 0;
 #pragma unroll
-      for (int m = 0; m < H; ++m) dv = t == m ? dz0[m] : dv;
-      if (t >= 0 && t < L) acc = __builtin_fmaf(w[k], dv, acc);
+      for (int m = 0; m < H; ++m) {
+        dv = t == m ? dz0[m] : dv;
+        tid = t == m ? id0[m] : tid;
+      }
+      if (t >= 0 && t < L && (!SEQ || tid == q.first_id)) acc = __builtin_fmaf(w[k], dv, acc);
     }
-    if (has_dfs) {
+    if (has_dfs && (!SEQ || q.first_id == q.last_id)) {
 #pragma unroll
       for (int m = 0; m < H; ++m)
         if (j == L - H + m) acc += dfs[m];
@@ -794,19 +895,19 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
 }
 
 // One segment: its loads, then its arithmetic, in the form for where it lies.
-template <class S, int K, bool SILU>
+template <class S, int K, bool SILU, bool SEQ>
 __device__ inline void reg_segment(const BwdArgs& a, const RegPos& p, int lane) {
-  RegLoads<S, K> q;
+  RegLoads<S, K, SEQ> q;
   const int64_t t1 = (p.seg + 1) * (64 * kBwdRegUnroll * S::V);
   if (t1 + K - 1 <= a.L) {
-    reg_issue<S, K, kSegInner>(a, p, lane, q);
-    reg_compute<S, K, SILU, kSegInner>(a, p, lane, q);
+    reg_issue<S, K, SEQ, kSegInner>(a, p, lane, q);
+    reg_compute<S, K, SILU, SEQ, kSegInner>(a, p, lane, q);
   } else if (t1 == a.L) {
-    reg_issue<S, K, kSegLast>(a, p, lane, q);
-    reg_compute<S, K, SILU, kSegLast>(a, p, lane, q);
+    reg_issue<S, K, SEQ, kSegLast>(a, p, lane, q);
+    reg_compute<S, K, SILU, SEQ, kSegLast>(a, p, lane, q);
   } else {
-    reg_issue<S, K, kSegEdge>(a, p, lane, q);
-    reg_compute<S, K, SILU, kSegEdge>(a, p, lane, q);
+    reg_issue<S, K, SEQ, kSegEdge>(a, p, lane, q);
+    reg_compute<S, K, SILU, SEQ, kSegEdge>(a, p, lane, q);
   }
 }
 
@@ -822,13 +923,14 @@ __device__ inline RegPos reg_pos(const BwdArgs& a, int64_t i) {
 // waited for once; other waves' arithmetic hides that latency.  (Issuing the next
 // segment's loads before the current one's arithmetic, in a wave that loops over
 // items, needs about 100 more registers, halves the waves per CU, and measured
-// slower; so did a fixed grid of 16 resident waves per CU looping over items.)
-template <class S, int K, bool SILU>
+// slower; so did a fixed grid of 16 resident waves per CU looping over items, and,
+// with seq_idx, items of 4 channels of a segment sharing its ids in registers.)
+template <class S, int K, bool SILU, bool SEQ>
 __global__ void __launch_bounds__(kBwdBlock) bwd_cf_reg_kernel(const BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t i = (int64_t)blockIdx.x * (kBwdBlock / 64) + wave;
-  if (i < a.B * a.C * a.ntt) reg_segment<S, K, SILU>(a, reg_pos(a, i), lane);
+  if (i < a.items) reg_segment<S, K, SILU, SEQ>(a, reg_pos(a, i), lane);
 }
 
 __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {
@@ -899,11 +1001,8 @@ int launch_one(const BwdArgs& a, int path, uint32_t grid, void* st) {
   const void* fn;
   int block = 64;
   if (path == kBwdPathRegCf) {
-    if constexpr (SEQ) return (int)hipErrorInvalidValue;   // the host never asks for it
-    else {
-      fn = reinterpret_cast<const void*>(&bwd_cf_reg_kernel<S, K, SILU>);
-      block = kBwdBlock;
-    }
+    fn = reinterpret_cast<const void*>(&bwd_cf_reg_kernel<S, K, SILU, SEQ>);
+    block = kBwdBlock;
   } else if (path == kBwdPathLdsCf)
     fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, false>);
   else if (path == kBwdPathLdsCl)

@@ -42,7 +42,8 @@ int choose_path(const ccv_bwd_args_t* a) {
     cf = cf && s[2] == 1 && stride_ok16(B, s[0], es) && stride_ok16(C, s[1], es);
     cl = cl && s[1] == 1 && stride_ok16(B, s[0], es) && stride_ok16(L, s[2], es);
   }
-  if (cf) return a->seq_idx ? kBwdPathLdsCf : kBwdPathRegCf;
+  // The register path reads a lane's ids as 16-byte vectors beside its x.
+  if (cf) return a->seq_idx && !aligned16(a->seq_idx) ? kBwdPathLdsCf : kBwdPathRegCf;
   if (cl) return kBwdPathLdsCl;
   return kBwdPathElement;
 }
@@ -173,6 +174,7 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   g.tpi = tpi;
   g.ngr = ngr;
   g.lanes = lanes;
+  g.items = items;
   g.w_dtype = a->w_dtype;
   g.off24 = std::max({a->x_stride[1], a->dout_stride[1], a->dx_stride[1]}) < (int64_t)(1 << 24) / es;
 

@@ -30,6 +30,7 @@ struct BwdArgs {
   int64_t fs_b, fs_c, fs_i;     // dfinal_states
   int64_t di_b, di_c, di_i;     // dinitial_states
   int64_t T, ntt, tpi, ngr, lanes;  // tile length, tiles per row, tiles per group, groups per row, B*ngr*C
+  int64_t items;            // work items of the register channel-first kernel (one wave each)
   int32_t w_dtype;
   int32_t off24;            // channel strides of x, dout and dx below 2^24 bytes (24-bit lane offsets)
 };
@@ -69,8 +70,9 @@ constexpr int kBwdFinalWaves = 16;  // waves of the final reduction kernel's wor
 // multiple of 16 / element size.
 enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2, kBwdPathRegCf = 3 };
 
-// The register-only channel-first path (no seq_idx; the layout conditions of the
-// LDS channel-first path): work items are segments of bwd_reg_span(dtype) steps of
+// The register-only channel-first path (the layout conditions of the LDS
+// channel-first path; with seq_idx, a 16-byte aligned seq_idx): work items are
+// segments of bwd_reg_span(dtype) steps of
 // one (b, c) row, numbered row-major; a partial row per (b, segment); a grid of
 // kBwdBlock-lane workgroups, one wave per item.
 int bwd_reg_span(int dtype);

@@ -280,10 +280,11 @@ int ccv_bwd_check(const ccv_bwd_args_t* args);
 
 /* Describe the launch ccv_bwd would make (host only; `plan` may be NULL): path
  * CCV_PATH_BACKWARD; vector 0 for the element path (one lane per (b, tile group, c),
- * any strides), 1 for the LDS-staged channel-first path (used with seq_idx), 2 for
- * the LDS-staged channel-last path, 3 for the register-only channel-first path
- * (without seq_idx: one wave per (b, c, segment of `span` steps), one partial row
- * per (b, segment), elems_per_lane = 16 / element size); the channel-first paths
+ * any strides), 1 for the LDS-staged channel-first path (used when seq_idx is not
+ * 16-byte aligned), 2 for the LDS-staged channel-last path, 3 for the
+ * register-only channel-first path (with or without seq_idx: one wave per (b, c,
+ * segment of `span` steps), one partial row per (b, segment), elems_per_lane =
+ * 16 / element size); the channel-first paths
  * need x, dout and dx unit-stride in time, the channel-last one in channels, all
  * 16-byte aligned, with L resp. C a multiple of 16 / element size.  span = time
  * steps per tile (per segment on path 3); unroll = consecutive tiles per work

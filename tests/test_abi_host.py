@@ -387,8 +387,11 @@ def test_bwd_workspace_size_is_the_partial_sums():
     a.x_dtype = ccv.CCV_F32
     parts = 2 * (1 << 20) // 1024                    # 2048 -> 64, then the final kernel
     assert ccv.ccv_bwd_workspace_size(a) == (parts + 64) * 128 * 4 * 4
-    # channel-first with seq_idx: the LDS path, a row per tile of 32 steps
+    # channel-first with seq_idx: the register path as well
     a = bargs(B=3, C=100, L=1000, K=3, ws=False, seq_idx=SEQ)
+    assert ccv.ccv_bwd_workspace_size(a) == 3 * 100 * (3 + 1) * 4
+    # ... unless seq_idx is not 16-byte aligned: the LDS path, a row per tile of 32 steps
+    a = bargs(B=3, C=100, L=1000, K=3, ws=False, seq_idx=SEQ + 4)
     parts = 3 * -(-1000 // 32)                       # 96 rows: the final kernel alone
     assert ccv.ccv_bwd_workspace_size(a) == parts * 100 * (3 + 1) * 4
     # channel-last: a row per group of 4 tiles
@@ -462,9 +465,12 @@ def test_bwd_plan():
     assert st == 0 and p.path == ccv.CCV_PATH_BACKWARD and p.vector == 3
     assert p.span == 2048 and p.unroll == 1 and p.elems_per_lane == 8
     assert p.work_items == 4 * 2048 * 2 and p.grid == 4 * 2048 * 2 // 4 and p.block == 256
-    # with seq_idx: the LDS-staged channel-first kernel, a 64-lane workgroup per
-    # (b, tile of 32 steps, group of 64 channels)
+    # with seq_idx: the register kernel too, its ids loaded beside x
     st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, seq_idx=SEQ))
+    assert st == 0 and p.vector == 3 and p.span == 2048 and p.work_items == 4 * 2048 * 2
+    # seq_idx not 16-byte aligned: the LDS-staged channel-first kernel, a 64-lane
+    # workgroup per (b, tile of 32 steps, group of 64 channels)
+    st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4096, seq_idx=SEQ + 4))
     assert st == 0 and p.vector == 1 and p.span == 32 and p.unroll == 1
     assert p.work_items == 4 * 128 * 32 and p.grid == p.work_items and p.block == 64
     # aligned channel-last: the LDS-staged channel-last kernel, 4 tiles per work item
@@ -477,6 +483,9 @@ def test_bwd_plan():
     st, p = ccv.ccv_bwd_plan(a)
     assert st == 0 and p.span == 1024 and p.vector == 3 and p.work_items == 64 and p.grid == 16
     a.seq_idx = SEQ
+    st, p = ccv.ccv_bwd_plan(a)
+    assert st == 0 and p.span == 1024 and p.vector == 3
+    a.seq_idx = SEQ + 4
     st, p = ccv.ccv_bwd_plan(a)
     assert st == 0 and p.span == 32 and p.vector == 1
     # unaligned or mixed layouts: the element kernel, one lane per (b, tile, c)

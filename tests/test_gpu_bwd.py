@@ -171,10 +171,10 @@ def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
     kernel, with a ragged last tile, a partial group of 64 channels, history,
     dfinal_states and seq_idx (short sequences, and long ones whose tiles mostly hold
     one id), and (register path) rows that end inside a segment or exactly at a
-    segment's end: dx and d(initial_states) have the same bits on every
-    path.  The LDS kernels (channel-last; channel-first with seq_idx) also give the
-    same dweight and dbias bits; the register-only channel-first kernel sums the
-    parameter gradients in another order, so there they meet the oracle's bound."""
+    segment's end, with and without seq_idx: dx and d(initial_states) have the same
+    bits on every path.  The channel-last LDS kernel also gives the same dweight and
+    dbias bits; the register-only channel-first kernel sums the parameter gradients
+    in another order, so there they meet the oracle's bound."""
     T = tile_steps(dtype)
     span = 64 * 4 * (4 if dtype == "f32" else 8)        # the register path's segment
     for K in KS:
@@ -182,7 +182,7 @@ def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
         for f in (dict(init=True, dfs=True), dict(seq=7), dict(seq=2)):
             # the register path: one partial segment; one segment ending at L; an inner
             # segment then one ending at L; an inner segment then a partial one
-            Ls = [4 * T + 8] + ([span, 2 * span, span + 40] if layout == "cf" and not f.get("seq") else [])
+            Ls = [4 * T + 8] + ([span, 2 * span, span + 40] if layout == "cf" else [])
             for L in Ls:
                 B, C = 2, 136
                 log(f"  bwd fast vs element {dtype} {layout} K={K} L={L} {f}")
@@ -192,7 +192,7 @@ def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
                     ids, H = w.seq_idx[0].tolist(), K - 1
                     assert any(len(set(ids[t0 - H:min(t0 + T + H, L)])) == 1 for t0 in range(T, L, T))
                 res = []
-                fast = (1 if f.get("seq") else 3) if layout == "cf" else 2
+                fast = 3 if layout == "cf" else 2
                 for force, want in (("0", fast), ("1", 0)):
                     monkeypatch.setenv("CCV_FORCE_SCALAR", force)
                     x = to_gpu_view(w.x_storage, w.x)
@@ -209,6 +209,41 @@ def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
                 if fast == 3:
                     monkeypatch.setenv("CCV_FORCE_SCALAR", "0")
                     check_bwd(w, dout, dfs, bool(f.get("init")), f"[register path K={K} L={L}]")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_unaligned_seq_idx_takes_the_lds_path(dtype):
+    """Channel-first with a seq_idx that is not 16-byte aligned (a view one element
+    into its buffer) runs the LDS-staged kernel; its dx and d(initial_states) have the
+    register path's bits, and every gradient meets the oracle."""
+    K, B, C, L = 4, 2, 70, 4 * 32 * 8
+    w = build(B, C, L, K, dtype, "cf", 5300, seq=9, init=True)
+    dout, dfs = grad_inputs(w, "cf", True, 5300)
+    x = to_gpu_view(w.x_storage, w.x)
+    buf = torch.zeros(B * L + 1, dtype=torch.int32, device="cuda")
+    buf[1:] = w.seq_idx.reshape(-1).cuda()
+    seq_off = buf[1:].view(B, L)
+    assert seq_off.data_ptr() % 16 != 0 and seq_off.is_contiguous()
+    res = {}
+    for name, seq in (("aligned", w.seq_idx.cuda()), ("unaligned", seq_off)):
+        plan = bwd_plan(x, w.weight.cuda(), dout.cuda(), seq)
+        assert plan.vector == (3 if name == "aligned" else 1), (name, plan.as_dict())
+        res[name] = ccv.causal_conv1d_bwd(x, w.weight.cuda(), w.bias.cuda(), dout.cuda(), seq,
+                                          to_gpu_view(w.init_storage, w.initial_states), dfs.cuda(), "silu",
+                                          return_dinitial_states=True)
+        torch.cuda.synchronize()
+    bits = torch.int32 if dtype == "f32" else torch.int16
+    for i, name in ((0, "dx"), (3, "dinit")):
+        assert torch.equal(res["aligned"][i].cpu().contiguous().view(bits),
+                           res["unaligned"][i].cpu().contiguous().view(bits)), name
+    c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
+    r = oracle_bwd(c, dout, dfs)
+    dx, dw, db, dinit = (t.cpu().contiguous() for t in res["unaligned"])
+    for name, got, ref, scale, kk in (("dx", dx, r["dx"], r["ex"], K + 2), ("dinit", dinit, r["dinit"], r["einit"], K + 2),
+                                      ("dw", dw, r["dw"], r["ew"], PARAM_TERMS_CAP),
+                                      ("db", db, r["db"], r["eb"], PARAM_TERMS_CAP)):
+        res_c = ocmp.compare(dtype_name(got), kk, raw(got), ref, scale)
+        assert res_c["n_bad"] == 0, (name, ocmp.describe_failures(res_c, ref, scale, raw(got), dtype_name(got)))
 
 
 def test_bwd_random_shapes():
