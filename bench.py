@@ -743,7 +743,7 @@ def bench_bwd(args, dev, props):
     log(f"[bench] bwd: {ms_per_step * 1e3:.2f} us/call, {gbps:.0f} GB/s")
     copy_gbps, empty_us = context_measurements(nbytes, dev, stream, min(args.steps, 200))
 
-    kernel_key = f"bwd_{w.x_dtype}_B{B}_C{C}_L{L}_K{K}"
+    kernel_key = f"bwd_{w.x_dtype}_B{B}_C{C}_L{L}_K{K}" + (f"_seq{args.seqs}" if args.seqs else "")
     sha = kernel_sources_sha256(BWD_SOURCES)
     result = {
         "metric": BWD_METRIC,

@@ -29,7 +29,8 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-
              "-I", CSRC, "-I", INCLUDE]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", CSRC, "-I", INCLUDE]
 
-KERNEL_SOURCES = ["ccv_cf.hip", "ccv_cl.hip", "ccv_update.hip", "ccv_bwd.hip", "ccv_bwd_static.hip"]
+KERNEL_SOURCES = ["ccv_cf.hip", "ccv_cl.hip", "ccv_update.hip", "ccv_bwd.hip", "ccv_bwd_static.hip",
+                  "ccv_device_info.hip"]
 HOST_SOURCES = ["ccv_api.cpp", "ccv_update_api.cpp", "ccv_bwd_api.cpp"]
 CALIB_SOURCES = ["ccv_calib.hip"]
 

@@ -37,7 +37,7 @@ int env_int(const char* name, int dflt) {
 }
 
 // Checks every argument and fills *plan (never NULL) with the launch to make.
-int validate(const ccv_fwd_args_t* a, Plan* plan) {
+int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
   if (!a) return CCV_E_NULL;
   if (a->struct_size != (int64_t)sizeof(ccv_fwd_args_t)) return CCV_E_ABI;
   if (a->B < 0 || a->C < 0 || a->L < 0) return CCV_E_SHAPE;
@@ -139,7 +139,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
     // overrides the choice.
     const bool heavy = es == 2 || a->activation == CCV_ACT_SILU;
     const int wpc = env_int("CCV_CF_WAVES_PER_CU", heavy ? 16 : 0);
-    const int64_t cap = wpc > 0 ? (int64_t)cu_count() * wpc : nwork;
+    const int64_t cap = wpc > 0 ? (int64_t)cu_count(cus) * wpc : nwork;
     c.nwaves = nwork < cap ? nwork : cap;
     P.vector = vec;
     P.unroll = kCfUnroll;
@@ -174,7 +174,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan) {
     c.vec_seq = a->seq_idx && aligned16(a->seq_idx) && (B <= 1 || (L & 3) == 0);
     c.vec_par = aligned16(a->weight) && (!a->bias || aligned16(a->bias));
     const int wpc = env_int("CCV_CL_WAVES_PER_CU", 0);
-    const int64_t cap = wpc > 0 ? (int64_t)cu_count() * wpc : nwork;
+    const int64_t cap = wpc > 0 ? (int64_t)cu_count(cus) * wpc : nwork;
     c.nwaves = nwork < cap ? nwork : cap;
     if (c.nwaves < 1) c.nwaves = 1;
     // Whole tiles of whole channel vectors take the straight-line path when all of
@@ -204,21 +204,27 @@ extern "C" {
 
 int ccv_fwd_check(const ccv_fwd_args_t* args) {
   Plan p;
-  return validate(args, &p);
+  return validate(args, &p, last_cu_count());
 }
 
+// Plans touch no device: they size the grid for the GPU of the latest launch
+// (256 CUs before any).
 int ccv_fwd_plan(const ccv_fwd_args_t* args, ccv_plan_t* out) {
   Plan p;
-  const int st = validate(args, &p);
+  const int st = validate(args, &p, last_cu_count());
   if (st == CCV_OK && out) *out = p.pub;
   return st;
 }
 
 int ccv_fwd(const ccv_fwd_args_t* args, void* hip_stream) {
+  // The grid is sized for the stream's own GPU; a validation error still comes
+  // first when the runtime cannot name that GPU.
+  const int cus = device_cu_count(hip_stream);
   Plan p;
-  const int st = validate(args, &p);
+  const int st = validate(args, &p, cus);
   if (st != CCV_OK) return st;
   if (p.pub.path == CCV_PATH_NONE || p.pub.grid == 0) return CCV_OK;
+  if (cus < 0) return CCV_E_HIP;
   int err;
   if (p.pub.path == CCV_PATH_CHANNEL_FIRST)
     err = launch_cf(p.cf, args->x_dtype, args->K, p.silu, p.seq, p.pub.vector != 0,

@@ -15,13 +15,13 @@ namespace checks {
 
 inline int elt_size(int dt) { return dt == CCV_F32 ? 4 : 2; }
 
-// Compute units of the GPU the launches go to.  Plans must not touch a device
-// (the checks run on machines without one), so this is a fixed property of the
-// target: MI355X has 256 CUs.  CCV_CU_COUNT overrides it for other parts.
-inline int cu_count() {
+// Compute units to size a grid for: CCV_CU_COUNT when set to a positive count,
+// else `device` (what the runtime reports for the call's GPU) when positive, else
+// 256, MI355X's count.
+inline int cu_count(int device) {
   const char* v = getenv("CCV_CU_COUNT");
-  const int n = v && *v ? atoi(v) : 256;
-  return n > 0 ? n : 256;
+  const int n = v && *v ? atoi(v) : 0;
+  return n > 0 ? n : (device > 0 ? device : 256);
 }
 
 // Largest element offset of an [n0, n1, n2] view with strides s (all >= 0), or

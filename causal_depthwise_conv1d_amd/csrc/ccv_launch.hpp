@@ -59,6 +59,13 @@ struct ClArgs {
   int32_t lds;       // whole tiles staged through LDS (tile == kClLdsRows)
 };
 
+// Compute units of the GPU that `stream` (a hipStream_t; NULL = the current
+// device's null stream) belongs to, read from the runtime once per device; -1 when
+// the runtime cannot say.  last_cu_count(): the count of the device of the latest
+// such query, 0 before any.
+int device_cu_count(void* stream);
+int last_cu_count();
+
 // Launch one kernel instance; returns a hipError_t value (0 = success).
 // dtype: CCV_DT_*; silu/seq/vec select the template instance.
 int launch_cf(const CfArgs& a, int dtype, int K, bool silu, bool seq, bool vec,

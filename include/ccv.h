@@ -137,15 +137,20 @@ typedef struct ccv_plan {
 
 /* Enqueue the forward on `hip_stream` (a hipStream_t; NULL = the null stream) and
  * return without waiting.  Returns CCV_OK, a validation error (nothing enqueued)
- * or CCV_E_HIP.  Faults of the kernel itself surface at the caller's next
- * synchronisation of that stream. */
+ * or CCV_E_HIP (also when the runtime cannot name the stream's GPU).  Faults of
+ * the kernel itself surface at the caller's next synchronisation of that stream.
+ * The grid is sized for the stream's GPU: its compute-unit count is read from the
+ * runtime on the first call on that GPU and kept; the environment variable
+ * CCV_CU_COUNT, when set to a positive count, replaces it. */
 int ccv_fwd(const ccv_fwd_args_t* args, void* hip_stream);
 
 /* Validate `args` exactly as ccv_fwd does, without touching any device. */
 int ccv_fwd_check(const ccv_fwd_args_t* args);
 
 /* Validate and describe the launch ccv_fwd would make, without touching any
- * device.  `plan` may be NULL. */
+ * device: the grid is sized for the GPU of the latest ccv_fwd call in this process
+ * (for 256 compute units, MI355X's count, before any; CCV_CU_COUNT as above).
+ * `plan` may be NULL. */
 int ccv_fwd_plan(const ccv_fwd_args_t* args, ccv_plan_t* plan);
 
 /* ---- update (decode): advance a K-1 step history in place ------------------------

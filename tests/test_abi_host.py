@@ -178,6 +178,19 @@ def test_plan_channel_first():
     assert p.grid * p.waves_per_group == min(p.work_items, 256 * 16)
 
 
+def test_plan_grid_follows_the_cu_count_override(monkeypatch):
+    # No launch has run in this process, so plans size the grid for 256 CUs;
+    # CCV_CU_COUNT replaces the count (a partitioned or smaller part).
+    _, p = ccv.ccv_fwd_plan(args(B=4, C=2048, L=4096))
+    assert p.grid * p.waves_per_group == 256 * 16
+    monkeypatch.setenv("CCV_CU_COUNT", "32")
+    _, p = ccv.ccv_fwd_plan(args(B=4, C=2048, L=4096))
+    assert p.grid * p.waves_per_group == 32 * 16
+    monkeypatch.setenv("CCV_CU_COUNT", "0")              # not a count: ignored
+    _, p = ccv.ccv_fwd_plan(args(B=4, C=2048, L=4096))
+    assert p.grid * p.waves_per_group == 256 * 16
+
+
 def test_plan_channel_first_light_calls_get_a_wave_per_segment():
     a = args(B=2, C=128, L=1 << 16, activation=ccv.CCV_ACT_NONE)
     a.x_dtype = a.w_dtype = ccv.CCV_F32

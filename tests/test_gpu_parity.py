@@ -237,6 +237,26 @@ def test_lds_staged_tiles_equal_register_tiles(dtype, monkeypatch):
         check_full(w, where=f"[LDS tiles {dtype} case {i}]")
 
 
+def test_grid_is_sized_for_the_device_cu_count(monkeypatch):
+    """A launch reads the GPU's compute-unit count from the runtime; plans made
+    after it size the grid for that GPU (16 waves per CU for bf16 with SiLU).  A
+    smaller count from CCV_CU_COUNT (an odd one, so the waves' segment walks end
+    unevenly) changes the grid, not the bits."""
+    w = build(4099, 96, 2, 4, "bf16", "cf", dict(bias=True, activation="silu"), seed=4400)
+    base = run_gpu(w)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    kw = gpu_args(w)
+    plan = ccv.plan_for(x=kw["x"], weight=kw["weight"], bias=kw["bias"], activation="silu")
+    assert plan["work_items"] > 7 * 16
+    assert plan["grid"] * plan["waves_per_group"] == min(plan["work_items"], cus * 16), (cus, plan)
+    monkeypatch.setenv("CCV_CU_COUNT", "7")
+    plan7 = ccv.plan_for(x=kw["x"], weight=kw["weight"], bias=kw["bias"], activation="silu")
+    assert plan7["grid"] * plan7["waves_per_group"] == 7 * 16, plan7
+    assert bits_equal(base[0], run_gpu(w)[0])
+    log(f"  {cus} CUs: grid {plan['grid']}; CCV_CU_COUNT=7: grid {plan7['grid']}, same bits")
+    check_full(w, where="[CU count]")
+
+
 @pytest.mark.parametrize("layout", ["cf", "cl"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_down_convert_rounds_to_nearest_even(dtype, layout):
