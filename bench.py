@@ -184,6 +184,27 @@ def back_to_back(step, steps, stream):
     return ev0.elapsed_time(ev1) * 1e3 / steps
 
 
+def sustained_warmup(step, warmup, stream, min_ms=100.0, max_calls=5000):
+    """W warm-up calls, and more until about `min_ms` of back-to-back work has run:
+    back-to-back calls of the backward on the large shapes run about 10% slower
+    for their first few tens of milliseconds of continuous load than afterwards
+    (30 timed calls after 5 warm-up calls against after 100 or more), so a short
+    warm-up would time the ramp.  Returns the number of warm-up calls made."""
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(3):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    est_ms = max(ev0.elapsed_time(ev1) / 3, 1e-3)
+    n = max(warmup, min(max_calls, math.ceil(min_ms / est_ms)))
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    return n
+
+
 def median(v):
     v = sorted(v)
     n = len(v)
@@ -582,9 +603,7 @@ def bench_update(args, dev, props):
         if rc != 0:
             raise RuntimeError(ccv.ccv_status_str(rc))
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_calls = sustained_warmup(step, args.warmup, stream)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for i in range(args.steps):
@@ -593,7 +612,7 @@ def bench_update(args, dev, props):
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
-    log(f"[bench] update: {ms_per_step * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+    log(f"[bench] update: {warm_calls} warm-up calls, then {ms_per_step * 1e3:.2f} us/call, {gbps:.0f} GB/s")
     copy_gbps, empty_us = context_measurements(nbytes, dev, stream, args.steps)
 
     kernel_key = f"update_{w.x_dtype}_B{B}_C{C}_L{L}_K{K}"
@@ -604,7 +623,7 @@ def bench_update(args, dev, props):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm_calls,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -623,6 +642,8 @@ def bench_update(args, dev, props):
             "plan": plan,
         },
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "timing": (f"K calls back to back (HIP events on the launch stream), after {warm_calls} warm-up "
+                   f"calls: at least W={args.warmup} and about 100 ms of continuous calls"),
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbps, 1),
@@ -729,9 +750,7 @@ def bench_bwd(args, dev, props):
     step(0)
     torch.cuda.synchronize()
     first = (sets[0][2].cpu(), dweight.cpu(), None if dbias is None else dbias.cpu())
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_calls = sustained_warmup(step, args.warmup, stream)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for i in range(args.steps):
@@ -740,7 +759,7 @@ def bench_bwd(args, dev, props):
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
-    log(f"[bench] bwd: {ms_per_step * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+    log(f"[bench] bwd: {warm_calls} warm-up calls, then {ms_per_step * 1e3:.2f} us/call, {gbps:.0f} GB/s")
     copy_gbps, empty_us = context_measurements(nbytes, dev, stream, min(args.steps, 200))
 
     kernel_key = f"bwd_{w.x_dtype}_B{B}_C{C}_L{L}_K{K}" + (f"_seq{args.seqs}" if args.seqs else "")
@@ -751,7 +770,7 @@ def bench_bwd(args, dev, props):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm_calls,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -770,6 +789,8 @@ def bench_bwd(args, dev, props):
             "plan": plan,
         },
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "timing": (f"K calls back to back (HIP events on the launch stream), after {warm_calls} warm-up "
+                   f"calls: at least W={args.warmup} and about 100 ms of continuous calls"),
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbps, 1),
