@@ -15,7 +15,9 @@ own pair of HIP events on the stream the kernel is launched on.  The headline
 value is the median; the roofline object uses the mean (the average launch
 duration).  Beside it, as context: K back-to-back calls rotating over >= 1 GiB of
 buffer sets, the same calls replayed from a HIP graph, a streaming copy kernel
-moving the same number of bytes, and the empty-kernel launch floor.
+moving the same number of bytes, the empty-kernel launch floor, and the
+rocprofv3 kernel-trace average of the flushed calls from the committed profile
+(`kernel_trace`, when that profile was taken on the current kernel sources).
 
 Effective bandwidth = algorithmic bytes / time, where the algorithmic bytes count
 x read once, out written once, and weight, bias, seq_idx and the states once each
@@ -108,6 +110,25 @@ def profile_traffic(kernel_key: str, sha: str):
     if not m_sha or not m_tr or m_sha.group(1) != sha:
         return None
     return int(m_tr.group(1))
+
+
+def profile_kernel_time(kernel_key: str, sha: str, nbytes: int):
+    """The rocprofv3 kernel-trace average of the forward kernel over the flushed
+    calls, from the committed trace summary, if it was taken on the current kernel
+    sources; otherwise None.  Shown beside the HIP-event figures, which also hold
+    the dispatch of each single call."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_trace.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    m_us = re.search(r"kernel_avg_us:\s*([0-9.]+)", text)
+    if not m_sha or not m_us or m_sha.group(1) != sha:
+        return None
+    us = float(m_us.group(1))
+    return {"us": us, "GBps": round(gbps(nbytes, us), 1), "frac": round(gbps(nbytes, us) / PEAK_HBM_GBPS, 4),
+            "source": f"profiles/{kernel_key}_trace.md: rocprofv3 --kernel-trace average over the flushed calls "
+                      "of a traced run of this bench"}
 
 
 HEADLINE_WORKLOAD = 5           # the largest single-GPU workload (2,147,489,280 bytes per call)
@@ -365,6 +386,7 @@ def measure_forward(n, args, dev, props, calib):
     traffic = profile_traffic(rec["kernel"], sha)
     rec["traffic_bytes"] = traffic
     rec["traffic_ratio"] = None if traffic is None else round(traffic / nbytes, 4)
+    rec["kernel_trace"] = profile_kernel_time(rec["kernel"], sha, nbytes)
     del sets, arg_refs
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -64,6 +64,20 @@ def test_profile_traffic_needs_the_current_sources(tmp_path, monkeypatch):
     assert bench.profile_traffic("missing", sha) is None
 
 
+def test_profile_kernel_time_needs_the_current_sources(tmp_path, monkeypatch):
+    """The kernel-trace figure beside the HIP-event ones comes from a committed
+    trace summary only while the kernel sources hash to the value it records."""
+    sha, other = "ab" * 32, "cd" * 32
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "k_trace.md").write_text(f"```\nkernel_avg_us: 25.0\nkernel_sources_sha256: {sha}\n```\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    got = bench.profile_kernel_time("k", sha, 200_000_000)
+    assert got["us"] == 25.0 and got["GBps"] == 8000.0 and got["frac"] == 1.0
+    assert bench.profile_kernel_time("k", other, 1) is None
+    assert bench.profile_kernel_time("missing", sha, 1) is None
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True,
                        timeout=300)
