@@ -427,3 +427,70 @@ def test_bwd_argument_errors_raise():
         ccv.causal_conv1d_bwd(x, w, None, x, return_dinitial_states=True)   # no initial_states
     with pytest.raises(ValueError):
         ccv.causal_conv1d_bwd(x, w, None, x, dx=x)                     # dx is dout: alias
+
+
+def _bwd_big(x, dout, dx, weight, bias, want_path):
+    """ccv_bwd through the C ABI on prepared device views; returns (plan, dweight, dbias)."""
+    C, K = weight.shape
+    dw = torch.empty(C, K, dtype=weight.dtype, device="cuda")
+    db = torch.empty(C, dtype=weight.dtype, device="cuda")
+    args = ccv.make_bwd_args(x, weight.cuda(), bias.cuda(), dout, dx, dw, db, activation="silu")
+    st, plan = ccv.ccv_bwd_plan(args)
+    assert st == 0 and plan.vector == want_path, plan.as_dict()
+    ws = torch.empty(max(16, ccv.ccv_bwd_workspace_size(args)), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    assert ccv.ccv_bwd(args) == 0
+    torch.cuda.synchronize()
+    return plan, dw, db
+
+
+def _check_all(x, dout, dx, dw, db, weight, bias, plan, where):
+    B, C, L = x.shape
+    c = case(x.cpu(), weight, bias, None, None, "silu")
+    r = oracle_bwd(c, dout.cpu())
+    pk = param_terms_for(plan, B, L, weight.shape[1])
+    for name, got, ref, scale, kk in (("dx", dx, r["dx"], r["ex"], weight.shape[1] + 2),
+                                      ("dweight", dw, r["dw"], r["ew"], pk), ("dbias", db, r["db"], r["eb"], pk)):
+        g = got.cpu().contiguous()
+        res = ocmp.compare(dtype_name(g), kk, raw(g), ref, scale)
+        assert res["n_bad"] == 0, f"{where} {name}: " + ocmp.describe_failures(res, ref, scale, raw(g), dtype_name(g))
+
+
+def test_bwd_offsets_beyond_4_gib():
+    """The backward on views more than 4 GiB past the buffer start: x and dx
+    channel-last views of 512 channels in rows of 8192 (two batches of 150,000
+    rows, 4.9 GB per buffer) on the channel-last LDS kernel, and x and dx
+    channel-first views of 2 channels with a channel stride of 2^31 + 4096
+    elements on the register kernel.  Every dx, dweight and dbias element matches
+    the oracle; the dx buffers keep their NaN outside the views."""
+    K, C, W, B, L = 4, 512, 8192, 2, 150_000
+    gc = torch.Generator().manual_seed(4601)
+    weight = (torch.randn(C, K, generator=gc) * 0.5).to(torch.bfloat16)
+    bias = (torch.randn(C, generator=gc) * 0.3).to(torch.bfloat16)
+    g = torch.Generator(device="cuda").manual_seed(4600)
+
+    xbuf = torch.full((B, L, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xbuf[:, :, :C] = torch.randn(B, L, C, dtype=torch.bfloat16, device="cuda", generator=g)
+    gbuf = torch.full_like(xbuf, float("nan"))
+    x, dx = xbuf[:, :, :C].transpose(1, 2), gbuf[:, :, :C].transpose(1, 2)
+    dout = torch.randn(B, L, C, dtype=torch.bfloat16, device="cuda", generator=g).transpose(1, 2)
+    plan, dw, db = _bwd_big(x, dout, dx, weight, bias, 2)
+    assert bool(torch.isnan(gbuf[:, :, C:]).all()), "a dx store landed outside the channel-last view"
+    _check_all(x, dout, dx, dw, db, weight, bias, plan, "channel-last")
+    log(f"  channel-last backward: rows up to {xbuf.numel() * 2 / 2 ** 30:.2f} GiB from the buffer start")
+    del xbuf, gbuf, x, dx, dout
+    torch.cuda.empty_cache()
+
+    C2, L2, S = 2, 5000, 2 ** 31 + 4096
+    xbuf = torch.full((C2 * S,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    x = xbuf.as_strided((1, C2, L2), (C2 * S, S, 1))
+    x.copy_(torch.randn(1, C2, L2, dtype=torch.bfloat16, device="cuda", generator=g))
+    gbuf = torch.full_like(xbuf, float("nan"))
+    dx = gbuf.as_strided((1, C2, L2), (C2 * S, S, 1))
+    dout = torch.randn(1, C2, L2, dtype=torch.bfloat16, device="cuda", generator=g)
+    plan, dw, db = _bwd_big(x, dout, dx, weight[:C2], bias[:C2], 3)
+    assert int(torch.isnan(gbuf).sum()) == gbuf.numel() - C2 * L2, "a dx store landed outside the channel-first view"
+    _check_all(x, dout, dx, dw, db, weight[:C2], bias[:C2], plan, "channel-first")
+    log(f"  channel-first backward: channel 1 at {S * 2 / 2 ** 30:.2f} GiB from the buffer start")
+    del xbuf, gbuf, x, dx, dout
+    torch.cuda.empty_cache()

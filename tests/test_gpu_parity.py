@@ -535,3 +535,69 @@ def test_argument_errors_raise():
     with pytest.raises(ValueError):
         ccv.causal_conv1d_fwd(x, torch.zeros(4, 4, device="cuda"),
                               final_states_out=torch.zeros(1, 4, 3, device="cuda"))
+
+
+
+def _compare_all(out_gpu, x_gpu, weight, bias, activation, where):
+    """Every output of out_gpu [B, C, L] against the oracle on all host cores."""
+    from oracle import compare as ocmp
+    from oracle.from_torch import case, dtype_name
+    y, s = case(x_gpu.cpu(), weight, bias, None, None, activation).fwd_threads(min(16, len(os.sched_getaffinity(0))))
+    g = out_gpu.cpu().contiguous()
+    res = ocmp.compare(dtype_name(g), weight.shape[1], raw(g), y, s)
+    assert res["n_bad"] == 0, where + ": " + ocmp.describe_failures(res, y, s, raw(g), dtype_name(g),
+                                                                     shape=tuple(g.shape))
+    return res
+
+
+def test_offsets_beyond_4_gib():
+    """Views whose elements lie more than 4 GiB past the buffer start, read and
+    written, on both kernels: a channel-last view of 512 channels in rows of 8192
+    (two batches of 150,000 rows: 4.9 GB per buffer, so batch 1 crosses the 4 GiB
+    line, with a ragged last tile), and a channel-first view of 2 channels whose
+    channel stride is 2^31 + 4096 elements (4.3 GB; whole segments and a ragged
+    tail).  Every output matches the oracle, and every element of the output
+    buffers outside the view keeps its NaN."""
+    K, C, W, B, L = 4, 512, 8192, 2, 150_000
+    gc = torch.Generator().manual_seed(4501)
+    weight = (torch.randn(C, K, generator=gc) * 0.5).to(torch.bfloat16)
+    bias = (torch.randn(C, generator=gc) * 0.3).to(torch.bfloat16)
+    wd, bd = weight.cuda(), bias.cuda()
+    g = torch.Generator(device="cuda").manual_seed(4500)
+    stream = torch.cuda.current_stream()
+
+    # channel-last
+    xbuf = torch.full((B, L, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xbuf[:, :, :C] = torch.randn(B, L, C, dtype=torch.bfloat16, device="cuda", generator=g)
+    obuf = torch.full_like(xbuf, float("nan"))
+    x, out = xbuf[:, :, :C].transpose(1, 2), obuf[:, :, :C].transpose(1, 2)
+    assert xbuf.numel() * 2 > 2 ** 32
+    args = ccv.make_args(x, wd, out, bd, None, None, None, "silu")
+    st, plan = ccv.ccv_fwd_plan(args)
+    assert st == 0 and plan.path == ccv.CCV_PATH_CHANNEL_LAST and plan.vector == 1 and plan.unroll == 8
+    assert ccv.ccv_fwd(args, stream) == 0
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(obuf[:, :, C:]).all()), "a store landed outside the channel-last view"
+    res = _compare_all(out, x, weight, bias, "silu", "channel-last")
+    log(f"  channel-last: rows up to {xbuf.numel() * 2 / 2 ** 30:.2f} GiB from the buffer start; "
+        f"{res['n']} outputs, max ulp {res['max_ulp']}")
+    del xbuf, obuf, x, out
+    torch.cuda.empty_cache()
+
+    # channel-first
+    C2, L2, S = 2, 5000, 2 ** 31 + 4096
+    xbuf = torch.full((C2 * S,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    x = xbuf.as_strided((1, C2, L2), (C2 * S, S, 1))
+    x.copy_(torch.randn(1, C2, L2, dtype=torch.bfloat16, device="cuda", generator=g))
+    obuf = torch.full_like(xbuf, float("nan"))
+    out = obuf.as_strided((1, C2, L2), (C2 * S, S, 1))
+    args = ccv.make_args(x, wd[:C2], out, bd[:C2], None, None, None, "silu")
+    st, plan = ccv.ccv_fwd_plan(args)
+    assert st == 0 and plan.path == ccv.CCV_PATH_CHANNEL_FIRST and plan.vector == 1
+    assert ccv.ccv_fwd(args, stream) == 0
+    torch.cuda.synchronize()
+    assert int(torch.isnan(obuf).sum()) == obuf.numel() - C2 * L2, "a store landed outside the channel-first view"
+    _compare_all(out, x, weight[:C2], bias[:C2], "silu", "channel-first")
+    log(f"  channel-first: channel 1 at {S * 2 / 2 ** 30:.2f} GiB from the buffer start")
+    del xbuf, obuf, x, out
+    torch.cuda.empty_cache()
