@@ -444,6 +444,15 @@ def main():
     stream = torch.cuda.current_stream()
     floor_us = empty_floor(stream, calib)
     log(f"[bench] empty kernel: {floor_us:.2f} us per launch")
+    flushed_floor = None
+    if not args.timed_only:
+        # The same single-call timing around an empty kernel: what a flushed call
+        # costs beyond its kernel's own duration (dispatch from an idle queue).
+        import ctypes
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        t = timed_calls(lambda i: calib.lib.ccv_calib_empty(sp), args.warmup, args.steps, calib, stream)
+        flushed_floor = {"median_us": round(median(t), 3), "min_us": round(min(t), 3), "max_us": round(max(t), 3)}
+        log(f"[bench] empty kernel as a flushed single call: {flushed_floor['median_us']:.2f} us (median)")
     ns = [args.workload] if args.workload else [1, 2, 3, 4, 5]
     head = args.workload or HEADLINE_WORKLOAD
     records = {}
@@ -492,6 +501,7 @@ def main():
             "headline_record": {k: v for k, v in r.items() if k != "oracle"},
             "per_workload": {str(n): v for n, v in records.items() if n != head},
             "empty_kernel_us": round(floor_us, 3),
+            "empty_kernel_flushed_call": flushed_floor,
             "device": props.name,
             "cu_count": props.multi_processor_count,
             "device_properties": device_properties(props),
