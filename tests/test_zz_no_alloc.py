@@ -3,7 +3,8 @@ array) against ccv_bwd (the same backward with a caller-provided workspace),
 through the C ABI: every gradient bit for bit, on two calls in a row, the second
 with a smaller input, so the second call runs over the first call's leftovers in
 the shared array.  The workspace path itself is checked against the oracle by the
-backward parity tests; here the oracle check is repeated for the static path."""
+backward parity tests; here the oracle check is repeated for the static path.
+Also the use it exists for: the call captured in a HIP graph and replayed."""
 import ctypes
 
 import numpy as np
@@ -105,3 +106,52 @@ def test_static_scratch_refuses_calls_beyond_its_size():
     assert ccv.ccv_bwd_workspace_size(a) > ccv.CCV_BWD_STATIC_SCRATCH_BYTES
     assert ccv.STATUS[ccv.lib().ccv_bwd_static(ctypes.byref(a), None)] == "CCV_E_SCRATCH"
     assert np.int64(ccv.CCV_BWD_STATIC_SCRATCH_BYTES) == 64 << 20
+
+
+@pytest.mark.parametrize("layout", ["cf", "cl"])
+def test_static_backward_in_a_graph(layout):
+    """The callers ccv_bwd_static is for: captured in a HIP graph (torch.cuda.graph)
+    with no workspace to allocate, and replayed with new inputs written eagerly in
+    between; every replay equals an eager ccv_bwd (workspace path) on the same
+    inputs bit for bit."""
+    B, C, L, K = 2, 136, 2100, 4
+    gw = torch.Generator().manual_seed(7900)
+    weight = (torch.randn(C, K, generator=gw) * 0.5).to(torch.bfloat16).cuda()
+    bias = (torch.randn(C, generator=gw) * 0.3).to(torch.bfloat16).cuda()
+
+    def fresh(seed):
+        g = torch.Generator().manual_seed(seed)
+        shape = (B, C, L) if layout == "cf" else (B, L, C)
+        x = torch.randn(*shape, generator=g).to(torch.bfloat16).cuda()
+        dout = torch.randn(*shape, generator=g).to(torch.bfloat16).cuda()
+        return (x, dout) if layout == "cf" else (x.transpose(1, 2), dout.transpose(1, 2))
+
+    x, dout = fresh(7901)
+    dx = ccv.empty_like_layout(x)
+    dw = torch.empty(C, K, dtype=torch.bfloat16, device="cuda")
+    db = torch.empty(C, dtype=torch.bfloat16, device="cuda")
+    a = ccv.make_bwd_args(x, weight, bias, dout, dx, dw, db, activation="silu")
+
+    def call():
+        st = ccv.ccv_bwd_static(a, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, ccv.ccv_status_str(st)
+
+    side = torch.cuda.Stream()                      # warm-up call off the capture
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for r in range(4):
+        nx, ndout = fresh(7910 + r)
+        x.copy_(nx)
+        dout.copy_(ndout)
+        ref = ccv.causal_conv1d_bwd(nx, weight, bias, ndout, activation="silu")
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("dx", "dweight", "dbias"), (dx, dw, db), ref):
+            assert same_bits(got.cpu().contiguous(), want.cpu().contiguous()), (layout, r, name)
