@@ -47,12 +47,25 @@ def grad_inputs(w, layout, with_dfs, seed):
     return dout, dfs
 
 
-def run_bwd(w, dout, dfs, want_dinit):
+def gpu_ids(w, seq_gpu=None):
+    return seq_gpu if seq_gpu is not None else (None if w.seq_idx is None else w.seq_idx.cuda())
+
+
+def unaligned_ids(w):
+    """w's seq_idx on the GPU, contiguous but 4 bytes off 16-byte alignment."""
+    buf = torch.zeros(w.B * w.L + 1, dtype=torch.int32, device="cuda")
+    buf[1:] = w.seq_idx.reshape(-1).cuda()
+    ids = buf[1:].view(w.B, w.L)
+    assert ids.data_ptr() % 16 != 0 and ids.is_contiguous()
+    return ids
+
+
+def run_bwd(w, dout, dfs, want_dinit, seq_gpu=None):
     x = to_gpu_view(w.x_storage, w.x)
     init = None if w.initial_states is None else to_gpu_view(w.init_storage, w.initial_states)
     res = ccv.causal_conv1d_bwd(
         x, w.weight.cuda(), None if w.bias is None else w.bias.cuda(), dout.cuda(),
-        None if w.seq_idx is None else w.seq_idx.cuda(), init, None if dfs is None else dfs.cuda(),
+        gpu_ids(w, seq_gpu), init, None if dfs is None else dfs.cuda(),
         w.activation, return_dinitial_states=want_dinit)
     torch.cuda.synchronize()
     return [None if t is None else t.cpu().contiguous() for t in res]
@@ -104,10 +117,10 @@ def param_terms(w, plan):
     return param_terms_for(plan, w.B, w.L, w.K)
 
 
-def check_bwd(w, dout, dfs, want_dinit, where):
-    dx, dw, db, dinit = run_bwd(w, dout, dfs, want_dinit)
-    plan = bwd_plan(to_gpu_view(w.x_storage, w.x), w.weight.cuda(), dout.cuda(),
-                    None if w.seq_idx is None else w.seq_idx.cuda())
+def check_bwd(w, dout, dfs, want_dinit, where, seq_gpu=None, want_path=None):
+    dx, dw, db, dinit = run_bwd(w, dout, dfs, want_dinit, seq_gpu)
+    plan = bwd_plan(to_gpu_view(w.x_storage, w.x), w.weight.cuda(), dout.cuda(), gpu_ids(w, seq_gpu))
+    assert want_path is None or plan.vector == want_path, plan.as_dict()
     c = case(w.x, w.weight, w.bias, w.seq_idx, w.initial_states, w.activation)
     r = oracle_bwd(c, dout, dfs)
     K = w.K
@@ -220,10 +233,7 @@ def test_bwd_unaligned_seq_idx_takes_the_lds_path(dtype):
     w = build(B, C, L, K, dtype, "cf", 5300, seq=9, init=True)
     dout, dfs = grad_inputs(w, "cf", True, 5300)
     x = to_gpu_view(w.x_storage, w.x)
-    buf = torch.zeros(B * L + 1, dtype=torch.int32, device="cuda")
-    buf[1:] = w.seq_idx.reshape(-1).cuda()
-    seq_off = buf[1:].view(B, L)
-    assert seq_off.data_ptr() % 16 != 0 and seq_off.is_contiguous()
+    seq_off = unaligned_ids(w)
     res = {}
     for name, seq in (("aligned", w.seq_idx.cuda()), ("unaligned", seq_off)):
         plan = bwd_plan(x, w.weight.cuda(), dout.cuda(), seq)
@@ -290,13 +300,15 @@ def test_bwd_random_long_rows():
 def test_bwd_reduction_with_level_kernels():
     """More than 512 partial rows: level kernels of the reduction tree run before the
     final kernel (2500 rows -> 79 -> the final kernel's 3 waves), with a partial
-    group of 64 channels; and the register-only path with 2048 partial rows."""
+    group of 64 channels, on the LDS channel-first path (a seq_idx one element off
+    16-byte alignment sends it there); and the register-only path with 2048 partial
+    rows."""
     for dtype, act in (("f32", None), ("bf16", "silu")):
-        w = build(2, 72, 40000, 3, dtype, "cf", 4700, init=True, act=act, seq=3)   # the LDS path
+        w = build(2, 72, 40000, 3, dtype, "cf", 4700, init=True, act=act, seq=3)
         assert w.B * -(-w.L // tile_steps(dtype)) == 2500
         dout, dfs = grad_inputs(w, "cf", True, 4700)
         log(f"  bwd level kernels {dtype}: B=2 C=72 L=40000 K=3")
-        check_bwd(w, dout, dfs, True, f"[levels {dtype}]")
+        check_bwd(w, dout, dfs, True, f"[levels {dtype}]", seq_gpu=unaligned_ids(w), want_path=1)
     w = build(2, 72, 1024 * 1024, 3, "f32", "cf", 4710, init=True, act=None)   # 2 x 1024 segments
     dout, dfs = grad_inputs(w, "cf", True, 4710)
     log("  bwd register path, 2048 partial rows: B=2 C=72 L=1M K=3")
