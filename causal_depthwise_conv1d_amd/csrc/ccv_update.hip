@@ -65,14 +65,21 @@ __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
   constexpr int V = S::V;
   constexpr int H = K - 1;
   constexpr int NWB = V * K * WB, NBB = V * WB;    // bytes of the lane's weights, biases
+  const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
+  // Every load before any arithmetic: weights, bias, history and the first step's
+  // x (a call with no new steps launches nothing, so L >= 1), so the lane waits
+  // for one memory latency rather than one per kind of operand.
   uint32_t wv[NWB / 4], bv[NBB / 4];
   load_param_block<NWB>(reinterpret_cast<uintptr_t>(a.w) + c * K * WB, wv);
-  load_param_block<NBB>(pick(a.bias != nullptr, reinterpret_cast<uintptr_t>(a.bias) + c * WB,
-                             reinterpret_cast<uintptr_t>(kZeroSrc)), bv);
+  load_param_block<NBB>(pick(a.bias != nullptr, reinterpret_cast<uintptr_t>(a.bias) + c * WB, zero), bv);
   u32x4 hv[H];
   raw* sp = static_cast<raw*>(a.state) + b * a.s_sb + c * H;
 #pragma unroll
-  for (int i = 0; i < H; ++i) hv[i] = load16(sp + i * V);
+  for (int i = 0; i < H; ++i) hv[i] = gload<u32x4>(reinterpret_cast<uintptr_t>(sp + i * V));
+  const uintptr_t xr = reinterpret_cast<uintptr_t>(static_cast<const raw*>(a.x) + b * a.x_sb + c);
+  const uintptr_t xs = (uintptr_t)a.x_sl * sizeof(raw);
+  u32x4 xv = gload16_stream(xr);
+  __builtin_amdgcn_sched_barrier(0);               // keep every load above the arithmetic
 
   float w[V][K], beta[V];
   raw hist[V][H];
@@ -85,14 +92,15 @@ __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
     for (int i = 0; i < H; ++i) hist[j][i] = get_elem<S>(hv, j * H + i);
   }
 
-  const raw* xr = static_cast<const raw*>(a.x) + b * a.x_sb + c;
   raw* orow = static_cast<raw*>(a.out) + b * a.o_sb + c;
-  for (int64_t t = 0; t < a.L; ++t) {
-    u32x4 xv[1] = {load16_stream(xr + t * a.x_sl)};
+  for (int64_t t = 0;;) {
+    // the next step's x in flight during this step's arithmetic (zeros past L)
+    const u32x4 xn = gload16_stream(pick(t + 1 < a.L, xr + (uintptr_t)(t + 1) * xs, zero));
+    const u32x4 xcur[1] = {xv};
     float y[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      const raw xe = get_elem<S>(xv, j);
+      const raw xe = get_elem<S>(xcur, j);
       float acc = beta[j];
 #pragma unroll
       for (int k = 0; k < H; ++k) acc = __builtin_fmaf(w[j][k], S::to_f(hist[j][k]), acc);
@@ -103,6 +111,8 @@ __device__ inline void update_rows_vec(const UpdArgs& a, int64_t b, int64_t c) {
       hist[j][H - 1] = xe;
     }
     store16_stream(orow + t * a.o_sl, S::pack(y));
+    if (++t >= a.L) break;
+    xv = xn;
   }
 
   raw flat[V * H];
