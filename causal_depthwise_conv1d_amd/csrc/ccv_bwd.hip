@@ -894,21 +894,75 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
   }
 }
 
-// One segment: its loads, then its arithmetic, in the form for where it lies.
+// With seq_idx: whether every step the segment's arithmetic reads carries one id
+// (the segment's own steps, the K-1 before it, which at t = 0 must be a given
+// history, and the V steps past it that feed the last vector's dx).  Then every
+// mask of the walk reads true, and the unmasked arithmetic gives the same bits.
+// The ids are loaded here on their own, so that neither form of the arithmetic
+// holds them (or the other form's values) in registers.
+template <class S, int K, int MODE>
+__device__ inline bool reg_one_sequence(const BwdArgs& a, const RegPos& p, int lane) {
+  constexpr bool EDGE = MODE == kSegEdge;
+  constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U;
+  const int64_t L = a.L, t0 = p.seg * SPAN, t1 = t0 + SPAN;
+  if (t0 == 0 && a.init == nullptr) return false;  // the history left of t = 0 never counts
+  const uintptr_t zero = reinterpret_cast<uintptr_t>(kZeroSrc);
+  const uintptr_t sr = reinterpret_cast<uintptr_t>(a.seq + p.b * L);
+  const int ref = __builtin_amdgcn_readfirstlane(gload<int32_t>(sr + t0 * 4));   // the id at t0
+  bool ok = true;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t t = t0 + (int64_t)(u * 64 + lane) * V;
+    const bool in = !EDGE || t < L;
+#pragma unroll
+    for (int r = 0; r < V / 4; ++r) {
+      const u32x4 v = gload<u32x4>(pick(in, sr + t * 4 + r * 16, zero));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ok = ok && ((EDGE && t + 4 * r + i >= L) || (int)dword(v, i) == ref);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < H; ++j) {                   // at t0 = 0 the history carries seq_idx[b, 0]
+    const int64_t src = t0 - H + j;
+    ok = ok && gload<int32_t>(src >= 0 ? sr + src * 4 : sr) == ref;
+  }
+  if constexpr (MODE != kSegLast) {
+#pragma unroll
+    for (int r = 0; r < V / 4; ++r) {
+      const u32x4 v = gload<u32x4>(pick(t1 < L, sr + t1 * 4 + r * 16, zero));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ok = ok && (t1 + 4 * r + i >= L || (int)dword(v, i) == ref);
+    }
+  }
+  return __all(ok);
+}
+
+// One segment: its loads, then its arithmetic, in the form for where it lies (and,
+// with seq_idx, unmasked when it holds one sequence).
+template <class S, int K, bool SILU, bool SEQ, int MODE>
+__device__ inline void reg_segment_in(const BwdArgs& a, const RegPos& p, int lane) {
+  if constexpr (SEQ) {
+    if (reg_one_sequence<S, K, MODE>(a, p, lane)) {
+      RegLoads<S, K, false> q;
+      reg_issue<S, K, false, MODE>(a, p, lane, q);
+      reg_compute<S, K, SILU, false, MODE>(a, p, lane, q);
+      return;
+    }
+  }
+  RegLoads<S, K, SEQ> q;
+  reg_issue<S, K, SEQ, MODE>(a, p, lane, q);
+  reg_compute<S, K, SILU, SEQ, MODE>(a, p, lane, q);
+}
+
 template <class S, int K, bool SILU, bool SEQ>
 __device__ inline void reg_segment(const BwdArgs& a, const RegPos& p, int lane) {
-  RegLoads<S, K, SEQ> q;
   const int64_t t1 = (p.seg + 1) * (64 * kBwdRegUnroll * S::V);
-  if (t1 + K - 1 <= a.L) {
-    reg_issue<S, K, SEQ, kSegInner>(a, p, lane, q);
-    reg_compute<S, K, SILU, SEQ, kSegInner>(a, p, lane, q);
-  } else if (t1 == a.L) {
-    reg_issue<S, K, SEQ, kSegLast>(a, p, lane, q);
-    reg_compute<S, K, SILU, SEQ, kSegLast>(a, p, lane, q);
-  } else {
-    reg_issue<S, K, SEQ, kSegEdge>(a, p, lane, q);
-    reg_compute<S, K, SILU, SEQ, kSegEdge>(a, p, lane, q);
-  }
+  if (t1 + K - 1 <= a.L)
+    reg_segment_in<S, K, SILU, SEQ, kSegInner>(a, p, lane);
+  else if (t1 == a.L)
+    reg_segment_in<S, K, SILU, SEQ, kSegLast>(a, p, lane);
+  else
+    reg_segment_in<S, K, SILU, SEQ, kSegEdge>(a, p, lane);
 }
 
 __device__ inline RegPos reg_pos(const BwdArgs& a, int64_t i) {

@@ -506,3 +506,37 @@ def test_bwd_offsets_beyond_4_gib():
     log(f"  channel-first backward: channel 1 at {S * 2 / 2 ** 30:.2f} GiB from the buffer start")
     del xbuf, gbuf, x, dx, dout
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_register_path_single_sequence_segments(dtype):
+    """The register kernel runs a segment that holds one sequence (its steps, the
+    K-1 before it and the V past it) without masks.  Sequence starts placed at and
+    around segment edges, so that segments on either side of each start take one
+    form or the other: dx and d(initial_states) have the bits of the LDS path (an
+    unaligned seq_idx sends the call there), and every gradient meets the oracle."""
+    K, B, C = 4, 1, 66
+    span = 64 * 4 * (4 if dtype == "f32" else 8)
+    L = 3 * span
+    starts_cases = [[span], [span + 2], [2 * span - 3], [2 * span + 7], [2 * span + 8], [span - 1, 2 * span + 1]]
+    for i, starts in enumerate(starts_cases):
+        for with_init in (False, True):
+            lengths = np.diff(np.concatenate([[0], starts, [L]])).tolist()
+            w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype=dtype, layout="cf", bias=True, init=with_init,
+                             seq_lengths=lengths, activation="silu", seed=5600 + i)
+            dout, dfs = grad_inputs(w, "cf", True, 5600 + i)
+            x = to_gpu_view(w.x_storage, w.x)
+            init = to_gpu_view(w.init_storage, w.initial_states) if with_init else None
+            res = {}
+            for name, seq, path in (("register", w.seq_idx.cuda(), 3), ("lds", unaligned_ids(w), 1)):
+                assert bwd_plan(x, w.weight.cuda(), dout.cuda(), seq).vector == path
+                res[name] = ccv.causal_conv1d_bwd(x, w.weight.cuda(), w.bias.cuda(), dout.cuda(), seq, init,
+                                                  dfs.cuda(), "silu", return_dinitial_states=with_init)
+                torch.cuda.synchronize()
+            bits = torch.int32 if dtype == "f32" else torch.int16
+            for j, name in ((0, "dx"), (3, "dinit")):
+                if res["register"][j] is not None:
+                    assert torch.equal(res["register"][j].cpu().contiguous().view(bits),
+                                       res["lds"][j].cpu().contiguous().view(bits)), (starts, with_init, name)
+            log(f"  register path {dtype}, sequence starts {starts}, history {with_init}")
+            check_bwd(w, dout, dfs, with_init, f"[single-sequence segments {starts}]", want_path=3)
