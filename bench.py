@@ -281,9 +281,17 @@ def empty_floor(stream, calib):
 
 
 def kernel_key_of(w, plan):
+    """The profile name of this call's forward kernel (the channel-last LDS forms,
+    chosen with CCV_CL_LDS, have their own: the plan shows which one runs)."""
     import causal_depthwise_conv1d_amd as ccv
-    return ("cf_fwd" if plan["path"] == ccv.CCV_PATH_CHANNEL_FIRST else "cl_fwd") + \
-        f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}" + ("" if w.w_dtype == w.x_dtype else f"_w{w.w_dtype}")
+    cl = plan["path"] == ccv.CCV_PATH_CHANNEL_LAST
+    form = ""
+    if cl and plan["channels_per_item"] == 256:
+        form = "_tr"
+    elif cl and plan["vector"] == 1 and plan["span"] == 16 and plan["unroll"] == 16:
+        form = "_lds"
+    return ("cl_fwd" if cl else "cf_fwd") + f"_{w.x_dtype}_B{w.B}_C{w.C}_L{w.L}_K{w.K}" + \
+        ("" if w.w_dtype == w.x_dtype else f"_w{w.w_dtype}") + form
 
 
 def measure_forward(n, args, dev, props, calib):
@@ -558,7 +566,8 @@ def graph_timing(fwd, arg_refs, nsets, nbytes, calls=100, reps=5):
 def env_overrides() -> dict:
     """The library's tuning / ablation environment variables set for this run (none
     in a default run; any set here change the launch the numbers come from)."""
-    names = ("CCV_CF_WAVES_PER_CU", "CCV_CL_WAVES_PER_CU", "CCV_CL_TILE_T", "CCV_CU_COUNT", "CCV_FORCE_SCALAR")
+    names = ("CCV_CF_WAVES_PER_CU", "CCV_CL_WAVES_PER_CU", "CCV_CL_TILE_T", "CCV_CL_LDS", "CCV_CU_COUNT",
+             "CCV_FORCE_SCALAR")
     return {n: os.environ[n] for n in names if n in os.environ}
 
 

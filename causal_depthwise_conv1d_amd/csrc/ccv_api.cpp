@@ -153,13 +153,20 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
     // 4855 at 64 rows) and the packed fp16 call (5027 vs 4998).
     int tile = env_int("CCV_CL_TILE_T", 32);
     if (tile < kClUnroll) tile = kClUnroll;
-    // CCV_CL_LDS=1: whole tiles staged through LDS, kClLdsRows rows each (measured
-    // against the register path; not the default).
-    c.lds = env_int("CCV_CL_LDS", 0) != 0;
-    if (c.lds) tile = kClLdsRows;
+    // CCV_CL_LDS=1: whole tiles staged through LDS, kClLdsRows rows each; =2: the
+    // transposing tile of kClTrChannels channels (both measured against the register
+    // path; neither is the default).
+    const bool vec_x = aligned16(a->x) && stride_ok16(B, a->x_stride[0], es) && stride_ok16(L, a->x_stride[2], es) &&
+                       (!want_out || (aligned16(a->out) && stride_ok16(B, a->out_stride[0], es) &&
+                                      stride_ok16(L, a->out_stride[2], es)));
+    c.lds = env_int("CCV_CL_LDS", 0);
+    if (c.lds == 2 && !(vec_x && C % V == 0 && !force_scalar)) c.lds = 0;
+    if (c.lds != 1 && c.lds != 2) c.lds = 0;
+    if (c.lds == 1) tile = kClLdsRows;
+    if (c.lds == 2) tile = cl_tr_rows(es);
     c.tile = tile;
     c.ntt = L > 0 ? (L + tile - 1) / tile : 1;
-    c.ncg = (C + 64 * V - 1) / (64 * V);
+    c.ncg = c.lds == 2 ? (C + kClTrChannels - 1) / kClTrChannels : (C + 64 * V - 1) / (64 * V);
     int64_t bcg;
     if (__builtin_mul_overflow(B, c.ncg, &bcg) || __builtin_mul_overflow(bcg, c.ntt, &nwork)) return CCV_E_SHAPE;
     bool vec = aligned16(a->x) && stride_ok16(B, c.x_sb, es) && stride_ok16(L, c.x_sl, es);
@@ -177,13 +184,15 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
     const int64_t cap = wpc > 0 ? (int64_t)cu_count(cus) * wpc : nwork;
     c.nwaves = nwork < cap ? nwork : cap;
     if (c.nwaves < 1) c.nwaves = 1;
+    if (c.lds == 2) c.nwaves = nwork * kWavesPerGroup;   // one workgroup (of kClTrChannels threads) per item
     // Whole tiles of whole channel vectors take the straight-line path when all of
     // their loads can be vectors; then two row batches are in flight per lane.
     const bool straight = P.vector && c.vec_par && tile % kClUnroll == 0 &&
                           (!a->initial_states || c.vec_init) && (!a->seq_idx || c.vec_seq);
-    P.unroll = straight ? (c.lds ? kClLdsRows : 2 * kClUnroll) : kClUnroll;
+    P.unroll = straight ? (c.lds ? tile : 2 * kClUnroll) : kClUnroll;
     P.span = tile;
-    P.channels_per_item = 64 * V;
+    P.channels_per_item = c.lds == 2 ? kClTrChannels : 64 * V;
+    if (c.lds == 2) P.unroll = tile;
   }
   const int64_t waves = path == CCV_PATH_CHANNEL_FIRST ? plan->cf.nwaves : plan->cl.nwaves;
   const int64_t grid = (waves + kWavesPerGroup - 1) / kWavesPerGroup;

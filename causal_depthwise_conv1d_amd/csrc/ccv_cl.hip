@@ -408,9 +408,130 @@ __global__ void __launch_bounds__(256) cl_fwd_lds_kernel(const ClArgs a) {
   cl_fwd_body<S, K, SILU, SEQ, true, WB, true>(a, (lds_u32x4*)rows);
 }
 
+// ---- the pages' tile, for comparison: load, change direction, compute, change back
+//
+// Ch.5 "Dao forward CUDA implementation", section "Load first, then change the
+// access direction": a workgroup stages a tile of time rows x channels in LDS with
+// loads along channels, each thread then owns one channel and runs its time
+// steps out of LDS, writes its outputs back into the tile, and the tile is stored
+// along channels again.  Here: kClTrChannels channels (one per thread) x TT rows
+// plus the K-1 rows above; the outputs overwrite their own inputs in place (a
+// thread's window already holds the history it needs).  All threads read and
+// write the same row at once, consecutive elements, so the tile needs no padding.
+// The arithmetic is the register path's term for term, so the bits are the same.
+// Opt-in (CCV_CL_LDS=2), for C a multiple of 16 / element size with aligned rows.
+template <class S>
+struct TrTile {
+  static constexpr int ES = sizeof(typename S::raw);
+  static constexpr int TT = cl_tr_rows(ES);                  // time rows per tile
+  static constexpr int CHUNKS = kClTrChannels * ES / 16;     // 16-byte pieces per row
+};
+
+template <class S, int K, bool SILU, bool SEQ>
+__global__ void __launch_bounds__(kClTrChannels) cl_fwd_tr_kernel(const ClArgs a) {
+  using raw = typename S::raw;
+  using G = TrTile<S>;
+  constexpr int H = K - 1, TT = G::TT, ROWS = TT + H, V = 16 / G::ES, N = kClTrChannels;
+  __shared__ u32x4 tile[ROWS * G::CHUNKS];
+  __shared__ int ids[ROWS];
+  const Common& m = a.m;
+  const int tid = threadIdx.x;
+  const int64_t item = xcd_order(blockIdx.x, m.xcd_q, m.xcd_r);
+  const int64_t cb = item % a.ncg, rest = item / a.ncg;
+  const int64_t b = rest / a.ntt, t0 = (rest % a.ntt) * TT;
+  const int64_t c0 = cb * N, L = m.L, C = m.C;
+  const raw* xb = static_cast<const raw*>(m.x) + b * a.x_sb;
+  const raw* ib = static_cast<const raw*>(m.init);
+
+  // Load along channels: rows t0-H .. t0+TT-1 (history or zeros left of t = 0,
+  // zeros past L or C), and the rows' sequence ids (the history's: seq_idx[b, 0]).
+  for (int q = tid; q < ROWS * G::CHUNKS; q += N) {
+    const int r = q / G::CHUNKS, k = q - r * G::CHUNKS;
+    const int64_t t = t0 - H + r, c = c0 + (int64_t)k * V;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < C && t >= 0 && t < L) {
+      v = load16(xb + t * a.x_sl + c);
+    } else if (c < C && t < 0 && ib) {
+      raw e[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) e[i] = ib[b * m.is_b + (c + i) * m.is_c + (t + H) * m.is_i];
+      __builtin_memcpy(&v, e, 16);
+    }
+    tile[q] = v;
+  }
+  if constexpr (SEQ) {
+    for (int r = tid; r < ROWS; r += N) {
+      const int64_t t = t0 - H + r;
+      ids[r] = (t >= 0 && t < L) ? m.seq[b * L + t] : (t < 0 && L > 0 ? m.seq[b * L] : 0);
+    }
+  }
+  __syncthreads();
+
+  // Change direction: this thread's channel, along time.
+  const int64_t c = c0 + tid;
+  raw* col = reinterpret_cast<raw*>(tile) + tid;   // element (row r, this channel) at col[r * N]
+  if (c < C) {
+    float w[K];
+    load_params<K>(m.w, m.w_dtype, c * K, w);
+    const float beta = m.bias ? load_param(m.bias, m.w_dtype, c) : 0.0f;
+    float win[K];
+    int wid[K];
+    bool wok[K];
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      win[j + 1] = S::to_f(col[j * N]);
+      wid[j + 1] = SEQ ? ids[j] : 0;
+      wok[j + 1] = t0 - H + j >= 0 || ib != nullptr;
+    }
+    for (int r = 0; r < TT && t0 + r < L; ++r) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        win[j] = win[j + 1];
+        wid[j] = wid[j + 1];
+        wok[j] = wok[j + 1];
+      }
+      win[H] = S::to_f(col[(H + r) * N]);
+      wid[H] = SEQ ? ids[H + r] : 0;
+      wok[H] = true;
+      float acc = beta;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float f = __builtin_fmaf(w[k], win[k], acc);
+        acc = (!SEQ || (wok[k] && wid[k] == wid[H])) ? f : acc;
+      }
+      col[(H + r) * N] = S::from_f(SILU ? silu(acc) : acc);   // over its own input
+    }
+    // final_states: the tile that holds the row's end writes this channel's.
+    if (m.fin && t0 + TT >= L) {
+      const int32_t* sr = m.seq ? m.seq + b * L : nullptr;
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const int64_t src = L - H + j;
+        raw v = 0;
+        if (src >= 0) v = xb[src * a.x_sl + c];
+        else if (ib) v = ib[b * m.is_b + c * m.is_c + (src + H) * m.is_i];
+        if (!final_kept(sr, L, src, ib != nullptr)) v = 0;
+        static_cast<raw*>(m.fin)[b * m.fs_b + c * m.fs_c + j * m.fs_i] = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Change back: store along channels.
+  raw* ob = static_cast<raw*>(m.out) + b * a.o_sb;
+  for (int q = tid; q < TT * G::CHUNKS; q += N) {
+    const int r = q / G::CHUNKS, k = q - r * G::CHUNKS;
+    const int64_t t = t0 + r, cc = c0 + (int64_t)k * V;
+    if (t < L && cc < C) store16_stream(ob + t * a.o_sl + cc, tile[(H + r) * G::CHUNKS + k]);
+  }
+}
+
 template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
 static int launch_one(const ClArgs& a, uint32_t grid, void* stream) {
   void* args[] = {const_cast<ClArgs*>(&a)};
+  if (VEC && a.lds == 2)
+    return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cl_fwd_tr_kernel<S, K, SILU, SEQ>), dim3(grid),
+                                dim3(kClTrChannels), args, 0, static_cast<hipStream_t>(stream));
   const void* fn = VEC && a.lds ? reinterpret_cast<const void*>(&cl_fwd_lds_kernel<S, K, SILU, SEQ, WB>)
                                 : reinterpret_cast<const void*>(&cl_fwd_kernel<S, K, SILU, SEQ, VEC, WB>);
   return (int)hipLaunchKernel(fn, dim3(grid), dim3(64 * kWavesPerGroup), args, 0, static_cast<hipStream_t>(stream));

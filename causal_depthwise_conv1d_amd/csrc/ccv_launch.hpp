@@ -56,7 +56,8 @@ struct ClArgs {
   int32_t vec_init;  // initial_states rows load as aligned 16-byte channel vectors
   int32_t vec_seq;   // seq_idx rows load as aligned 16-byte vectors of 4 ids
   int32_t vec_par;   // weight and bias blocks of a lane load as aligned 16-byte vectors
-  int32_t lds;       // whole tiles staged through LDS (tile == kClLdsRows)
+  int32_t lds;       // 1: whole tiles staged through LDS (tile == kClLdsRows); 2: the
+                     // transposing tile (kClTrChannels channels, one workgroup per item)
 };
 
 // Compute units of the GPU that `stream` (a hipStream_t; NULL = the current
@@ -78,5 +79,8 @@ constexpr int kWavesPerGroup = 4;
 constexpr int kCfUnroll = 4;     // 16-byte vectors per lane per segment
 constexpr int kClUnroll = 4;     // time rows loaded ahead per lane
 constexpr int kClLdsRows = 16;   // rows of a tile staged through LDS
+constexpr int kClTrChannels = 256;   // channels (threads) of a transposing tile
+constexpr int cl_tr_rows(int es) { return es == 2 ? 64 : 32; }   // its time rows (LDS near 34 KB)
+static_assert(kClTrChannels == 64 * kWavesPerGroup, "a transposing tile is one workgroup");
 
 }  // namespace ccv

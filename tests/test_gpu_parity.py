@@ -257,6 +257,36 @@ def test_grid_is_sized_for_the_device_cu_count(monkeypatch):
     check_full(w, where="[CU count]")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_transposing_tiles_equal_register_tiles(dtype, monkeypatch):
+    """The pages' channel-last tile (CCV_CL_LDS=2: 256 channels x 64 rows, 32 for
+    fp32, staged along channels, computed one channel per thread along time, stored
+    along channels) gives the register path's bits: partial channel blocks, ragged
+    time tails, rows shorter than a tile, bias, SiLU, seq_idx, history and final
+    states; and agrees with the oracle."""
+    V = 16 // ES[dtype]
+    cases = [(2, 1024, 300, 4, dict(bias=True, init=True, final=True, activation="silu")),
+             (1, 600 - 600 % V, 777, 3, dict(bias=True, seq=9, activation="silu")),
+             (2, 520, 96, 2, dict(bias=False, seq=3, init=True, final=True, activation=None)),
+             (3, 256, 2, 4, dict(bias=True, init=True, final=True, activation="silu"))]
+    for i, (B, C, L, K, feats) in enumerate(cases):
+        w = build(L, C, B, K, dtype, "cl", feats, seed=4800 + i)
+        res = []
+        for mode in ("0", "2"):
+            monkeypatch.setenv("CCV_CL_LDS", mode)
+            kw = gpu_args(w)
+            plan = ccv.plan_for(x=kw["x"], weight=kw["weight"], bias=kw["bias"], seq_idx=kw["seq_idx"],
+                                initial_states=kw["initial_states"], activation=kw["activation"])
+            if mode == "2":
+                assert plan["channels_per_item"] == 256 and plan["span"] == (32 if dtype == "f32" else 64), plan
+            res.append(run_gpu(w))
+        log(f"  transposing tiles {dtype} B={B} C={C} L={L} K={K} {feats}")
+        assert bits_equal(res[0][0], res[1][0]), (i, "out")
+        if w.return_final_states:
+            assert bits_equal(res[0][1], res[1][1]), (i, "final states")
+        check_full(w, where=f"[transposing tiles {dtype} case {i}]")
+
+
 @pytest.mark.parametrize("layout", ["cf", "cl"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_down_convert_rounds_to_nearest_even(dtype, layout):
