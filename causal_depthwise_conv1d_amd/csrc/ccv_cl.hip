@@ -22,6 +22,8 @@
 // is issued before the current batch's arithmetic.  seq_idx ids are shared by all
 // channels of a row, so the masks are wave-uniform, and a batch whose window
 // holds one sequence skips the masking altogether.
+#include <type_traits>
+
 #include "ccv_device.hpp"
 
 namespace ccv {
@@ -37,17 +39,18 @@ __device__ inline TilePos tile_pos(const ClArgs& a, int64_t item) {
 }
 
 // The K-tap stencil (and SiLU) for one time row of this lane's V channels.
-// rows[k] is the extended input row t-H+k (k = K-1 is row t itself).
-template <class S, int K, bool SILU>
+// rows[k] is the extended input row t-H+k (k = K-1 is row t itself).  MASKED
+// is a template argument so that the unmasked form holds no selects at all.
+template <class S, int K, bool SILU, bool MASKED>
 __device__ inline void row_stencil(const float (&w)[S::V][K], const float (&beta)[S::V],
                                    const float* const (&rows)[K], const bool (&keep)[K],
-                                   bool masked, float (&y)[S::V]) {
+                                   float (&y)[S::V]) {
 #pragma unroll
   for (int i = 0; i < S::V; ++i) {
     float acc = beta[i];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      if (masked) acc = keep[k] ? __builtin_fmaf(w[i][k], rows[k][i], acc) : acc;
+      if (MASKED) acc = keep[k] ? __builtin_fmaf(w[i][k], rows[k][i], acc) : acc;
       else acc = __builtin_fmaf(w[i][k], rows[k][i], acc);
     }
     y[i] = SILU ? silu(acc) : acc;
@@ -168,30 +171,38 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane, ld
       for (int j = 1; j < K; ++j) one = one && wok[j] && wid[j] == id[0];
       masked = !one;
     }
+    // The batch's rows, with or without the masks; two copies of the code, chosen
+    // per batch on a wave-uniform flag (as one code with the flag folded into
+    // every term, each output paid K-1 selects).
+    auto batch = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // Slide: drop the oldest row, append row t + u.
+      for (int u = 0; u < U; ++u) {
+        // Slide: drop the oldest row, append row t + u.
 #pragma unroll
-      for (int j = 0; j < H; ++j) {
+        for (int j = 0; j < H; ++j) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) win[j][i] = win[j + 1][i];
-        wid[j] = wid[j + 1];
-        wok[j] = wok[j + 1];
+          for (int i = 0; i < V; ++i) win[j][i] = win[j + 1][i];
+          wid[j] = wid[j + 1];
+          wok[j] = wok[j + 1];
+        }
+        S::unpack(r[u], win[H]);
+        wid[H] = SEQ ? id[u] : 0;
+        wok[H] = true;
+        const float* rows[K];
+        bool keep[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          rows[k] = win[k];
+          keep[k] = !SEQ || (wok[k] && wid[k] == wid[H]);
+        }
+        float y[V];
+        row_stencil<S, K, SILU, MASKED>(w, beta, rows, keep, y);
+        gstore16_stream(ob + (t + u) * os + lx, S::pack(y));
       }
-      S::unpack(r[u], win[H]);
-      wid[H] = SEQ ? id[u] : 0;
-      wok[H] = true;
-      const float* rows[K];
-      bool keep[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        rows[k] = win[k];
-        keep[k] = !SEQ || (wok[k] && wid[k] == wid[H]);
-      }
-      float y[V];
-      row_stencil<S, K, SILU>(w, beta, rows, keep, masked, y);
-      gstore16_stream(ob + (t + u) * os + lx, S::pack(y));
-    }
+    };
+    if (SEQ && __builtin_expect(masked, 0)) batch(std::true_type{});
+    else batch(std::false_type{});
   };
 
   if constexpr (LDSM) {
@@ -310,7 +321,7 @@ __device__ inline void tile_general(const ClArgs& a, const TilePos& p, int lane)
         keep[k] = !SEQ || (rr >= 0 ? id[rr] == id[u] : (hok[H + rr] && hid[H + rr] == id[u]));
       }
       float y[V];
-      row_stencil<S, K, SILU>(w, beta, rows, keep, SEQ, y);
+      row_stencil<S, K, SILU, SEQ>(w, beta, rows, keep, y);
       if (tr < t1) {
         if (full) {
           store16(ob + tr * a.o_sl, S::pack(y));
