@@ -144,6 +144,22 @@ typedef struct ccv_plan {
  * CCV_CU_COUNT, when set to a positive count, replaces it. */
 int ccv_fwd(const ccv_fwd_args_t* args, void* hip_stream);
 
+/* Launch tuning and ablation switches, read from the environment at each call of
+ * ccv_fwd / ccv_fwd_plan (none is needed; every setting gives the same results,
+ * bit for bit):
+ *   CCV_CU_COUNT=n         size grids for n compute units (see ccv_fwd).
+ *   CCV_CF_WAVES_PER_CU=n  channel-first: a grid of n waves per compute unit, each
+ *                          walking several segments (0: one wave per segment).
+ *   CCV_CL_WAVES_PER_CU=n  channel-last: the same for tiles (default 0).
+ *   CCV_CL_TILE_T=n        channel-last: time rows per tile (default 32, at least 4).
+ *   CCV_CL_LDS=1 | 2       channel-last: tiles staged through LDS (16 rows), or the
+ *                          transposing tile of 256 channels (16-byte aligned
+ *                          layouts only; others keep the default path).
+ *   CCV_FORCE_SCALAR=1     element-wise loads and stores (read by ccv_update and
+ *                          ccv_bwd too; the backward's dweight and dbias are then
+ *                          summed in another fixed order, so they agree to rounding).
+ * The plan (ccv_fwd_plan) shows the launch they lead to. */
+
 /* Validate `args` exactly as ccv_fwd does, without touching any device. */
 int ccv_fwd_check(const ccv_fwd_args_t* args);
 
