@@ -218,6 +218,29 @@ def test_plan_channel_last_strided_view():
     assert p.work_items == 8 * (4096 // 512) * -(-8192 // p.span)
 
 
+def test_plan_channel_last_lds_forms(monkeypatch):
+    """CCV_CL_LDS picks the LDS-staged tile (1: 16 rows of 64 * V channels per wave)
+    or the transposing tile (2: 256 channels by 64 rows for 16-bit data, one
+    workgroup per item); an unaligned layout or an unknown value keeps the register
+    tiles (32 rows)."""
+    view = dict(B=8, C=4096, L=8192, layout="cl", x_stride=(8192 * 10240, 1, 10240))
+    _, p0 = ccv.ccv_fwd_plan(args(**view))
+    assert (p0.span, p0.channels_per_item) == (32, 512)
+    monkeypatch.setenv("CCV_CL_LDS", "1")
+    _, p = ccv.ccv_fwd_plan(args(**view))
+    assert (p.span, p.unroll, p.channels_per_item, p.vector) == (16, 16, 512, 1)
+    assert p.work_items == 8 * 8 * (8192 // 16)
+    monkeypatch.setenv("CCV_CL_LDS", "2")
+    _, p = ccv.ccv_fwd_plan(args(**view))
+    assert (p.span, p.channels_per_item) == (64, 256)
+    assert p.work_items == 8 * (4096 // 256) * (8192 // 64) == p.grid     # a workgroup per item
+    _, p = ccv.ccv_fwd_plan(args(layout="cl", x_stride=(1000 * 67, 1, 67)))
+    assert (p.vector, p.channels_per_item) == (0, 64 * 8)                    # unaligned rows
+    monkeypatch.setenv("CCV_CL_LDS", "7")
+    _, p = ccv.ccv_fwd_plan(args(**view))
+    assert (p.span, p.channels_per_item) == (p0.span, p0.channels_per_item)
+
+
 def test_plan_falls_back_to_element_access_when_unaligned():
     # channel offset 3 in a bf16 buffer: base not 16-byte aligned
     _, p = ccv.ccv_fwd_plan(args(layout="cl", x=X + 6, x_stride=(1000 * 72, 1, 72)))
