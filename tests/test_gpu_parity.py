@@ -502,9 +502,14 @@ def test_element_path_equals_vector_path(dtype, layout, monkeypatch):
     assert bits_equal(fa.cpu(), fb.cpu())
 
 
-def test_channel_last_tile_sweep_bit_identical(monkeypatch):
+@pytest.mark.parametrize("packed", [False, True])
+def test_channel_last_tile_sweep_bit_identical(packed, monkeypatch):
+    """Every tile length gives the same bits; with packed sequences (short ones, so
+    that many 4-row batches straddle a start) both the masked and the unmasked
+    batch code run at every tile length, single-batch tiles included."""
     w = wl.make_case(B=2, C=520, L=2000, K=4, x_dtype="f16", layout="cl", bias=True, init=True,
-                     final=True, activation="silu", seed=14)
+                     final=True, activation="silu", seed=14,
+                     seq_lengths=seq_lengths(2000, 60, 14) if packed else None)
     kw = gpu_args(w)
     ref, fref = ccv.causal_conv1d_fwd(**kw)
     for tile in (4, 8, 13, 32, 100, 256, 4096):
@@ -512,6 +517,7 @@ def test_channel_last_tile_sweep_bit_identical(monkeypatch):
         o, f = ccv.causal_conv1d_fwd(**kw)
         torch.cuda.synchronize()
         assert bits_equal(o.cpu(), ref.cpu()) and bits_equal(f.cpu(), fref.cpu()), tile
+    check_full(w, where=f"[tile sweep, packed={packed}]")
 
 
 def test_noncontiguous_input_is_copied_and_reported():
