@@ -53,7 +53,7 @@ __device__ inline SegPos row_pos(const Common& m, int64_t row, int64_t t0) {
 
 // Issue the loads of whole segment p (when `valid`; otherwise harmless loads of
 // zeros, so the instruction stream is the same either way).
-template <class S, int K, bool SEQ, int WB>
+template <class S, int K, bool SEQ, int WB, bool TAIL>
 __device__ inline void issue_segment(const CfArgs& a, const SegPos& p, bool valid, int lane,
                                      SegLoads<S, K, SEQ, WB>& q) {
   constexpr int V = S::V;
@@ -65,18 +65,38 @@ __device__ inline void issue_segment(const CfArgs& a, const SegPos& p, bool vali
   const uintptr_t xrow = reinterpret_cast<uintptr_t>(m.x) + (p.b * a.x_sb + p.c * a.x_sc) * ES;
   const uintptr_t srow = reinterpret_cast<uintptr_t>(m.seq) + p.b * m.L * 4;
 
-  const uintptr_t dbase = pick(valid, xrow + (p.t0 + lane * V) * ES, zero);
-  const uintptr_t dstep = valid ? 64 * V * ES : 0;
+  if constexpr (!TAIL) {
+    const uintptr_t dbase = pick(valid, xrow + (p.t0 + lane * V) * ES, zero);
+    const uintptr_t dstep = valid ? 64 * V * ES : 0;
 #pragma unroll
-  for (int u = 0; u < kCfUnroll; ++u) q.d[u] = gload16_stream(dbase + u * dstep);
-  if constexpr (SEQ) {
-    const uintptr_t sbase = pick(valid, srow + (p.t0 + lane * V) * 4, zero);
-    const uintptr_t sstep = valid ? 64 * V * 4 : 0;
-    const uintptr_t squad = valid ? 16 : 0;
+    for (int u = 0; u < kCfUnroll; ++u) q.d[u] = gload16_stream(dbase + u * dstep);
+    if constexpr (SEQ) {
+      const uintptr_t sbase = pick(valid, srow + (p.t0 + lane * V) * 4, zero);
+      const uintptr_t sstep = valid ? 64 * V * 4 : 0;
+      const uintptr_t squad = valid ? 16 : 0;
 #pragma unroll
-    for (int u = 0; u < kCfUnroll; ++u)
+      for (int u = 0; u < kCfUnroll; ++u)
 #pragma unroll
-      for (int r = 0; r < V / 4; ++r) q.sid[u][r] = gload<u32x4>(sbase + u * sstep + r * squad);
+        for (int r = 0; r < V / 4; ++r) q.sid[u][r] = gload<u32x4>(sbase + u * sstep + r * squad);
+    }
+  } else {
+    // A row's last segment that ends early (L a multiple of V, not of the span): a
+    // vector at or past L loads the segment's first vector instead (in bounds; its
+    // outputs are not stored, and no halo flows from it into a vector before L).
+    const int64_t vrem = m.L - p.t0;               // steps of the row from t0 on
+    const uintptr_t dbase = pick(valid, xrow + p.t0 * ES, zero);
+    const uintptr_t sbase = pick(valid, srow + p.t0 * 4, zero);
+#pragma unroll
+    for (int u = 0; u < kCfUnroll; ++u) {
+      const int64_t e = (int64_t)(u * 64 + lane) * V;
+      const bool in = valid && e < vrem;
+      q.d[u] = gload16_stream(dbase + (in ? (uint32_t)e * ES : 0u));
+      if constexpr (SEQ) {
+#pragma unroll
+        for (int r = 0; r < V / 4; ++r)
+          q.sid[u][r] = gload<u32x4>(sbase + (in ? (uint32_t)e * 4 + r * 16 : 0u));
+      }
+    }
   }
   const uintptr_t wbase = pick(valid, reinterpret_cast<uintptr_t>(m.w) + p.c * K * WB, zero);
   const uintptr_t wstep = valid ? WB : 0;
@@ -146,7 +166,7 @@ __device__ inline void first_flags(int64_t t0, int lane, bool has_init, bool (&f
 }
 
 // Arithmetic and stores of a whole segment from its prefetched loads.
-template <class S, int K, bool SILU, bool SEQ, int WB>
+template <class S, int K, bool SILU, bool SEQ, int WB, bool TAIL>
 __device__ inline void compute_whole(const CfArgs& a, const SegPos& p, int lane,
                                      const SegLoads<S, K, SEQ, WB>& q) {
   constexpr int V = S::V;
@@ -179,7 +199,7 @@ __device__ inline void compute_whole(const CfArgs& a, const SegPos& p, int lane,
         for (int i = 0; i < 4; ++i) id[4 * r + i] = (int)dword(q.sid[u][r], i);
     }
     stencil_vector<S, K, SILU, SEQ>(e, id, carry, carry_id, u == 0, first_ok, w, beta, y);
-    store16_stream(ol + u * 64 * V, S::pack(y));
+    if (!TAIL || p.t0 + (int64_t)(u * 64 + lane) * V < m.L) store16_stream(ol + u * 64 * V, S::pack(y));
   }
 }
 
@@ -287,31 +307,32 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
     SegLoads<S, K, SEQ, WB> qa, qb;
     int64_t i = w0;
     SegPos pa{b, c, seg * a.span}, pb;
-    issue_segment<S, K, SEQ, WB>(a, pa, true, lane, qa);
+    issue_segment<S, K, SEQ, WB, false>(a, pa, true, lane, qa);
     while (true) {
       const int64_t i1 = i + W;
       if (i1 >= n1) {                               // last segment of this wave
-        compute_whole<S, K, SILU, SEQ, WB>(a, pa, lane, qa);
+        compute_whole<S, K, SILU, SEQ, WB, false>(a, pa, lane, qa);
         break;
       }
       advance();
       pb = SegPos{b, c, seg * a.span};
-      issue_segment<S, K, SEQ, WB>(a, pb, true, lane, qb);
-      compute_whole<S, K, SILU, SEQ, WB>(a, pa, lane, qa);
+      issue_segment<S, K, SEQ, WB, false>(a, pb, true, lane, qb);
+      compute_whole<S, K, SILU, SEQ, WB, false>(a, pa, lane, qa);
       const int64_t i2 = i1 + W;
       if (i2 >= n1) {
-        compute_whole<S, K, SILU, SEQ, WB>(a, pb, lane, qb);
+        compute_whole<S, K, SILU, SEQ, WB, false>(a, pb, lane, qb);
         break;
       }
       advance();
       pa = SegPos{b, c, seg * a.span};
-      issue_segment<S, K, SEQ, WB>(a, pa, true, lane, qa);
-      compute_whole<S, K, SILU, SEQ, WB>(a, pb, lane, qb);
+      issue_segment<S, K, SEQ, WB, false>(a, pa, true, lane, qa);
+      compute_whole<S, K, SILU, SEQ, WB, false>(a, pb, lane, qb);
       i = i2;
     }
   }
 
-  // Phase 2: the other segments (ragged tails, or all of them when unaligned).
+  // Phase 2: the other segments (ragged tails, or all of them when unaligned; a
+  // ragged tail of whole vectors is left to the tail kernel below).
   const int64_t ntail = a.nseg - nfull;
   const int64_t n2 = m.L > 0 ? rows * ntail : 0;
   for (int64_t j = w0; j < n2; j += W) {
@@ -324,8 +345,46 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
     for (int64_t r = w0; r < rows; r += W) final_states_row<S, K>(a, row_pos(m, r, 0), lane);
 }
 
+// The rows' last, shorter segments when L is a multiple of V but not of the span
+// (16-byte rows): one wave per row takes segment nfull on the 16-byte path, its
+// lanes past L storing nothing, instead of the element path.  A kernel of its own,
+// launched after the main one, so that the main kernel's code (and its register
+// count, hence its occupancy) stays that of the whole segments.
+template <class S, int K, bool SILU, bool SEQ, int WB>
+__global__ void __launch_bounds__(256) cf_fwd_tail_kernel(const CfArgs a) {
+  const Common& m = a.m;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r = (int64_t)blockIdx.x * kWavesPerGroup + wave;
+  if (r >= m.B * m.C) return;                       // whole wave leaves together
+  const int64_t b = r / m.C;
+  const SegPos p{b, r - b * m.C, a.nfull * a.span};
+  SegLoads<S, K, SEQ, WB> q;
+  issue_segment<S, K, SEQ, WB, true>(a, p, true, lane, q);
+  compute_whole<S, K, SILU, SEQ, WB, true>(a, p, lane, q);
+}
+
 template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
 static int launch_one(const CfArgs& a, uint32_t grid, void* stream) {
+  if constexpr (VEC) {
+    const int64_t L = a.m.L;
+    if (L > 0 && L % S::V == 0 && L % a.span != 0) {   // main kernel without the tails, then the tails
+      CfArgs main = a;
+      main.nseg -= 1;
+      void* args[] = {&main};
+      int e = (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_kernel<S, K, SILU, SEQ, VEC, WB>),
+                                   dim3(grid), dim3(64 * kWavesPerGroup), args, 0,
+                                   static_cast<hipStream_t>(stream));
+      if (e) return e;
+      const int64_t rows = a.m.B * a.m.C;
+      const int64_t tgrid = (rows + kWavesPerGroup - 1) / kWavesPerGroup;
+      if (tgrid > INT32_MAX) return (int)hipErrorInvalidValue;
+      void* targs[] = {const_cast<CfArgs*>(&a)};
+      return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_tail_kernel<S, K, SILU, SEQ, WB>),
+                                  dim3((uint32_t)tgrid), dim3(64 * kWavesPerGroup), targs, 0,
+                                  static_cast<hipStream_t>(stream));
+    }
+  }
   void* args[] = {const_cast<CfArgs*>(&a)};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_kernel<S, K, SILU, SEQ, VEC, WB>),
                               dim3(grid), dim3(64 * kWavesPerGroup), args, 0,

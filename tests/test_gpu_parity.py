@@ -378,16 +378,21 @@ def _guarded(shape_alloc, view_fn, dtype, n_guard=4096):
 
 
 @pytest.mark.parametrize("layout", ["cf", "cl"])
-def test_guard_bands_untouched(layout):
+@pytest.mark.parametrize("L", [1037, 1040])
+def test_guard_bands_untouched(layout, L):
     """out and final_states live inside NaN-filled buffers: everything outside the
-    views must be untouched (elements are written exactly once, in place)."""
-    B, C, L, K = 2, 72, 1037, 4
+    views must be untouched (elements are written exactly once, in place).  With
+    L = 1040 the channel-first rows take the 16-byte path, whose one segment per
+    row ends at L, so the lanes past it must store nothing."""
+    B, C, K = 2, 72, 4
     w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype="bf16", layout=layout, bias=True, init=True,
                      final=True, activation="silu", seed=6)
     kw = gpu_args(w)
     dt = kw["x"].dtype
     if layout == "cf":
         obuf, out = _guarded((B, C + 2, L + 8), lambda t: t[:, 1:1 + C, :L], dt)
+        if L % 8 == 0:
+            assert ccv.plan_for(x=kw["x"], weight=kw["weight"], out=out)["vector"] == 1
     else:
         obuf, out = _guarded((B, L, C + 8), lambda t: t[:, :, :C].transpose(1, 2), dt)
     fbuf, fs = _guarded((B, K - 1, C + 4), lambda t: t[:, :, 2:2 + C].transpose(1, 2), dt)
@@ -500,6 +505,35 @@ def test_element_path_equals_vector_path(dtype, layout, monkeypatch):
     eq = bits_equal(a.cpu(), b.cpu())
     assert eq, eq
     assert bits_equal(fa.cpu(), fb.cpu())
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_channel_first_ragged_last_segment(dtype, monkeypatch):
+    """L a multiple of 16 / element size but not of a segment: the row's last
+    segment runs on the 16-byte path with its lanes past L storing nothing.  Same
+    bits as the element path and every output against the oracle, for contiguous
+    rows and rows with a padded pitch (the guard-band test checks that nothing is
+    written past L)."""
+    V = 16 // ES[dtype]
+    span = 64 * 4 * V
+    cases = [(2, 6, 2 * span + V, 4, dict(bias=True, init=True, final=True, activation="silu")),
+             (3, 5, span - V, 3, dict(bias=True, seq=7, activation="silu")),
+             (1, 4, 3 * V, 2, dict(bias=False, init=True, final=True, activation=None)),
+             (2, 3, span + 17 * V, 4, dict(bias=True, seq=5, init=True, final=True, activation="silu"))]
+    for i, (B, C, L, K, feats) in enumerate(cases):
+        for layout in ("cf", "cf_pitch"):
+            w = build(L, C, B, K, dtype, layout, feats, seed=4900 + i)
+            kw = gpu_args(w)
+            assert ccv.plan_for(x=kw["x"], weight=kw["weight"])["vector"] == 1
+            a = run_gpu(w)
+            monkeypatch.setenv("CCV_FORCE_SCALAR", "1")
+            b = run_gpu(w)
+            monkeypatch.delenv("CCV_FORCE_SCALAR")
+            log(f"  ragged last segment {dtype} {layout} B={B} C={C} L={L} K={K} {feats}")
+            assert bits_equal(a[0], b[0]), (i, layout)
+            if w.return_final_states:
+                assert bits_equal(a[1], b[1]), (i, layout)
+            check_full(w, where=f"[ragged last segment {dtype} {layout} case {i}]")
 
 
 @pytest.mark.parametrize("packed", [False, True])
