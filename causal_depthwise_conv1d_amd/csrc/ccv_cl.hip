@@ -206,6 +206,11 @@ __device__ inline void tile_fast(const ClArgs& a, const TilePos& p, int lane, ld
   };
 
   if constexpr (LDSM) {
+    // Wait for every global-to-LDS load of the tile before the first read of it.
+    // The compiler's own waits do not cover these loads reliably: it once left the
+    // ids' load in flight at the first read of the ids, so a batch could take the
+    // previous tile's ids and the wrong masks.
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0); expcnt, lgkmcnt not waited
 #pragma unroll 1
     for (int j = 0; j < NLB; ++j) {
 #pragma unroll
