@@ -7,10 +7,11 @@
 // That version's other limits are lifted, since the page calls them limits of
 // the version and not of the mathematics: states and seq_idx work with either
 // layout and with each other (the history is the row's first sequence's, the
-// final states the row's last sequence's), and channel-last needs no
-// multiple-of-8 alignment (an element-wise path serves unaligned views).
+// final states the row's last sequence's), and neither layout needs
+// multiple-of-8 alignment (channel-first rows take unaligned 16-byte accesses,
+// an element-wise path serves unaligned channel-last views).
 //
-// Nothing here touches a device except ccv_fwd's single kernel launch.
+// Nothing here touches a device except ccv_fwd's kernel launches.
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -116,6 +117,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
   plan->silu = a->activation == CCV_ACT_SILU;
   plan->seq = a->seq_idx != nullptr;
   int64_t nwork;
+  int64_t tail_groups = 0;
 
   if (path == CCV_PATH_CHANNEL_FIRST) {
     CfArgs& c = plan->cf;
@@ -123,12 +125,18 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
     c.o_sb = a->out_stride[0]; c.o_sc = a->out_stride[1];
     c.span = (int64_t)64 * V * kCfUnroll;
     c.nseg = L > 0 ? (L + c.span - 1) / c.span : 1;
-    bool vec = aligned16(a->x) && stride_ok16(B, c.x_sb, es) && stride_ok16(C, c.x_sc, es);
-    if (want_out) vec = vec && aligned16(a->out) && stride_ok16(B, c.o_sb, es) && stride_ok16(C, c.o_sc, es);
-    if (a->seq_idx) vec = vec && aligned16(a->seq_idx) && (B <= 1 || (L & 3) == 0);
-    vec = vec && !force_scalar;
+    // Rows of any length and element offset take the 16-byte path: gfx950 serves
+    // 16-byte accesses at any element alignment (measured on MI355X: a bf16 copy
+    // offset by 2 bytes moves 5330 GB/s against 6040 aligned, back to back), and the
+    // one vector per row that straddles L moves element by element.
+    const bool vec = !force_scalar;
     c.nfull = vec ? L / c.span : 0;
     if (__builtin_mul_overflow(rows, c.nseg, &nwork)) return CCV_E_SHAPE;
+    // A row's last, shorter segment (L not a multiple of the span) runs in one wave
+    // of its own in workgroups appended to the grid; the waves counted here take
+    // the whole segments.
+    const bool tails = vec && L > 0 && L % c.span != 0;
+    const int64_t nmain = tails ? rows * c.nfull : nwork;
     // Waves launched.  Arithmetic-heavy calls (16-bit storage packs twice the
     // outputs into each byte; SiLU adds two transcendentals per output) run a grid
     // of 16 waves per CU, each walking its segments with the next one's loads in
@@ -139,8 +147,9 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
     // overrides the choice.
     const bool heavy = es == 2 || a->activation == CCV_ACT_SILU;
     const int wpc = env_int("CCV_CF_WAVES_PER_CU", heavy ? 16 : 0);
-    const int64_t cap = wpc > 0 ? (int64_t)cu_count(cus) * wpc : nwork;
-    c.nwaves = nwork < cap ? nwork : cap;
+    const int64_t cap = wpc > 0 ? (int64_t)cu_count(cus) * wpc : nmain;
+    c.nwaves = nmain < cap ? nmain : cap;
+    tail_groups = tails ? (rows + kWavesPerGroup - 1) / kWavesPerGroup : 0;
     P.vector = vec;
     P.unroll = kCfUnroll;
     P.span = c.span;
@@ -195,7 +204,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
     if (c.lds == 2) P.unroll = tile;
   }
   const int64_t waves = path == CCV_PATH_CHANNEL_FIRST ? plan->cf.nwaves : plan->cl.nwaves;
-  const int64_t grid = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t grid = (waves + kWavesPerGroup - 1) / kWavesPerGroup + tail_groups;
   if (grid > INT32_MAX) return CCV_E_SHAPE;
   m.nwork = nwork;
   m.xcd_q = (uint32_t)(grid / 8);

@@ -80,21 +80,38 @@ __device__ inline void issue_segment(const CfArgs& a, const SegPos& p, bool vali
         for (int r = 0; r < V / 4; ++r) q.sid[u][r] = gload<u32x4>(sbase + u * sstep + r * squad);
     }
   } else {
-    // A row's last segment that ends early (L a multiple of V, not of the span): a
-    // vector at or past L loads the segment's first vector instead (in bounds; its
-    // outputs are not stored, and no halo flows from it into a vector before L).
+    // A row's last segment, shorter than the span.  Vectors that end at or before L
+    // load as 16 bytes; a vector at or past L loads the segment's first vector
+    // instead (in bounds; its outputs are not stored, and no halo flows from it
+    // into a vector before L).  When L is not a multiple of V, the one vector that
+    // straddles L is read element by element, zeros past L, so no access leaves
+    // the row.  Wave-wide vector groups that start at or past L load nothing (the
+    // arithmetic skips them too).
     const int64_t vrem = m.L - p.t0;               // steps of the row from t0 on
     const uintptr_t dbase = pick(valid, xrow + p.t0 * ES, zero);
     const uintptr_t sbase = pick(valid, srow + p.t0 * 4, zero);
 #pragma unroll
     for (int u = 0; u < kCfUnroll; ++u) {
+      if ((int64_t)u * 64 * V >= vrem) break;
       const int64_t e = (int64_t)(u * 64 + lane) * V;
-      const bool in = valid && e < vrem;
-      q.d[u] = gload16_stream(dbase + (in ? (uint32_t)e * ES : 0u));
+      const bool whole = valid && e + V <= vrem;
+      q.d[u] = gload16_stream(dbase + (whole ? (uint32_t)e * ES : 0u));
       if constexpr (SEQ) {
 #pragma unroll
         for (int r = 0; r < V / 4; ++r)
-          q.sid[u][r] = gload<u32x4>(sbase + (in ? (uint32_t)e * 4 + r * 16 : 0u));
+          q.sid[u][r] = gload<u32x4>(sbase + (whole ? (uint32_t)e * 4 + r * 16 : 0u));
+      }
+      if (valid && e < vrem && e + V > vrem) {
+        raw part[V];
+        int32_t part_id[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const bool in = e + i < vrem;
+          part[i] = in ? gload<raw>(dbase + (uint32_t)(e + i) * ES) : raw(0);
+          part_id[i] = (SEQ && in) ? gload<int32_t>(sbase + (uint32_t)(e + i) * 4) : 0;
+        }
+        __builtin_memcpy(&q.d[u], part, 16);
+        if constexpr (SEQ) __builtin_memcpy(&q.sid[u][0], part_id, V * 4);
       }
     }
   }
@@ -189,6 +206,7 @@ __device__ inline void compute_whole(const CfArgs& a, const SegPos& p, int lane,
   raw* __restrict__ ol = static_cast<raw*>(m.out) + p.b * a.o_sb + p.c * a.o_sc + p.t0 + lane * V;
 #pragma unroll
   for (int u = 0; u < kCfUnroll; ++u) {
+    if (TAIL && p.t0 + (int64_t)u * 64 * V >= m.L) break;   // the wave's vectors are all past L
     float e[V], y[V];
     int id[V];
     S::unpack(q.d[u], e);
@@ -199,7 +217,18 @@ __device__ inline void compute_whole(const CfArgs& a, const SegPos& p, int lane,
         for (int i = 0; i < 4; ++i) id[4 * r + i] = (int)dword(q.sid[u][r], i);
     }
     stencil_vector<S, K, SILU, SEQ>(e, id, carry, carry_id, u == 0, first_ok, w, beta, y);
-    if (!TAIL || p.t0 + (int64_t)(u * 64 + lane) * V < m.L) store16_stream(ol + u * 64 * V, S::pack(y));
+    if constexpr (!TAIL) {
+      store16_stream(ol + u * 64 * V, S::pack(y));
+    } else {
+      const int64_t left = m.L - (p.t0 + (int64_t)(u * 64 + lane) * V);
+      if (left >= V) {
+        store16_stream(ol + u * 64 * V, S::pack(y));
+      } else if (left > 0) {                       // the vector that straddles L
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (i < left) ol[u * 64 * V + i] = S::from_f(y[i]);
+      }
+    }
   }
 }
 
@@ -277,9 +306,29 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
   // XCD one contiguous range does.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t w0 = (int64_t)blockIdx.x * kWavesPerGroup + wave;
+  const int64_t rows = m.B * m.C;
+  // With 16-byte rows whose length is not a multiple of the span, workgroups
+  // appended after those of the whole segments give each row's last, shorter
+  // segment a wave of its own (lanes past L store nothing, the vector that
+  // straddles L moves element by element); that wave also writes the row's final
+  // states.  They share the launch, so they run beside the whole segments instead
+  // of after them.
+  const bool tails = VEC && m.L > 0 && a.nseg > a.nfull;
+  if constexpr (VEC) {
+    const int64_t wmain = (a.nwaves + kWavesPerGroup - 1) / kWavesPerGroup * kWavesPerGroup;
+    if (w0 >= wmain) {
+      const int64_t r = w0 - wmain;
+      if (!tails || r >= rows) return;              // whole wave leaves together
+      const SegPos p = row_pos(m, r, a.nfull * a.span);
+      SegLoads<S, K, SEQ, WB> q;
+      issue_segment<S, K, SEQ, WB, true>(a, p, true, lane, q);
+      compute_whole<S, K, SILU, SEQ, WB, true>(a, p, lane, q);
+      if (m.fin) final_states_row<S, K>(a, p, lane);
+      return;
+    }
+  }
   if (w0 >= a.nwaves) return;                       // whole wave leaves together
   const int64_t W = a.nwaves;
-  const int64_t rows = m.B * m.C;
 
   // Phase 1: whole segments, two sets of loads in flight.  The next segment's
   // loads are issued before the current segment's arithmetic; the body is
@@ -331,60 +380,22 @@ __global__ void __launch_bounds__(256) cf_fwd_kernel(const CfArgs a) {
     }
   }
 
-  // Phase 2: the other segments (ragged tails, or all of them when unaligned; a
-  // ragged tail of whole vectors is left to the tail kernel below).
-  const int64_t ntail = a.nseg - nfull;
-  const int64_t n2 = m.L > 0 ? rows * ntail : 0;
-  for (int64_t j = w0; j < n2; j += W) {
-    const int64_t row = j / ntail;
-    compute_partial<S, K, SILU, SEQ>(a, row_pos(m, row, (nfull + j % ntail) * a.span), lane);
+  // Phase 2 (element path only): every segment, element by element.
+  if constexpr (!VEC) {
+    const int64_t n2 = m.L > 0 ? rows * a.nseg : 0;
+    for (int64_t j = w0; j < n2; j += W) {
+      const int64_t row = j / a.nseg;
+      compute_partial<S, K, SILU, SEQ>(a, row_pos(m, row, (j % a.nseg) * a.span), lane);
+    }
   }
 
-  // Phase 3: final states.
-  if (m.fin)
+  // Phase 3: final states (the appended waves write them when there are tails).
+  if (m.fin && !tails)
     for (int64_t r = w0; r < rows; r += W) final_states_row<S, K>(a, row_pos(m, r, 0), lane);
-}
-
-// The rows' last, shorter segments when L is a multiple of V but not of the span
-// (16-byte rows): one wave per row takes segment nfull on the 16-byte path, its
-// lanes past L storing nothing, instead of the element path.  A kernel of its own,
-// launched after the main one, so that the main kernel's code (and its register
-// count, hence its occupancy) stays that of the whole segments.
-template <class S, int K, bool SILU, bool SEQ, int WB>
-__global__ void __launch_bounds__(256) cf_fwd_tail_kernel(const CfArgs a) {
-  const Common& m = a.m;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t r = (int64_t)blockIdx.x * kWavesPerGroup + wave;
-  if (r >= m.B * m.C) return;                       // whole wave leaves together
-  const int64_t b = r / m.C;
-  const SegPos p{b, r - b * m.C, a.nfull * a.span};
-  SegLoads<S, K, SEQ, WB> q;
-  issue_segment<S, K, SEQ, WB, true>(a, p, true, lane, q);
-  compute_whole<S, K, SILU, SEQ, WB, true>(a, p, lane, q);
 }
 
 template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB>
 static int launch_one(const CfArgs& a, uint32_t grid, void* stream) {
-  if constexpr (VEC) {
-    const int64_t L = a.m.L;
-    if (L > 0 && L % S::V == 0 && L % a.span != 0) {   // main kernel without the tails, then the tails
-      CfArgs main = a;
-      main.nseg -= 1;
-      void* args[] = {&main};
-      int e = (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_kernel<S, K, SILU, SEQ, VEC, WB>),
-                                   dim3(grid), dim3(64 * kWavesPerGroup), args, 0,
-                                   static_cast<hipStream_t>(stream));
-      if (e) return e;
-      const int64_t rows = a.m.B * a.m.C;
-      const int64_t tgrid = (rows + kWavesPerGroup - 1) / kWavesPerGroup;
-      if (tgrid > INT32_MAX) return (int)hipErrorInvalidValue;
-      void* targs[] = {const_cast<CfArgs*>(&a)};
-      return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_tail_kernel<S, K, SILU, SEQ, WB>),
-                                  dim3((uint32_t)tgrid), dim3(64 * kWavesPerGroup), targs, 0,
-                                  static_cast<hipStream_t>(stream));
-    }
-  }
   void* args[] = {const_cast<CfArgs*>(&a)};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&cf_fwd_kernel<S, K, SILU, SEQ, VEC, WB>),
                               dim3(grid), dim3(64 * kWavesPerGroup), args, 0,

@@ -121,16 +121,23 @@ typedef enum {
 
 typedef struct ccv_plan {
   int32_t path;            /* ccv_path_t; NONE when there is nothing to compute or write */
-  int32_t vector;          /* 1: 16-byte loads and stores; 0: element loads and stores */
+  int32_t vector;          /* 1: 16-byte loads and stores; 0: element loads and stores.
+                              Channel-first rows take 16-byte accesses at any length and
+                              element offset (the vector that straddles L moves element by
+                              element); channel-last needs 16-byte aligned rows */
   int32_t elems_per_lane;  /* elements one lane holds per 16-byte vector (16 / element size) */
   int32_t unroll;          /* vectors (channel-first) or time rows (channel-last) in flight per
                               lane; channel-last: 8 when whole tiles take the straight-line
                               path (the row batch being computed and the next one; weights,
                               bias, history rows and seq_idx ids as vectors), 4 otherwise */
-  int64_t grid;            /* workgroups launched */
+  int64_t grid;            /* workgroups launched (channel-first with L not a multiple of
+                              span: the whole segments' workgroups, then one wave per row for
+                              the row's last, shorter segment) */
   int32_t block;           /* threads per workgroup */
   int32_t waves_per_group; /* independent wave work items per workgroup */
-  int64_t work_items;      /* wave work items (grid * waves_per_group rounded down to the need) */
+  int64_t work_items;      /* wave work items (channel-first: B*C rows times ceil(L / span)
+                              segments; otherwise grid * waves_per_group rounded down to the
+                              need) */
   int64_t span;            /* channel-first: time steps per work item; channel-last: time rows per work item */
   int64_t channels_per_item; /* channel-last: channels per work item; channel-first: 1 */
 } ccv_plan_t;

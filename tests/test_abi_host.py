@@ -178,6 +178,21 @@ def test_plan_channel_first():
     assert p.grid * p.waves_per_group == min(p.work_items, 256 * 16)
 
 
+def test_plan_channel_first_short_last_segments_get_workgroups_of_their_own():
+    # L not a multiple of the span: the whole segments keep their grid (16 waves per
+    # CU for bf16 + SiLU), and one wave per row, in workgroups appended to the grid,
+    # takes the row's last, shorter segment.
+    rows = 4 * 2048
+    _, p = ccv.ccv_fwd_plan(args(B=4, C=2048, L=4097))
+    assert p.vector == 1 and p.work_items == rows * 3
+    assert p.grid == min(rows * 2, 256 * 16) // p.waves_per_group + rows // p.waves_per_group
+    # rows shorter than a span: only the appended workgroups
+    a = args(B=8, C=1024, L=1001, activation=ccv.CCV_ACT_NONE)
+    a.x_dtype = a.w_dtype = ccv.CCV_F32
+    _, p = ccv.ccv_fwd_plan(a)
+    assert p.span == 1024 and p.grid == 8 * 1024 // p.waves_per_group
+
+
 def test_plan_grid_follows_the_cu_count_override(monkeypatch):
     # No launch has run in this process, so plans size the grid for 256 CUs;
     # CCV_CU_COUNT replaces the count (a partitioned or smaller part).
@@ -248,11 +263,18 @@ def test_plan_falls_back_to_element_access_when_unaligned():
     # odd time stride breaks alignment of every row after the first
     _, p = ccv.ccv_fwd_plan(args(layout="cl", x_stride=(1000 * 67, 1, 67)))
     assert p.vector == 0
+
+
+def test_channel_first_takes_16_byte_accesses_at_any_alignment(monkeypatch):
+    # Channel-first rows of any length and offset take the 16-byte path (the GPU
+    # serves unaligned 16-byte accesses; the vector that straddles L goes element
+    # by element); only CCV_FORCE_SCALAR selects the element path.
+    for kw in (dict(x_stride=(64 * 1001, 1001, 1)), dict(seq_idx=SEQ + 4), dict(seq_idx=SEQ, L=1002),
+               dict(x=X + 6), dict(L=3, x_stride=(192, 3, 1), out_stride=(192, 3, 1))):
+        _, p = ccv.ccv_fwd_plan(args(layout="cf", **kw))
+        assert p.path == ccv.CCV_PATH_CHANNEL_FIRST and p.vector == 1, kw
+    monkeypatch.setenv("CCV_FORCE_SCALAR", "1")
     _, p = ccv.ccv_fwd_plan(args(layout="cf", x_stride=(64 * 1001, 1001, 1)))
-    assert p.vector == 0
-    _, p = ccv.ccv_fwd_plan(args(layout="cf", seq_idx=SEQ + 4))
-    assert p.vector == 0
-    _, p = ccv.ccv_fwd_plan(args(layout="cf", seq_idx=SEQ, L=1002))
     assert p.vector == 0
 
 

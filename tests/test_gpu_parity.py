@@ -239,19 +239,23 @@ def test_lds_staged_tiles_equal_register_tiles(dtype, monkeypatch):
 
 def test_grid_is_sized_for_the_device_cu_count(monkeypatch):
     """A launch reads the GPU's compute-unit count from the runtime; plans made
-    after it size the grid for that GPU (16 waves per CU for bf16 with SiLU).  A
-    smaller count from CCV_CU_COUNT (an odd one, so the waves' segment walks end
-    unevenly) changes the grid, not the bits."""
-    w = build(4099, 96, 2, 4, "bf16", "cf", dict(bias=True, activation="silu"), seed=4400)
+    after it size the grid for that GPU (16 waves per CU for bf16 with SiLU, for
+    the whole segments; L = 4099 adds a workgroup per 4 rows for the rows' last,
+    shorter segments).  A smaller count from CCV_CU_COUNT (an odd one, so the
+    waves' segment walks end unevenly) changes the grid, not the bits."""
+    B, C, L = 2, 96, 4099
+    w = build(L, C, B, 4, "bf16", "cf", dict(bias=True, activation="silu"), seed=4400)
     base = run_gpu(w)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     kw = gpu_args(w)
     plan = ccv.plan_for(x=kw["x"], weight=kw["weight"], bias=kw["bias"], activation="silu")
-    assert plan["work_items"] > 7 * 16
-    assert plan["grid"] * plan["waves_per_group"] == min(plan["work_items"], cus * 16), (cus, plan)
+    whole = B * C * (L // plan["span"])
+    tail_groups = -(-B * C // plan["waves_per_group"])
+    assert L % plan["span"] and whole > 7 * 16
+    assert plan["grid"] == -(-min(whole, cus * 16) // plan["waves_per_group"]) + tail_groups, (cus, plan)
     monkeypatch.setenv("CCV_CU_COUNT", "7")
     plan7 = ccv.plan_for(x=kw["x"], weight=kw["weight"], bias=kw["bias"], activation="silu")
-    assert plan7["grid"] * plan7["waves_per_group"] == 7 * 16, plan7
+    assert plan7["grid"] == 7 * 16 // plan7["waves_per_group"] + tail_groups, plan7
     assert bits_equal(base[0], run_gpu(w)[0])
     log(f"  {cus} CUs: grid {plan['grid']}; CCV_CU_COUNT=7: grid {plan7['grid']}, same bits")
     check_full(w, where="[CU count]")
@@ -378,12 +382,13 @@ def _guarded(shape_alloc, view_fn, dtype, n_guard=4096):
 
 
 @pytest.mark.parametrize("layout", ["cf", "cl"])
-@pytest.mark.parametrize("L", [1037, 1040])
+@pytest.mark.parametrize("L", [1037, 1040, 3])
 def test_guard_bands_untouched(layout, L):
     """out and final_states live inside NaN-filled buffers: everything outside the
-    views must be untouched (elements are written exactly once, in place).  With
-    L = 1040 the channel-first rows take the 16-byte path, whose one segment per
-    row ends at L, so the lanes past it must store nothing."""
+    views must be untouched (elements are written exactly once, in place).  The
+    channel-first rows take the 16-byte path, whose one segment per row ends at L:
+    the lanes past it must store nothing, and with L = 1037 and 3 (rows not 16-byte
+    aligned) the vector that straddles L must store only its elements before L."""
     B, C, K = 2, 72, 4
     w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype="bf16", layout=layout, bias=True, init=True,
                      final=True, activation="silu", seed=6)
@@ -391,8 +396,7 @@ def test_guard_bands_untouched(layout, L):
     dt = kw["x"].dtype
     if layout == "cf":
         obuf, out = _guarded((B, C + 2, L + 8), lambda t: t[:, 1:1 + C, :L], dt)
-        if L % 8 == 0:
-            assert ccv.plan_for(x=kw["x"], weight=kw["weight"], out=out)["vector"] == 1
+        assert ccv.plan_for(x=kw["x"], weight=kw["weight"], out=out)["vector"] == 1
     else:
         obuf, out = _guarded((B, L, C + 8), lambda t: t[:, :, :C].transpose(1, 2), dt)
     fbuf, fs = _guarded((B, K - 1, C + 4), lambda t: t[:, :, 2:2 + C].transpose(1, 2), dt)
@@ -509,19 +513,28 @@ def test_element_path_equals_vector_path(dtype, layout, monkeypatch):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_channel_first_ragged_last_segment(dtype, monkeypatch):
-    """L a multiple of 16 / element size but not of a segment: the row's last
-    segment runs on the 16-byte path with its lanes past L storing nothing.  Same
-    bits as the element path and every output against the oracle, for contiguous
-    rows and rows with a padded pitch (the guard-band test checks that nothing is
+    """L not a multiple of a segment: the row's last segment runs on the 16-byte
+    path with its lanes past L storing nothing; when L is not a multiple of 16 /
+    element size either, the rows are not 16-byte aligned and the one vector that
+    straddles L moves element by element.  Same bits as the element path and every
+    output against the oracle, for contiguous rows, rows with a padded pitch and an
+    unaligned window of a bigger buffer (the guard-band test checks that nothing is
     written past L)."""
     V = 16 // ES[dtype]
     span = 64 * 4 * V
     cases = [(2, 6, 2 * span + V, 4, dict(bias=True, init=True, final=True, activation="silu")),
              (3, 5, span - V, 3, dict(bias=True, seq=7, activation="silu")),
              (1, 4, 3 * V, 2, dict(bias=False, init=True, final=True, activation=None)),
-             (2, 3, span + 17 * V, 4, dict(bias=True, seq=5, init=True, final=True, activation="silu"))]
+             (2, 3, span + 17 * V, 4, dict(bias=True, seq=5, init=True, final=True, activation="silu")),
+             # rows of a length that is not a multiple of the vector
+             (2, 6, 2 * span + V + 3, 4, dict(bias=True, init=True, final=True, activation="silu")),
+             (3, 5, span - 1, 3, dict(bias=True, seq=7, activation="silu")),
+             (2, 7, span + 1, 2, dict(bias=False, seq=3, init=True, final=True, activation=None)),
+             (3, 9, V - 1, 4, dict(bias=True, init=True, final=True, activation="silu")),
+             (2, 5, 2, 3, dict(bias=True, seq=1, init=True, final=True, activation="silu")),
+             (1, 3, 5 * span, 4, dict(bias=True, seq=11, init=True, final=True, activation="silu"))]
     for i, (B, C, L, K, feats) in enumerate(cases):
-        for layout in ("cf", "cf_pitch"):
+        for layout in ("cf", "cf_pitch", "cf_view"):
             w = build(L, C, B, K, dtype, layout, feats, seed=4900 + i)
             kw = gpu_args(w)
             assert ccv.plan_for(x=kw["x"], weight=kw["weight"])["vector"] == 1
