@@ -575,11 +575,58 @@ struct RegPos {
 };
 
 // Where a segment lies in its row: inside with the K-1 steps past it
-// (t0 + span + K - 1 <= L), ending exactly at L (every vector inside, nothing
-// past it), or anything else (the row's last, partial segment).
+// (t0 + span + K - 1 <= L; with ODD rows, the V steps past it), ending exactly at
+// L (every vector inside, nothing past it), or anything else (the row's last,
+// partial segment).
 enum { kSegInner = 0, kSegLast = 1, kSegEdge = 2 };
 
-template <class S, int K, bool SEQ, int MODE>
+// ODD: rows that are not 16-byte aligned (L not a multiple of V, or an offset
+// view).  Their 16-byte accesses are unaligned (the GPU serves them), the one
+// vector that straddles L moves element by element, and loads whose address is
+// the same in every lane go element by element: the compiler may turn such a
+// 16-byte load into a scalar load, which ignores the address's low two bits.
+
+// Elements e .. e+V-1 of a row (element 0 at `base`) as one 16-byte vector: a
+// single load when they all lie before `n`, else element by element with zeros
+// from n on, so no access leaves the row.
+template <class raw, int V>
+__device__ inline u32x4 load_row_vec(uintptr_t base, int64_t e, int64_t n) {
+  if (e + V <= n) return gload16_stream(base + e * (int64_t)sizeof(raw));
+  raw part[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) part[i] = e + i < n ? gload<raw>(base + (e + i) * (int64_t)sizeof(raw)) : raw(0);
+  u32x4 v;
+  __builtin_memcpy(&v, part, 16);
+  return v;
+}
+
+// The ids of steps t .. t+V-1 of a row of seq_idx (step 0 at `base`), zeros from n on.
+template <int V>
+__device__ inline void load_row_ids(uintptr_t base, int64_t t, int64_t n, u32x4 (&out)[V / 4]) {
+  if (t + V <= n) {
+#pragma unroll
+    for (int r = 0; r < V / 4; ++r) out[r] = gload<u32x4>(base + t * 4 + r * 16);
+    return;
+  }
+  int32_t part[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) part[i] = t + i < n ? gload<int32_t>(base + (t + i) * 4) : 0;
+  __builtin_memcpy(&out[0], part, V * 4);
+}
+
+// Elements t .. t+N-1 of a row (zeros from n on) in the low elements of a 16-byte
+// vector, by element loads (for addresses that are the same in every lane).
+template <class T, int N>
+__device__ inline u32x4 load_row_head(uintptr_t base, int64_t t, int64_t n) {
+  T part[16 / sizeof(T)] = {};
+#pragma unroll
+  for (int j = 0; j < N; ++j) part[j] = t + j < n ? gload<T>(base + (t + j) * (int64_t)sizeof(T)) : T(0);
+  u32x4 v;
+  __builtin_memcpy(&v, part, 16);
+  return v;
+}
+
+template <class S, int K, bool SEQ, int MODE, bool ODD>
 __device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, RegLoads<S, K, SEQ>& q) {
   using raw = typename S::raw;
   constexpr bool EDGE = MODE == kSegEdge;
@@ -594,7 +641,11 @@ __device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, Re
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t o = lo + (uint32_t)(u * 64 * V * ES);
-    if constexpr (EDGE) {
+    if constexpr (EDGE && ODD) {
+      const int64_t e = (int64_t)(u * 64 + lane) * V;
+      q.xv[u] = load_row_vec<raw, V>(xs, e, L - t0);
+      q.gv[u] = load_row_vec<raw, V>(gs, e, L - t0);
+    } else if constexpr (EDGE) {
       const bool ok = t0 + (int64_t)(u * 64 + lane) * V < L;
       q.xv[u] = gload16_stream(pick(ok, xs + o, zero));
       q.gv[u] = gload16_stream(pick(ok, gs + o, zero));
@@ -603,7 +654,10 @@ __device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, Re
       q.gv[u] = gload16_stream(gs + o);
     }
   }
-  if constexpr (EDGE) {
+  if constexpr (ODD && MODE != kSegLast) {         // the H steps past the segment (all it reads)
+    q.hx = load_row_head<raw, H>(reinterpret_cast<uintptr_t>(xr), t1, L);
+    q.hg = load_row_head<raw, H>(reinterpret_cast<uintptr_t>(gr), t1, L);
+  } else if constexpr (EDGE) {
     q.hx = gload<u32x4>(pick(t1 < L, reinterpret_cast<uintptr_t>(xr + t1), zero));
     q.hg = gload<u32x4>(pick(t1 < L, reinterpret_cast<uintptr_t>(gr + t1), zero));
   } else if constexpr (MODE == kSegLast) {
@@ -626,13 +680,23 @@ __device__ inline void reg_issue(const BwdArgs& a, const RegPos& p, int lane, Re
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t t = t0 + (int64_t)(u * 64 + lane) * V;
-      const uintptr_t at = pick(!EDGE || t < L, sr + t * 4, zero);
+      if constexpr (EDGE && ODD) {
+        load_row_ids<V>(sr, t, L, q.iv[u]);
+      } else {
+        const uintptr_t at = pick(!EDGE || t < L, sr + t * 4, zero);
 #pragma unroll
-      for (int r = 0; r < V / 4; ++r) q.iv[u][r] = gload<u32x4>(at + (EDGE && t >= L ? 0 : r * 16));
+        for (int r = 0; r < V / 4; ++r) q.iv[u][r] = gload<u32x4>(at + (EDGE && t >= L ? 0 : r * 16));
+      }
     }
-    const uintptr_t ah = pick(MODE != kSegLast && t1 < L, sr + t1 * 4, zero);
+    if constexpr (ODD) {                           // ids of the H steps past the segment
 #pragma unroll
-    for (int r = 0; r < V / 4; ++r) q.hi[r] = gload<u32x4>(ah + (MODE != kSegLast && t1 < L ? r * 16 : 0));
+      for (int r = 0; r < V / 4; ++r) q.hi[r] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (MODE != kSegLast) q.hi[0] = load_row_head<int32_t, H>(sr, t1, L);
+    } else {
+      const uintptr_t ah = pick(MODE != kSegLast && t1 < L, sr + t1 * 4, zero);
+#pragma unroll
+      for (int r = 0; r < V / 4; ++r) q.hi[r] = gload<u32x4>(ah + (MODE != kSegLast && t1 < L ? r * 16 : 0));
+    }
 #pragma unroll
     for (int j = 0; j < H; ++j) {
       const int64_t src = t0 - H + j;              // the history carries seq_idx[b, 0]
@@ -660,7 +724,7 @@ __device__ inline float reg_param(uint32_t d, int dtype, int64_t i) {
 // no position needs a check, but lane 63 of the last vector holds the row's last
 // H steps: it skips the taps that would read dz past L and adds dfinal_states,
 // exactly as the checked form does.  kSegEdge: every check in place.
-template <class S, int K, bool SILU, bool SEQ, int MODE>
+template <class S, int K, bool SILU, bool SEQ, int MODE, bool ODD>
 __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, const RegLoads<S, K, SEQ>& q) {
   using raw = typename S::raw;
   constexpr bool EDGE = MODE == kSegEdge, LAST = MODE == kSegLast;
@@ -733,9 +797,20 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
       }
       y[i] = acc;
     }
-    const u32x4 pk = S::pack(y);
-    if (!EDGE || base < L)
-      store16_stream(reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(dxr + t0) + lo + u * 64 * V * ES), pk);
+    if constexpr (ODD && EDGE) {
+      raw* const dst = reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(dxr + t0) + lo + u * 64 * V * ES);
+      if (base + V <= L) {
+        store16_stream(dst, S::pack(y));
+      } else if (base < L) {                       // the vector that straddles L
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (base + i < L) dst[i] = S::from_f(y[i]);
+      }
+    } else {
+      const u32x4 pk = S::pack(y);
+      if (!EDGE || base < L)
+        store16_stream(reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(dxr + t0) + lo + u * 64 * V * ES), pk);
+    }
   };
 
   // Lane 0 of the row's first vector: whether each of the H history steps before
@@ -743,7 +818,8 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
   const bool lead = lane == 0 && t0 == 0 && a.init == nullptr;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool ok = !EDGE || t0 + (int64_t)(u * 64 + lane) * V < L;
+    const int64_t tv = t0 + (int64_t)(u * 64 + lane) * V;   // this lane's vector's first step
+    const bool okv = !EDGE || tv < L;
     float e[V], g[V];
     S::unpack(q.xv[u], e);
     S::unpack(q.gv[u], g);
@@ -781,6 +857,7 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
         z = keep[k] ? f : z;
       }
       const float d = SILU ? g[i] * silu_slope(z) : g[i];
+      const bool ok = ODD && EDGE ? tv + i < L : okv;   // ODD: the straddling vector's steps past L
       dz[i] = ok ? d : 0.0f;
       if (ok) {
 #pragma unroll
@@ -900,7 +977,7 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
 // mask of the walk reads true, and the unmasked arithmetic gives the same bits.
 // The ids are loaded here on their own, so that neither form of the arithmetic
 // holds them (or the other form's values) in registers.
-template <class S, int K, int MODE>
+template <class S, int K, int MODE, bool ODD>
 __device__ inline bool reg_one_sequence(const BwdArgs& a, const RegPos& p, int lane) {
   constexpr bool EDGE = MODE == kSegEdge;
   constexpr int V = S::V, U = kBwdRegUnroll, H = K - 1, SPAN = 64 * V * U;
@@ -913,12 +990,21 @@ __device__ inline bool reg_one_sequence(const BwdArgs& a, const RegPos& p, int l
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t t = t0 + (int64_t)(u * 64 + lane) * V;
-    const bool in = !EDGE || t < L;
+    if constexpr (ODD && EDGE) {
+      u32x4 iv[V / 4];
+      load_row_ids<V>(sr, t, L, iv);
 #pragma unroll
-    for (int r = 0; r < V / 4; ++r) {
-      const u32x4 v = gload<u32x4>(pick(in, sr + t * 4 + r * 16, zero));
+      for (int r = 0; r < V / 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ok = ok && ((EDGE && t + 4 * r + i >= L) || (int)dword(v, i) == ref);
+        for (int i = 0; i < 4; ++i) ok = ok && (t + 4 * r + i >= L || (int)dword(iv[r], i) == ref);
+    } else {
+      const bool in = !EDGE || t < L;
+#pragma unroll
+      for (int r = 0; r < V / 4; ++r) {
+        const u32x4 v = gload<u32x4>(pick(in, sr + t * 4 + r * 16, zero));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ok = ok && ((EDGE && t + 4 * r + i >= L) || (int)dword(v, i) == ref);
+      }
     }
   }
 #pragma unroll
@@ -926,7 +1012,10 @@ __device__ inline bool reg_one_sequence(const BwdArgs& a, const RegPos& p, int l
     const int64_t src = t0 - H + j;
     ok = ok && gload<int32_t>(src >= 0 ? sr + src * 4 : sr) == ref;
   }
-  if constexpr (MODE != kSegLast) {
+  if constexpr (MODE != kSegLast && ODD) {        // the V steps past the segment, as dwords
+#pragma unroll
+    for (int i = 0; i < V; ++i) ok = ok && (t1 + i >= L || gload<int32_t>(sr + (t1 + i) * 4) == ref);
+  } else if constexpr (MODE != kSegLast) {
 #pragma unroll
     for (int r = 0; r < V / 4; ++r) {
       const u32x4 v = gload<u32x4>(pick(t1 < L, sr + t1 * 4 + r * 16, zero));
@@ -939,30 +1028,30 @@ __device__ inline bool reg_one_sequence(const BwdArgs& a, const RegPos& p, int l
 
 // One segment: its loads, then its arithmetic, in the form for where it lies (and,
 // with seq_idx, unmasked when it holds one sequence).
-template <class S, int K, bool SILU, bool SEQ, int MODE>
+template <class S, int K, bool SILU, bool SEQ, int MODE, bool ODD>
 __device__ inline void reg_segment_in(const BwdArgs& a, const RegPos& p, int lane) {
   if constexpr (SEQ) {
-    if (reg_one_sequence<S, K, MODE>(a, p, lane)) {
+    if (reg_one_sequence<S, K, MODE, ODD>(a, p, lane)) {
       RegLoads<S, K, false> q;
-      reg_issue<S, K, false, MODE>(a, p, lane, q);
-      reg_compute<S, K, SILU, false, MODE>(a, p, lane, q);
+      reg_issue<S, K, false, MODE, ODD>(a, p, lane, q);
+      reg_compute<S, K, SILU, false, MODE, ODD>(a, p, lane, q);
       return;
     }
   }
   RegLoads<S, K, SEQ> q;
-  reg_issue<S, K, SEQ, MODE>(a, p, lane, q);
-  reg_compute<S, K, SILU, SEQ, MODE>(a, p, lane, q);
+  reg_issue<S, K, SEQ, MODE, ODD>(a, p, lane, q);
+  reg_compute<S, K, SILU, SEQ, MODE, ODD>(a, p, lane, q);
 }
 
-template <class S, int K, bool SILU, bool SEQ>
+template <class S, int K, bool SILU, bool SEQ, bool ODD>
 __device__ inline void reg_segment(const BwdArgs& a, const RegPos& p, int lane) {
   const int64_t t1 = (p.seg + 1) * (64 * kBwdRegUnroll * S::V);
-  if (t1 + K - 1 <= a.L)
-    reg_segment_in<S, K, SILU, SEQ, kSegInner>(a, p, lane);
+  if (t1 + (ODD ? S::V : K - 1) <= a.L)
+    reg_segment_in<S, K, SILU, SEQ, kSegInner, ODD>(a, p, lane);
   else if (t1 == a.L)
-    reg_segment_in<S, K, SILU, SEQ, kSegLast>(a, p, lane);
+    reg_segment_in<S, K, SILU, SEQ, kSegLast, ODD>(a, p, lane);
   else
-    reg_segment_in<S, K, SILU, SEQ, kSegEdge>(a, p, lane);
+    reg_segment_in<S, K, SILU, SEQ, kSegEdge, ODD>(a, p, lane);
 }
 
 __device__ inline RegPos reg_pos(const BwdArgs& a, int64_t i) {
@@ -979,12 +1068,12 @@ __device__ inline RegPos reg_pos(const BwdArgs& a, int64_t i) {
 // items, needs about 100 more registers, halves the waves per CU, and measured
 // slower; so did a fixed grid of 16 resident waves per CU looping over items, and,
 // with seq_idx, items of 4 channels of a segment sharing its ids in registers.)
-template <class S, int K, bool SILU, bool SEQ>
+template <class S, int K, bool SILU, bool SEQ, bool ODD>
 __global__ void __launch_bounds__(kBwdBlock) bwd_cf_reg_kernel(const BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t i = (int64_t)blockIdx.x * (kBwdBlock / 64) + wave;
-  if (i < a.items) reg_segment<S, K, SILU, SEQ>(a, reg_pos(a, i), lane);
+  if (i < a.items) reg_segment<S, K, SILU, SEQ, ODD>(a, reg_pos(a, i), lane);
 }
 
 __device__ inline void store_param(void* p, int dtype, int64_t i, float v) {
@@ -1055,7 +1144,10 @@ int launch_one(const BwdArgs& a, int path, uint32_t grid, void* st) {
   const void* fn;
   int block = 64;
   if (path == kBwdPathRegCf) {
-    fn = reinterpret_cast<const void*>(&bwd_cf_reg_kernel<S, K, SILU, SEQ>);
+    fn = reinterpret_cast<const void*>(&bwd_cf_reg_kernel<S, K, SILU, SEQ, false>);
+    block = kBwdBlock;
+  } else if (path == kBwdPathRegCfOdd) {
+    fn = reinterpret_cast<const void*>(&bwd_cf_reg_kernel<S, K, SILU, SEQ, true>);
     block = kBwdBlock;
   } else if (path == kBwdPathLdsCf)
     fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, false>);

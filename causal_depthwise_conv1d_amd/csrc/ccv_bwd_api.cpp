@@ -35,15 +35,21 @@ int choose_path(const ccv_bwd_args_t* a) {
   const int es = elt_size(a->x_dtype);
   const int V = 16 / es;
   const int64_t B = a->B, C = a->C, L = a->L;
-  if (!aligned16(a->x) || !aligned16(a->dout) || !aligned16(a->dx)) return kBwdPathElement;
+  const bool aligned = aligned16(a->x) && aligned16(a->dout) && aligned16(a->dx);
   const int64_t* st[3] = {a->x_stride, a->dout_stride, a->dx_stride};
-  bool cf = L % V == 0, cl = C % V == 0;
+  // Channel-first rows of any length and offset take the register path (16-byte
+  // accesses at any element alignment; the vector that straddles L moves element
+  // by element).  The LDS-staged kernels need 16-byte aligned rows.
+  bool cf = true, cf16 = aligned && L % V == 0, cl = aligned && C % V == 0;
   for (const int64_t* s : st) {
-    cf = cf && s[2] == 1 && stride_ok16(B, s[0], es) && stride_ok16(C, s[1], es);
+    cf = cf && s[2] == 1;
+    cf16 = cf16 && s[2] == 1 && stride_ok16(B, s[0], es) && stride_ok16(C, s[1], es);
     cl = cl && s[1] == 1 && stride_ok16(B, s[0], es) && stride_ok16(L, s[2], es);
   }
-  // The register path reads a lane's ids as 16-byte vectors beside its x.
-  if (cf) return a->seq_idx && !aligned16(a->seq_idx) ? kBwdPathLdsCf : kBwdPathRegCf;
+  // The register path reads a lane's ids as 16-byte vectors beside its x; ids that
+  // are not 16-byte aligned go through the LDS-staged kernel.
+  if (cf && a->seq_idx && !aligned16(a->seq_idx)) return cf16 ? kBwdPathLdsCf : kBwdPathElement;
+  if (cf) return cf16 ? kBwdPathRegCf : kBwdPathRegCfOdd;
   if (cl) return kBwdPathLdsCl;
   return kBwdPathElement;
 }
@@ -101,7 +107,7 @@ int validate(const ccv_bwd_args_t* a, BwdPlan* p, bool check_workspace = true) {
   // register-only channel-first path: segments of its own span, one per partial row,
   // one wave per (b, c, segment).
   const int path = rows ? choose_path(a) : kBwdPathElement;
-  const bool reg = path == kBwdPathRegCf;
+  const bool reg = path == kBwdPathRegCf || path == kBwdPathRegCfOdd;
   const int64_t T = reg ? bwd_reg_span(a->x_dtype) : bwd_tile_steps(a->x_dtype);
   const int64_t ntt = L > 0 ? (L + T - 1) / T : 1;
   const bool channel_unit = (a->x_stride[1] == 1 || C <= 1) && !(a->x_stride[2] == 1 && L > 1);
@@ -217,8 +223,9 @@ int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan) {
   *plan = ccv_plan_t{};
   const bool lds = p.path == kBwdPathLdsCf || p.path == kBwdPathLdsCl;
   plan->path = p.grid || p.rgrid ? CCV_PATH_BACKWARD : CCV_PATH_NONE;
-  plan->vector = p.path;
-  plan->elems_per_lane = p.path == kBwdPathRegCf ? 16 / elt_size(args->x_dtype) : 1;
+  const bool reg = p.path == kBwdPathRegCf || p.path == kBwdPathRegCfOdd;
+  plan->vector = reg ? kBwdPathRegCf : p.path;
+  plan->elems_per_lane = reg ? 16 / elt_size(args->x_dtype) : 1;
   plan->unroll = (int32_t)p.a.tpi;
   plan->grid = p.grid;
   plan->block = lds ? 64 : kBwdBlock;

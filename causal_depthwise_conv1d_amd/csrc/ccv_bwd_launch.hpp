@@ -68,10 +68,13 @@ constexpr int kBwdFinalWaves = 16;  // waves of the final reduction kernel's wor
 // which need x, dout and dx unit-stride in the same dimension (time for CF,
 // channels for CL), 16-byte aligned bases and strides, and L (CF) or C (CL) a
 // multiple of 16 / element size.
-enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2, kBwdPathRegCf = 3 };
+// kBwdPathRegCfOdd is the register path on rows that are not 16-byte aligned (its
+// own kernel instantiation, so that the aligned kernel's code is unchanged); the
+// plan reports it as kBwdPathRegCf.
+enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2, kBwdPathRegCf = 3, kBwdPathRegCfOdd = 4 };
 
-// The register-only channel-first path (the layout conditions of the LDS
-// channel-first path; with seq_idx, a 16-byte aligned seq_idx): work items are
+// The register-only channel-first path (x, dout and dx unit-stride in time, any
+// alignment; with seq_idx, a 16-byte aligned seq_idx): work items are
 // segments of bwd_reg_span(dtype) steps of
 // one (b, c) row, numbered row-major; a partial row per (b, segment); a grid of
 // kBwdBlock-lane workgroups, one wave per item.

@@ -546,9 +546,15 @@ def test_bwd_plan():
     a.seq_idx = SEQ + 4
     st, p = ccv.ccv_bwd_plan(a)
     assert st == 0 and p.span == 32 and p.vector == 1
-    # unaligned or mixed layouts: the element kernel, one lane per (b, tile, c)
-    st, p = ccv.ccv_bwd_plan(bargs(B=4, C=2048, L=4095, x_stride=(2048 * 4095, 4095, 1),
-                                   dout_stride=(2048 * 4095, 4095, 1), dx_stride=(2048 * 4095, 4095, 1)))
+    # channel-first rows that are not 16-byte aligned (L = 4095): the register kernel,
+    # its vector that straddles L moving element by element
+    odd = dict(B=4, C=2048, L=4095, x_stride=(2048 * 4095, 4095, 1), dout_stride=(2048 * 4095, 4095, 1),
+               dx_stride=(2048 * 4095, 4095, 1))
+    st, p = ccv.ccv_bwd_plan(bargs(**odd))
+    assert st == 0 and p.vector == 3 and p.span == 2048 and p.work_items == 4 * 2048 * 2
+    # ... with ids that are not 16-byte aligned either, and mixed layouts: the element
+    # kernel, one lane per (b, tile, c)
+    st, p = ccv.ccv_bwd_plan(bargs(seq_idx=SEQ + 4, **odd))
     assert st == 0 and p.vector == 0 and p.work_items == 4 * 128 * 2048 and p.grid == 4 * 128 * 2048 // 256
     assert ccv.ccv_bwd_plan(bargs(dx_stride=(64 * 1000, 1, 64)))[1].vector == 0
 

@@ -180,12 +180,12 @@ def test_bwd_matches_oracle(dtype, K, layout):
 @pytest.mark.parametrize("layout", ["cf", "cl"])
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
-    """The kernels chosen for aligned unit-stride layouts against the element
-    kernel, with a ragged last tile, a partial group of 64 channels, history,
-    dfinal_states and seq_idx (short sequences, and long ones whose tiles mostly hold
-    one id), and (register path) rows that end inside a segment or exactly at a
-    segment's end, with and without seq_idx: dx and d(initial_states) have the same
-    bits on every path.  The channel-last LDS kernel also gives the same dweight and
+    """The kernels chosen for unit-stride layouts against the element kernel, with a
+    ragged last tile, a partial group of 64 channels, history, dfinal_states and
+    seq_idx (short sequences, and long ones whose tiles mostly hold one id), and
+    (register path) rows that end inside a segment or exactly at a segment's end,
+    and rows whose length is not a multiple of the vector, with and without seq_idx:
+    dx and d(initial_states) have the same bits on every path.  The channel-last LDS kernel also gives the same dweight and
     dbias bits; the register-only channel-first kernel sums the parameter gradients
     in another order, so there they meet the oracle's bound."""
     T = tile_steps(dtype)
@@ -194,14 +194,17 @@ def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
         # seq=2: long sequences, so most LDS tiles hold one id and take the unmasked walk
         for f in (dict(init=True, dfs=True), dict(seq=7), dict(seq=2)):
             # the register path: one partial segment; one segment ending at L; an inner
-            # segment then one ending at L; an inner segment then a partial one
-            Ls = [4 * T + 8] + ([span, 2 * span, span + 40] if layout == "cf" else [])
+            # segment then one ending at L; an inner segment then a partial one; rows
+            # that are not 16-byte aligned (L not a multiple of the vector), one of them
+            # shorter than a vector for bf16 / f16
+            Ls = [4 * T + 8] + ([span, 2 * span, span + 40, span + 41, 2 * span + 3, 5]
+                                if layout == "cf" else [])
             for L in Ls:
                 B, C = 2, 136
                 log(f"  bwd fast vs element {dtype} {layout} K={K} L={L} {f}")
                 w = build(B, C, L, K, dtype, layout, 5100 + K, seq=f.get("seq"), init=f.get("init", False))
                 dout, dfs = grad_inputs(w, layout, f.get("dfs", False), 5100 + K)
-                if f.get("seq") == 2:                  # some tile right of t = 0 holds a single id
+                if f.get("seq") == 2 and L > T:        # some tile right of t = 0 holds a single id
                     ids, H = w.seq_idx[0].tolist(), K - 1
                     assert any(len(set(ids[t0 - H:min(t0 + T + H, L)])) == 1 for t0 in range(T, L, T))
                 res = []
