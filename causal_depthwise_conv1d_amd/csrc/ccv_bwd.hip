@@ -816,8 +816,27 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
   // Lane 0 of the row's first vector: whether each of the H history steps before
   // it has an id (without a history, steps left of t = 0 have none and never count).
   const bool lead = lane == 0 && t0 == 0 && a.init == nullptr;
+  bool done = false;                               // ODD: the rest of the segment lies past L
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    if constexpr (ODD && EDGE) {
+      if (u > 0 && t0 + (int64_t)u * 64 * V >= L) {
+        // Group u and those after it lie past L: none of their steps has an output
+        // or a parameter-gradient term, and the taps of group u-1 that would read
+        // their dz are outside [0, L) and skipped by position.  Store group u-1
+        // and stop (a wave-uniform exit).
+        float next[H];
+        int nid[H];
+#pragma unroll
+        for (int m = 0; m < H; ++m) {
+          next[m] = shift_out(0.0f, dzp[m]);
+          nid[m] = SEQ ? shift_out(0, idp[m]) : 0;
+        }
+        put_dx(u - 1, dzp, idp, next, nid);
+        done = true;
+        break;
+      }
+    }
     const int64_t tv = t0 + (int64_t)(u * 64 + lane) * V;   // this lane's vector's first step
     const bool okv = !EDGE || tv < L;
     float e[V], g[V];
@@ -893,7 +912,8 @@ __device__ inline void reg_compute(const BwdArgs& a, const RegPos& p, int lane, 
     }
   }
   // dz of the H steps past the segment (zero past L), for the last vector's lane 63.
-  if constexpr (LAST) {
+  if (done) {
+  } else if constexpr (LAST) {
     const float none[H] = {};
     const int none_id[H] = {};
     float next[H];
