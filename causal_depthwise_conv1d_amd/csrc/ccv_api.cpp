@@ -8,8 +8,8 @@
 // the version and not of the mathematics: states and seq_idx work with either
 // layout and with each other (the history is the row's first sequence's, the
 // final states the row's last sequence's), and neither layout needs
-// multiple-of-8 alignment (channel-first rows take unaligned 16-byte accesses,
-// an element-wise path serves unaligned channel-last views).
+// multiple-of-8 alignment (both take unaligned 16-byte accesses; a partial vector
+// at a row's or a channel group's end moves element by element).
 //
 // Nothing here touches a device except ccv_fwd's kernel launches.
 #include <stdint.h>
@@ -169,6 +169,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
                        (!want_out || (aligned16(a->out) && stride_ok16(B, a->out_stride[0], es) &&
                                       stride_ok16(L, a->out_stride[2], es)));
     c.lds = env_int("CCV_CL_LDS", 0);
+    if (c.lds == 1 && !(vec_x && !force_scalar)) c.lds = 0;   // global-to-LDS loads: aligned rows
     if (c.lds == 2 && !(vec_x && C % V == 0 && !force_scalar)) c.lds = 0;
     if (c.lds != 1 && c.lds != 2) c.lds = 0;
     if (c.lds == 1) tile = kClLdsRows;
@@ -178,9 +179,10 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
     c.ncg = c.lds == 2 ? (C + kClTrChannels - 1) / kClTrChannels : (C + 64 * V - 1) / (64 * V);
     int64_t bcg;
     if (__builtin_mul_overflow(B, c.ncg, &bcg) || __builtin_mul_overflow(bcg, c.ntt, &nwork)) return CCV_E_SHAPE;
-    bool vec = aligned16(a->x) && stride_ok16(B, c.x_sb, es) && stride_ok16(L, c.x_sl, es);
-    if (want_out) vec = vec && aligned16(a->out) && stride_ok16(B, c.o_sb, es) && stride_ok16(L, c.o_sl, es);
-    P.vector = vec && !force_scalar;
+    // Whole channel vectors take 16-byte accesses at any alignment (time rows that
+    // are not 16-byte aligned: C not a multiple of V, or an offset channel view);
+    // a lane's last, partial channel vector moves element by element.
+    P.vector = !force_scalar;
     // Whole tiles take 16-byte loads for the history rows from initial_states, the
     // rows of 4 sequence ids and each lane's weight / bias block when those are
     // aligned (otherwise those tiles take the element path).

@@ -250,17 +250,26 @@ def test_plan_channel_last_lds_forms(monkeypatch):
     assert (p.span, p.channels_per_item) == (64, 256)
     assert p.work_items == 8 * (4096 // 256) * (8192 // 64) == p.grid     # a workgroup per item
     _, p = ccv.ccv_fwd_plan(args(layout="cl", x_stride=(1000 * 67, 1, 67)))
-    assert (p.vector, p.channels_per_item) == (0, 64 * 8)                    # unaligned rows
+    assert (p.vector, p.channels_per_item) == (1, 64 * 8)                    # unaligned rows: registers
     monkeypatch.setenv("CCV_CL_LDS", "7")
     _, p = ccv.ccv_fwd_plan(args(**view))
     assert (p.span, p.channels_per_item) == (p0.span, p0.channels_per_item)
 
 
-def test_plan_falls_back_to_element_access_when_unaligned():
-    # channel offset 3 in a bf16 buffer: base not 16-byte aligned
-    _, p = ccv.ccv_fwd_plan(args(layout="cl", x=X + 6, x_stride=(1000 * 72, 1, 72)))
-    assert p.vector == 0
-    # odd time stride breaks alignment of every row after the first
+def test_plan_channel_last_unaligned_rows_keep_16_byte_accesses(monkeypatch):
+    # channel offset 3 in a bf16 buffer (base not 16-byte aligned) and an odd time
+    # stride (every row after the first unaligned): whole channel vectors still take
+    # 16-byte accesses; the LDS-staged forms need aligned rows and fall back to the
+    # register tiles; CCV_FORCE_SCALAR selects the element path
+    for kw in (dict(x=X + 6, x_stride=(1000 * 72, 1, 72)), dict(x_stride=(1000 * 67, 1, 67))):
+        _, p = ccv.ccv_fwd_plan(args(layout="cl", **kw))
+        assert p.vector == 1 and p.span == 32, kw
+        for lds in ("1", "2"):
+            monkeypatch.setenv("CCV_CL_LDS", lds)
+            _, p = ccv.ccv_fwd_plan(args(layout="cl", **kw))
+            assert p.vector == 1 and p.span == 32 and p.channels_per_item == 64 * 8, (kw, lds)
+        monkeypatch.delenv("CCV_CL_LDS")
+    monkeypatch.setenv("CCV_FORCE_SCALAR", "1")
     _, p = ccv.ccv_fwd_plan(args(layout="cl", x_stride=(1000 * 67, 1, 67)))
     assert p.vector == 0
 

@@ -549,6 +549,31 @@ def test_channel_first_ragged_last_segment(dtype, monkeypatch):
             check_full(w, where=f"[ragged last segment {dtype} {layout} case {i}]")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_channel_last_unaligned_rows(dtype, monkeypatch):
+    """Channel-last time rows that are not 16-byte aligned (C not a multiple of
+    16 / element size, or a view at channel offset 3): whole channel vectors take
+    unaligned 16-byte accesses on the register tiles, a lane's partial vector moves
+    element by element.  Same bits as the element path, every output against the
+    oracle, several whole channel groups plus a partial one."""
+    cases = [(2, 1100, 300, 4, "cl_misaligned", dict(bias=True, init=True, final=True, activation="silu")),
+             (1, 1027, 257, 3, "cl", dict(bias=True, seq=9, activation="silu")),
+             (2, 600, 130, 2, "cl", dict(bias=False, init=True, final=True, seq=4, activation=None))]
+    for i, (B, C, L, K, layout, feats) in enumerate(cases):
+        w = build(L, C, B, K, dtype, layout, feats, seed=5200 + i)
+        kw = gpu_args(w)
+        assert ccv.plan_for(x=kw["x"], weight=kw["weight"])["vector"] == 1
+        a = run_gpu(w)
+        monkeypatch.setenv("CCV_FORCE_SCALAR", "1")
+        b = run_gpu(w)
+        monkeypatch.delenv("CCV_FORCE_SCALAR")
+        log(f"  unaligned channel-last rows {dtype} {layout} B={B} C={C} L={L} K={K} {feats}")
+        assert bits_equal(a[0], b[0]), (i, layout)
+        if w.return_final_states:
+            assert bits_equal(a[1], b[1]), (i, layout)
+        check_full(w, where=f"[unaligned channel-last rows {dtype} case {i}]")
+
+
 @pytest.mark.parametrize("packed", [False, True])
 def test_channel_last_tile_sweep_bit_identical(packed, monkeypatch):
     """Every tile length gives the same bits; with packed sequences (short ones, so
