@@ -185,7 +185,7 @@ int validate(const ccv_fwd_args_t* a, Plan* plan, int cus) {
     P.vector = !force_scalar;
     // Whole tiles take 16-byte loads for the history rows from initial_states, the
     // rows of 4 sequence ids and each lane's weight / bias block when those are
-    // aligned (otherwise those tiles take the element path).
+    // aligned (otherwise those tiles take the general tile code).
     const int64_t* is = a->init_stride;
     c.vec_init = a->initial_states && is[1] == 1 && aligned16(a->initial_states) &&
                  stride_ok16(B, is[0], es) && stride_ok16(K - 1, is[2], es);

@@ -232,8 +232,8 @@ __device__ inline void compute_whole(const CfArgs& a, const SegPos& p, int lane,
   }
 }
 
-// A segment that is not whole (the row's last, ragged one) or not 16-byte
-// aligned: element loads and stores, bounds-checked against L.
+// A segment on the element path (CCV_FORCE_SCALAR): element loads and stores,
+// bounds-checked against L.
 template <class S, int K, bool SILU, bool SEQ>
 __device__ inline void compute_partial(const CfArgs& a, const SegPos& p, int lane) {
   constexpr int V = S::V;

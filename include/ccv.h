@@ -124,7 +124,8 @@ typedef struct ccv_plan {
   int32_t vector;          /* 1: 16-byte loads and stores; 0: element loads and stores.
                               Channel-first rows take 16-byte accesses at any length and
                               element offset (the vector that straddles L moves element by
-                              element); channel-last needs 16-byte aligned rows */
+                              element); channel-last whole channel vectors too (a
+                              lane's partial vector moves element by element) */
   int32_t elems_per_lane;  /* elements one lane holds per 16-byte vector (16 / element size) */
   int32_t unroll;          /* vectors (channel-first) or time rows (channel-last) in flight per
                               lane; channel-last: 8 when whole tiles take the straight-line
@@ -161,7 +162,8 @@ int ccv_fwd(const ccv_fwd_args_t* args, void* hip_stream);
  *   CCV_CL_TILE_T=n        channel-last: time rows per tile (default 32, at least 4).
  *   CCV_CL_LDS=1 | 2       channel-last: tiles staged through LDS (16 rows), or the
  *                          transposing tile of 256 channels (16-byte aligned
- *                          layouts only; others keep the default path).
+ *                          rows only, and C a multiple of 16 / element size for
+ *                          the transposing tile; others keep the default path).
  *   CCV_FORCE_SCALAR=1     element-wise loads and stores (read by ccv_update and
  *                          ccv_bwd too; the backward's dweight and dbias are then
  *                          summed in another fixed order, so they agree to rounding).
@@ -312,9 +314,11 @@ int ccv_bwd_check(const ccv_bwd_args_t* args);
  * 16-byte aligned), 2 for the LDS-staged channel-last path, 3 for the
  * register-only channel-first path (with or without seq_idx: one wave per (b, c,
  * segment of `span` steps), one partial row per (b, segment), elems_per_lane =
- * 16 / element size); the channel-first paths
- * need x, dout and dx unit-stride in time, the channel-last one in channels, all
- * 16-byte aligned, with L resp. C a multiple of 16 / element size.  span = time
+ * 16 / element size); the channel-first paths need x, dout and dx unit-stride in
+ * time, the channel-last one in channels.  The register path takes rows of any
+ * length and offset (unaligned 16-byte accesses, the vector that straddles L
+ * element by element); the LDS-staged paths need 16-byte aligned rows with L
+ * resp. C a multiple of 16 / element size.  span = time
  * steps per tile (per segment on path 3); unroll = consecutive tiles per work
  * item (summed into one partial row: 4 when x is unit-stride in channels, else 1);
  * channels_per_item = channels per work item; work_items, grid, block of the
