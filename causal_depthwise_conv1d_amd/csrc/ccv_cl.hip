@@ -376,6 +376,52 @@ __device__ inline void final_states_group(const ClArgs& a, int64_t b, int64_t cg
   }
 }
 
+// The last channel group when it holds only a few channels (C not a multiple of
+// 64 * V, at most kClNarrowVectors * V channels left): lane r takes time row t0 + r
+// of the tile and walks the group's channels, so a wave moves up to 64 rows per
+// instruction where the general code would keep a lane or two busy.  The
+// arithmetic is the general code's, term for term (bias first, then the taps
+// oldest first, the history from initial_states or zeros, the same masks).
+constexpr int kClNarrowVectors = 4;
+
+template <class S, int K, bool SILU, bool SEQ>
+__device__ inline void tile_narrow(const ClArgs& a, const TilePos& p, int lane) {
+  constexpr int H = K - 1;
+  using raw = typename S::raw;
+  const Common& m = a.m;
+  const int64_t L = m.L;
+  const int64_t c0 = p.cg * (64 * S::V);
+  const int nch = (int)(m.C - c0);
+  const int64_t t0 = p.tt * a.tile;
+  const int64_t t1 = (t0 + a.tile < L) ? t0 + a.tile : L;
+  const raw* __restrict__ xb = static_cast<const raw*>(m.x) + p.b * a.x_sb + c0;
+  raw* __restrict__ ob = static_cast<raw*>(m.out) + p.b * a.o_sb + c0;
+  const raw* __restrict__ ib = static_cast<const raw*>(m.init);
+  const int32_t* __restrict__ sr = SEQ ? m.seq + p.b * L : nullptr;
+  for (int64_t t = t0 + lane; t < t1; t += 64) {
+    const int id = SEQ ? sr[t] : 0;
+    bool keep[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t src = t - H + k;               // left of t = 0: the first sequence's history
+      keep[k] = !SEQ || (src >= 0 ? sr[src] == id : (ib != nullptr && sr[0] == id));
+    }
+    for (int i = 0; i < nch; ++i) {
+      const int64_t c = c0 + i;
+      float acc = m.bias ? load_param(m.bias, m.w_dtype, c) : 0.0f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t src = t - H + k;
+        const float xv = src >= 0 ? S::to_f(xb[src * a.x_sl + i])
+                                  : (ib ? S::to_f(ib[p.b * m.is_b + c * m.is_c + (src + H) * m.is_i]) : 0.0f);
+        const float f = __builtin_fmaf(load_param(m.w, m.w_dtype, c * K + k), xv, acc);
+        acc = SEQ ? (keep[k] ? f : acc) : f;
+      }
+      ob[t * a.o_sl + i] = S::from_f(SILU ? silu(acc) : acc);
+    }
+  }
+}
+
 template <class S, int K, bool SILU, bool SEQ, bool VEC, int WB, bool LDSM>
 __device__ inline void cl_fwd_body(const ClArgs& a, lds_u32x4* rows) {
   constexpr int V = S::V;
@@ -397,6 +443,10 @@ __device__ inline void cl_fwd_body(const ClArgs& a, lds_u32x4* rows) {
                           (t0 >= K - 1 || m.init == nullptr || a.vec_init) && (!SEQ || a.vec_seq);
         if (fast) {
           tile_fast<S, K, SILU, SEQ, WB, LDSM>(a, p, lane, LDSM ? rows + wave * (kClLdsRows * 64 + 16) : rows);
+          continue;
+        }
+        if (m.C - p.cg * (64 * V) <= kClNarrowVectors * V) {
+          tile_narrow<S, K, SILU, SEQ>(a, p, lane);
           continue;
         }
       }

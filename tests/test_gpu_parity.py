@@ -554,11 +554,15 @@ def test_channel_last_unaligned_rows(dtype, monkeypatch):
     """Channel-last time rows that are not 16-byte aligned (C not a multiple of
     16 / element size, or a view at channel offset 3): whole channel vectors take
     unaligned 16-byte accesses on the register tiles, a lane's partial vector moves
-    element by element.  Same bits as the element path, every output against the
-    oracle, several whole channel groups plus a partial one."""
+    element by element, and a last group of a few channels runs with lanes over time
+    rows.  Same bits as the element path, every output against the oracle, several
+    whole channel groups plus a partial one."""
     cases = [(2, 1100, 300, 4, "cl_misaligned", dict(bias=True, init=True, final=True, activation="silu")),
              (1, 1027, 257, 3, "cl", dict(bias=True, seq=9, activation="silu")),
-             (2, 600, 130, 2, "cl", dict(bias=False, init=True, final=True, seq=4, activation=None))]
+             (2, 600, 130, 2, "cl", dict(bias=False, init=True, final=True, seq=4, activation=None)),
+             # a last channel group of 6 channels: lanes walk time rows there
+             (2, 1030, 200, 4, "cl", dict(bias=True, init=True, final=True, seq=5, activation="silu")),
+             (1, 1030, 70, 3, "cl_misaligned", dict(bias=True, init=True, activation=None))]
     for i, (B, C, L, K, layout, feats) in enumerate(cases):
         w = build(L, C, B, K, dtype, layout, feats, seed=5200 + i)
         kw = gpu_args(w)
