@@ -246,7 +246,23 @@ struct Staged {
 // consecutive lanes read one step's 64 channels.  `ln` is the lane index made
 // opaque to the compiler per tile, so that it recomputes the row offsets rather
 // than keeping one per load in registers for the whole kernel.
-template <class S, bool CL, bool SEQ>
+// The V channels ck .. ck+V-1 of one channel-last step row (element ck at `p`),
+// zeros from channel C on, by element loads (the vector that straddles C when C
+// is not a multiple of V).
+template <class raw, int V>
+__device__ inline u32x4 load_channels_upto(const raw* p, int64_t ck, int64_t C) {
+  raw part[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) part[i] = ck + i < C ? p[i] : raw(0);
+  u32x4 v;
+  __builtin_memcpy(&v, part, 16);
+  return v;
+}
+
+// ODD (channel-last only): step rows that are not 16-byte aligned (C not a
+// multiple of V, or an offset channel view): unaligned 16-byte loads, and the
+// vector that straddles C element by element.
+template <class S, bool CL, bool SEQ, bool ODD>
 __device__ inline void stage_issue(const BwdArgs& a, const typename S::raw* xb, const typename S::raw* gb,
                                    const int32_t* sr, int64_t c0, int64_t t0, int ln, Staged<S>& st) {
   constexpr int V = S::V, NX = Staged<S>::NX, NG = Staged<S>::NG, NS = 64 / V;
@@ -292,15 +308,30 @@ __device__ inline void stage_issue(const BwdArgs& a, const typename S::raw* xb, 
   } else {
     const int64_t ck = c0 + (ln % NS) * V;         // the lane's first channel
     const int s0 = ln / NS;                        // and first step
+    const bool whole = ODD ? ck + V <= C : ck < C;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int64_t p = t0 - V + s0 + i * V;
-      st.x[i] = gload<u32x4>(pick(ck < C && p >= 0 && p < L, reinterpret_cast<uintptr_t>(xb + p * a.x_sl + ck), zero));
+      st.x[i] = gload<u32x4>(pick(whole && p >= 0 && p < L, reinterpret_cast<uintptr_t>(xb + p * a.x_sl + ck), zero));
     }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int64_t p = t0 + s0 + i * V;
-      st.g[i] = gload<u32x4>(pick(ck < C && p < L, reinterpret_cast<uintptr_t>(gb + p * a.d_sl + ck), zero));
+      st.g[i] = gload<u32x4>(pick(whole && p < L, reinterpret_cast<uintptr_t>(gb + p * a.d_sl + ck), zero));
+    }
+    if constexpr (ODD) {
+      if (ck < C && ck + V > C) {                  // the vector that straddles C
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+          const int64_t p = t0 - V + s0 + i * V;
+          if (p >= 0 && p < L) st.x[i] = load_channels_upto<typename S::raw, V>(xb + p * a.x_sl + ck, ck, C);
+        }
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+          const int64_t p = t0 + s0 + i * V;
+          if (p < L) st.g[i] = load_channels_upto<typename S::raw, V>(gb + p * a.d_sl + ck, ck, C);
+        }
+      }
     }
   }
 }
@@ -342,7 +373,7 @@ __device__ inline void stage_put(typename S::raw* lx, typename S::raw* lg, int32
 // 16-byte stores.  Channel-first tiles are channel-major with an odd dword pitch
 // (the walk's reads, one channel per lane, fall in distinct banks); channel-last
 // tiles step-major.
-template <class S, int K, bool SILU, bool SEQ, bool CL>
+template <class S, int K, bool SILU, bool SEQ, bool CL, bool ODD>
 __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
   using raw = typename S::raw;
   using G = LdsGeom<S>;
@@ -410,18 +441,30 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
       } else {
         const int64_t ck = c0 + (ln % NS) * V;
         const int s = ln / NS + i * V;
-        if (ck < C && s < dx_n) store16_stream(db + (dx_t0 + s) * a.g_sl + ck, dxv[i]);
+        if constexpr (ODD) {
+          if (s < dx_n && ck + V <= C) {
+            store16_stream(db + (dx_t0 + s) * a.g_sl + ck, dxv[i]);
+          } else if (s < dx_n && ck < C) {          // the vector that straddles C
+            raw part[V];
+            __builtin_memcpy(part, &dxv[i], 16);
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+              if (ck + e < C) db[(dx_t0 + s) * a.g_sl + ck + e] = part[e];
+          }
+        } else {
+          if (ck < C && s < dx_n) store16_stream(db + (dx_t0 + s) * a.g_sl + ck, dxv[i]);
+        }
       }
     }
   };
 
   const int32_t* sr = SEQ ? a.seq + b * L : nullptr;
-  if constexpr (PREFETCH) stage_issue<S, CL, SEQ>(a, xb, gb, sr, c0, tt0 * a.T, lane, st);
+  if constexpr (PREFETCH) stage_issue<S, CL, SEQ, ODD>(a, xb, gb, sr, c0, tt0 * a.T, lane, st);
   for (int64_t tt = tt0; tt < tt1; ++tt) {
     const int64_t t0 = tt * a.T;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    if constexpr (!PREFETCH) stage_issue<S, CL, SEQ>(a, xb, gb, sr, c0, t0, ln, st);
+    if constexpr (!PREFETCH) stage_issue<S, CL, SEQ, ODD>(a, xb, gb, sr, c0, t0, ln, st);
     __syncthreads();                               // the previous tile's dx has left LDS
     stage_put<S, CL, SEQ>(lx, lg, lids, ln, st);
     if (t0 == 0 && a.init && c < C) {              // the history left of t = 0
@@ -432,7 +475,7 @@ __global__ void __launch_bounds__(64) bwd_lds_kernel(const BwdArgs a) {
     }
     if (dx_t0 >= 0) store_dx(ln);
     if constexpr (PREFETCH)
-      if (tt + 1 < tt1) stage_issue<S, CL, SEQ>(a, xb, gb, sr, c0, t0 + a.T, ln, st);
+      if (tt + 1 < tt1) stage_issue<S, CL, SEQ, ODD>(a, xb, gb, sr, c0, t0 + a.T, ln, st);
     __syncthreads();
 
     // With seq_idx, a tile right of the history whose rows t0-H .. t0+T+H-1 (those
@@ -1170,9 +1213,11 @@ int launch_one(const BwdArgs& a, int path, uint32_t grid, void* st) {
     fn = reinterpret_cast<const void*>(&bwd_cf_reg_kernel<S, K, SILU, SEQ, true>);
     block = kBwdBlock;
   } else if (path == kBwdPathLdsCf)
-    fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, false>);
+    fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, false, false>);
   else if (path == kBwdPathLdsCl)
-    fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, true>);
+    fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, true, false>);
+  else if (path == kBwdPathLdsClOdd)
+    fn = reinterpret_cast<const void*>(&bwd_lds_kernel<S, K, SILU, SEQ, true, true>);
   else {
     fn = reinterpret_cast<const void*>(&bwd_kernel<S, K, SILU, SEQ>);
     block = kBwdBlock;

@@ -40,17 +40,20 @@ int choose_path(const ccv_bwd_args_t* a) {
   // Channel-first rows of any length and offset take the register path (16-byte
   // accesses at any element alignment; the vector that straddles L moves element
   // by element).  The LDS-staged kernels need 16-byte aligned rows.
-  bool cf = true, cf16 = aligned && L % V == 0, cl = aligned && C % V == 0;
+  // Channel-last step rows that are not 16-byte aligned (C not a multiple of V, or
+  // an offset channel view) take the LDS-staged channel-last kernel's own variant.
+  bool cf = true, cf16 = aligned && L % V == 0, cl = true, cl16 = aligned && C % V == 0;
   for (const int64_t* s : st) {
     cf = cf && s[2] == 1;
     cf16 = cf16 && s[2] == 1 && stride_ok16(B, s[0], es) && stride_ok16(C, s[1], es);
-    cl = cl && s[1] == 1 && stride_ok16(B, s[0], es) && stride_ok16(L, s[2], es);
+    cl = cl && s[1] == 1;
+    cl16 = cl16 && s[1] == 1 && stride_ok16(B, s[0], es) && stride_ok16(L, s[2], es);
   }
   // The register path reads a lane's ids as 16-byte vectors beside its x; ids that
   // are not 16-byte aligned go through the LDS-staged kernel.
   if (cf && a->seq_idx && !aligned16(a->seq_idx)) return cf16 ? kBwdPathLdsCf : kBwdPathElement;
   if (cf) return cf16 ? kBwdPathRegCf : kBwdPathRegCfOdd;
-  if (cl) return kBwdPathLdsCl;
+  if (cl) return cl16 ? kBwdPathLdsCl : kBwdPathLdsClOdd;
   return kBwdPathElement;
 }
 
@@ -221,10 +224,10 @@ int ccv_bwd_plan(const ccv_bwd_args_t* args, ccv_plan_t* plan) {
   const int st = validate(args, &p, false);      // a plan is wanted before the workspace exists
   if (st != CCV_OK || !plan) return st;
   *plan = ccv_plan_t{};
-  const bool lds = p.path == kBwdPathLdsCf || p.path == kBwdPathLdsCl;
+  const bool lds = p.path == kBwdPathLdsCf || p.path == kBwdPathLdsCl || p.path == kBwdPathLdsClOdd;
   plan->path = p.grid || p.rgrid ? CCV_PATH_BACKWARD : CCV_PATH_NONE;
   const bool reg = p.path == kBwdPathRegCf || p.path == kBwdPathRegCfOdd;
-  plan->vector = reg ? kBwdPathRegCf : p.path;
+  plan->vector = reg ? kBwdPathRegCf : p.path == kBwdPathLdsClOdd ? kBwdPathLdsCl : p.path;
   plan->elems_per_lane = reg ? 16 / elt_size(args->x_dtype) : 1;
   plan->unroll = (int32_t)p.a.tpi;
   plan->grid = p.grid;

@@ -68,10 +68,12 @@ constexpr int kBwdFinalWaves = 16;  // waves of the final reduction kernel's wor
 // which need x, dout and dx unit-stride in the same dimension (time for CF,
 // channels for CL), 16-byte aligned bases and strides, and L (CF) or C (CL) a
 // multiple of 16 / element size.
-// kBwdPathRegCfOdd is the register path on rows that are not 16-byte aligned (its
-// own kernel instantiation, so that the aligned kernel's code is unchanged); the
-// plan reports it as kBwdPathRegCf.
-enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2, kBwdPathRegCf = 3, kBwdPathRegCfOdd = 4 };
+// kBwdPathRegCfOdd and kBwdPathLdsClOdd are the register channel-first and the
+// LDS-staged channel-last paths on rows that are not 16-byte aligned (kernel
+// instantiations of their own, so that the aligned kernels' code is unchanged);
+// the plan reports them as kBwdPathRegCf and kBwdPathLdsCl.
+enum { kBwdPathElement = 0, kBwdPathLdsCf = 1, kBwdPathLdsCl = 2, kBwdPathRegCf = 3, kBwdPathRegCfOdd = 4,
+       kBwdPathLdsClOdd = 5 };
 
 // The register-only channel-first path (x, dout and dx unit-stride in time, any
 // alignment; with seq_idx, a 16-byte aligned seq_idx): work items are

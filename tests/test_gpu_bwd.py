@@ -228,6 +228,42 @@ def test_bwd_fast_paths_equal_element_path(dtype, layout, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_channel_last_unaligned_rows(dtype, monkeypatch):
+    """Channel-last step rows that are not 16-byte aligned (C not a multiple of 16 /
+    element size, or a view at an odd channel offset) run the LDS-staged channel-last
+    kernel's own variant: unaligned 16-byte loads and stores, the channel vector
+    that straddles C element by element.  Every gradient has the element path's
+    bits (the two share the walk and the tile grouping) and meets the oracle."""
+    T = tile_steps(dtype)
+    for i, (B, C, L, layout, f) in enumerate([(2, 139, 4 * T + 9, "cl", dict(init=True, dfs=True)),
+                                              (1, 70, 3 * T + 1, "cl", dict(seq=5)),
+                                              (2, 75, 2 * T + 5, "cl_odd", dict(seq=3, init=True, dfs=True))]):
+        K = 4
+        kw = dict(layout="cl", c_pad=5, c_off=3) if layout == "cl_odd" else dict(layout="cl")
+        lengths = wl.packed_lengths(L, f["seq"], 1, 5400 + i).tolist() if f.get("seq") else None
+        w = wl.make_case(B=B, C=C, L=L, K=K, x_dtype=dtype, bias=True, init=f.get("init", False),
+                         seq_lengths=lengths, activation="silu", seed=5400 + i, **kw)
+        dout, dfs = grad_inputs(w, "cl", f.get("dfs", False), 5400 + i)
+        res = []
+        for force, want in (("0", 2), ("1", 0)):
+            monkeypatch.setenv("CCV_FORCE_SCALAR", force)
+            x = to_gpu_view(w.x_storage, w.x)
+            args = ccv.make_bwd_args(x, w.weight.cuda(), w.bias.cuda(), dout.cuda(), ccv.empty_like_layout(x),
+                                     torch.empty(C, K, dtype=w.weight.dtype, device="cuda"),
+                                     seq_idx=None if w.seq_idx is None else w.seq_idx.cuda())
+            st, plan = ccv.ccv_bwd_plan(args)
+            assert st == 0 and plan.vector == want, (force, plan.as_dict())
+            res.append(run_bwd(w, dout, dfs, bool(f.get("init"))))
+        monkeypatch.setenv("CCV_FORCE_SCALAR", "0")
+        log(f"  bwd channel-last unaligned rows {dtype} {layout} B={B} C={C} L={L} {f}")
+        bits = torch.int32 if dtype == "f32" else torch.int16
+        for name, t0, t1 in zip(("dx", "dweight", "dbias", "dinit"), *res):
+            if t0 is not None:
+                assert torch.equal(t0.view(bits), t1.view(bits)), (i, name)
+        check_bwd(w, dout, dfs, bool(f.get("init")), f"[channel-last unaligned rows {dtype} case {i}]")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_bwd_unaligned_seq_idx_takes_the_lds_path(dtype):
     """Channel-first with a seq_idx that is not 16-byte aligned (a view one element
     into its buffer) runs the LDS-staged kernel; its dx and d(initial_states) have the
