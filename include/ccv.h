@@ -315,10 +315,11 @@ int ccv_bwd_check(const ccv_bwd_args_t* args);
  * register-only channel-first path (with or without seq_idx: one wave per (b, c,
  * segment of `span` steps), one partial row per (b, segment), elems_per_lane =
  * 16 / element size); the channel-first paths need x, dout and dx unit-stride in
- * time, the channel-last one in channels.  The register path takes rows of any
- * length and offset (unaligned 16-byte accesses, the vector that straddles L
- * element by element); the LDS-staged paths need 16-byte aligned rows with L
- * resp. C a multiple of 16 / element size.  span = time
+ * time, the channel-last one in channels.  The register path and the channel-last
+ * path take rows of any length and offset (unaligned 16-byte accesses, the vector
+ * that straddles L resp. C element by element); the LDS-staged channel-first path
+ * (seq_idx not 16-byte aligned) needs 16-byte aligned rows with L a multiple of
+ * 16 / element size.  span = time
  * steps per tile (per segment on path 3); unroll = consecutive tiles per work
  * item (summed into one partial row: 4 when x is unit-stride in channels, else 1);
  * channels_per_item = channels per work item; work_items, grid, block of the
